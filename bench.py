@@ -1,0 +1,347 @@
+#!/usr/bin/env python
+"""Benchmark of the hybrid-head mixer hot path on one MI355X.
+
+A step is one pass of the path over one batch of synthetic input, through the
+C ABI: shared input projection -> sliding-window/meta attention -> W_O ->
+selective scan -> fused gate/RMSNorm/beta/sum epilogue -> output projection,
+for the 1.5B-shaped SWA layer at 8K (16 x 8192 real tokens + 128 meta tokens,
+K/V handed from the preceding layer).  `value` is that layer's prefill
+tokens/s.  The same run times, as further workloads, the B=128 decode step of a
+KV-sharing producer/consumer pair (ring cache 1024, meta prefix 128) and the
+global-attention and 300M-ablation layers, plus per-stage HIP-event timings
+recorded by the library on the launch stream, roofline fractions per stage and
+the fp64 CPU oracle on a bounded sample (the CPU baseline).
+
+Inputs are resident in HBM before the timed region; the meta prefix is
+prepared before it (it is input independent and computed once per layer).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "hybrid-head mixer tokens/s (8K prefill, B=128 decode) + % HBM/MFMA peak"
+PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
+PEAK_BF16 = 2.5e15         # dense bf16 MFMA FLOP/s
+PEAK_F32_VEC = 157.3e12    # fp32 vector FLOP/s (packed); non-packed lane-op rate is half
+N_CU, CLK = 256, 2.4e9
+PEAK_VALU_LANE_OPS = N_CU * 64 * CLK        # non-packed fp32 lane-ops/s (39.3 T)
+
+STAGES = ["in_proj", "kv_write", "attention", "w_o", "ssm", "epilogue", "out_proj"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# --- algorithmic work per launch ----------------------------------------------------
+
+def visible_keys(s, T):
+    """Sum over real queries of visible keys (meta + window, or all earlier)."""
+    M, W = s.n_meta, s.window
+    if W <= 0:
+        return T * M + T * (T + 1) // 2
+    full = max(0, T - W)
+    ramp = min(T, W)
+    return T * M + ramp * (ramp + 1) // 2 + full * W
+
+
+def prefill_work(s, B, T):
+    es = 2 if s.dtype == "bf16" else 4
+    R = B * T
+    hq, E, N, d = s.n_heads * s.head_dim, s.d_inner, s.d_state, s.d_model
+    w = {
+        "in_proj": ("mfma", 2.0 * R * d * s.n_in),
+        "attention": ("mfma", 4.0 * s.head_dim * s.n_heads * B * visible_keys(s, T)),
+        "w_o": ("mfma", 2.0 * R * hq * E),
+        "out_proj": ("mfma", 2.0 * R * E * d),
+        # u, dt read; y written; B, C read; final state written
+        "ssm": ("hbm", float(R * E * es * 3 + R * 2 * N * es + B * E * N * 4)),
+        # Ao, y, z read; F written
+        "epilogue": ("hbm", float(R * E * es * 4)),
+    }
+    if s.own_kv:
+        w["kv_write"] = ("hbm", float(R * s.n_kv_heads * s.head_dim * es * 2 * 2))
+    return w
+
+
+def decode_work(s, B, pos, cache_len):
+    es = 2 if s.dtype == "bf16" else 4
+    E, N, d = s.d_inner, s.d_state, s.d_model
+    W = s.window if s.window > 0 else cache_len
+    keys = min(pos + 1, W)
+    kvb = s.n_kv_heads * s.head_dim * es
+    w = {
+        "in_proj": ("hbm", float(s.n_in * d * es + B * d * es + B * s.n_in * es)),
+        "attention": ("hbm", float(B * keys * kvb * 2 + s.n_meta * kvb * 2 + B * s.n_heads * s.head_dim * es * 2)),
+        "w_o": ("hbm", float(E * s.n_heads * s.head_dim * es)),
+        "ssm": ("hbm", float(B * E * N * 4 * 2 + B * E * es * 3 + B * 2 * N * es)),
+        "epilogue": ("hbm", float(B * E * es * 4)),
+        "out_proj": ("hbm", float(d * E * es)),
+    }
+    if s.own_kv:
+        w["kv_write"] = ("hbm", float(B * kvb * 2 * 2))
+    return w
+
+
+def roofline_entry(stage, kind, amount, ms):
+    if ms <= 0:
+        return None
+    if kind == "mfma":
+        ach = amount / (ms * 1e-3)
+        return {"kernel": stage, "bound": "mfma", "achieved": ach / 1e12, "peak": PEAK_BF16 / 1e12,
+                "unit": "TFLOP/s", "frac": ach / PEAK_BF16, "ms": ms}
+    ach = amount / (ms * 1e-3)
+    return {"kernel": stage, "bound": "hbm", "achieved": ach / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+            "frac": ach / PEAK_HBM, "ms": ms}
+
+
+def scan_alu_entry(s, B, T, ms):
+    """The scan also against the VALU ceiling: per (t, c, n) one exp, two multiplies and two FMAs
+    (5 lane-ops), non-packed fp32 issue rate 256 CU x 64 lanes x 2.4 GHz."""
+    ops = 5.0 * B * T * s.d_inner * s.d_state
+    ach = ops / (ms * 1e-3)
+    return {"kernel": "ssm", "bound": "alu", "achieved": ach / 1e12, "peak": PEAK_VALU_LANE_OPS / 1e12,
+            "unit": "Tlane-op/s", "frac": ach / PEAK_VALU_LANE_OPS, "ms": ms}
+
+
+# --- traffic measured by rocprofv3 counters (optional, committed under profiles/) ---------
+
+KERNEL_SOURCES = {"attention": "attn_prefill.hip", "ssm": "scan.hip", "epilogue": "epilogue.hip"}
+
+
+def measured_traffic(stage):
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    src = KERNEL_SOURCES.get(stage)
+    if not src or not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(stage)
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    sha = hashlib.sha256(open(os.path.join(ROOT, "hybrid_attention_ssm_swa_amd", "csrc", src), "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None      # the kernel changed since the counters were taken
+    return rec.get("bytes_per_launch")
+
+
+# --- GPU timing ------------------------------------------------------------------------
+
+def timed(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        fn(i)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def stage_profile(layers, fn, steps):
+    """Mean per-stage ms over `steps` calls, from the library's HIP events."""
+    import torch
+    from hybrid_attention_ssm_swa_amd import _lib as L
+    for lay in layers:
+        L.hymba_layer_profile(lay.handle, True)
+    sums = [[0.0] * len(STAGES) for _ in layers]
+    for i in range(steps):
+        fn(i)
+        torch.cuda.synchronize()
+        for j, lay in enumerate(layers):
+            ms = L.hymba_layer_profile_read(lay.handle)
+            for k in range(len(STAGES)):
+                sums[j][k] += ms[k]
+    for lay in layers:
+        L.hymba_layer_profile(lay.handle, False)
+    return [[x / steps for x in row] for row in sums]
+
+
+def bench_prefill(cfg_id, steps, warmup):
+    import torch
+    from hybrid_attention_ssm_swa_amd.layer import MixerLayer, make_kv, upload
+    from hymba_synth import config_by_id
+    from hymba_synth.generate import make_config_case
+    cfg = config_by_id(cfg_id)
+    s = cfg.shape
+    t = time.time()
+    case = make_config_case(cfg_id)
+    log(f"[bench] config {cfg_id} ({cfg.name}) inputs generated in {time.time() - t:.1f}s")
+    dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+    layer = MixerLayer(s, case.params)
+    x = upload(case.x, dt, "cuda")
+    keep = []
+    kv = None
+    if not s.own_kv:
+        keep = [upload(a, layer.act_dtype, "cuda") for a in (case.k_meta, case.v_meta, case.k, case.v)]
+        kv = make_kv(*keep)
+    del case
+    y = torch.empty_like(x)
+    layer.prepare(kv)
+    torch.cuda.synchronize()
+    ms = timed(lambda i: layer.prefill(x, kv, None, y), steps, warmup)
+    stage_ms = stage_profile([layer], lambda i: layer.prefill(x, kv, None, y), steps)[0]
+    B, T = cfg.batch, cfg.seq
+    work = prefill_work(s, B, T)
+    ents = []
+    for k, name in enumerate(STAGES):
+        if name in work and stage_ms[k] > 0:
+            e = roofline_entry(name, work[name][0], work[name][1], stage_ms[k])
+            e["traffic"] = measured_traffic(name)
+            ents.append(e)
+    ents.append(scan_alu_entry(s, B, T, stage_ms[STAGES.index("ssm")]))
+    out = {"tokens_per_s": B * T / (ms * 1e-3), "ms_per_step": ms, "batch": B, "seq": T,
+           "stage_ms": dict(zip(STAGES, stage_ms)), "kernels": ents}
+    layer.close()
+    del x, y, keep
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_decode(cfg_id, steps, warmup):
+    import torch
+    from hybrid_attention_ssm_swa_amd.layer import MixerLayer, make_kv, upload
+    from hymba_synth import config_by_id
+    from hymba_synth.generate import make_config_case
+    cfg = config_by_id(cfg_id)
+    s, sc = cfg.shape, cfg.consumer_shape
+    case = make_config_case(cfg_id)
+    dt = torch.bfloat16
+    prod = MixerLayer(s, case.producer)
+    cons = MixerLayer(sc, case.consumer)
+    cons.bind(prod)
+    # two sets of cache + states, alternated, so the 256 MB last-level cache cannot hold a step's data
+    sets = []
+    for _ in range(2):
+        kc, vc = upload(case.k_cache, prod.act_dtype, "cuda"), upload(case.v_cache, prod.act_dtype, "cuda")
+        sets.append((kc, vc, make_kv(k_cache=kc, v_cache=vc), torch.from_numpy(case.state_p).cuda(),
+                     torch.from_numpy(case.state_c).cuda()))
+    x = upload(case.x, dt, "cuda")
+    xc = upload(case.x_c, dt, "cuda")
+    pos = torch.from_numpy(case.pos).cuda()
+    yp, yc = torch.empty_like(x), torch.empty_like(xc)
+    prod.prepare()
+    cons.prepare()
+    torch.cuda.synchronize()
+
+    def step(i):
+        _, _, kv, stp, stc = sets[i % 2]
+        prod.decode(x, pos, kv, stp, yp)
+        cons.decode(xc, pos, kv, stc, yc)
+
+    ms = timed(step, steps, warmup)
+    pst, cst = stage_profile([prod, cons], step, steps)
+    B, p, C = cfg.batch, cfg.seq, s.window
+    ents = {}
+    for role, lay_s, st in (("producer", s, pst), ("consumer", sc, cst)):
+        work = decode_work(lay_s, B, p, C)
+        ents[role] = [dict(roofline_entry(n, work[n][0], work[n][1], st[k]), traffic=None)
+                      for k, n in enumerate(STAGES) if n in work and st[k] > 0]
+    out = {"tokens_per_s_per_layer": B / (ms * 1e-3 / 2), "ms_per_pair_step": ms, "batch": B, "pos": p,
+           "producer_stage_ms": dict(zip(STAGES, pst)), "consumer_stage_ms": dict(zip(STAGES, cst)),
+           "kernels": ents}
+    prod.close()
+    cons.close()
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
+# --- CPU baseline: the fp64 oracle on a bounded sample ---------------------------------------
+
+def cpu_baseline(budget_s=12.0, max_seqs=3):
+    from hymba_synth.generate import make_config_case
+    from oracle import hymba_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    case = make_config_case(2)
+    done, t0 = 0, time.time()
+    while done < max_seqs and (time.time() - t0) < budget_s:
+        orc.layer_forward(case.params, case.x[done], case.k_meta, case.v_meta, case.k[done], case.v[done])
+        done += 1
+    el = time.time() - t0
+    return {"value": done * case.seq / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {case.batch} sequences (x{case.seq} tokens) of the 8K SWA KV-consumer workload, "
+                      f"fp64 NumPy, {el:.1f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--main-only", action="store_true", help="time only the 8K prefill workload")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from hybrid_attention_ssm_swa_amd import load_library
+    load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    main_run = bench_prefill(2, args.steps, args.warmup)
+    log(f"[bench] 8K SWA prefill: {main_run['tokens_per_s']:.0f} tok/s, {main_run['ms_per_step']:.3f} ms/step")
+    workloads = {}
+    if not args.main_only:
+        workloads["decode_b128_pair"] = bench_decode(4, args.steps, args.warmup)
+        log(f"[bench] decode: {workloads['decode_b128_pair']['tokens_per_s_per_layer']:.0f} tok/s/layer")
+        workloads["global_8k_prefill"] = bench_prefill(3, max(3, args.steps // 2), args.warmup)
+        log(f"[bench] 8K global prefill: {workloads['global_8k_prefill']['tokens_per_s']:.0f} tok/s")
+        workloads["ablation300m_prefill"] = bench_prefill(1, args.steps, args.warmup)
+        log(f"[bench] 300M SWA prefill: {workloads['ablation300m_prefill']['tokens_per_s']:.0f} tok/s")
+
+    kernels = [k for k in main_run["kernels"] if k["bound"] != "alu"]
+    dominant = max(kernels, key=lambda k: k["ms"])
+    roof = {k: dominant[k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac")}
+    roof["traffic"] = dominant.get("traffic")
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+    line = {
+        "metric": METRIC,
+        "value": main_run["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_run["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "1.5B-shaped SWA mixer layer, 8K prefill, K/V handed from the previous layer: "
+                               "B=16 x T=8192 (+128 meta), d=1600, 25 heads x 64 (5 KV heads), window 1024, "
+                               "SSM d_inner 3200, state 16",
+                   "global_batch": 16, "seq_len": 8192, "parallelism": "single-gpu"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "stage_ms": main_run["stage_ms"],
+        "kernels": main_run["kernels"],
+        "workloads": workloads,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,17 @@
+"""MI355X (gfx950) implementation of the Hymba hybrid-head mixer.
+
+The computation lives in libhymba_mixer.so (HIP kernels + hipBLASLt GEMMs
+behind a C ABI, include/hymba_mixer.h).  This package is its Python binding:
+``_lib`` mirrors the C functions by name; ``layer.MixerLayer`` manages device
+memory (torch) around one layer.  Importing works without the library; the
+first call loads it and raises if it has not been built.
+"""
+from ._lib import (  # noqa: F401
+    HYMBA_BF16, HYMBA_F16, HYMBA_F32, HymbaError, LIB_PATH, EXPORTED, load_library,
+    hymba_layer_cfg, hymba_layer_weights, hymba_kv,
+    hymba_layer_persistent_bytes, hymba_layer_create, hymba_layer_destroy, hymba_kv_share_bind,
+    hymba_mixer_workspace_bytes, hymba_layer_prepare, hymba_mixer_prefill, hymba_mixer_decode,
+    hymba_layer_meta_outputs, hymba_last_error, hymba_status_string,
+    hymba_kernel_attention, hymba_kernel_selective_scan, hymba_kernel_epilogue,
+    hymba_layer_profile, hymba_layer_profile_read, hymba_stage_name, HYMBA_N_STAGES,
+)

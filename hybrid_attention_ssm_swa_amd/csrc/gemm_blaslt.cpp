@@ -1,0 +1,102 @@
+// hipBLASLt plans for the three projections of the mixer (shared input
+// projection, attention W_O, output projection).  Row-major Y = X W^T is the
+// column-major product Y^T = W^T-op(A = W) x X: A = W with op T (K-contiguous),
+// B = X with op N, both K-contiguous ("TN"), the layout MFMA GEMMs prefer.
+// Plans (descriptors + heuristic algorithm) are cached per device and shape.
+#include "gemm_blaslt.h"
+
+#include <hipblaslt/hipblaslt.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
+
+namespace hymba {
+
+namespace {
+
+struct Plan {
+  hipblasLtMatmulDesc_t desc = nullptr;
+  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
+  hipblasLtMatmulAlgo_t algo;
+  size_t ws_needed = 0;
+};
+
+using Key = std::tuple<int, int, int, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, size_t>;
+
+hipDataType dt_of(GemmType t) { return t == GT_F16 ? HIP_R_16F : t == GT_BF16 ? HIP_R_16BF : HIP_R_32F; }
+
+struct State {
+  std::mutex mu;
+  std::map<int, hipblasLtHandle_t> handles;
+  std::map<Key, Plan> plans;
+};
+
+State& state() {
+  static State* s = new State();   // lives until process exit (handles are per device)
+  return *s;
+}
+
+}  // namespace
+
+int gemm_16(GemmType in_type, GemmType out_type, const void* X, int64_t ldx, const void* W, int64_t ldw,
+            void* Y, int64_t ldy, int64_t rows, int64_t out, int64_t in, void* ws, size_t ws_bytes,
+            hipStream_t s, const char** err) {
+  if (rows <= 0 || out <= 0) return 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) { *err = "hipGetDevice failed"; return -5; }
+  State& st = state();
+  Plan plan;
+  hipblasLtHandle_t handle;
+  {
+    std::lock_guard<std::mutex> lock(st.mu);
+    auto hit = st.handles.find(dev);
+    if (hit == st.handles.end()) {
+      hipblasLtHandle_t h;
+      if (hipblasLtCreate(&h) != HIPBLAS_STATUS_SUCCESS) { *err = "hipblasLtCreate failed"; return -5; }
+      hit = st.handles.emplace(dev, h).first;
+    }
+    handle = hit->second;
+    const Key key{dev, static_cast<int>(in_type), static_cast<int>(out_type), rows, out, in, ldx, ldw, ldy, ws_bytes};
+    auto it = st.plans.find(key);
+    if (it == st.plans.end()) {
+      Plan p;
+      hipblasOperation_t opA = HIPBLAS_OP_T, opB = HIPBLAS_OP_N;
+      bool ok = hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS;
+      ok = ok && hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opA, sizeof(opA)) == HIPBLAS_STATUS_SUCCESS;
+      ok = ok && hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opB, sizeof(opB)) == HIPBLAS_STATUS_SUCCESS;
+      // A: W stored [out, in] row-major = column-major (in x out), ld = ldw
+      ok = ok && hipblasLtMatrixLayoutCreate(&p.la, dt_of(in_type), in, out, ldw) == HIPBLAS_STATUS_SUCCESS;
+      // B: X stored [rows, in] row-major = column-major (in x rows), ld = ldx
+      ok = ok && hipblasLtMatrixLayoutCreate(&p.lb, dt_of(in_type), in, rows, ldx) == HIPBLAS_STATUS_SUCCESS;
+      // C/D: Y stored [rows, out] row-major = column-major (out x rows), ld = ldy
+      ok = ok && hipblasLtMatrixLayoutCreate(&p.lc, dt_of(out_type), out, rows, ldy) == HIPBLAS_STATUS_SUCCESS;
+      if (!ok) { *err = "hipBLASLt descriptor creation failed"; return -5; }
+      hipblasLtMatmulPreference_t pref;
+      uint64_t wsb = ws_bytes;
+      hipblasLtMatmulPreferenceCreate(&pref);
+      hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof(wsb));
+      hipblasLtMatmulHeuristicResult_t res[8];
+      int n = 0;
+      const hipblasStatus_t hs = hipblasLtMatmulAlgoGetHeuristic(handle, p.desc, p.la, p.lb, p.lc, p.lc,
+                                                                 pref, 8, res, &n);
+      hipblasLtMatmulPreferenceDestroy(pref);
+      if (hs != HIPBLAS_STATUS_SUCCESS || n == 0) {
+        *err = "hipBLASLt found no algorithm for this GEMM shape";
+        return -2;
+      }
+      p.algo = res[0].algo;
+      p.ws_needed = res[0].workspaceSize;
+      it = st.plans.emplace(key, p).first;
+    }
+    plan = it->second;
+  }
+  const float alpha = 1.f, beta = 0.f;
+  const hipblasStatus_t rs = hipblasLtMatmul(handle, plan.desc, &alpha, W, plan.la, X, plan.lb, &beta, Y,
+                                             plan.lc, Y, plan.lc, &plan.algo, ws, ws_bytes, s);
+  if (rs != HIPBLAS_STATUS_SUCCESS) { *err = "hipblasLtMatmul failed"; return -5; }
+  return 0;
+}
+
+}  // namespace hymba

@@ -1,0 +1,764 @@
+// C ABI of the hybrid-head mixer: validation, persistent/workspace carving,
+// the meta-prefix preparation and the launch sequence of prefill and decode.
+// Every step of the layer runs in this library's HIP kernels (attention,
+// scan, epilogue, K/V movement, conversions) or its hipBLASLt projection GEMMs.
+//
+// Types: an fp32 layer stores and computes in fp32.  A bf16 layer keeps bf16
+// at its boundary (x, y, weights) and uses fp16 activations inside (shared
+// projection, attention operands and output, W_O output, scan output, fused
+// epilogue output, the K/V it exchanges and caches) with fp32 accumulation
+// and fp32 SSM state; its weights get fp16 copies in the persistent buffer.
+#include "hymba_mixer.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+#include <string>
+
+#include "gemm_blaslt.h"
+#include "kernels.h"
+
+using namespace hymba;
+
+struct hymba_layer {
+  hymba_layer_cfg cfg;
+  hymba_layer_weights w;
+  // persistent buffer carve
+  char* k_meta = nullptr;      // [M, Hkv, hd] activation type
+  char* v_meta = nullptr;
+  float* h_meta = nullptr;     // [E, N]
+  char* y_meta = nullptr;      // [M, d] storage type
+  float* A2 = nullptr;         // [E, N] A * log2(e)
+  half_t* w_in16 = nullptr;    // bf16 layers: fp16 copies of the weights
+  half_t* w_o16 = nullptr;
+  half_t* w_out16 = nullptr;
+  bool prepared = false;
+  bool weights_ready = false;
+  const hymba_layer* producer = nullptr;   // consumer: bound producer
+  const hymba_layer* consumer = nullptr;   // producer: its bound consumer (pairs only)
+  const void* prep_kmeta = nullptr;        // consumer: meta K/V used by the last prepare
+  const void* prep_vmeta = nullptr;
+  // column offsets of the shared projection
+  int64_t n_in = 0, off_k = 0, off_v = 0, off_u = 0, off_z = 0, off_dt = 0, off_b = 0;
+  // stage timing
+  bool profiling = false;
+  bool ev_ready = false;
+  hipEvent_t ev_begin[HYMBA_N_STAGES] = {};
+  hipEvent_t ev_end[HYMBA_N_STAGES] = {};
+  bool ev_used[HYMBA_N_STAGES] = {};
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int32_t hip_fail(hipError_t e, const char* what) {
+  return fail(HYMBA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)                              \
+  do {                                                   \
+    hipError_t e_ = (expr);                              \
+    if (e_ != hipSuccess) return hip_fail(e_, what);     \
+  } while (0)
+
+#define STATUS_TRY(expr)            \
+  do {                              \
+    int32_t s_ = (expr);            \
+    if (s_ != HYMBA_OK) return s_;  \
+  } while (0)
+
+// Records begin/end events of one stage when the layer is profiling.
+struct StageTimer {
+  const hymba_layer& L;
+  int stage;
+  hipStream_t s;
+  StageTimer(const hymba_layer& l, int st, hipStream_t stream) : L(l), stage(st), s(stream) {
+    if (L.profiling) {
+      hipEventRecord(L.ev_begin[stage], s);
+      const_cast<hymba_layer&>(L).ev_used[stage] = true;
+    }
+  }
+  ~StageTimer() {
+    if (L.profiling) hipEventRecord(L.ev_end[stage], s);
+  }
+};
+enum { ST_IN_PROJ = 0, ST_KV = 1, ST_ATTN = 2, ST_WO = 3, ST_SSM = 4, ST_EPI = 5, ST_OUT = 6 };
+const char* kStageNames[HYMBA_N_STAGES] = {"in_proj", "kv_write", "attention", "w_o", "ssm", "epilogue", "out_proj"};
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline bool is_bf16(const hymba_layer_cfg& c) { return c.dtype == HYMBA_BF16; }
+inline size_t storage_size(const hymba_layer_cfg& c) { return is_bf16(c) ? 2 : 4; }
+inline size_t act_size(const hymba_layer_cfg& c) { return is_bf16(c) ? 2 : 4; }
+
+int64_t n_in_of(const hymba_layer_cfg& c) {
+  const int64_t q = (int64_t)c.n_heads * c.head_dim;
+  const int64_t kv = c.own_kv ? 2 * (int64_t)c.n_kv_heads * c.head_dim : 0;
+  return q + kv + 3 * (int64_t)c.d_inner + 2 * (int64_t)c.d_state;
+}
+
+int32_t check_cfg(const hymba_layer_cfg* c) {
+  if (!c) return fail(HYMBA_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->d_model < 1 || c->n_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 1 || c->d_inner < 1 ||
+      c->d_state < 1 || c->n_meta < 0)
+    return fail(HYMBA_ERR_INVALID_ARG, "dimensions must be positive (n_meta >= 0)");
+  if (c->n_heads % c->n_kv_heads != 0)
+    return fail(HYMBA_ERR_INVALID_ARG, "n_heads (%d) must be a multiple of n_kv_heads (%d)", c->n_heads,
+                c->n_kv_heads);
+  if (c->dtype != HYMBA_F32 && c->dtype != HYMBA_BF16)
+    return fail(HYMBA_ERR_INVALID_ARG, "dtype must be HYMBA_F32 or HYMBA_BF16");
+  if (c->own_kv != 0 && c->own_kv != 1) return fail(HYMBA_ERR_INVALID_ARG, "own_kv must be 0 or 1");
+  if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps))
+    return fail(HYMBA_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
+  if (c->d_state != 8 && c->d_state != 16)
+    return fail(HYMBA_ERR_UNSUPPORTED, "d_state must be 8 or 16 (got %d)", c->d_state);
+  if (c->d_inner % 8 != 0) return fail(HYMBA_ERR_UNSUPPORTED, "d_inner must be a multiple of 8");
+  if (c->d_model % 8 != 0) return fail(HYMBA_ERR_UNSUPPORTED, "d_model must be a multiple of 8");
+  if (c->dtype == HYMBA_BF16) {
+    if (!attn_mfma_supported(c->head_dim, c->n_heads, c->n_kv_heads, c->n_meta))
+      return fail(HYMBA_ERR_UNSUPPORTED,
+                  "bf16 layers need head_dim 64, n_heads/n_kv_heads <= 8 and n_meta <= 128");
+  } else {
+    if (c->head_dim != 32 && c->head_dim != 64)
+      return fail(HYMBA_ERR_UNSUPPORTED, "fp32 attention needs head_dim 32 or 64");
+    if (c->n_heads / c->n_kv_heads > 8)
+      return fail(HYMBA_ERR_UNSUPPORTED, "n_heads/n_kv_heads must be <= 8");
+  }
+  return HYMBA_OK;
+}
+
+struct PersistLayout {
+  size_t k_meta, v_meta, h_meta, y_meta, A2, w_in16, w_o16, w_out16, total;
+};
+
+PersistLayout persist_layout(const hymba_layer_cfg& c) {
+  const size_t as = act_size(c), ss = storage_size(c);
+  PersistLayout p{};
+  size_t off = 0;
+  const size_t kv = (size_t)c.n_meta * c.n_kv_heads * c.head_dim * as;
+  p.k_meta = off; off += align_up(kv);
+  p.v_meta = off; off += align_up(kv);
+  p.h_meta = off; off += align_up((size_t)c.d_inner * c.d_state * 4);
+  p.y_meta = off; off += align_up((size_t)c.n_meta * c.d_model * ss);
+  p.A2 = off; off += align_up((size_t)c.d_inner * c.d_state * 4);
+  if (is_bf16(c)) {
+    const size_t hq = (size_t)c.n_heads * c.head_dim;
+    p.w_in16 = off; off += align_up((size_t)n_in_of(c) * c.d_model * 2);
+    p.w_o16 = off; off += align_up((size_t)c.d_inner * hq * 2);
+    p.w_out16 = off; off += align_up((size_t)c.d_model * c.d_inner * 2);
+  }
+  p.total = off;
+  return p;
+}
+
+struct WsLayout {
+  size_t X16, P, bc32, O, Ao, Ys, F, Y32, gemm, part, total;
+  int64_t rows;
+};
+
+WsLayout ws_layout(const hymba_layer& L, int64_t batch, int64_t seq) {
+  const hymba_layer_cfg& c = L.cfg;
+  const size_t as = act_size(c);
+  const bool b16 = is_bf16(c);
+  const int64_t rows = std::max<int64_t>(batch * seq, c.n_meta);
+  WsLayout w{};
+  w.rows = rows;
+  size_t off = 0;
+  w.X16 = off; off += b16 ? align_up((size_t)rows * c.d_model * 2) : 0;
+  w.P = off; off += align_up((size_t)rows * L.n_in * as);
+  w.bc32 = off; off += b16 ? align_up((size_t)rows * 2 * c.d_state * 4) : 0;
+  w.O = off; off += align_up((size_t)rows * c.n_heads * c.head_dim * as);
+  w.Ao = off; off += align_up((size_t)rows * c.d_inner * as);
+  w.Ys = off; off += align_up((size_t)rows * c.d_inner * as);
+  w.F = off; off += align_up((size_t)rows * c.d_inner * as);
+  w.Y32 = off; off += b16 ? align_up((size_t)rows * c.d_model * 4) : 0;
+  w.gemm = off; off += b16 ? kGemmWorkspaceBytes : 0;
+  w.part = off;
+  off += align_up((size_t)std::max<int64_t>(batch, 1) * c.n_heads * kDecodeMaxSplits * (c.head_dim + 2) * 4);
+  w.total = off;
+  return w;
+}
+
+// Y[rows, out] = X[rows, in] . W[out, in]^T.  fp32 layers: fp32 kernel.  bf16
+// layers: fp16 operands through hipBLASLt, output fp16 (out32 = false) or fp32.
+int32_t project(const hymba_layer& L, const void* X, int64_t ldx, const void* W, int64_t ldw, void* Y,
+                int64_t ldy, int64_t rows, int64_t out, int64_t in, bool out32, char* ws, const WsLayout& wl,
+                hipStream_t s) {
+  if (is_bf16(L.cfg)) {
+    const char* err = nullptr;
+    const int r = gemm_16(GT_F16, out32 ? GT_F32 : GT_F16, X, ldx, W, ldw, Y, ldy, rows, out, in, ws + wl.gemm,
+                          kGemmWorkspaceBytes, s, &err);
+    if (r != 0) return fail(r == -2 ? HYMBA_ERR_UNSUPPORTED : HYMBA_ERR_HIP, "projection GEMM: %s", err);
+    return HYMBA_OK;
+  }
+  HIP_TRY(launch_gemm_f32(static_cast<const float*>(X), ldx, static_cast<const float*>(W), ldw,
+                          static_cast<float*>(Y), ldy, rows, static_cast<int>(out), static_cast<int>(in), s),
+          "fp32 projection GEMM launch");
+  return HYMBA_OK;
+}
+
+template <typename CT>
+int32_t run_attention(const hymba_layer_cfg& c, const CT* q, int64_t ld_q, const CT* k, const CT* v,
+                      int64_t ld_kv, int64_t seq_stride, const CT* k_meta, const CT* v_meta, int n_meta, CT* o,
+                      int64_t ld_o, int B, int T_, int window, hipStream_t s) {
+  AttnArgs<CT> a{};
+  a.q = q; a.ld_q = ld_q;
+  a.k = k; a.v = v; a.ld_kv = ld_kv; a.kv_seq_stride = seq_stride;
+  a.k_meta = k_meta; a.v_meta = v_meta; a.ld_meta = (int64_t)c.n_kv_heads * c.head_dim; a.n_meta = n_meta;
+  a.o = o; a.ld_o = ld_o;
+  a.B = B; a.T = T_; a.n_heads = c.n_heads; a.n_kv_heads = c.n_kv_heads; a.head_dim = c.head_dim;
+  a.window = window; a.qb_per_wg = 0;
+  a.scale_log2 = kLog2e / std::sqrt(static_cast<float>(c.head_dim));
+  if constexpr (sizeof(CT) == 2) {
+    HIP_TRY(launch_attn_prefill_mfma(a, s), "attention launch");
+  } else {
+    HIP_TRY(launch_attn_prefill_f32(a, s), "attention launch");
+  }
+  return HYMBA_OK;
+}
+
+// Meta K/V the layer attends to, or NULL if unavailable.
+void meta_kv_of(const hymba_layer& L, const hymba_kv* kv, const void** km, const void** vm) {
+  if (L.cfg.own_kv) { *km = L.k_meta; *vm = L.v_meta; return; }
+  if (L.producer) { *km = L.producer->k_meta; *vm = L.producer->v_meta; return; }
+  *km = kv ? kv->k_meta : nullptr;
+  *vm = kv ? kv->v_meta : nullptr;
+}
+
+// Shared projection of `rows` rows of x (storage type) into P (activation type).
+template <typename CT>
+int32_t in_projection(const hymba_layer& L, const void* x, int64_t rows, char* ws, const WsLayout& wl,
+                      hipStream_t s) {
+  const hymba_layer_cfg& c = L.cfg;
+  StageTimer st(L, ST_IN_PROJ, s);
+  if (is_bf16(c)) {
+    half_t* x16 = reinterpret_cast<half_t*>(ws + wl.X16);
+    HIP_TRY(launch_convert(static_cast<const bf16_t*>(x), c.d_model, x16, c.d_model, rows, c.d_model, s),
+            "input conversion");
+    STATUS_TRY(project(L, x16, c.d_model, L.w_in16, c.d_model, ws + wl.P, L.n_in, rows, L.n_in, c.d_model, false,
+                       ws, wl, s));
+    // B/C columns as fp32 for the scan's scalar loads
+    HIP_TRY(launch_convert(reinterpret_cast<const half_t*>(ws + wl.P) + L.off_b, L.n_in,
+                           reinterpret_cast<float*>(ws + wl.bc32), 2 * c.d_state, rows, 2 * c.d_state, s),
+            "B/C conversion");
+    return HYMBA_OK;
+  }
+  return project(L, x, c.d_model, L.w.w_in, c.d_model, ws + wl.P, L.n_in, rows, L.n_in, c.d_model, false, ws, wl,
+                 s);
+}
+
+// W_O, fused epilogue, output projection of `rows` rows; y_out in storage type.
+template <typename CT>
+int32_t tail(const hymba_layer& L, char* ws, const WsLayout& wl, int64_t rows, void* y_out, hipStream_t s) {
+  const hymba_layer_cfg& c = L.cfg;
+  const int64_t hq = (int64_t)c.n_heads * c.head_dim;
+  const bool b16 = is_bf16(c);
+  {
+    StageTimer st(L, ST_WO, s);
+    STATUS_TRY(project(L, ws + wl.O, hq, b16 ? (const void*)L.w_o16 : L.w.w_o, hq, ws + wl.Ao, c.d_inner, rows,
+                       c.d_inner, hq, false, ws, wl, s));
+  }
+  {
+    StageTimer st(L, ST_EPI, s);
+    EpiArgs<CT> e{};
+    const CT* P = reinterpret_cast<const CT*>(ws + wl.P);
+    e.ao = reinterpret_cast<const CT*>(ws + wl.Ao); e.ld_ao = c.d_inner;
+    e.y = reinterpret_cast<const CT*>(ws + wl.Ys); e.ld_y = c.d_inner;
+    e.z = P + L.off_z; e.ld_z = L.n_in;
+    e.beta1 = L.w.beta1; e.beta2 = L.w.beta2;
+    e.f = reinterpret_cast<CT*>(ws + wl.F); e.ld_f = c.d_inner;
+    e.rows = rows; e.E = c.d_inner; e.eps = c.rms_eps;
+    HIP_TRY(launch_epilogue(e, s), "epilogue launch");
+  }
+  StageTimer st(L, ST_OUT, s);
+  if (b16) {
+    float* y32 = reinterpret_cast<float*>(ws + wl.Y32);
+    STATUS_TRY(project(L, ws + wl.F, c.d_inner, L.w_out16, c.d_inner, y32, c.d_model, rows, c.d_model, c.d_inner,
+                       true, ws, wl, s));
+    HIP_TRY(launch_convert(y32, c.d_model, static_cast<bf16_t*>(y_out), c.d_model, rows, c.d_model, s),
+            "output conversion");
+    return HYMBA_OK;
+  }
+  return project(L, ws + wl.F, c.d_inner, L.w.w_out, c.d_inner, y_out, c.d_model, rows, c.d_model, c.d_inner,
+                 false, ws, wl, s);
+}
+
+template <typename CT>
+ScanArgs<CT> scan_args(const hymba_layer& L, char* ws, const WsLayout& wl, int B, int T_, const float* h0,
+                       float* h_out) {
+  const hymba_layer_cfg& c = L.cfg;
+  const CT* P = reinterpret_cast<const CT*>(ws + wl.P);
+  ScanArgs<CT> sa{};
+  sa.u = P + L.off_u; sa.dt = P + L.off_dt; sa.ld = L.n_in;
+  if (is_bf16(c)) {
+    sa.bc = reinterpret_cast<const float*>(ws + wl.bc32); sa.ld_bc = 2 * c.d_state;
+  } else {
+    sa.bc = reinterpret_cast<const float*>(P + L.off_b); sa.ld_bc = L.n_in;
+  }
+  sa.A2 = L.A2; sa.D = L.w.D; sa.dt_bias = L.w.dt_bias;
+  sa.h0 = h0; sa.h0_bstride = 0;
+  sa.y = reinterpret_cast<CT*>(ws + wl.Ys); sa.ldy = c.d_inner;
+  sa.h_out = h_out;
+  sa.B = B; sa.T = T_; sa.E = c.d_inner; sa.N = c.d_state;
+  return sa;
+}
+
+template <typename CT>
+int32_t prepare_impl(hymba_layer& L, const hymba_kv* kv, char* ws, const WsLayout& wl, hipStream_t s) {
+  const hymba_layer_cfg& c = L.cfg;
+  const int M = c.n_meta;
+  if (!L.weights_ready) {
+    HIP_TRY(launch_scale_copy(L.w.A, L.A2, (int64_t)c.d_inner * c.d_state, kLog2e, s), "A scaling");
+    if (is_bf16(c)) {
+      const int64_t hq = (int64_t)c.n_heads * c.head_dim;
+      HIP_TRY(launch_convert(static_cast<const bf16_t*>(L.w.w_in), c.d_model, L.w_in16, c.d_model, L.n_in,
+                             c.d_model, s), "weight conversion");
+      HIP_TRY(launch_convert(static_cast<const bf16_t*>(L.w.w_o), hq, L.w_o16, hq, c.d_inner, hq, s),
+              "weight conversion");
+      HIP_TRY(launch_convert(static_cast<const bf16_t*>(L.w.w_out), c.d_inner, L.w_out16, c.d_inner, c.d_model,
+                             c.d_inner, s), "weight conversion");
+    }
+    L.weights_ready = true;
+  }
+  const void *km = nullptr, *vm = nullptr;
+  if (!c.own_kv) {
+    meta_kv_of(L, kv, &km, &vm);
+    if (M > 0 && L.producer && !L.producer->prepared)
+      return fail(HYMBA_ERR_BIND, "the bound producer must be prepared before its consumer");
+    if (M > 0 && (!km || !vm))
+      return fail(HYMBA_ERR_INVALID_ARG, "an unbound consumer needs kv->k_meta and kv->v_meta");
+  }
+  if (M == 0) {
+    HIP_TRY(launch_fill(L.h_meta, (int64_t)c.d_inner * c.d_state, 0.f, s), "state clear");
+    L.prepared = true;
+    L.prep_kmeta = km; L.prep_vmeta = vm;
+    return HYMBA_OK;
+  }
+  STATUS_TRY(in_projection<CT>(L, L.w.meta, M, ws, wl, s));
+  const CT* P = reinterpret_cast<const CT*>(ws + wl.P);
+  const int64_t kvw = (int64_t)c.n_kv_heads * c.head_dim;
+  const CT *kk, *vv;
+  int64_t ld_kv;
+  if (c.own_kv) {
+    KvWriteArgs<CT> a{};
+    a.k_src = P + L.off_k; a.v_src = P + L.off_v; a.ld_src = L.n_in;
+    a.k_full = reinterpret_cast<CT*>(L.k_meta); a.v_full = reinterpret_cast<CT*>(L.v_meta);
+    a.B = 1; a.T = M; a.n_kv_heads = c.n_kv_heads; a.head_dim = c.head_dim;
+    HIP_TRY(launch_kv_write(a, s), "meta K/V write");
+    kk = P + L.off_k; vv = P + L.off_v; ld_kv = L.n_in;
+    km = L.k_meta; vm = L.v_meta;
+  } else {
+    kk = static_cast<const CT*>(km); vv = static_cast<const CT*>(vm); ld_kv = kvw;
+  }
+  // meta rows attend causally among themselves: a global pass with no prefix
+  STATUS_TRY(run_attention<CT>(c, P, L.n_in, kk, vv, ld_kv, (int64_t)M * ld_kv, nullptr, nullptr, 0,
+                               reinterpret_cast<CT*>(ws + wl.O), (int64_t)c.n_heads * c.head_dim, 1, M, 0, s));
+  HIP_TRY(launch_selective_scan(scan_args<CT>(L, ws, wl, 1, M, nullptr, L.h_meta), s), "meta scan launch");
+  STATUS_TRY(tail<CT>(L, ws, wl, M, L.y_meta, s));
+  L.prepared = true;
+  L.prep_kmeta = km; L.prep_vmeta = vm;
+  return HYMBA_OK;
+}
+
+int32_t ensure_prepared(hymba_layer& L, const hymba_kv* kv, char* ws, const WsLayout& wl, hipStream_t s) {
+  if (L.prepared && !L.cfg.own_kv && !L.producer && L.cfg.n_meta > 0 && kv &&
+      (kv->k_meta != L.prep_kmeta || kv->v_meta != L.prep_vmeta))
+    L.prepared = false;   // an unbound consumer was handed different meta K/V
+  if (L.prepared) return HYMBA_OK;
+  return is_bf16(L.cfg) ? prepare_impl<half_t>(L, kv, ws, wl, s) : prepare_impl<float>(L, kv, ws, wl, s);
+}
+
+template <typename CT>
+int32_t prefill_impl(hymba_layer& L, const void* x, int B, int T_, void* y, const hymba_kv* kv, float* state_out,
+                     char* ws, const WsLayout& wl, hipStream_t s) {
+  for (bool& u : L.ev_used) u = false;
+  const hymba_layer_cfg& c = L.cfg;
+  const int64_t rows = (int64_t)B * T_;
+  const int64_t kvw = (int64_t)c.n_kv_heads * c.head_dim;
+  STATUS_TRY(in_projection<CT>(L, x, rows, ws, wl, s));
+  const CT* P = reinterpret_cast<const CT*>(ws + wl.P);
+  const CT *k, *v;
+  int64_t ld_kv, seq_stride;
+  if (c.own_kv) {
+    k = P + L.off_k; v = P + L.off_v; ld_kv = L.n_in; seq_stride = (int64_t)T_ * L.n_in;
+    if (kv && (kv->k || kv->k_cache)) {
+      StageTimer st(L, ST_KV, s);
+      KvWriteArgs<CT> a{};
+      a.k_src = P + L.off_k; a.v_src = P + L.off_v; a.ld_src = L.n_in;
+      a.k_full = static_cast<CT*>(kv->k); a.v_full = static_cast<CT*>(kv->v);
+      a.k_cache = static_cast<CT*>(kv->k_cache); a.v_cache = static_cast<CT*>(kv->v_cache);
+      a.cache_len = kv->cache_len;
+      a.B = B; a.T = T_; a.n_kv_heads = c.n_kv_heads; a.head_dim = c.head_dim;
+      HIP_TRY(launch_kv_write(a, s), "K/V write");
+    }
+  } else {
+    k = static_cast<const CT*>(kv->k); v = static_cast<const CT*>(kv->v);
+    ld_kv = kvw; seq_stride = (int64_t)T_ * kvw;
+  }
+  const void *km, *vm;
+  meta_kv_of(L, kv, &km, &vm);
+  {
+    StageTimer st(L, ST_ATTN, s);
+    STATUS_TRY(run_attention<CT>(c, P, L.n_in, k, v, ld_kv, seq_stride, static_cast<const CT*>(km),
+                                 static_cast<const CT*>(vm), c.n_meta, reinterpret_cast<CT*>(ws + wl.O),
+                                 (int64_t)c.n_heads * c.head_dim, B, T_, c.window, s));
+  }
+  {
+    StageTimer st(L, ST_SSM, s);
+    HIP_TRY(launch_selective_scan(scan_args<CT>(L, ws, wl, B, T_, L.h_meta, state_out), s), "scan launch");
+  }
+  return tail<CT>(L, ws, wl, rows, y, s);
+}
+
+template <typename CT>
+int32_t decode_impl(hymba_layer& L, const void* x, const int64_t* pos, int B, void* y, const hymba_kv* kv,
+                    float* state, char* ws, const WsLayout& wl, hipStream_t s) {
+  for (bool& u : L.ev_used) u = false;
+  const hymba_layer_cfg& c = L.cfg;
+  STATUS_TRY(in_projection<CT>(L, x, B, ws, wl, s));
+  const CT* P = reinterpret_cast<const CT*>(ws + wl.P);
+  if (c.own_kv) {
+    StageTimer st(L, ST_KV, s);
+    KvWriteArgs<CT> a{};
+    a.k_src = P + L.off_k; a.v_src = P + L.off_v; a.ld_src = L.n_in;
+    a.k_cache = static_cast<CT*>(kv->k_cache); a.v_cache = static_cast<CT*>(kv->v_cache);
+    a.cache_len = kv->cache_len; a.pos = pos;
+    a.B = B; a.T = 1; a.n_kv_heads = c.n_kv_heads; a.head_dim = c.head_dim;
+    HIP_TRY(launch_kv_write(a, s), "cache slot write");
+  }
+  const void *km, *vm;
+  meta_kv_of(L, kv, &km, &vm);
+  const int weff = c.window > 0 ? c.window : kv->cache_len;
+  const int splits = decode_attn_splits(B, c.n_kv_heads, c.n_meta + std::min(weff, kv->cache_len));
+  if (splits < 1) return fail(HYMBA_ERR_UNSUPPORTED, "decode key range too long for the split-K kernel");
+  {
+    StageTimer st(L, ST_ATTN, s);
+    DecAttnArgs<CT> a{};
+    a.q = P; a.ld_q = L.n_in;
+    a.k_meta = static_cast<const CT*>(km); a.v_meta = static_cast<const CT*>(vm);
+    a.ld_meta = (int64_t)c.n_kv_heads * c.head_dim; a.n_meta = c.n_meta;
+    a.k_cache = static_cast<const CT*>(kv->k_cache); a.v_cache = static_cast<const CT*>(kv->v_cache);
+    a.cache_len = kv->cache_len; a.pos = pos;
+    a.o = reinterpret_cast<CT*>(ws + wl.O); a.ld_o = (int64_t)c.n_heads * c.head_dim;
+    a.part = reinterpret_cast<float*>(ws + wl.part);
+    a.B = B; a.n_heads = c.n_heads; a.n_kv_heads = c.n_kv_heads; a.head_dim = c.head_dim;
+    a.window = c.window; a.splits = splits;
+    a.scale_log2 = kLog2e / std::sqrt(static_cast<float>(c.head_dim));
+    HIP_TRY(launch_decode_attn(a, s), "decode attention launch");
+  }
+  {
+    StageTimer tm(L, ST_SSM, s);
+    StepArgs<CT> st{};
+    st.u = P + L.off_u; st.dt = P + L.off_dt; st.bc = P + L.off_b; st.ld = L.n_in;
+    st.A2 = L.A2; st.D = L.w.D; st.dt_bias = L.w.dt_bias; st.h = state;
+    st.y = reinterpret_cast<CT*>(ws + wl.Ys); st.ldy = c.d_inner;
+    st.B = B; st.E = c.d_inner; st.N = c.d_state;
+    HIP_TRY(launch_ssm_step(st, s), "SSM step launch");
+  }
+  return tail<CT>(L, ws, wl, B, y, s);
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t hymba_layer_persistent_bytes(const hymba_layer_cfg* cfg) {
+  if (check_cfg(cfg) != HYMBA_OK) return 0;
+  return persist_layout(*cfg).total;
+}
+
+int32_t hymba_layer_create(const hymba_layer_cfg* cfg, const hymba_layer_weights* w, void* persistent,
+                           size_t persistent_bytes, hymba_layer** out) {
+  if (!out) return fail(HYMBA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  STATUS_TRY(check_cfg(cfg));
+  if (!w) return fail(HYMBA_ERR_INVALID_ARG, "weights is NULL");
+  if (!w->w_in || !w->w_o || !w->w_out || !w->A || !w->D || !w->dt_bias || !w->beta1 || !w->beta2)
+    return fail(HYMBA_ERR_INVALID_ARG, "a weight pointer is NULL");
+  if (cfg->n_meta > 0 && !w->meta) return fail(HYMBA_ERR_INVALID_ARG, "meta rows pointer is NULL");
+  if (!persistent) return fail(HYMBA_ERR_INVALID_ARG, "persistent buffer is NULL");
+  if (!aligned(persistent, kAlign)) return fail(HYMBA_ERR_INVALID_ARG, "persistent buffer must be 256-byte aligned");
+  const PersistLayout pl = persist_layout(*cfg);
+  if (persistent_bytes < pl.total)
+    return fail(HYMBA_ERR_WORKSPACE, "persistent buffer has %zu bytes, needs %zu", persistent_bytes, pl.total);
+  hymba_layer* L = new (std::nothrow) hymba_layer();
+  if (!L) return fail(HYMBA_ERR_INVALID_ARG, "host allocation failed");
+  L->cfg = *cfg;
+  L->w = *w;
+  char* base = static_cast<char*>(persistent);
+  L->k_meta = base + pl.k_meta;
+  L->v_meta = base + pl.v_meta;
+  L->h_meta = reinterpret_cast<float*>(base + pl.h_meta);
+  L->y_meta = base + pl.y_meta;
+  L->A2 = reinterpret_cast<float*>(base + pl.A2);
+  if (is_bf16(*cfg)) {
+    L->w_in16 = reinterpret_cast<half_t*>(base + pl.w_in16);
+    L->w_o16 = reinterpret_cast<half_t*>(base + pl.w_o16);
+    L->w_out16 = reinterpret_cast<half_t*>(base + pl.w_out16);
+  }
+  const int64_t q = (int64_t)cfg->n_heads * cfg->head_dim, kvw = (int64_t)cfg->n_kv_heads * cfg->head_dim;
+  L->n_in = n_in_of(*cfg);
+  L->off_k = q;
+  L->off_v = q + kvw;
+  L->off_u = q + (cfg->own_kv ? 2 * kvw : 0);
+  L->off_z = L->off_u + cfg->d_inner;
+  L->off_dt = L->off_z + cfg->d_inner;
+  L->off_b = L->off_dt + cfg->d_inner;
+  *out = L;
+  return HYMBA_OK;
+}
+
+void hymba_layer_destroy(hymba_layer* L) {
+  if (!L) return;
+  if (L->ev_ready) {
+    for (int i = 0; i < HYMBA_N_STAGES; ++i) {
+      hipEventDestroy(L->ev_begin[i]);
+      hipEventDestroy(L->ev_end[i]);
+    }
+  }
+  if (L->producer && L->producer->consumer == L) const_cast<hymba_layer*>(L->producer)->consumer = nullptr;
+  if (L->consumer && L->consumer->producer == L) const_cast<hymba_layer*>(L->consumer)->producer = nullptr;
+  delete L;
+}
+
+int32_t hymba_kv_share_bind(hymba_layer* consumer, const hymba_layer* producer) {
+  if (!consumer) return fail(HYMBA_ERR_INVALID_ARG, "consumer is NULL");
+  if (producer == consumer) return fail(HYMBA_ERR_BIND, "a layer cannot share K/V with itself");
+  if (consumer->cfg.own_kv) return fail(HYMBA_ERR_BIND, "the consumer must be created with own_kv = 0");
+  if (!producer) {
+    if (consumer->producer) const_cast<hymba_layer*>(consumer->producer)->consumer = nullptr;
+    consumer->producer = nullptr;
+    consumer->prepared = false;
+    return HYMBA_OK;
+  }
+  const hymba_layer_cfg &c = consumer->cfg, &p = producer->cfg;
+  if (!p.own_kv) return fail(HYMBA_ERR_BIND, "the producer must own its K/V (own_kv = 1)");
+  if (c.n_kv_heads != p.n_kv_heads || c.head_dim != p.head_dim || c.n_meta != p.n_meta || c.dtype != p.dtype)
+    return fail(HYMBA_ERR_BIND, "producer and consumer differ in n_kv_heads, head_dim, n_meta or dtype");
+  if ((c.window > 0) != (p.window > 0) || (c.window > 0 && c.window != p.window))
+    return fail(HYMBA_ERR_BIND, "producer and consumer must have the same attention window");
+  if (producer->consumer && producer->consumer != consumer)
+    return fail(HYMBA_ERR_BIND, "the producer already has a consumer (K/V are shared by pairs)");
+  if (consumer->producer && consumer->producer != producer)
+    const_cast<hymba_layer*>(consumer->producer)->consumer = nullptr;
+  consumer->producer = producer;
+  const_cast<hymba_layer*>(producer)->consumer = consumer;
+  consumer->prepared = false;
+  return HYMBA_OK;
+}
+
+size_t hymba_mixer_workspace_bytes(const hymba_layer* L, int32_t batch, int32_t seq) {
+  if (!L || batch < 1 || seq < 1) return 0;
+  return ws_layout(*L, batch, seq).total;
+}
+
+int32_t hymba_layer_prepare(hymba_layer* L, const hymba_kv* kv, void* ws, size_t ws_bytes, void* stream) {
+  if (!L) return fail(HYMBA_ERR_INVALID_ARG, "layer is NULL");
+  if (!ws) return fail(HYMBA_ERR_INVALID_ARG, "workspace is NULL");
+  const WsLayout wl = ws_layout(*L, 1, 1);
+  if (ws_bytes < wl.total) return fail(HYMBA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, wl.total);
+  L->prepared = false;
+  return ensure_prepared(*L, kv, static_cast<char*>(ws), wl, static_cast<hipStream_t>(stream));
+}
+
+int32_t hymba_mixer_prefill(hymba_layer* L, const void* x, int32_t B, int32_t T, void* y, const hymba_kv* kv,
+                            float* ssm_state_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!L) return fail(HYMBA_ERR_INVALID_ARG, "layer is NULL");
+  if (!x || !y || !ws) return fail(HYMBA_ERR_INVALID_ARG, "x, y and workspace must be non-NULL");
+  if (B < 1 || T < 1) return fail(HYMBA_ERR_INVALID_ARG, "B and T must be >= 1 (got %d, %d)", B, T);
+  const hymba_layer_cfg& c = L->cfg;
+  if (!c.own_kv) {
+    if (!kv || !kv->k || !kv->v) return fail(HYMBA_ERR_INVALID_ARG, "a consumer needs kv->k and kv->v");
+    if (!L->producer && c.n_meta > 0 && (!kv->k_meta || !kv->v_meta))
+      return fail(HYMBA_ERR_INVALID_ARG, "an unbound consumer needs kv->k_meta and kv->v_meta");
+  } else if (kv) {
+    if ((kv->k != nullptr) != (kv->v != nullptr)) return fail(HYMBA_ERR_INVALID_ARG, "kv->k and kv->v go together");
+    if ((kv->k_cache != nullptr) != (kv->v_cache != nullptr))
+      return fail(HYMBA_ERR_INVALID_ARG, "kv->k_cache and kv->v_cache go together");
+    if (kv->k_cache && kv->cache_len < 1) return fail(HYMBA_ERR_INVALID_ARG, "cache_len must be >= 1");
+  }
+  const WsLayout wl = ws_layout(*L, B, T);
+  if (ws_bytes < wl.total) return fail(HYMBA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, wl.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  STATUS_TRY(ensure_prepared(*L, kv, w, wl, s));
+  return is_bf16(c) ? prefill_impl<half_t>(*L, x, B, T, y, kv, ssm_state_out, w, wl, s)
+                    : prefill_impl<float>(*L, x, B, T, y, kv, ssm_state_out, w, wl, s);
+}
+
+int32_t hymba_mixer_decode(hymba_layer* L, const void* x_t, const int64_t* pos, int32_t B, void* y_t,
+                           const hymba_kv* kv, float* ssm_state, void* ws, size_t ws_bytes, void* stream) {
+  if (!L) return fail(HYMBA_ERR_INVALID_ARG, "layer is NULL");
+  if (!x_t || !y_t || !pos || !ssm_state || !ws)
+    return fail(HYMBA_ERR_INVALID_ARG, "x_t, pos, y_t, ssm_state and workspace must be non-NULL");
+  if (B < 1) return fail(HYMBA_ERR_INVALID_ARG, "B must be >= 1");
+  if (!kv || !kv->k_cache || !kv->v_cache) return fail(HYMBA_ERR_INVALID_ARG, "decode needs kv->k_cache and kv->v_cache");
+  const hymba_layer_cfg& c = L->cfg;
+  if (kv->cache_len < 1) return fail(HYMBA_ERR_INVALID_ARG, "cache_len must be >= 1");
+  if (c.window > 0 && kv->cache_len < c.window)
+    return fail(HYMBA_ERR_INVALID_ARG, "a sliding-window cache needs cache_len >= window (%d < %d)", kv->cache_len,
+                c.window);
+  if (!c.own_kv && !L->producer && c.n_meta > 0 && (!kv->k_meta || !kv->v_meta))
+    return fail(HYMBA_ERR_INVALID_ARG, "an unbound consumer needs kv->k_meta and kv->v_meta");
+  const WsLayout wl = ws_layout(*L, B, 1);
+  if (ws_bytes < wl.total) return fail(HYMBA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, wl.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  STATUS_TRY(ensure_prepared(*L, kv, w, wl, s));
+  return is_bf16(c) ? decode_impl<half_t>(*L, x_t, pos, B, y_t, kv, ssm_state, w, wl, s)
+                    : decode_impl<float>(*L, x_t, pos, B, y_t, kv, ssm_state, w, wl, s);
+}
+
+int32_t hymba_layer_meta_outputs(const hymba_layer* L, const void** k_meta, const void** v_meta,
+                                 const float** h_meta, const void** y_meta) {
+  if (!L) return fail(HYMBA_ERR_INVALID_ARG, "layer is NULL");
+  if (!L->prepared) return fail(HYMBA_ERR_INVALID_ARG, "layer is not prepared");
+  if (k_meta) *k_meta = L->cfg.own_kv ? L->k_meta : nullptr;
+  if (v_meta) *v_meta = L->cfg.own_kv ? L->v_meta : nullptr;
+  if (h_meta) *h_meta = L->h_meta;
+  if (y_meta) *y_meta = L->y_meta;
+  return HYMBA_OK;
+}
+
+int32_t hymba_layer_profile(hymba_layer* L, int32_t enable) {
+  if (!L) return fail(HYMBA_ERR_INVALID_ARG, "layer is NULL");
+  if (enable && !L->ev_ready) {
+    for (int i = 0; i < HYMBA_N_STAGES; ++i) {
+      HIP_TRY(hipEventCreate(&L->ev_begin[i]), "event create");
+      HIP_TRY(hipEventCreate(&L->ev_end[i]), "event create");
+    }
+    L->ev_ready = true;
+  }
+  L->profiling = enable != 0;
+  for (bool& u : L->ev_used) u = false;
+  return HYMBA_OK;
+}
+
+int32_t hymba_layer_profile_read(hymba_layer* L, float* stage_ms, int32_t n) {
+  if (!L || !stage_ms || n < 0) return fail(HYMBA_ERR_INVALID_ARG, "bad arguments");
+  for (int i = 0; i < n && i < HYMBA_N_STAGES; ++i) {
+    stage_ms[i] = 0.f;
+    if (!L->ev_ready || !L->ev_used[i]) continue;
+    HIP_TRY(hipEventSynchronize(L->ev_end[i]), "event synchronize");
+    HIP_TRY(hipEventElapsedTime(&stage_ms[i], L->ev_begin[i], L->ev_end[i]), "event elapsed time");
+  }
+  for (int i = HYMBA_N_STAGES; i < n; ++i) stage_ms[i] = 0.f;
+  return HYMBA_OK;
+}
+
+const char* hymba_stage_name(int32_t stage) {
+  return (stage >= 0 && stage < HYMBA_N_STAGES) ? kStageNames[stage] : "unknown";
+}
+
+const char* hymba_last_error(void) { return g_err.c_str(); }
+
+const char* hymba_status_string(int32_t status) {
+  switch (status) {
+    case HYMBA_OK: return "HYMBA_OK";
+    case HYMBA_ERR_INVALID_ARG: return "HYMBA_ERR_INVALID_ARG";
+    case HYMBA_ERR_UNSUPPORTED: return "HYMBA_ERR_UNSUPPORTED";
+    case HYMBA_ERR_WORKSPACE: return "HYMBA_ERR_WORKSPACE";
+    case HYMBA_ERR_BIND: return "HYMBA_ERR_BIND";
+    case HYMBA_ERR_HIP: return "HYMBA_ERR_HIP";
+    default: return "HYMBA_UNKNOWN_STATUS";
+  }
+}
+
+int32_t hymba_kernel_attention(int32_t dtype, const void* q, int64_t ld_q, const void* k, const void* v,
+                               int64_t ld_kv, int64_t kv_seq_stride, const void* k_meta, const void* v_meta,
+                               int32_t n_meta, void* o, int64_t ld_o, int32_t B, int32_t T, int32_t n_heads,
+                               int32_t n_kv_heads, int32_t head_dim, int32_t window, void* stream) {
+  if (!q || !k || !v || !o || (n_meta > 0 && (!k_meta || !v_meta)))
+    return fail(HYMBA_ERR_INVALID_ARG, "NULL pointer");
+  if (B < 1 || T < 1 || n_meta < 0 || n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads)
+    return fail(HYMBA_ERR_INVALID_ARG, "bad dimensions");
+  hymba_layer_cfg c{};
+  c.n_heads = n_heads; c.n_kv_heads = n_kv_heads; c.head_dim = head_dim;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == HYMBA_F16 || dtype == HYMBA_BF16) {
+    if (!attn_mfma_supported(head_dim, n_heads, n_kv_heads, n_meta))
+      return fail(HYMBA_ERR_UNSUPPORTED, "16-bit attention shape not supported");
+    if (dtype == HYMBA_F16)
+      return run_attention<half_t>(c, static_cast<const half_t*>(q), ld_q, static_cast<const half_t*>(k),
+                                   static_cast<const half_t*>(v), ld_kv, kv_seq_stride,
+                                   static_cast<const half_t*>(k_meta), static_cast<const half_t*>(v_meta), n_meta,
+                                   static_cast<half_t*>(o), ld_o, B, T, window, s);
+    return run_attention<bf16_t>(c, static_cast<const bf16_t*>(q), ld_q, static_cast<const bf16_t*>(k),
+                                 static_cast<const bf16_t*>(v), ld_kv, kv_seq_stride,
+                                 static_cast<const bf16_t*>(k_meta), static_cast<const bf16_t*>(v_meta), n_meta,
+                                 static_cast<bf16_t*>(o), ld_o, B, T, window, s);
+  }
+  if (dtype != HYMBA_F32) return fail(HYMBA_ERR_INVALID_ARG, "bad dtype");
+  if (head_dim != 32 && head_dim != 64) return fail(HYMBA_ERR_UNSUPPORTED, "fp32 attention head_dim");
+  return run_attention<float>(c, static_cast<const float*>(q), ld_q, static_cast<const float*>(k),
+                              static_cast<const float*>(v), ld_kv, kv_seq_stride, static_cast<const float*>(k_meta),
+                              static_cast<const float*>(v_meta), n_meta, static_cast<float*>(o), ld_o, B, T, window,
+                              s);
+}
+
+int32_t hymba_kernel_selective_scan(int32_t dtype, const void* u, const void* dt, int64_t ld, const float* bc,
+                                    int64_t ld_bc, const float* A, const float* D, const float* dt_bias,
+                                    const float* h0, void* y, int64_t ldy, float* h_out, int32_t B, int32_t T,
+                                    int32_t E, int32_t N, void* ws, size_t ws_bytes, void* stream) {
+  if (!u || !dt || !bc || !A || !D || !dt_bias || !y || !ws) return fail(HYMBA_ERR_INVALID_ARG, "NULL pointer");
+  if (B < 1 || T < 1 || E < 1) return fail(HYMBA_ERR_INVALID_ARG, "bad dimensions");
+  if (N != 8 && N != 16) return fail(HYMBA_ERR_UNSUPPORTED, "N must be 8 or 16");
+  if (dtype != HYMBA_F16 && dtype != HYMBA_F32)
+    return fail(HYMBA_ERR_INVALID_ARG, "scan dtype must be HYMBA_F32 or HYMBA_F16");
+  if (ws_bytes < (size_t)E * N * 4) return fail(HYMBA_ERR_WORKSPACE, "workspace too small");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* A2 = static_cast<float*>(ws);
+  HIP_TRY(launch_scale_copy(A, A2, (int64_t)E * N, kLog2e, s), "A scaling");
+  if (dtype == HYMBA_F16) {
+    ScanArgs<half_t> a{static_cast<const half_t*>(u), static_cast<const half_t*>(dt), ld, bc, ld_bc, A2, D,
+                       dt_bias, h0, 0, static_cast<half_t*>(y), ldy, h_out, B, T, E, N};
+    HIP_TRY(launch_selective_scan(a, s), "scan launch");
+  } else if (dtype == HYMBA_F32) {
+    ScanArgs<float> a{static_cast<const float*>(u), static_cast<const float*>(dt), ld, bc, ld_bc, A2, D, dt_bias,
+                      h0, 0, static_cast<float*>(y), ldy, h_out, B, T, E, N};
+    HIP_TRY(launch_selective_scan(a, s), "scan launch");
+  } else {
+    return fail(HYMBA_ERR_INVALID_ARG, "scan dtype must be HYMBA_F32 or HYMBA_F16");
+  }
+  return HYMBA_OK;
+}
+
+int32_t hymba_kernel_epilogue(int32_t dtype, const void* ao, int64_t ld_ao, const void* y, int64_t ld_y,
+                              const void* z, int64_t ld_z, const float* beta1, const float* beta2, void* f,
+                              int64_t ld_f, int64_t rows, int32_t E, float eps, void* stream) {
+  if (!ao || !y || !z || !beta1 || !beta2 || !f) return fail(HYMBA_ERR_INVALID_ARG, "NULL pointer");
+  if (rows < 0 || E < 1) return fail(HYMBA_ERR_INVALID_ARG, "bad dimensions");
+  if (E % 8) return fail(HYMBA_ERR_UNSUPPORTED, "E must be a multiple of 8");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == HYMBA_F16) {
+    EpiArgs<half_t> a{static_cast<const half_t*>(ao), ld_ao, static_cast<const half_t*>(y), ld_y,
+                      static_cast<const half_t*>(z), ld_z, beta1, beta2, static_cast<half_t*>(f), ld_f, rows, E, eps};
+    HIP_TRY(launch_epilogue(a, s), "epilogue launch");
+  } else if (dtype == HYMBA_F32) {
+    EpiArgs<float> a{static_cast<const float*>(ao), ld_ao, static_cast<const float*>(y), ld_y,
+                     static_cast<const float*>(z), ld_z, beta1, beta2, static_cast<float*>(f), ld_f, rows, E, eps};
+    HIP_TRY(launch_epilogue(a, s), "epilogue launch");
+  } else {
+    return fail(HYMBA_ERR_INVALID_ARG, "epilogue dtype must be HYMBA_F32 or HYMBA_F16");
+  }
+  return HYMBA_OK;
+}
+
+}  // extern "C"

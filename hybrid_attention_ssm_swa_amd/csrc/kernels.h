@@ -1,0 +1,135 @@
+// Kernel launch interface used by the C-ABI layer (host side).  Every pointer
+// is device memory; row-major layouts with explicit leading dimensions (in
+// elements) so kernels can read column slices of the shared projection.
+// "Activation type" CT is fp32 for fp32 layers and fp16 for bf16 layers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace hymba {
+
+// ---- prefill attention ------------------------------------------------------
+// Q: row (b*T + t), head h at column h*hd.  K/V real rows: row t of sequence b
+// at k + b*kv_seq_stride + t*ld_kv, KV head g at column g*hd.  Meta K/V:
+// [n_meta, Hkv, hd] (row stride ld_meta).  O: row (b*T + t), head h at h*hd.
+template <typename ET>
+struct AttnArgs {
+  const ET* q; int64_t ld_q;
+  const ET* k; const ET* v; int64_t ld_kv; int64_t kv_seq_stride;
+  const ET* k_meta; const ET* v_meta; int64_t ld_meta; int n_meta;
+  ET* o; int64_t ld_o;
+  int B, T, n_heads, n_kv_heads, head_dim, window, qb_per_wg;
+  float scale_log2;   // log2(e) / sqrt(hd)
+};
+// MFMA kernel (hd = 64), fp16 or bf16 operands, fp32 accumulation.
+hipError_t launch_attn_prefill_mfma(const AttnArgs<half_t>& a, hipStream_t s);
+hipError_t launch_attn_prefill_mfma(const AttnArgs<bf16_t>& a, hipStream_t s);
+// VALU kernel, fp32 (hd 32 or 64).
+hipError_t launch_attn_prefill_f32(const AttnArgs<float>& a, hipStream_t s);
+bool attn_mfma_supported(int head_dim, int n_heads, int n_kv_heads, int n_meta);
+
+// ---- selective scan (prefill) and one-token state update (decode) -------------
+// u, dt: [rows, E] slices (row stride ld); bc: fp32 rows with B_t at
+// bc[0..N) and C_t at bc[N..2N) (row stride ld_bc).  A2 = A * log2(e) [E, N];
+// h0 [E, N] per sequence stride h0_bstride (0 = shared by the batch, null =
+// zeros).  y: [rows, E] (row stride ldy), the ungated SSM output; h_out:
+// [B, E, N] final state (nullable).
+template <typename CT>
+struct ScanArgs {
+  const CT* u; const CT* dt; int64_t ld;
+  const float* bc; int64_t ld_bc;
+  const float* A2; const float* D; const float* dt_bias;
+  const float* h0; int64_t h0_bstride;
+  CT* y; int64_t ldy;
+  float* h_out;
+  int B, T, E, N;
+};
+hipError_t launch_selective_scan(const ScanArgs<float>& a, hipStream_t s);
+hipError_t launch_selective_scan(const ScanArgs<half_t>& a, hipStream_t s);
+
+// h: [B, E, N] fp32 updated in place; row b of u/dt/bc is sequence b (bc in the
+// activation type, B at bc[0..N), C at bc[N..2N)).
+template <typename CT>
+struct StepArgs {
+  const CT* u; const CT* dt; const CT* bc; int64_t ld;
+  const float* A2; const float* D; const float* dt_bias;
+  float* h;
+  CT* y; int64_t ldy;
+  int B, E, N;
+};
+hipError_t launch_ssm_step(const StepArgs<float>& a, hipStream_t s);
+hipError_t launch_ssm_step(const StepArgs<half_t>& a, hipStream_t s);
+
+// ---- fused epilogue: F = beta1*rms(Ao) + beta2*rms(y*silu(z)) ------------------
+template <typename CT>
+struct EpiArgs {
+  const CT* ao; int64_t ld_ao;
+  const CT* y; int64_t ld_y;
+  const CT* z; int64_t ld_z;
+  const float* beta1; const float* beta2;
+  CT* f; int64_t ld_f;
+  int64_t rows; int E; float eps;
+};
+hipError_t launch_epilogue(const EpiArgs<float>& a, hipStream_t s);
+hipError_t launch_epilogue(const EpiArgs<half_t>& a, hipStream_t s);
+
+// ---- K/V movement -------------------------------------------------------------
+// Source rows (b*T + t) with KV head g at column g*hd.  Writes, when non-null,
+// the full K/V [B, T, Hkv, hd] and the cache [B, Hkv, C, hd]: with pos == null
+// (prefill) token t >= T - C goes to slot t mod C; with pos != null (decode,
+// T == 1) the token goes to slot pos[b] mod C (nothing for pos[b] < 0).
+template <typename CT>
+struct KvWriteArgs {
+  const CT* k_src; const CT* v_src; int64_t ld_src;
+  CT* k_full; CT* v_full;
+  CT* k_cache; CT* v_cache; int cache_len;
+  const int64_t* pos;
+  int B, T, n_kv_heads, head_dim;
+};
+hipError_t launch_kv_write(const KvWriteArgs<float>& a, hipStream_t s);
+hipError_t launch_kv_write(const KvWriteArgs<half_t>& a, hipStream_t s);
+
+// ---- decode attention -----------------------------------------------------------
+// One query token per sequence (row b of q).  Keys: n_meta meta keys, then the
+// real tokens max(0, p-Weff+1)..p (p = pos[b]) read from cache slot r mod C,
+// Weff = window > 0 ? window : C.  Split over `splits` key ranges; partials
+// [B, H, splits, hd + 2] in `part`, combined into o (row b, head h at h*hd).
+template <typename CT>
+struct DecAttnArgs {
+  const CT* q; int64_t ld_q;
+  const CT* k_meta; const CT* v_meta; int64_t ld_meta; int n_meta;
+  const CT* k_cache; const CT* v_cache; int cache_len;
+  const int64_t* pos;
+  CT* o; int64_t ld_o;
+  float* part;
+  int B, n_heads, n_kv_heads, head_dim, window, splits;
+  float scale_log2;
+};
+hipError_t launch_decode_attn(const DecAttnArgs<float>& a, hipStream_t s);
+hipError_t launch_decode_attn(const DecAttnArgs<half_t>& a, hipStream_t s);
+int decode_attn_splits(int B, int n_kv_heads, int n_keys_max);
+constexpr int kDecodeMaxSplits = 64;
+constexpr int kDecodeMaxHd = 128;
+
+// ---- fp32 GEMM: Y[rows, out] = X[rows, in] . W[out, in]^T ----------------------
+hipError_t launch_gemm_f32(const float* X, int64_t ldx, const float* W, int64_t ldw, float* Y,
+                           int64_t ldy, int64_t rows, int out, int in, hipStream_t s);
+
+// ---- element-type conversion of a strided [rows, cols] block (cols % 4 == 0) -----
+hipError_t launch_convert(const bf16_t* src, int64_t ld_src, half_t* dst, int64_t ld_dst, int64_t rows,
+                          int64_t cols, hipStream_t s);
+hipError_t launch_convert(const half_t* src, int64_t ld_src, float* dst, int64_t ld_dst, int64_t rows,
+                          int64_t cols, hipStream_t s);
+hipError_t launch_convert(const float* src, int64_t ld_src, bf16_t* dst, int64_t ld_dst, int64_t rows,
+                          int64_t cols, hipStream_t s);
+hipError_t launch_convert(const half_t* src, int64_t ld_src, bf16_t* dst, int64_t ld_dst, int64_t rows,
+                          int64_t cols, hipStream_t s);
+
+// ---- misc ----------------------------------------------------------------------
+hipError_t launch_scale_copy(const float* src, float* dst, int64_t n, float scale, hipStream_t s);
+hipError_t launch_fill(float* dst, int64_t n, float value, hipStream_t s);
+
+}  // namespace hymba

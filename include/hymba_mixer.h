@@ -1,0 +1,236 @@
+/*
+ * hymba_mixer.h -- C ABI of the Hymba hybrid-head mixer library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer (Hymba summary, greeksharifa.github.io, section 2.1, Eq. 3):
+ *
+ *     X~ = [meta rows ; X]                                   (section 2.3)
+ *     [Q | K | V | U | Z | dt | B | C] = X~ W_in^T           (one shared projection)
+ *     Ao = SWA_or_global_attention(Q, K, V) W_O^T            (section 2.2)
+ *     y  = selective_scan(U, dt, B, C; A, D, dt_bias)        (SSM heads)
+ *     F  = beta1 * rms(Ao) + beta2 * rms(y * SiLU(Z))        (normalise, scale, sum)
+ *     Y  = F W_out^T
+ *
+ * Attention: a real query sees all meta keys plus the `window` most recent
+ * real keys including itself (window <= 0: every earlier key); query head h
+ * uses KV head floor(h * n_kv_heads / n_heads).  Consecutive layers may share
+ * K/V (section 2.2): a consumer layer has no K/V columns in W_in and reads its
+ * producer's K/V.  The meta rows are input independent (section 2.3), so their
+ * K/V, SSM state and outputs are computed once per layer ("prepare") and
+ * reused by every call.
+ *
+ * Widths: Nin = H*hd + (own_kv ? 2*Hkv*hd : 0) + 3*E + 2*N.  All matrices are
+ * row-major.  Weights are [out_features, in_features]: W_in [Nin, d],
+ * W_O [E, H*hd], W_out [d, E].
+ *
+ * Memory: every pointer passed to the library is device memory owned by the
+ * caller, except the configuration structs, which are read on the host during
+ * the call.  The library allocates no device memory of its own: per-layer
+ * state lives in the caller's `persistent` buffer, scratch in the caller's
+ * workspace (the GEMM library creates its per-device handle on first use).
+ * Weight pointers are borrowed and must stay valid for the lifetime of the
+ * handle.
+ *
+ * Streams: `stream` is a hipStream_t (NULL = the default stream).  Work is
+ * enqueued asynchronously; a call returns after validation and launch.
+ * Argument errors are reported synchronously before any device work; a
+ * device fault surfaces at the caller's next synchronisation.
+ *
+ * Errors: every int32_t function returns HYMBA_OK (0) or a negative status;
+ * hymba_last_error() returns a thread-local description of the last failure.
+ * No C++ exception crosses this interface.  A handle must not be used from
+ * two threads or two streams at the same time.
+ */
+#ifndef HYMBA_MIXER_H
+#define HYMBA_MIXER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HYMBA_OK 0
+#define HYMBA_ERR_INVALID_ARG (-1) /* null pointer, bad dimension, T < 1, H % Hkv != 0 */
+#define HYMBA_ERR_UNSUPPORTED (-2) /* dtype, head dim or shape with no kernel          */
+#define HYMBA_ERR_WORKSPACE (-3)   /* workspace or persistent buffer too small          */
+#define HYMBA_ERR_BIND (-4)        /* KV-sharing misuse                                  */
+#define HYMBA_ERR_HIP (-5)         /* HIP runtime / library error                         */
+
+/* Layer types (hymba_layer_cfg.dtype):
+ *   HYMBA_F32:  x, y, weights and activations fp32.
+ *   HYMBA_BF16: x, y and weight matrices bf16; activations (the shared
+ *               projection, attention operands/outputs, the K/V exchanged
+ *               through hymba_kv and kept in caches, SSM and fused outputs)
+ *               fp16 with fp32 accumulation; SSM state and the vector
+ *               parameters fp32.  fp16 keeps 11 significand bits where bf16
+ *               keeps 8, at the same MFMA rate and the same bytes moved.
+ * HYMBA_F16 names fp16 operands for the per-kernel entry points only. */
+#define HYMBA_F32 0
+#define HYMBA_BF16 1
+#define HYMBA_F16 2
+
+typedef struct hymba_layer_cfg {
+  int32_t d_model;    /* d                                                         */
+  int32_t n_heads;    /* H query heads                                             */
+  int32_t n_kv_heads; /* Hkv key/value heads (H % Hkv == 0)                         */
+  int32_t head_dim;   /* hd: 64 for bf16; 32 or 64 for fp32                        */
+  int32_t d_inner;    /* E: SSM channels = fused width (multiple of 8)             */
+  int32_t d_state;    /* N: SSM state per channel (8 or 16)                        */
+  int32_t n_meta;     /* M meta tokens (0..128)                                    */
+  int32_t window;     /* > 0: sliding window of real keys incl. self; <= 0: global */
+  int32_t own_kv;     /* 1: projects its own K/V (producer); 0: consumer           */
+  int32_t dtype;      /* HYMBA_F32 or HYMBA_BF16                                   */
+  float rms_eps;      /* epsilon inside the RMS norm's square root (e.g. 1e-6)     */
+} hymba_layer_cfg;
+
+/* Device pointers.  Matrices in the storage dtype; vectors fp32. */
+typedef struct hymba_layer_weights {
+  const void* w_in;     /* [Nin, d]                                         */
+  const void* w_o;      /* [E, H*hd]                                        */
+  const void* w_out;    /* [d, E]                                           */
+  const void* meta;     /* [M, d] meta-token rows                           */
+  const float* A;       /* [E, N]  state decay rates (negative)             */
+  const float* D;       /* [E]     skip weights                             */
+  const float* dt_bias; /* [E]     added before softplus                    */
+  const float* beta1;   /* [E]     attention-branch scale                   */
+  const float* beta2;   /* [E]     SSM-branch scale                         */
+} hymba_layer_weights;
+
+/* K/V handed between layers and kept for decode.  Device pointers in the
+ * layer's activation type (fp32 for HYMBA_F32, fp16 for HYMBA_BF16); any of
+ * them may be NULL where noted. */
+typedef struct hymba_kv {
+  /* Meta K/V [M, Hkv, hd] of an unbound consumer (read).  Ignored by a
+   * producer and by a consumer bound with hymba_kv_share_bind. */
+  const void* k_meta;
+  const void* v_meta;
+  /* Prefill K/V of the real tokens [B, T, Hkv, hd]: a producer writes them
+   * when non-NULL; a consumer reads them (required). */
+  void* k;
+  void* v;
+  /* Decode cache [B, Hkv, cache_len, hd]; real token r lives in slot
+   * r mod cache_len.  Prefill of a producer writes the last cache_len tokens
+   * when non-NULL; decode of a producer writes slot pos mod cache_len and
+   * then attends; decode of a consumer only reads.  A sliding-window layer
+   * needs cache_len >= window; a global layer attends to the last cache_len
+   * real tokens. */
+  void* k_cache;
+  void* v_cache;
+  int32_t cache_len;
+} hymba_kv;
+
+typedef struct hymba_layer hymba_layer;
+
+/* Bytes of the caller-owned per-layer buffer (meta-prefix K/V, SSM state and
+ * outputs, scaled decay rates).  0 if cfg is invalid. */
+size_t hymba_layer_persistent_bytes(const hymba_layer_cfg* cfg);
+
+/* Validates cfg, records the weights and carves `persistent` (device, at least
+ * hymba_layer_persistent_bytes bytes, 256-byte aligned).  *out receives the
+ * handle.  No device work. */
+int32_t hymba_layer_create(const hymba_layer_cfg* cfg, const hymba_layer_weights* w,
+                           void* persistent, size_t persistent_bytes, hymba_layer** out);
+
+void hymba_layer_destroy(hymba_layer* layer);
+
+/* Cross-layer KV sharing (Hymba summary section 2.2): `consumer` (own_kv == 0)
+ * will read the K/V of `producer` (own_kv == 1), whose meta K/V it uses for
+ * its own meta prefix.  Shapes (Hkv, hd, M, dtype) must match; pairs only;
+ * producer == NULL unbinds.  Invalidates the consumer's prepared prefix.  Host
+ * only; returns HYMBA_ERR_BIND on misuse. */
+int32_t hymba_kv_share_bind(hymba_layer* consumer, const hymba_layer* producer);
+
+/* Workspace bytes for prefill of [batch, seq] or decode (seq = 1) of `batch`
+ * sequences; covers the meta-prefix preparation as well. */
+size_t hymba_mixer_workspace_bytes(const hymba_layer* layer, int32_t batch, int32_t seq);
+
+/* Runs the layer on its meta rows alone (Hymba summary section 2.3): fills
+ * the meta K/V (producer), the SSM state after the prefix and the meta rows'
+ * outputs in the persistent buffer.  A consumer needs its producer prepared
+ * (bound) or kv->k_meta / kv->v_meta (unbound).  prefill/decode call it
+ * themselves when needed; calling it explicitly keeps it out of timed work. */
+int32_t hymba_layer_prepare(hymba_layer* layer, const hymba_kv* kv, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Prefill of B sequences of T real tokens, continuing from the meta prefix.
+ * x [B, T, d] -> y [B, T, d].  ssm_state_out [B, E, N] fp32 receives the final
+ * SSM state (may be NULL).  kv as described above. */
+int32_t hymba_mixer_prefill(hymba_layer* layer, const void* x, int32_t B, int32_t T, void* y,
+                            const hymba_kv* kv, float* ssm_state_out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* One decode step: x_t [B, d] -> y_t [B, d] for the token at real index
+ * pos[b] (device int64 [B]).  ssm_state [B, E, N] fp32 holds the state after
+ * token pos-1 and is updated in place.  A producer writes its new K/V into
+ * slot pos mod cache_len before attending; the consumer of the pair must be
+ * called after it with the same kv. */
+int32_t hymba_mixer_decode(hymba_layer* layer, const void* x_t, const int64_t* pos, int32_t B,
+                           void* y_t, const hymba_kv* kv, float* ssm_state, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Device pointers of the prepared meta prefix inside the persistent buffer:
+ * K/V [M, Hkv, hd] in the activation type (producer only, else NULL), SSM
+ * state after the prefix [E, N] fp32, outputs of the meta rows [M, d] in the
+ * storage type.  HYMBA_ERR_INVALID_ARG if the layer is not prepared. */
+int32_t hymba_layer_meta_outputs(const hymba_layer* layer, const void** k_meta,
+                                 const void** v_meta, const float** h_meta, const void** y_meta);
+
+const char* hymba_last_error(void);
+const char* hymba_status_string(int32_t status);
+
+/* ---- stage timing ----------------------------------------------------------
+ * With profiling enabled, prefill/decode/prepare record a HIP event before and
+ * after each stage of the layer on the call's stream.  Stages:
+ *   0 shared input projection   1 K/V write        2 attention
+ *   3 W_O projection            4 SSM (scan/step)  5 fused epilogue
+ *   6 output projection
+ * hymba_layer_profile_read waits for the last call's events and writes the
+ * per-stage milliseconds (0 for stages that did not run) into stage_ms[0..n).
+ * Host only apart from event creation on first enable.                      */
+#define HYMBA_N_STAGES 7
+int32_t hymba_layer_profile(hymba_layer* layer, int32_t enable);
+int32_t hymba_layer_profile_read(hymba_layer* layer, float* stage_ms, int32_t n);
+const char* hymba_stage_name(int32_t stage);
+
+/* ---- per-kernel entry points (parity tests and profiling) -----------------
+ * Each runs one kernel of the path on caller buffers, with the same layouts
+ * the layer uses internally.  dtype names the element type of the 16/32-bit
+ * operands: HYMBA_F32, HYMBA_F16 (what bf16 layers use inside) or, for the
+ * attention kernel only, HYMBA_BF16.                                          */
+
+/* Prefill attention.  q: rows (b*T + t), ld_q; head h at column h*hd.
+ * k/v: row t of sequence b at k + b*kv_seq_stride + t*ld_kv, KV head g at
+ * column g*hd.  k_meta/v_meta: [M, Hkv, hd].  o: rows (b*T + t), ld_o. */
+int32_t hymba_kernel_attention(int32_t dtype, const void* q, int64_t ld_q, const void* k,
+                               const void* v, int64_t ld_kv, int64_t kv_seq_stride,
+                               const void* k_meta, const void* v_meta, int32_t n_meta, void* o,
+                               int64_t ld_o, int32_t B, int32_t T, int32_t n_heads,
+                               int32_t n_kv_heads, int32_t head_dim, int32_t window, void* stream);
+
+/* Selective scan over B sequences of T rows.  u, dt: [B*T, E] slices with
+ * row stride ld (HYMBA_F32 or HYMBA_F16); bc: fp32 rows with B_t at
+ * bc[0..N) and C_t at bc[N..2N) (row stride ld_bc).  A [E, N], D, dt_bias [E]
+ * fp32 (A is the decay rate, not scaled).  h0 [E, N] fp32 shared initial
+ * state or NULL (zero).  y [B*T, E] (row stride ldy) receives the ungated
+ * output; h_out [B, E, N] fp32 the final state (may be NULL).
+ * workspace: >= E*N*4 bytes. */
+int32_t hymba_kernel_selective_scan(int32_t dtype, const void* u, const void* dt, int64_t ld,
+                                    const float* bc, int64_t ld_bc, const float* A, const float* D,
+                                    const float* dt_bias, const float* h0, void* y, int64_t ldy,
+                                    float* h_out, int32_t B, int32_t T, int32_t E, int32_t N,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Fused epilogue over `rows` tokens: F = beta1*rms(ao) + beta2*rms(y*SiLU(z))
+ * (dtype HYMBA_F32 or HYMBA_F16). */
+int32_t hymba_kernel_epilogue(int32_t dtype, const void* ao, int64_t ld_ao, const void* y,
+                              int64_t ld_y, const void* z, int64_t ld_z, const float* beta1,
+                              const float* beta2, void* f, int64_t ld_f, int64_t rows, int32_t E,
+                              float eps, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYMBA_MIXER_H */

@@ -1,0 +1,182 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented status before
+any device work (no GPU needed: create/bind/size functions never touch the
+device, and the hot calls validate first)."""
+import os
+import re
+
+import pytest
+
+import hybrid_attention_ssm_swa_amd as H
+from hybrid_attention_ssm_swa_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hymba_mixer.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="library not built")
+
+FAKE = 1 << 20   # an aligned, never-dereferenced stand-in for device pointers
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hymba_[a-z_]+)\s*\(", text)))
+
+
+def _cfg(**kw):
+    base = dict(d_model=64, n_heads=4, n_kv_heads=2, head_dim=32, d_inner=64, d_state=8, n_meta=4,
+                window=8, own_kv=1, dtype=L.HYMBA_F32, rms_eps=1e-6)
+    base.update(kw)
+    c = L.hymba_layer_cfg()
+    for k, v in base.items():
+        setattr(c, k, v)
+    return c
+
+
+def _weights():
+    w = L.hymba_layer_weights()
+    for f, _ in w._fields_:
+        setattr(w, f, FAKE)
+    return w
+
+
+def _create(cfg):
+    n = L.hymba_layer_persistent_bytes(cfg)
+    assert n > 0
+    return L.hymba_layer_create(cfg, _weights(), FAKE, n)
+
+
+def test_every_declared_function_is_exported():
+    lib = L.load_library()
+    declared = _declared_functions()
+    assert len(declared) >= 14
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(L.EXPORTED)
+
+
+def test_status_strings():
+    assert H.hymba_status_string(0) == "HYMBA_OK"
+    assert H.hymba_status_string(-4) == "HYMBA_ERR_BIND"
+    assert H.hymba_status_string(-99) == "HYMBA_UNKNOWN_STATUS"
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_heads=3), L.HYMBA_ERR_INVALID_ARG),
+    (dict(d_model=0), L.HYMBA_ERR_INVALID_ARG),
+    (dict(dtype=7), L.HYMBA_ERR_INVALID_ARG),
+    (dict(d_state=12), L.HYMBA_ERR_UNSUPPORTED),
+    (dict(head_dim=48), L.HYMBA_ERR_UNSUPPORTED),
+    (dict(dtype=L.HYMBA_BF16, head_dim=32), L.HYMBA_ERR_UNSUPPORTED),
+    (dict(dtype=L.HYMBA_BF16, head_dim=64, n_meta=200), L.HYMBA_ERR_UNSUPPORTED),
+    (dict(d_inner=60), L.HYMBA_ERR_UNSUPPORTED),
+])
+def test_create_rejects_bad_configs(kw, code):
+    cfg = _cfg(**kw)
+    assert L.hymba_layer_persistent_bytes(cfg) == 0
+    with pytest.raises(L.HymbaError) as e:
+        L.hymba_layer_create(cfg, _weights(), FAKE, 1 << 30)
+    assert e.value.status == code
+
+
+def test_create_checks_buffers():
+    cfg = _cfg()
+    n = L.hymba_layer_persistent_bytes(cfg)
+    with pytest.raises(L.HymbaError) as e:
+        L.hymba_layer_create(cfg, _weights(), FAKE, n - 1)
+    assert e.value.status == L.HYMBA_ERR_WORKSPACE
+    with pytest.raises(L.HymbaError) as e:
+        L.hymba_layer_create(cfg, _weights(), FAKE + 16, n)
+    assert e.value.status == L.HYMBA_ERR_INVALID_ARG
+    w = _weights()
+    w.w_o = None
+    with pytest.raises(L.HymbaError) as e:
+        L.hymba_layer_create(cfg, w, FAKE, n)
+    assert e.value.status == L.HYMBA_ERR_INVALID_ARG
+
+
+def test_bind_rules():
+    prod = _create(_cfg(own_kv=1))
+    cons = _create(_cfg(own_kv=0))
+    cons2 = _create(_cfg(own_kv=0))
+    other = _create(_cfg(own_kv=0, n_meta=5))
+    try:
+        for bad in [(cons, cons), (prod, cons), (cons, cons2), (other, prod)]:
+            with pytest.raises(L.HymbaError) as e:
+                L.hymba_kv_share_bind(*bad)
+            assert e.value.status == L.HYMBA_ERR_BIND
+        L.hymba_kv_share_bind(cons, prod)
+        with pytest.raises(L.HymbaError) as e:       # pairs only
+            L.hymba_kv_share_bind(cons2, prod)
+        assert e.value.status == L.HYMBA_ERR_BIND
+        L.hymba_kv_share_bind(cons, None)             # unbind frees the producer
+        L.hymba_kv_share_bind(cons2, prod)
+        wrong_window = _create(_cfg(own_kv=0, window=0))
+        with pytest.raises(L.HymbaError) as e:
+            L.hymba_kv_share_bind(wrong_window, prod)
+        assert e.value.status == L.HYMBA_ERR_BIND
+        L.hymba_layer_destroy(wrong_window)
+    finally:
+        for h in (prod, cons, cons2, other):
+            L.hymba_layer_destroy(h)
+
+
+def test_workspace_grows_with_tokens():
+    h = _create(_cfg())
+    try:
+        a = L.hymba_mixer_workspace_bytes(h, 1, 16)
+        b = L.hymba_mixer_workspace_bytes(h, 2, 16)
+        assert 0 < a < b
+        assert L.hymba_mixer_workspace_bytes(h, 0, 16) == 0
+    finally:
+        L.hymba_layer_destroy(h)
+
+
+def test_hot_calls_validate_before_device_work():
+    h = _create(_cfg())
+    cons = _create(_cfg(own_kv=0))
+    try:
+        ws = L.hymba_mixer_workspace_bytes(h, 1, 4)
+        with pytest.raises(L.HymbaError) as e:
+            L.hymba_mixer_prefill(h, FAKE, 1, 0, FAKE, None, None, FAKE, ws, None)
+        assert e.value.status == L.HYMBA_ERR_INVALID_ARG
+        with pytest.raises(L.HymbaError) as e:
+            L.hymba_mixer_prefill(h, FAKE, 1, 4, FAKE, None, None, FAKE, ws - 1, None)
+        assert e.value.status == L.HYMBA_ERR_WORKSPACE
+        with pytest.raises(L.HymbaError) as e:   # consumer without K/V
+            L.hymba_mixer_prefill(cons, FAKE, 1, 4, FAKE, None, None, FAKE, ws, None)
+        assert e.value.status == L.HYMBA_ERR_INVALID_ARG
+        kv = L.hymba_kv()
+        kv.k_cache = kv.v_cache = FAKE
+        kv.cache_len = 4                           # window 8 needs >= 8 slots
+        with pytest.raises(L.HymbaError) as e:
+            L.hymba_mixer_decode(h, FAKE, FAKE, 1, FAKE, kv, FAKE, FAKE, 1 << 30, None)
+        assert e.value.status == L.HYMBA_ERR_INVALID_ARG
+        with pytest.raises(L.HymbaError) as e:     # no cache at all
+            L.hymba_mixer_decode(h, FAKE, FAKE, 1, FAKE, None, FAKE, FAKE, 1 << 30, None)
+        assert e.value.status == L.HYMBA_ERR_INVALID_ARG
+        with pytest.raises(L.HymbaError) as e:
+            L.hymba_layer_meta_outputs(h)          # not prepared yet
+        assert e.value.status == L.HYMBA_ERR_INVALID_ARG
+    finally:
+        L.hymba_layer_destroy(h)
+        L.hymba_layer_destroy(cons)
+
+
+def test_kernel_entry_points_validate():
+    with pytest.raises(L.HymbaError) as e:
+        L.hymba_kernel_attention(L.HYMBA_BF16, FAKE, 64, FAKE, FAKE, 64, 64, FAKE, FAKE, 4, FAKE, 64, 1, 4, 4, 2,
+                                 32, 8, None)
+    assert e.value.status == L.HYMBA_ERR_UNSUPPORTED
+    with pytest.raises(L.HymbaError) as e:
+        L.hymba_kernel_selective_scan(L.HYMBA_F32, FAKE, FAKE, 8, FAKE, 8, FAKE, FAKE, FAKE, None, FAKE, 8, None,
+                                      1, 4, 8, 4, FAKE, 1 << 20, None)
+    assert e.value.status == L.HYMBA_ERR_UNSUPPORTED
+    with pytest.raises(L.HymbaError) as e:
+        L.hymba_kernel_selective_scan(L.HYMBA_BF16, FAKE, FAKE, 8, FAKE, 8, FAKE, FAKE, FAKE, None, FAKE, 8, None,
+                                      1, 4, 8, 8, FAKE, 1 << 20, None)
+    assert e.value.status == L.HYMBA_ERR_INVALID_ARG
+    with pytest.raises(L.HymbaError) as e:
+        L.hymba_kernel_epilogue(L.HYMBA_F32, FAKE, 12, FAKE, 12, FAKE, 12, FAKE, FAKE, FAKE, 12, 3, 12, 1e-6, None)
+    assert e.value.status == L.HYMBA_ERR_UNSUPPORTED
