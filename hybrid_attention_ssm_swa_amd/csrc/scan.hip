@@ -10,12 +10,8 @@
 //   y_t[c]    = sum_n C_t[n] * h_t[c, n] + D[c] * u_t[c]
 // The gate (y * SiLU(z)) is applied in the fused epilogue.
 //
-// Prefill mapping: one lane per (sequence, channel) with all N fp32 states in
-// VGPRs, walking the sequence in order; B_t and C_t are the same for every
-// channel of a token, so a wave reads them through the scalar unit (uniform
-// address) and every multiply takes them as SGPR operands.  exp uses
-// A2 = A * log2(e), precomputed once per layer, so each (t, c, n) costs one
-// v_exp_f32, two multiplies and two FMAs.  The diagonal recurrence is bound by
+// exp uses A2 = A * log2(e), precomputed once per layer, so each (t, c, n)
+// costs one v_exp_f32, two multiplies and two FMAs.  The diagonal recurrence is bound by
 // this VALU work rather than by memory (the Griffin summary, hyeon-jae.tistory.com
 // section 1, notes diagonal RNN layers are memory bound on TPU; here the
 // per-state exp dominates).
@@ -26,86 +22,145 @@ namespace hymba {
 
 namespace {
 
-// Raw (unconverted) inputs of one time step.  Loads of the next step are
-// issued into a second StepIn before the current step is computed and only
-// converted when that step runs, so their latency hides behind a step's VALU
-// work.  B/C are fp32 and wave-uniform: they land in SGPRs (scalar loads).
-template <typename CT, int N>
-struct StepIn {
-  CT u, dt;
-  float bc[2 * N];
-  __device__ __forceinline__ void load(const CT* up, const CT* dp, const float* bcp) {
-    u = *up;
-    dt = *dp;
-#pragma unroll
-    for (int i = 0; i < 2 * N; ++i) bc[i] = bcp[i];
-  }
-  __device__ __forceinline__ float uf() const { return static_cast<float>(u); }
-  __device__ __forceinline__ float dtf() const { return static_cast<float>(dt); }
-  __device__ __forceinline__ float b(int n) const { return bc[n]; }
-  __device__ __forceinline__ float c(int n) const { return bc[N + n]; }
-};
+// Prefill mapping.  A channel's N states are split over WPC = N / NS waves of
+// one workgroup (wave w owns states [w*NS, (w+1)*NS) of 64 consecutive
+// channels, one channel per lane), which gives WPC times more waves than
+// channels/64 and so fills every SIMD even at batch 16.  Time runs in chunks
+// of TC steps, and everything a chunk needs is fetched one chunk ahead so HBM
+// and L2 latency hide behind a chunk of arithmetic: u/dt into registers, the
+// wave's B/C columns (uniform across its lanes) into registers and then into
+// the wave's LDS slice, read back per step as broadcast LDS reads.  The
+// per-wave partial outputs of a chunk are summed across the WPC waves through
+// LDS once per chunk (double-buffered, one barrier per chunk).
+constexpr int kTC = 16;
 
-template <typename T, int N>
-__device__ __forceinline__ float scan_step(const StepIn<T, N>& in, const float (&a2)[N], float (&h)[N],
-                                           float Dc, float bias) {
-  const float uv = in.uf();
-  const float delta = softplus_f(in.dtf() + bias);
-  const float du = delta * uv;
-  float acc = Dc * uv;
-#pragma unroll
-  for (int n = 0; n < N; ++n) {
-    const float dA = fast_exp2(delta * a2[n]);
-    h[n] = fmaf(dA, h[n], du * in.b(n));
-    acc = fmaf(in.c(n), h[n], acc);
-  }
-  return acc;
-}
-
-template <typename T, int N>
-__global__ __launch_bounds__(64) void selective_scan_kernel(
+template <typename T, int N, int NS>
+__global__ __launch_bounds__(64 * (N / NS)) void selective_scan_kernel(
     const T* __restrict__ u, const T* __restrict__ dt, int64_t ld, const float* __restrict__ bc, int64_t ld_bc,
     const float* __restrict__ A2, const float* __restrict__ Dp, const float* __restrict__ dt_bias,
     const float* __restrict__ h0, int64_t h0_bstride, T* __restrict__ y, int64_t ldy,
     float* __restrict__ h_out, int T_len, int E) {
+  constexpr int WPC = N / NS;
+  constexpr int Q = NS / 4;                 // float4 per step of B (and of C)
+  constexpr int ITEMS = kTC * 2 * Q;        // float4 per chunk of this wave's B/C
+  constexpr int PER_LANE = (ITEMS + 63) / 64;
+  __shared__ float ys[2][WPC][kTC][64];
+  __shared__ float4 bcs[2][WPC][kTC][2 * Q];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int b = blockIdx.y;
-  const int c = blockIdx.x * 64 + threadIdx.x;
+  const int c = blockIdx.x * 64 + lane;
   const bool active = c < E;
   const int cc = active ? c : E - 1;
-  float a2[N], h[N];
+  const int n0 = wave * NS;
+  float a2[NS], h[NS];
 #pragma unroll
-  for (int n = 0; n < N; ++n) {
-    a2[n] = A2[(int64_t)cc * N + n];
-    h[n] = h0 ? h0[b * h0_bstride + (int64_t)cc * N + n] : 0.f;
+  for (int n = 0; n < NS; ++n) {
+    a2[n] = A2[(int64_t)cc * N + n0 + n];
+    h[n] = h0 ? h0[b * h0_bstride + (int64_t)cc * N + n0 + n] : 0.f;
   }
-  const float Dc = Dp[cc], bias = dt_bias[cc];
+  const float Dc = wave == 0 ? Dp[cc] : 0.f;   // the skip term enters one partial sum only
+  const float bias = dt_bias[cc];
   const int64_t row0 = (int64_t)b * T_len;
   const T* up = u + row0 * ld + cc;
   const T* dp = dt + row0 * ld + cc;
-  const float* bcp = bc + row0 * ld_bc;
-  T* yp = y + row0 * ldy + cc;
-
-  // Prefetches are unconditional (the row index is clamped to the last row) so
-  // the number of loads in flight is the same on every path and the wait before
-  // a step only covers that step's own inputs.
-  StepIn<T, N> s0, s1;
-  s0.load(up, dp, bcp);
+  const float* bcrow = bc + row0 * ld_bc;
+  T* yrow = y + row0 * ldy + c;
   const int last = T_len - 1;
-  for (int t = 0; t < T_len; t += 2) {
-    const int64_t r1 = min(t + 1, last);
-    s1.load(up + r1 * ld, dp + r1 * ld, bcp + r1 * ld_bc);
-    const float y0 = scan_step<T, N>(s0, a2, h, Dc, bias);
-    if (active) Elem<T>::store(yp + (int64_t)t * ldy, y0);
-    if (t + 1 >= T_len) break;
-    const int64_t r2 = min(t + 2, last);
-    s0.load(up + r2 * ld, dp + r2 * ld, bcp + r2 * ld_bc);
-    const float y1 = scan_step<T, N>(s1, a2, h, Dc, bias);
-    if (active) Elem<T>::store(yp + (int64_t)(t + 1) * ldy, y1);
+
+  // B/C item i of a chunk starting at t: step i / (2Q); j = i % (2Q) < Q -> B[n0 + 4j..],
+  // else C[n0 + 4(j - Q)..]
+  auto fetch_bc = [&](float4 (&r)[PER_LANE], int t) {
+#pragma unroll
+    for (int k = 0; k < PER_LANE; ++k) {
+      const int i = lane + 64 * k;
+      if (i < ITEMS) {
+        const int st = i / (2 * Q), j = i % (2 * Q);
+        const int64_t row = min(t + st, last);
+        const int col = j < Q ? n0 + 4 * j : N + n0 + 4 * (j - Q);
+        r[k] = *reinterpret_cast<const float4*>(bcrow + row * ld_bc + col);
+      }
+    }
+  };
+  auto stash_bc = [&](const float4 (&r)[PER_LANE], int bb) {
+#pragma unroll
+    for (int k = 0; k < PER_LANE; ++k) {
+      const int i = lane + 64 * k;
+      if (i < ITEMS) bcs[bb][wave][i / (2 * Q)][i % (2 * Q)] = r[k];
+    }
+  };
+
+  T un[kTC], dn[kTC];
+  float4 bcr[PER_LANE];
+#pragma unroll
+  for (int s = 0; s < kTC; ++s) {
+    const int64_t r = min(s, last);
+    un[s] = up[r * ld];
+    dn[s] = dp[r * ld];
+  }
+  fetch_bc(bcr, 0);
+  int buf = 0;
+  stash_bc(bcr, buf);
+  for (int t0 = 0; t0 < T_len; t0 += kTC) {
+    T uc[kTC], dc[kTC];
+#pragma unroll
+    for (int s = 0; s < kTC; ++s) { uc[s] = un[s]; dc[s] = dn[s]; }
+    // everything for the next chunk (rows clamped, always in bounds)
+#pragma unroll
+    for (int s = 0; s < kTC; ++s) {
+      const int64_t r = min(t0 + kTC + s, last);
+      un[s] = up[r * ld];
+      dn[s] = dp[r * ld];
+    }
+    fetch_bc(bcr, t0 + kTC);
+    const int len = min(kTC, T_len - t0);
+    float part[kTC];
+#pragma unroll
+    for (int s = 0; s < kTC; ++s) {
+      part[s] = 0.f;
+      if (s < len) {
+        float bb[NS], cb[NS];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+          const float4 vb = bcs[buf][wave][s][q], vc = bcs[buf][wave][s][Q + q];
+          bb[4 * q] = vb.x; bb[4 * q + 1] = vb.y; bb[4 * q + 2] = vb.z; bb[4 * q + 3] = vb.w;
+          cb[4 * q] = vc.x; cb[4 * q + 1] = vc.y; cb[4 * q + 2] = vc.z; cb[4 * q + 3] = vc.w;
+        }
+        const float uv = static_cast<float>(uc[s]);
+        const float delta = softplus_f(static_cast<float>(dc[s]) + bias);
+        const float du = delta * uv;
+        float acc = Dc * uv;
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+          const float dA = fast_exp2(delta * a2[n]);
+          h[n] = fmaf(dA, h[n], du * bb[n]);
+          acc = fmaf(cb[n], h[n], acc);
+        }
+        part[s] = acc;
+      }
+    }
+    if constexpr (WPC == 1) {
+#pragma unroll
+      for (int s = 0; s < kTC; ++s)
+        if (s < len && active) Elem<T>::store(yrow + (int64_t)(t0 + s) * ldy, part[s]);
+    } else {
+#pragma unroll
+      for (int s = 0; s < kTC; ++s) ys[buf][wave][s][lane] = part[s];
+      __syncthreads();
+      for (int s = wave; s < len; s += WPC) {
+        float yv = 0.f;
+#pragma unroll
+        for (int w = 0; w < WPC; ++w) yv += ys[buf][w][s][lane];
+        if (active) Elem<T>::store(yrow + (int64_t)(t0 + s) * ldy, yv);
+      }
+    }
+    buf ^= 1;
+    stash_bc(bcr, buf);   // this wave's own slice: ordered by the wave's LDS queue
   }
   if (active && h_out) {
-    float* ho = h_out + ((int64_t)b * E + c) * N;
+    float* ho = h_out + ((int64_t)b * E + c) * N + n0;
 #pragma unroll
-    for (int n = 0; n < N; ++n) ho[n] = h[n];
+    for (int n = 0; n < NS; ++n) ho[n] = h[n];
   }
 }
 
@@ -148,19 +203,34 @@ __global__ __launch_bounds__(256) void ssm_step_kernel(StepArgs<T> a) {
   }
 }
 
+// States per wave: the fewest waves per channel group (largest NS, least
+// per-step overhead) that still gives ~1.5 waves per SIMD of the 1024.
+inline int scan_states_per_wave(int B, int E, int N) {
+  const int64_t groups = (int64_t)B * ceil_div(E, 64);
+  int ns = N;
+  while (ns > 4 && groups * (N / ns) < 1536) ns >>= 1;
+  return ns;
+}
+
+template <typename T, int N, int NS>
+void scan_launch(const ScanArgs<T>& a, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>(ceil_div(a.E, 64)), a.B), block(64 * (N / NS));
+  hipLaunchKernelGGL((selective_scan_kernel<T, N, NS>), grid, block, 0, s, a.u, a.dt, a.ld, a.bc, a.ld_bc, a.A2,
+                     a.D, a.dt_bias, a.h0, a.h0_bstride, a.y, a.ldy, a.h_out, a.T, a.E);
+}
+
 template <typename T>
 hipError_t scan_dispatch(const ScanArgs<T>& a, hipStream_t s) {
-  dim3 grid(static_cast<unsigned>(ceil_div(a.E, 64)), a.B), block(64);
-  switch (a.N) {
-    case 8:
-      hipLaunchKernelGGL((selective_scan_kernel<T, 8>), grid, block, 0, s, a.u, a.dt, a.ld, a.bc, a.ld_bc, a.A2,
-                         a.D, a.dt_bias, a.h0, a.h0_bstride, a.y, a.ldy, a.h_out, a.T, a.E);
-      break;
-    case 16:
-      hipLaunchKernelGGL((selective_scan_kernel<T, 16>), grid, block, 0, s, a.u, a.dt, a.ld, a.bc, a.ld_bc, a.A2,
-                         a.D, a.dt_bias, a.h0, a.h0_bstride, a.y, a.ldy, a.h_out, a.T, a.E);
-      break;
-    default: return hipErrorInvalidValue;
+  const int ns = scan_states_per_wave(a.B, a.E, a.N);
+  if (a.N == 8) {
+    if (ns == 8) scan_launch<T, 8, 8>(a, s);
+    else scan_launch<T, 8, 4>(a, s);
+  } else if (a.N == 16) {
+    if (ns == 16) scan_launch<T, 16, 16>(a, s);
+    else if (ns == 8) scan_launch<T, 16, 8>(a, s);
+    else scan_launch<T, 16, 4>(a, s);
+  } else {
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
