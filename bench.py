@@ -20,9 +20,11 @@ prepared before it (it is input independent and computed once per layer).
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
+import shlex
 import sys
 import time
 
@@ -36,7 +38,7 @@ PEAK_F32_VEC = 157.3e12    # fp32 vector FLOP/s (packed); non-packed lane-op rat
 N_CU, CLK = 256, 2.4e9
 PEAK_VALU_LANE_OPS = N_CU * 64 * CLK        # non-packed fp32 lane-ops/s (39.3 T)
 
-STAGES = ["in_proj", "kv_write", "attention", "w_o", "ssm", "epilogue", "out_proj"]
+STAGES = ["in_proj", "kv_write", "attention", "w_o", "ssm", "epilogue", "out_proj", "convert"]
 
 
 def log(*a):
@@ -55,6 +57,12 @@ def visible_keys(s, T):
     return T * M + ramp * (ramp + 1) // 2 + full * W
 
 
+def conversion_bytes(s, R):
+    """bf16 layers: x bf16 -> fp16 (read 2 + write 2 B per element), the B/C columns fp16 -> fp32
+    (2 + 4), the output fp32 -> bf16 (4 + 2)."""
+    return float(R * s.d_model * 4 + R * 2 * s.d_state * 6 + R * s.d_model * 6)
+
+
 def prefill_work(s, B, T):
     es = 2 if s.dtype == "bf16" else 4
     R = B * T
@@ -69,6 +77,8 @@ def prefill_work(s, B, T):
         # Ao, y, z read; F written
         "epilogue": ("hbm", float(R * E * es * 4)),
     }
+    if s.dtype == "bf16":
+        w["convert"] = ("hbm", conversion_bytes(s, R))
     if s.own_kv:
         w["kv_write"] = ("hbm", float(R * s.n_kv_heads * s.head_dim * es * 2 * 2))
     return w
@@ -88,6 +98,8 @@ def decode_work(s, B, pos, cache_len):
         "epilogue": ("hbm", float(B * E * es * 4)),
         "out_proj": ("hbm", float(d * E * es)),
     }
+    if s.dtype == "bf16":
+        w["convert"] = ("hbm", conversion_bytes(s, B))
     if s.own_kv:
         w["kv_write"] = ("hbm", float(B * kvb * 2 * 2))
     return w
@@ -116,7 +128,15 @@ def scan_alu_entry(s, B, T, ms):
 
 # --- traffic measured by rocprofv3 counters (optional, committed under profiles/) ---------
 
-KERNEL_SOURCES = {"attention": "attn_prefill.hip", "ssm": "scan.hip", "epilogue": "epilogue.hip"}
+# source whose change invalidates a stage's recorded counters (GEMMs: the plan selection code)
+KERNEL_SOURCES = {"attention": "attn_prefill.hip", "ssm": "scan.hip", "epilogue": "epilogue.hip",
+                  "in_proj": "gemm_blaslt.cpp", "w_o": "gemm_blaslt.cpp", "out_proj": "gemm_blaslt.cpp",
+                  "convert": "convert.hip", "kv_write": "decode.hip"}
+
+
+def source_sha(stage):
+    src = KERNEL_SOURCES[stage]
+    return hashlib.sha256(open(os.path.join(ROOT, "hybrid_attention_ssm_swa_amd", "csrc", src), "rb").read()).hexdigest()
 
 
 def measured_traffic(stage):
@@ -130,19 +150,15 @@ def measured_traffic(stage):
         return None
     if not rec:
         return None
-    sha = hashlib.sha256(open(os.path.join(ROOT, "hybrid_attention_ssm_swa_amd", "csrc", src), "rb").read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    if rec.get("source_sha256") != source_sha(stage):
         return None      # the kernel changed since the counters were taken
     return rec.get("bytes_per_launch")
 
 
 # --- GPU timing ------------------------------------------------------------------------
 
-def timed(fn, steps, warmup):
+def _time_loop(fn, steps):
     import torch
-    for _ in range(warmup):
-        fn(0)
-    torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -153,23 +169,25 @@ def timed(fn, steps, warmup):
     return t0.elapsed_time(t1) / steps
 
 
-def stage_profile(layers, fn, steps):
-    """Mean per-stage ms over `steps` calls, from the library's HIP events."""
+def timed(layers, fn, steps, warmup):
+    """Runs `warmup` untimed steps, then times exactly `steps` steps between two events on the
+    launch stream (the throughput figure).  A second timed region of `steps` steps follows with
+    the library recording a HIP event pair around every kernel of each layer on the same stream;
+    the per-stage means come from it (the event pairs slow a step by a few percent, so the
+    throughput comes from the first region).  Returns (ms per step, ms per step while recording,
+    per-layer list of mean ms per call for each stage)."""
     import torch
     from hybrid_attention_ssm_swa_amd import _lib as L
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    ms = _time_loop(fn, steps)
     for lay in layers:
         L.hymba_layer_profile(lay.handle, True)
-    sums = [[0.0] * len(STAGES) for _ in layers]
-    for i in range(steps):
-        fn(i)
-        torch.cuda.synchronize()
-        for j, lay in enumerate(layers):
-            ms = L.hymba_layer_profile_read(lay.handle)
-            for k in range(len(STAGES)):
-                sums[j][k] += ms[k]
+    ms_rec = _time_loop(fn, steps)
     for lay in layers:
         L.hymba_layer_profile(lay.handle, False)
-    return [[x / steps for x in row] for row in sums]
+    return ms, ms_rec, [L.hymba_layer_profile_read(lay.handle) for lay in layers]
 
 
 def bench_prefill(cfg_id, steps, warmup):
@@ -194,8 +212,7 @@ def bench_prefill(cfg_id, steps, warmup):
     y = torch.empty_like(x)
     layer.prepare(kv)
     torch.cuda.synchronize()
-    ms = timed(lambda i: layer.prefill(x, kv, None, y), steps, warmup)
-    stage_ms = stage_profile([layer], lambda i: layer.prefill(x, kv, None, y), steps)[0]
+    ms, ms_rec, (stage_ms,) = timed([layer], lambda i: layer.prefill(x, kv, None, y), steps, warmup)
     B, T = cfg.batch, cfg.seq
     work = prefill_work(s, B, T)
     ents = []
@@ -205,7 +222,8 @@ def bench_prefill(cfg_id, steps, warmup):
             e["traffic"] = measured_traffic(name)
             ents.append(e)
     ents.append(scan_alu_entry(s, B, T, stage_ms[STAGES.index("ssm")]))
-    out = {"tokens_per_s": B * T / (ms * 1e-3), "ms_per_step": ms, "batch": B, "seq": T,
+    out = {"tokens_per_s": B * T / (ms * 1e-3), "ms_per_step": ms, "ms_per_step_recording": ms_rec,
+           "batch": B, "seq": T,
            "stage_ms": dict(zip(STAGES, stage_ms)), "kernels": ents}
     layer.close()
     del x, y, keep
@@ -244,15 +262,15 @@ def bench_decode(cfg_id, steps, warmup):
         prod.decode(x, pos, kv, stp, yp)
         cons.decode(xc, pos, kv, stc, yc)
 
-    ms = timed(step, steps, warmup)
-    pst, cst = stage_profile([prod, cons], step, steps)
+    ms, ms_rec, (pst, cst) = timed([prod, cons], step, steps, warmup)
     B, p, C = cfg.batch, cfg.seq, s.window
     ents = {}
     for role, lay_s, st in (("producer", s, pst), ("consumer", sc, cst)):
         work = decode_work(lay_s, B, p, C)
         ents[role] = [dict(roofline_entry(n, work[n][0], work[n][1], st[k]), traffic=None)
                       for k, n in enumerate(STAGES) if n in work and st[k] > 0]
-    out = {"tokens_per_s_per_layer": B / (ms * 1e-3 / 2), "ms_per_pair_step": ms, "batch": B, "pos": p,
+    out = {"tokens_per_s_per_layer": B / (ms * 1e-3 / 2), "ms_per_pair_step": ms,
+           "ms_per_pair_step_recording": ms_rec, "batch": B, "pos": p,
            "producer_stage_ms": dict(zip(STAGES, pst)), "consumer_stage_ms": dict(zip(STAGES, cst)),
            "kernels": ents}
     prod.close()
@@ -260,6 +278,140 @@ def bench_decode(cfg_id, steps, warmup):
     del sets
     torch.cuda.empty_cache()
     return out
+
+
+# --- rocprofv3 summaries (run on the host after the profiled runs) ----------------------------
+
+COPY_PROBE_BYTES = 1 << 30      # the plain copy kernel (torch.neg over fp32) reads and writes this much
+
+
+def copy_probe():
+    """A plain elementwise kernel of known traffic, to scale the HBM counters by."""
+    import torch
+    a = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
+
+
+def _kernel_stage(name):
+    for key, st in (("swa_meta_attn", "attention"), ("attn_f32", "attention"), ("decode_attn", "attention"),
+                    ("decode_combine", "attention"), ("selective_scan", "ssm"), ("ssm_step", "ssm"),
+                    ("epilogue_kernel", "epilogue"), ("convert_kernel", "convert"), ("kv_write", "kv_write"),
+                    ("neg_kernel", "copy_probe")):
+        if key in name:
+            return st
+    if "Cijk" in name or "gemm" in name.lower():   # hipBLASLt (Tensile) kernels
+        return "gemm"
+    return "other"
+
+
+def _csv_rows(root, suffix):
+    rows = []
+    for dp, _, fs in os.walk(root):
+        for f in sorted(fs):
+            if f.endswith(suffix):
+                with open(os.path.join(dp, f), newline="") as fh:
+                    rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _grid(r):
+    if "Grid_Size_X" in r:
+        return "x".join(r[k] for k in ("Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"))
+    return r.get("Grid_Size", "?")
+
+
+def _label(rows):
+    """Dispatches in issue order with their stage.  A GEMM takes its stage from the kernel issued
+    before it: after the scan it is W_O, after the epilogue the output projection, otherwise
+    (after an input conversion or at the start of a call) the input projection."""
+    out, prev = [], None
+    for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
+        st = _kernel_stage(r["Kernel_Name"])
+        if st == "gemm":
+            st = {"ssm": "w_o", "epilogue": "out_proj"}.get(prev, "in_proj")
+        out.append((st, r))
+        prev = st
+    return out
+
+
+def _main_groups(labelled, value):
+    """Per stage, the (kernel, grid) group with the most dispatches (the timed steps; the one-off
+    meta-prefix pass runs the same kernels on a smaller grid): {stage: (name, grid, calls, mean)}.
+    The conversions of a bf16 call are three kernels: their means are summed."""
+    groups = {}
+    for st, r in labelled:
+        groups.setdefault(st, {}).setdefault((r["Kernel_Name"], _grid(r)), []).append(value(r))
+    best = {}
+    for st, g in groups.items():
+        (name, grid), vals = max(g.items(), key=lambda kv: (len(kv[1]), sum(kv[1])))
+        if st == "convert":
+            top = [v for v in g.values() if len(v) == len(vals)]
+            best[st] = ("convert_kernel (%d kinds)" % len(top), "several", len(vals),
+                        sum(sum(v) / len(v) for v in top))
+        else:
+            best[st] = (name, grid, len(vals), sum(vals) / len(vals))
+    return best
+
+
+def summarize_rocprof(trace_dir, bench_json, fetch_dir, write_dir, command, out_txt, out_json):
+    lines = [f"# rocprofv3 summary: {command['title']}",
+             "# profiled command (repository root, one MI355X):",
+             f"#   {command['trace']}",
+             "# summarized on the host with:",
+             f"#   {command['summary']}", ""]
+    trace = _label(_csv_rows(trace_dir, "kernel_trace.csv"))
+    per_stage = _main_groups(trace, lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    bench = None
+    if bench_json and os.path.exists(bench_json):
+        txt = [l for l in open(bench_json).read().splitlines() if l.startswith("{")]
+        bench = json.loads(txt[-1]) if txt else None
+    lines.append("## per-stage kernel of the timed steps (kernel_trace.csv, dispatch-order attribution)")
+    lines.append(f"{'stage':<10} {'calls':>5} {'avg_us':>10} {'bench_us':>10}  grid            kernel")
+    for st in STAGES + ["copy_probe"]:
+        if st not in per_stage:
+            continue
+        name, grid, calls, avg = per_stage[st]
+        bus = f"{bench['stage_ms'][st] * 1e3:.1f}" if bench and st in bench.get("stage_ms", {}) else ""
+        lines.append(f"{st:<10} {calls:>5} {avg:>10.1f} {bus:>10}  {grid:<15} {name[:90]}")
+    stats = _csv_rows(trace_dir, "kernel_stats.csv")
+    if stats:
+        lines += ["", "## kernel_stats.csv (top 12 by total time)",
+                  f"{'calls':>6} {'total_ms':>10} {'avg_us':>10} {'pct':>6}  kernel"]
+        stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
+        for r in stats[:12]:
+            lines.append(f"{int(r['Calls']):>6} {float(r['TotalDurationNs']) / 1e6:>10.3f} "
+                         f"{float(r['AverageNs']) / 1e3:>10.1f} {float(r['Percentage']):>6.2f}  {r['Name'][:90]}")
+    traffic = None
+    if fetch_dir and write_dir:
+        def counter(d, cname):
+            rows = [r for r in _csv_rows(d, "counter_collection.csv") if r["Counter_Name"] == cname]
+            return _main_groups(_label(rows), lambda r: float(r["Counter_Value"]))
+        fetch, write = counter(fetch_dir, "FETCH_SIZE"), counter(write_dir, "WRITE_SIZE")
+        f_fetch = COPY_PROBE_BYTES / (fetch["copy_probe"][3] * 1024)
+        f_write = COPY_PROBE_BYTES / (write["copy_probe"][3] * 1024)
+        traffic = {"copy_probe": {"bytes_read": COPY_PROBE_BYTES, "bytes_written": COPY_PROBE_BYTES,
+                                  "fetch_kib": fetch["copy_probe"][3], "write_kib": write["copy_probe"][3],
+                                  "fetch_scale": f_fetch, "write_scale": f_write},
+                   "command": command}
+        lines += ["", "## HBM traffic per launch (FETCH_SIZE and WRITE_SIZE in separate passes, KiB per dispatch,",
+                  f"## scaled by the plain copy kernel: fetch x{f_fetch:.4f}, write x{f_write:.4f})",
+                  f"{'stage':<10} {'fetch_KiB':>12} {'write_KiB':>12} {'bytes/launch':>14}"]
+        for st in STAGES:
+            if st in fetch and st in write:
+                fk, wk = fetch[st][3], write[st][3]
+                b = fk * 1024 * f_fetch + wk * 1024 * f_write
+                traffic[st] = {"kernel": fetch[st][0][:120], "grid": fetch[st][1], "fetch_kib": fk, "write_kib": wk,
+                               "bytes_per_launch": b, "source_sha256": source_sha(st)}
+                lines.append(f"{st:<10} {fk:>12.0f} {wk:>12.0f} {b:>14.4g}")
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+    if traffic is not None and out_json:
+        json.dump(traffic, open(out_json, "w"), indent=1)
+    print("\n".join(lines))
 
 
 # --- CPU baseline: the fp64 oracle on a bounded sample ---------------------------------------
@@ -290,7 +442,23 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--main-only", action="store_true", help="time only the 8K prefill workload")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain copy kernel of known size (for scaling HBM counters)")
+    ap.add_argument("--summarize-rocprof", metavar="TRACE_DIR",
+                    help="host only: write profiles/ summaries from rocprofv3 csv output and exit")
+    ap.add_argument("--bench-json", help="with --summarize-rocprof: the profiled run's JSON line")
+    ap.add_argument("--pmc-fetch", help="with --summarize-rocprof: rocprofv3 --pmc FETCH_SIZE output dir")
+    ap.add_argument("--pmc-write", help="with --summarize-rocprof: rocprofv3 --pmc WRITE_SIZE output dir")
+    ap.add_argument("--profile-cmd", help="with --summarize-rocprof: the profiled command, for the header")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        cmd = {"title": "1.5B-shaped SWA mixer layer, 8K prefill (B=16 x 8192 + 128 meta), K/V handed in",
+               "trace": args.profile_cmd or "(not given)",
+               "summary": "python3 " + shlex.join(os.path.relpath(a) if os.path.exists(a) else a for a in sys.argv)}
+        summarize_rocprof(args.summarize_rocprof, args.bench_json, args.pmc_fetch, args.pmc_write, cmd,
+                          os.path.join(ROOT, "profiles", "kernels_swa8k_prefill.txt"),
+                          os.path.join(ROOT, "profiles", "pmc_traffic.json"))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -301,6 +469,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
 
+    if args.copy_probe:
+        copy_probe()
     main_run = bench_prefill(2, args.steps, args.warmup)
     log(f"[bench] 8K SWA prefill: {main_run['tokens_per_s']:.0f} tok/s, {main_run['ms_per_step']:.3f} ms/step")
     workloads = {}

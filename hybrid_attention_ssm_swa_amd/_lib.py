@@ -33,7 +33,7 @@ EXPORTED = [
     "hymba_kernel_selective_scan", "hymba_kernel_epilogue",
     "hymba_layer_profile", "hymba_layer_profile_read", "hymba_stage_name",
 ]
-HYMBA_N_STAGES = 7
+HYMBA_N_STAGES = 8
 
 
 class HymbaError(RuntimeError):
@@ -203,7 +203,8 @@ def hymba_layer_profile(layer: int, enable: bool) -> None:
 
 
 def hymba_layer_profile_read(layer: int):
-    """Per-stage milliseconds of the layer's last call (list of HYMBA_N_STAGES floats)."""
+    """Mean per-call milliseconds of each stage over the calls recorded since profiling was enabled
+    (list of HYMBA_N_STAGES floats)."""
     buf = (c_float * HYMBA_N_STAGES)()
     _check(load_library().hymba_layer_profile_read(layer, buf, HYMBA_N_STAGES))
     return [float(x) for x in buf]

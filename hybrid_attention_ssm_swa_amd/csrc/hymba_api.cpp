@@ -18,6 +18,7 @@
 #include <cstdio>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "gemm_blaslt.h"
 #include "kernels.h"
@@ -44,12 +45,13 @@ struct hymba_layer {
   const void* prep_vmeta = nullptr;
   // column offsets of the shared projection
   int64_t n_in = 0, off_k = 0, off_v = 0, off_u = 0, off_z = 0, off_dt = 0, off_b = 0;
-  // stage timing
+  // stage timing: a pool of begin/end event pairs, one pair per timed interval of each hot call
   bool profiling = false;
-  bool ev_ready = false;
-  hipEvent_t ev_begin[HYMBA_N_STAGES] = {};
-  hipEvent_t ev_end[HYMBA_N_STAGES] = {};
-  bool ev_used[HYMBA_N_STAGES] = {};
+  std::vector<hipEvent_t> ev;          // 2 * kProfPairs events once profiling was first enabled
+  std::vector<int8_t> ev_stage;        // stage of each used pair
+  int ev_next = 0;                     // pairs used since profiling was enabled
+  int prof_calls = 0;                  // prefill/decode calls recorded since then
+  bool prof_overflow = false;
 };
 
 namespace {
@@ -82,23 +84,27 @@ int32_t hip_fail(hipError_t e, const char* what) {
     if (s_ != HYMBA_OK) return s_;  \
   } while (0)
 
-// Records begin/end events of one stage when the layer is profiling.
+constexpr int kProfPairs = 1024;
+
+// Brackets one stage interval with a pair of events from the layer's pool when it is profiling.
 struct StageTimer {
-  const hymba_layer& L;
-  int stage;
+  hymba_layer& L;
   hipStream_t s;
-  StageTimer(const hymba_layer& l, int st, hipStream_t stream) : L(l), stage(st), s(stream) {
-    if (L.profiling) {
-      hipEventRecord(L.ev_begin[stage], s);
-      const_cast<hymba_layer&>(L).ev_used[stage] = true;
-    }
+  int pair = -1;
+  StageTimer(const hymba_layer& l, int stage, hipStream_t stream) : L(const_cast<hymba_layer&>(l)), s(stream) {
+    if (!L.profiling) return;
+    if (L.ev_next >= kProfPairs) { L.prof_overflow = true; return; }
+    pair = L.ev_next++;
+    L.ev_stage[pair] = static_cast<int8_t>(stage);
+    hipEventRecord(L.ev[2 * pair], s);
   }
   ~StageTimer() {
-    if (L.profiling) hipEventRecord(L.ev_end[stage], s);
+    if (pair >= 0) hipEventRecord(L.ev[2 * pair + 1], s);
   }
 };
-enum { ST_IN_PROJ = 0, ST_KV = 1, ST_ATTN = 2, ST_WO = 3, ST_SSM = 4, ST_EPI = 5, ST_OUT = 6 };
-const char* kStageNames[HYMBA_N_STAGES] = {"in_proj", "kv_write", "attention", "w_o", "ssm", "epilogue", "out_proj"};
+enum { ST_IN_PROJ = 0, ST_KV = 1, ST_ATTN = 2, ST_WO = 3, ST_SSM = 4, ST_EPI = 5, ST_OUT = 6, ST_CVT = 7 };
+const char* kStageNames[HYMBA_N_STAGES] = {"in_proj", "kv_write", "attention", "w_o",
+                                           "ssm",     "epilogue", "out_proj",  "convert"};
 
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -245,19 +251,26 @@ template <typename CT>
 int32_t in_projection(const hymba_layer& L, const void* x, int64_t rows, char* ws, const WsLayout& wl,
                       hipStream_t s) {
   const hymba_layer_cfg& c = L.cfg;
-  StageTimer st(L, ST_IN_PROJ, s);
   if (is_bf16(c)) {
     half_t* x16 = reinterpret_cast<half_t*>(ws + wl.X16);
-    HIP_TRY(launch_convert(static_cast<const bf16_t*>(x), c.d_model, x16, c.d_model, rows, c.d_model, s),
-            "input conversion");
-    STATUS_TRY(project(L, x16, c.d_model, L.w_in16, c.d_model, ws + wl.P, L.n_in, rows, L.n_in, c.d_model, false,
-                       ws, wl, s));
-    // B/C columns as fp32 for the scan's scalar loads
+    {
+      StageTimer st(L, ST_CVT, s);
+      HIP_TRY(launch_convert(static_cast<const bf16_t*>(x), c.d_model, x16, c.d_model, rows, c.d_model, s),
+              "input conversion");
+    }
+    {
+      StageTimer st(L, ST_IN_PROJ, s);
+      STATUS_TRY(project(L, x16, c.d_model, L.w_in16, c.d_model, ws + wl.P, L.n_in, rows, L.n_in, c.d_model,
+                         false, ws, wl, s));
+    }
+    // B/C columns as fp32 for the scan
+    StageTimer st(L, ST_CVT, s);
     HIP_TRY(launch_convert(reinterpret_cast<const half_t*>(ws + wl.P) + L.off_b, L.n_in,
                            reinterpret_cast<float*>(ws + wl.bc32), 2 * c.d_state, rows, 2 * c.d_state, s),
             "B/C conversion");
     return HYMBA_OK;
   }
+  StageTimer st(L, ST_IN_PROJ, s);
   return project(L, x, c.d_model, L.w.w_in, c.d_model, ws + wl.P, L.n_in, rows, L.n_in, c.d_model, false, ws, wl,
                  s);
 }
@@ -285,15 +298,19 @@ int32_t tail(const hymba_layer& L, char* ws, const WsLayout& wl, int64_t rows, v
     e.rows = rows; e.E = c.d_inner; e.eps = c.rms_eps;
     HIP_TRY(launch_epilogue(e, s), "epilogue launch");
   }
-  StageTimer st(L, ST_OUT, s);
   if (b16) {
     float* y32 = reinterpret_cast<float*>(ws + wl.Y32);
-    STATUS_TRY(project(L, ws + wl.F, c.d_inner, L.w_out16, c.d_inner, y32, c.d_model, rows, c.d_model, c.d_inner,
-                       true, ws, wl, s));
+    {
+      StageTimer st(L, ST_OUT, s);
+      STATUS_TRY(project(L, ws + wl.F, c.d_inner, L.w_out16, c.d_inner, y32, c.d_model, rows, c.d_model,
+                         c.d_inner, true, ws, wl, s));
+    }
+    StageTimer st(L, ST_CVT, s);
     HIP_TRY(launch_convert(y32, c.d_model, static_cast<bf16_t*>(y_out), c.d_model, rows, c.d_model, s),
             "output conversion");
     return HYMBA_OK;
   }
+  StageTimer st(L, ST_OUT, s);
   return project(L, ws + wl.F, c.d_inner, L.w.w_out, c.d_inner, y_out, c.d_model, rows, c.d_model, c.d_inner,
                  false, ws, wl, s);
 }
@@ -380,13 +397,17 @@ int32_t ensure_prepared(hymba_layer& L, const hymba_kv* kv, char* ws, const WsLa
       (kv->k_meta != L.prep_kmeta || kv->v_meta != L.prep_vmeta))
     L.prepared = false;   // an unbound consumer was handed different meta K/V
   if (L.prepared) return HYMBA_OK;
-  return is_bf16(L.cfg) ? prepare_impl<half_t>(L, kv, ws, wl, s) : prepare_impl<float>(L, kv, ws, wl, s);
+  const bool prof = L.profiling;   // the one-off meta-prefix pass is not part of a call's stage timings
+  L.profiling = false;
+  const int32_t r = is_bf16(L.cfg) ? prepare_impl<half_t>(L, kv, ws, wl, s) : prepare_impl<float>(L, kv, ws, wl, s);
+  L.profiling = prof;
+  return r;
 }
 
 template <typename CT>
 int32_t prefill_impl(hymba_layer& L, const void* x, int B, int T_, void* y, const hymba_kv* kv, float* state_out,
                      char* ws, const WsLayout& wl, hipStream_t s) {
-  for (bool& u : L.ev_used) u = false;
+  if (L.profiling) ++L.prof_calls;
   const hymba_layer_cfg& c = L.cfg;
   const int64_t rows = (int64_t)B * T_;
   const int64_t kvw = (int64_t)c.n_kv_heads * c.head_dim;
@@ -428,7 +449,7 @@ int32_t prefill_impl(hymba_layer& L, const void* x, int B, int T_, void* y, cons
 template <typename CT>
 int32_t decode_impl(hymba_layer& L, const void* x, const int64_t* pos, int B, void* y, const hymba_kv* kv,
                     float* state, char* ws, const WsLayout& wl, hipStream_t s) {
-  for (bool& u : L.ev_used) u = false;
+  if (L.profiling) ++L.prof_calls;
   const hymba_layer_cfg& c = L.cfg;
   STATUS_TRY(in_projection<CT>(L, x, B, ws, wl, s));
   const CT* P = reinterpret_cast<const CT*>(ws + wl.P);
@@ -527,12 +548,7 @@ int32_t hymba_layer_create(const hymba_layer_cfg* cfg, const hymba_layer_weights
 
 void hymba_layer_destroy(hymba_layer* L) {
   if (!L) return;
-  if (L->ev_ready) {
-    for (int i = 0; i < HYMBA_N_STAGES; ++i) {
-      hipEventDestroy(L->ev_begin[i]);
-      hipEventDestroy(L->ev_end[i]);
-    }
-  }
+  for (hipEvent_t e : L->ev) hipEventDestroy(e);
   if (L->producer && L->producer->consumer == L) const_cast<hymba_layer*>(L->producer)->consumer = nullptr;
   if (L->consumer && L->consumer->producer == L) const_cast<hymba_layer*>(L->consumer)->producer = nullptr;
   delete L;
@@ -639,27 +655,44 @@ int32_t hymba_layer_meta_outputs(const hymba_layer* L, const void** k_meta, cons
 
 int32_t hymba_layer_profile(hymba_layer* L, int32_t enable) {
   if (!L) return fail(HYMBA_ERR_INVALID_ARG, "layer is NULL");
-  if (enable && !L->ev_ready) {
-    for (int i = 0; i < HYMBA_N_STAGES; ++i) {
-      HIP_TRY(hipEventCreate(&L->ev_begin[i]), "event create");
-      HIP_TRY(hipEventCreate(&L->ev_end[i]), "event create");
-    }
-    L->ev_ready = true;
+  if (!enable) {
+    L->profiling = false;
+    return HYMBA_OK;
   }
-  L->profiling = enable != 0;
-  for (bool& u : L->ev_used) u = false;
+  if (L->ev.empty()) {
+    L->ev.assign(2 * kProfPairs, nullptr);
+    L->ev_stage.assign(kProfPairs, 0);
+    for (hipEvent_t& e : L->ev) {
+      const hipError_t r = hipEventCreate(&e);
+      if (r != hipSuccess) {
+        for (hipEvent_t& f : L->ev)
+          if (f) hipEventDestroy(f);
+        L->ev.clear();
+        return hip_fail(r, "event create");
+      }
+    }
+  }
+  L->profiling = true;
+  L->ev_next = 0;
+  L->prof_calls = 0;
+  L->prof_overflow = false;
   return HYMBA_OK;
 }
 
 int32_t hymba_layer_profile_read(hymba_layer* L, float* stage_ms, int32_t n) {
   if (!L || !stage_ms || n < 0) return fail(HYMBA_ERR_INVALID_ARG, "bad arguments");
-  for (int i = 0; i < n && i < HYMBA_N_STAGES; ++i) {
-    stage_ms[i] = 0.f;
-    if (!L->ev_ready || !L->ev_used[i]) continue;
-    HIP_TRY(hipEventSynchronize(L->ev_end[i]), "event synchronize");
-    HIP_TRY(hipEventElapsedTime(&stage_ms[i], L->ev_begin[i], L->ev_end[i]), "event elapsed time");
+  for (int i = 0; i < n; ++i) stage_ms[i] = 0.f;
+  if (L->prof_overflow)
+    return fail(HYMBA_ERR_WORKSPACE, "more than %d timed intervals since profiling was enabled", kProfPairs);
+  double sum[HYMBA_N_STAGES] = {};
+  if (L->ev_next > 0) HIP_TRY(hipEventSynchronize(L->ev[2 * L->ev_next - 1]), "event synchronize");
+  for (int p = 0; p < L->ev_next; ++p) {
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, L->ev[2 * p], L->ev[2 * p + 1]), "event elapsed time");
+    sum[L->ev_stage[p]] += ms;
   }
-  for (int i = HYMBA_N_STAGES; i < n; ++i) stage_ms[i] = 0.f;
+  const int calls = L->prof_calls > 0 ? L->prof_calls : 1;
+  for (int i = 0; i < n && i < HYMBA_N_STAGES; ++i) stage_ms[i] = static_cast<float>(sum[i] / calls);
   return HYMBA_OK;
 }
 

@@ -181,15 +181,23 @@ const char* hymba_last_error(void);
 const char* hymba_status_string(int32_t status);
 
 /* ---- stage timing ----------------------------------------------------------
- * With profiling enabled, prefill/decode/prepare record a HIP event before and
- * after each stage of the layer on the call's stream.  Stages:
- *   0 shared input projection   1 K/V write        2 attention
- *   3 W_O projection            4 SSM (scan/step)  5 fused epilogue
- *   6 output projection
- * hymba_layer_profile_read waits for the last call's events and writes the
- * per-stage milliseconds (0 for stages that did not run) into stage_ms[0..n).
- * Host only apart from event creation on first enable.                      */
-#define HYMBA_N_STAGES 7
+ * hymba_layer_profile(layer, 1) starts a recording: from then on every
+ * prefill/decode call brackets each of its stage intervals with a pair of HIP
+ * events on the call's stream (the one-off meta-prefix pass of a prepare is
+ * not recorded).  Each timed interval covers exactly one kernel launch.
+ * Stages:
+ *   0 shared input projection GEMM   1 K/V write            2 attention
+ *   3 W_O projection GEMM            4 SSM (scan / step)    5 fused epilogue
+ *   6 output projection GEMM         7 storage/activation type conversions
+ * hymba_layer_profile(layer, 0) stops recording and keeps what was recorded.
+ * hymba_layer_profile_read waits for the last recorded event and writes, per
+ * stage, the summed interval time divided by the number of recorded calls
+ * (mean milliseconds per call; 0 for stages that did not run) into
+ * stage_ms[0..n).  At most 1024 intervals are kept per recording; beyond
+ * that the read fails with HYMBA_ERR_WORKSPACE (stage_ms zeroed).  The first
+ * enable creates the events (HYMBA_ERR_HIP on failure); nothing else touches
+ * the device.                                                               */
+#define HYMBA_N_STAGES 8
 int32_t hymba_layer_profile(hymba_layer* layer, int32_t enable);
 int32_t hymba_layer_profile_read(hymba_layer* layer, float* stage_ms, int32_t n);
 const char* hymba_stage_name(int32_t stage);

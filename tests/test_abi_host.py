@@ -180,3 +180,15 @@ def test_kernel_entry_points_validate():
     with pytest.raises(L.HymbaError) as e:
         L.hymba_kernel_epilogue(L.HYMBA_F32, FAKE, 12, FAKE, 12, FAKE, 12, FAKE, FAKE, FAKE, 12, 3, 12, 1e-6, None)
     assert e.value.status == L.HYMBA_ERR_UNSUPPORTED
+
+
+def test_stage_names_and_profile_read_without_recording():
+    names = [L.hymba_stage_name(i) for i in range(L.HYMBA_N_STAGES)]
+    assert names == ["in_proj", "kv_write", "attention", "w_o", "ssm", "epilogue", "out_proj", "convert"]
+    assert L.hymba_stage_name(L.HYMBA_N_STAGES) == "unknown"
+    h = _create(_cfg())
+    try:
+        assert L.hymba_layer_profile_read(h) == [0.0] * L.HYMBA_N_STAGES   # nothing recorded: no device call
+        L.hymba_layer_profile(h, False)
+    finally:
+        L.hymba_layer_destroy(h)

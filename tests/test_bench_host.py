@@ -1,0 +1,91 @@
+"""Host logic of bench.py: algorithmic work figures and the rocprofv3 summary's attribution of
+dispatches to stages (no GPU: synthetic rocprofv3-style csv rows)."""
+import csv
+import json
+import os
+
+import pytest
+
+import bench
+from hymba_synth import CONFIGS
+
+
+def test_visible_keys_matches_brute_force():
+    for M, W, T in [(3, 4, 10), (0, 1, 5), (2, 0, 7), (5, 16, 9)]:
+        s = CONFIGS[0].shape.with_(n_meta=M, window=W)
+        brute = sum(M + (i + 1 if W == 0 else min(i + 1, W)) for i in range(T))
+        assert bench.visible_keys(s, T) == brute
+
+
+def test_prefill_work_stages():
+    s = CONFIGS[2].shape
+    w = bench.prefill_work(s, 16, 8192)
+    assert set(w) == {"in_proj", "attention", "w_o", "out_proj", "ssm", "epilogue", "convert"}
+    R = 16 * 8192
+    assert w["in_proj"] == ("mfma", 2.0 * R * s.d_model * s.n_in)
+    assert w["epilogue"] == ("hbm", float(R * s.d_inner * 2 * 4))
+    assert "kv_write" in bench.prefill_work(CONFIGS[1].shape, 8, 2048)
+
+
+def _trace_rows():
+    seq = ["convert_kernel<a>", "Cijk_gemm", "convert_kernel<b>", "swa_meta_attn_kernel<h>",
+           "selective_scan_kernel<h,16,8>", "Cijk_gemm", "epilogue_kernel<h>", "Cijk_gemm", "convert_kernel<c>"]
+    rows, d, t = [], 0, 0
+    # one small meta pass, then three timed calls, then the copy probe
+    for grid, calls in (("64", 1), ("4096", 3)):
+        for _ in range(calls):
+            for k in seq:
+                dur = {"Cijk_gemm": 100, "swa_meta_attn_kernel<h>": 50}.get(k, 10) * (1 if grid == "64" else 10)
+                rows.append({"Dispatch_Id": str(d), "Kernel_Name": k, "Grid_Size": grid,
+                             "Start_Timestamp": str(t), "End_Timestamp": str(t + dur * 1000)})
+                d += 1
+                t += dur * 1000 + 5
+    rows.append({"Dispatch_Id": str(d), "Kernel_Name": "vectorized_elementwise_kernel<neg_kernel>",
+                 "Grid_Size": "9", "Start_Timestamp": "0", "End_Timestamp": "1000"})
+    return rows
+
+
+def test_dispatch_labels():
+    lab = [st for st, _ in bench._label(_trace_rows())]
+    assert lab[:9] == ["convert", "in_proj", "convert", "attention", "ssm", "w_o", "epilogue", "out_proj",
+                       "convert"]
+    assert lab[-1] == "copy_probe"
+    g = bench._main_groups(bench._label(_trace_rows()),
+                           lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    assert g["in_proj"][1:] == ("4096", 3, 1000.0)
+    assert g["attention"][2:] == (3, 500.0)
+    assert g["convert"][2:] == (3, 300.0)      # three conversion kernels summed
+
+
+def _write(path, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=list(rows[0]))
+        w.writeheader()
+        w.writerows(rows)
+
+
+def test_summary_traffic_scaling(tmp_path):
+    rows = _trace_rows()
+    _write(str(tmp_path / "trace" / "host" / "1_kernel_trace.csv"), rows)
+    fetch, write = [], []
+    for r in rows:
+        k = bench._kernel_stage(r["Kernel_Name"])
+        big = r["Grid_Size"] != "64"
+        f = 2 * 1024 ** 2 if k == "copy_probe" else (100.0 if big else 1.0)   # KiB: the probe reads 2x too much
+        base = {"Dispatch_Id": r["Dispatch_Id"], "Kernel_Name": r["Kernel_Name"], "Grid_Size": r["Grid_Size"]}
+        fetch.append(dict(base, Counter_Name="FETCH_SIZE", Counter_Value=str(f)))
+        write.append(dict(base, Counter_Name="WRITE_SIZE", Counter_Value=str(f / 2)))
+    _write(str(tmp_path / "fetch" / "h" / "1_counter_collection.csv"), fetch)
+    _write(str(tmp_path / "write" / "h" / "1_counter_collection.csv"), write)
+    out_txt, out_json = str(tmp_path / "s.txt"), str(tmp_path / "t.json")
+    cmd = {"title": "t", "trace": "x", "summary": "y"}
+    bench.summarize_rocprof(str(tmp_path / "trace"), None, str(tmp_path / "fetch"), str(tmp_path / "write"), cmd,
+                            out_txt, out_json)
+    t = json.load(open(out_json))
+    assert t["copy_probe"]["fetch_scale"] == pytest.approx(0.5)
+    assert t["copy_probe"]["write_scale"] == pytest.approx(1.0)
+    # 100 KiB fetched (x0.5) + 50 KiB written (x1.0)
+    assert t["attention"]["bytes_per_launch"] == pytest.approx(100 * 1024 * 0.5 + 50 * 1024)
+    assert t["attention"]["source_sha256"] == bench.source_sha("attention")
+    assert "in_proj" in open(out_txt).read()
