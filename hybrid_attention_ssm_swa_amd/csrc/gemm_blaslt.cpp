@@ -2,11 +2,18 @@
 // projection, attention W_O, output projection).  Row-major Y = X W^T is the
 // column-major product Y^T = W^T-op(A = W) x X: A = W with op T (K-contiguous),
 // B = X with op N, both K-contiguous ("TN"), the layout MFMA GEMMs prefer.
-// Plans (descriptors + heuristic algorithm) are cached per device and shape.
+// Plans (descriptors + algorithm) are cached per device and shape.  The
+// algorithm is the fastest of hipBLASLt's heuristic candidates, timed once on
+// the first call's own operands and stream (skipped while the stream is being
+// captured, or when the environment sets HYMBA_GEMM_TUNE=0: then the first
+// candidate is taken).
 #include "gemm_blaslt.h"
 
 #include <hipblaslt/hipblaslt.h>
 
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -36,6 +43,35 @@ struct State {
 State& state() {
   static State* s = new State();   // lives until process exit (handles are per device)
   return *s;
+}
+
+bool env_flag(const char* name, bool dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  return std::strcmp(v, "0") != 0;
+}
+
+// Mean milliseconds of `reps` runs of one candidate (after one untimed run), or a negative value if
+// it fails.
+float time_candidate(hipblasLtHandle_t handle, const Plan& p, const hipblasLtMatmulAlgo_t& algo, const void* W,
+                     const void* X, void* Y, void* ws, size_t ws_bytes, hipStream_t s, int reps) {
+  const float alpha = 1.f, beta = 0.f;
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess) return -1.f;
+  if (hipEventCreate(&e1) != hipSuccess) { hipEventDestroy(e0); return -1.f; }
+  float ms = -1.f;
+  bool ok = hipblasLtMatmul(handle, p.desc, &alpha, W, p.la, X, p.lb, &beta, Y, p.lc, Y, p.lc, &algo, ws,
+                            ws_bytes, s) == HIPBLAS_STATUS_SUCCESS;
+  ok = ok && hipEventRecord(e0, s) == hipSuccess;
+  for (int r = 0; ok && r < reps; ++r)
+    ok = hipblasLtMatmul(handle, p.desc, &alpha, W, p.la, X, p.lb, &beta, Y, p.lc, Y, p.lc, &algo, ws, ws_bytes,
+                         s) == HIPBLAS_STATUS_SUCCESS;
+  ok = ok && hipEventRecord(e1, s) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+  if (ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess) ms /= reps;
+  else ms = -1.f;
+  hipEventDestroy(e0);
+  hipEventDestroy(e1);
+  return ms;
 }
 
 }  // namespace
@@ -77,17 +113,33 @@ int gemm_16(GemmType in_type, GemmType out_type, const void* X, int64_t ldx, con
       uint64_t wsb = ws_bytes;
       hipblasLtMatmulPreferenceCreate(&pref);
       hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof(wsb));
-      hipblasLtMatmulHeuristicResult_t res[8];
+      constexpr int kCand = 16;
+      hipblasLtMatmulHeuristicResult_t res[kCand];
       int n = 0;
       const hipblasStatus_t hs = hipblasLtMatmulAlgoGetHeuristic(handle, p.desc, p.la, p.lb, p.lc, p.lc,
-                                                                 pref, 8, res, &n);
+                                                                 pref, kCand, res, &n);
       hipblasLtMatmulPreferenceDestroy(pref);
       if (hs != HIPBLAS_STATUS_SUCCESS || n == 0) {
         *err = "hipBLASLt found no algorithm for this GEMM shape";
         return -2;
       }
-      p.algo = res[0].algo;
-      p.ws_needed = res[0].workspaceSize;
+      int best = 0;
+      hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(s, &cap) != hipSuccess) cap = hipStreamCaptureStatusActive;
+      if (n > 1 && cap == hipStreamCaptureStatusNone && env_flag("HYMBA_GEMM_TUNE", true)) {
+        const bool log = env_flag("HYMBA_GEMM_TUNE_LOG", false);
+        float best_ms = -1.f;
+        for (int i = 0; i < n; ++i) {
+          if (res[i].workspaceSize > ws_bytes) continue;
+          const float ms = time_candidate(handle, p, res[i].algo, W, X, Y, ws, ws_bytes, s, 3);
+          if (log)
+            std::fprintf(stderr, "[hymba gemm] rows %lld out %lld in %lld candidate %d: %.4f ms\n",
+                         (long long)rows, (long long)out, (long long)in, i, ms);
+          if (ms > 0.f && (best_ms < 0.f || ms < best_ms)) { best_ms = ms; best = i; }
+        }
+      }
+      p.algo = res[best].algo;
+      p.ws_needed = res[best].workspaceSize;
       it = st.plans.emplace(key, p).first;
     }
     plan = it->second;
