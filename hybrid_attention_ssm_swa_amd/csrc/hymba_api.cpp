@@ -753,6 +753,8 @@ int32_t hymba_kernel_selective_scan(int32_t dtype, const void* u, const void* dt
   if (!u || !dt || !bc || !A || !D || !dt_bias || !y || !ws) return fail(HYMBA_ERR_INVALID_ARG, "NULL pointer");
   if (B < 1 || T < 1 || E < 1) return fail(HYMBA_ERR_INVALID_ARG, "bad dimensions");
   if (N != 8 && N != 16) return fail(HYMBA_ERR_UNSUPPORTED, "N must be 8 or 16");
+  if (ld < E || ldy < E || ld_bc < 2 * N || ld_bc % 4 != 0 || !aligned(bc, 16))
+    return fail(HYMBA_ERR_INVALID_ARG, "strides: ld, ldy >= E; ld_bc >= 2N, a multiple of 4, bc 16-byte aligned");
   if (dtype != HYMBA_F16 && dtype != HYMBA_F32)
     return fail(HYMBA_ERR_INVALID_ARG, "scan dtype must be HYMBA_F32 or HYMBA_F16");
   if (ws_bytes < (size_t)E * N * 4) return fail(HYMBA_ERR_WORKSPACE, "workspace too small");

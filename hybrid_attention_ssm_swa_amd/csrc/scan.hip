@@ -25,14 +25,20 @@ namespace {
 // Prefill mapping.  A channel's N states are split over WPC = N / NS waves of
 // one workgroup (wave w owns states [w*NS, (w+1)*NS) of 64 consecutive
 // channels, one channel per lane), which gives WPC times more waves than
-// channels/64 and so fills every SIMD even at batch 16.  Time runs in chunks
-// of TC steps, and everything a chunk needs is fetched one chunk ahead so HBM
-// and L2 latency hide behind a chunk of arithmetic: u/dt into registers, the
-// wave's B/C columns (uniform across its lanes) into registers and then into
-// the wave's LDS slice, read back per step as broadcast LDS reads.  The
-// per-wave partial outputs of a chunk are summed across the WPC waves through
-// LDS once per chunk (double-buffered, one barrier per chunk).
+// channels/64 and so keeps several waves on every SIMD even at batch 16.
+// Time runs in chunks of kTC steps with everything a chunk needs fetched one
+// chunk ahead, so HBM/L2 latency hides behind a chunk of arithmetic.  Work
+// shared by the WPC waves of a channel is done once per workgroup and passed
+// through LDS: wave w turns the raw dt/u of steps s = w (mod WPC) of the next
+// chunk into (delta, delta*u) pairs, the workgroup loads the chunk's B/C rows
+// (uniform over the 64 channels) once, and every wave reads both back per
+// step (B/C as broadcast reads).  Each wave's partial sums over its states
+// meet in LDS once per chunk; the wave that prepared step s also adds the skip
+// term D*u and stores y.
 constexpr int kTC = 16;
+
+template <int NS> struct BcVec { typedef float4 type; };
+template <> struct BcVec<2> { typedef float2 type; };
 
 template <typename T, int N, int NS>
 __global__ __launch_bounds__(64 * (N / NS)) void selective_scan_kernel(
@@ -41,11 +47,16 @@ __global__ __launch_bounds__(64 * (N / NS)) void selective_scan_kernel(
     const float* __restrict__ h0, int64_t h0_bstride, T* __restrict__ y, int64_t ldy,
     float* __restrict__ h_out, int T_len, int E) {
   constexpr int WPC = N / NS;
-  constexpr int Q = NS / 4;                 // float4 per step of B (and of C)
-  constexpr int ITEMS = kTC * 2 * Q;        // float4 per chunk of this wave's B/C
-  constexpr int PER_LANE = (ITEMS + 63) / 64;
-  __shared__ float ys[2][WPC][kTC][64];
-  __shared__ float4 bcs[2][WPC][kTC][2 * Q];
+  constexpr int SPW = kTC / WPC;                   // steps each wave prepares per chunk
+  constexpr int ROW4 = 2 * N / 4;                  // float4 per B/C row
+  constexpr int ITEMS = kTC * ROW4;                // float4 per chunk of B/C rows
+  constexpr int PER_T = (ITEMS + 64 * WPC - 1) / (64 * WPC);
+  typedef typename BcVec<NS>::type BV;
+  constexpr int VW = sizeof(BV) / sizeof(float);
+  static_assert(kTC % WPC == 0 && NS % VW == 0, "scan tiling");
+  __shared__ float2 dd[2][kTC][64];                // (delta, delta * u) per step and channel
+  __shared__ float4 bcs[2][kTC][ROW4];             // B row then C row per step
+  __shared__ float ys[WPC > 1 ? WPC : 1][kTC][64]; // per-wave partial y of a chunk
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int b = blockIdx.y;
@@ -59,7 +70,7 @@ __global__ __launch_bounds__(64 * (N / NS)) void selective_scan_kernel(
     a2[n] = A2[(int64_t)cc * N + n0 + n];
     h[n] = h0 ? h0[b * h0_bstride + (int64_t)cc * N + n0 + n] : 0.f;
   }
-  const float Dc = wave == 0 ? Dp[cc] : 0.f;   // the skip term enters one partial sum only
+  const float Dc = Dp[cc];
   const float bias = dt_bias[cc];
   const int64_t row0 = (int64_t)b * T_len;
   const T* up = u + row0 * ld + cc;
@@ -68,72 +79,76 @@ __global__ __launch_bounds__(64 * (N / NS)) void selective_scan_kernel(
   T* yrow = y + row0 * ldy + c;
   const int last = T_len - 1;
 
-  // B/C item i of a chunk starting at t: step i / (2Q); j = i % (2Q) < Q -> B[n0 + 4j..],
-  // else C[n0 + 4(j - Q)..]
-  auto fetch_bc = [&](float4 (&r)[PER_LANE], int t) {
+  T un[SPW], dn[SPW];
+  float4 bcr[PER_T];
+  // raw inputs of chunk t (rows clamped: always in bounds); this wave's steps s = wave + WPC j
+  auto fetch = [&](int t) {
 #pragma unroll
-    for (int k = 0; k < PER_LANE; ++k) {
-      const int i = lane + 64 * k;
+    for (int j = 0; j < SPW; ++j) {
+      const int64_t r = min(t + wave + WPC * j, last);
+      un[j] = up[r * ld];
+      dn[j] = dp[r * ld];
+    }
+#pragma unroll
+    for (int k = 0; k < PER_T; ++k) {
+      const int i = threadIdx.x + 64 * WPC * k;
       if (i < ITEMS) {
-        const int st = i / (2 * Q), j = i % (2 * Q);
-        const int64_t row = min(t + st, last);
-        const int col = j < Q ? n0 + 4 * j : N + n0 + 4 * (j - Q);
-        r[k] = *reinterpret_cast<const float4*>(bcrow + row * ld_bc + col);
+        const int64_t r = min(t + i / ROW4, last);
+        bcr[k] = *reinterpret_cast<const float4*>(bcrow + r * ld_bc + 4 * (i % ROW4));
       }
     }
   };
-  auto stash_bc = [&](const float4 (&r)[PER_LANE], int bb) {
+  // publish the fetched chunk into LDS buffer bb; returns D * u of this wave's steps
+  float skip_next[SPW];
+  auto publish = [&](int bb) {
 #pragma unroll
-    for (int k = 0; k < PER_LANE; ++k) {
-      const int i = lane + 64 * k;
-      if (i < ITEMS) bcs[bb][wave][i / (2 * Q)][i % (2 * Q)] = r[k];
+    for (int j = 0; j < SPW; ++j) {
+      const float uv = static_cast<float>(un[j]);
+      const float delta = softplus_f(static_cast<float>(dn[j]) + bias);
+      dd[bb][wave + WPC * j][lane] = make_float2(delta, delta * uv);
+      skip_next[j] = Dc * uv;
+    }
+#pragma unroll
+    for (int k = 0; k < PER_T; ++k) {
+      const int i = threadIdx.x + 64 * WPC * k;
+      if (i < ITEMS) bcs[bb][i / ROW4][i % ROW4] = bcr[k];
     }
   };
 
-  T un[kTC], dn[kTC];
-  float4 bcr[PER_LANE];
+  fetch(0);
+  publish(0);
+  float skip[SPW];
 #pragma unroll
-  for (int s = 0; s < kTC; ++s) {
-    const int64_t r = min(s, last);
-    un[s] = up[r * ld];
-    dn[s] = dp[r * ld];
-  }
-  fetch_bc(bcr, 0);
+  for (int j = 0; j < SPW; ++j) skip[j] = skip_next[j];
+  fetch(kTC);
+  __syncthreads();
   int buf = 0;
-  stash_bc(bcr, buf);
   for (int t0 = 0; t0 < T_len; t0 += kTC) {
-    T uc[kTC], dc[kTC];
-#pragma unroll
-    for (int s = 0; s < kTC; ++s) { uc[s] = un[s]; dc[s] = dn[s]; }
-    // everything for the next chunk (rows clamped, always in bounds)
-#pragma unroll
-    for (int s = 0; s < kTC; ++s) {
-      const int64_t r = min(t0 + kTC + s, last);
-      un[s] = up[r * ld];
-      dn[s] = dp[r * ld];
-    }
-    fetch_bc(bcr, t0 + kTC);
+    publish(buf ^ 1);          // chunk t0 + kTC (fetched one chunk ago)
+    fetch(t0 + 2 * kTC);
     const int len = min(kTC, T_len - t0);
+    const float* bcsf = reinterpret_cast<const float*>(&bcs[buf][0][0]);
     float part[kTC];
 #pragma unroll
     for (int s = 0; s < kTC; ++s) {
       part[s] = 0.f;
       if (s < len) {
+        const float2 d = dd[buf][s][lane];
         float bb[NS], cb[NS];
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-          const float4 vb = bcs[buf][wave][s][q], vc = bcs[buf][wave][s][Q + q];
-          bb[4 * q] = vb.x; bb[4 * q + 1] = vb.y; bb[4 * q + 2] = vb.z; bb[4 * q + 3] = vb.w;
-          cb[4 * q] = vc.x; cb[4 * q + 1] = vc.y; cb[4 * q + 2] = vc.z; cb[4 * q + 3] = vc.w;
+        for (int q = 0; q < NS / VW; ++q) {
+          const BV vb = *reinterpret_cast<const BV*>(bcsf + s * 2 * N + n0 + VW * q);
+          const BV vc = *reinterpret_cast<const BV*>(bcsf + s * 2 * N + N + n0 + VW * q);
+          const float* pb = reinterpret_cast<const float*>(&vb);
+          const float* pc = reinterpret_cast<const float*>(&vc);
+#pragma unroll
+          for (int e = 0; e < VW; ++e) { bb[VW * q + e] = pb[e]; cb[VW * q + e] = pc[e]; }
         }
-        const float uv = static_cast<float>(uc[s]);
-        const float delta = softplus_f(static_cast<float>(dc[s]) + bias);
-        const float du = delta * uv;
-        float acc = Dc * uv;
+        float acc = 0.f;
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
-          const float dA = fast_exp2(delta * a2[n]);
-          h[n] = fmaf(dA, h[n], du * bb[n]);
+          const float dA = fast_exp2(d.x * a2[n]);
+          h[n] = fmaf(dA, h[n], d.y * bb[n]);
           acc = fmaf(cb[n], h[n], acc);
         }
         part[s] = acc;
@@ -142,20 +157,27 @@ __global__ __launch_bounds__(64 * (N / NS)) void selective_scan_kernel(
     if constexpr (WPC == 1) {
 #pragma unroll
       for (int s = 0; s < kTC; ++s)
-        if (s < len && active) Elem<T>::store(yrow + (int64_t)(t0 + s) * ldy, part[s]);
+        if (s < len && active) Elem<T>::store(yrow + (int64_t)(t0 + s) * ldy, part[s] + skip[s]);
+      __syncthreads();         // the next chunk's LDS buffer is ready
     } else {
 #pragma unroll
-      for (int s = 0; s < kTC; ++s) ys[buf][wave][s][lane] = part[s];
+      for (int s = 0; s < kTC; ++s) ys[wave][s][lane] = part[s];
       __syncthreads();
-      for (int s = wave; s < len; s += WPC) {
-        float yv = 0.f;
 #pragma unroll
-        for (int w = 0; w < WPC; ++w) yv += ys[buf][w][s][lane];
-        if (active) Elem<T>::store(yrow + (int64_t)(t0 + s) * ldy, yv);
+      for (int j = 0; j < SPW; ++j) {
+        const int s = wave + WPC * j;
+        if (s < len) {
+          float yv = skip[j];
+#pragma unroll
+          for (int w = 0; w < WPC; ++w) yv += ys[w][s][lane];
+          if (active) Elem<T>::store(yrow + (int64_t)(t0 + s) * ldy, yv);
+        }
       }
+      __syncthreads();         // ys is rewritten by the next chunk
     }
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) skip[j] = skip_next[j];
     buf ^= 1;
-    stash_bc(bcr, buf);   // this wave's own slice: ordered by the wave's LDS queue
   }
   if (active && h_out) {
     float* ho = h_out + ((int64_t)b * E + c) * N + n0;
@@ -204,11 +226,14 @@ __global__ __launch_bounds__(256) void ssm_step_kernel(StepArgs<T> a) {
 }
 
 // States per wave: the fewest waves per channel group (largest NS, least
-// per-step overhead) that still gives ~1.5 waves per SIMD of the 1024.
+// per-step overhead) that still gives ~HYMBA_SCAN_WAVES waves over the 1024 SIMDs.
+#ifndef HYMBA_SCAN_WAVES
+#define HYMBA_SCAN_WAVES 3072
+#endif
 inline int scan_states_per_wave(int B, int E, int N) {
   const int64_t groups = (int64_t)B * ceil_div(E, 64);
-  int ns = N;
-  while (ns > 4 && groups * (N / ns) < 1536) ns >>= 1;
+  int ns = N < 8 ? N : 8;   // one wave holding all 16 states runs out of registers
+  while (ns > 2 && groups * (N / ns) < HYMBA_SCAN_WAVES) ns >>= 1;
   return ns;
 }
 
@@ -224,11 +249,12 @@ hipError_t scan_dispatch(const ScanArgs<T>& a, hipStream_t s) {
   const int ns = scan_states_per_wave(a.B, a.E, a.N);
   if (a.N == 8) {
     if (ns == 8) scan_launch<T, 8, 8>(a, s);
-    else scan_launch<T, 8, 4>(a, s);
+    else if (ns == 4) scan_launch<T, 8, 4>(a, s);
+    else scan_launch<T, 8, 2>(a, s);
   } else if (a.N == 16) {
-    if (ns == 16) scan_launch<T, 16, 16>(a, s);
-    else if (ns == 8) scan_launch<T, 16, 8>(a, s);
-    else scan_launch<T, 16, 4>(a, s);
+    if (ns == 8) scan_launch<T, 16, 8>(a, s);
+    else if (ns == 4) scan_launch<T, 16, 4>(a, s);
+    else scan_launch<T, 16, 2>(a, s);
   } else {
     return hipErrorInvalidValue;
   }

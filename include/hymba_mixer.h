@@ -219,7 +219,8 @@ int32_t hymba_kernel_attention(int32_t dtype, const void* q, int64_t ld_q, const
 
 /* Selective scan over B sequences of T rows.  u, dt: [B*T, E] slices with
  * row stride ld (HYMBA_F32 or HYMBA_F16); bc: fp32 rows with B_t at
- * bc[0..N) and C_t at bc[N..2N) (row stride ld_bc).  A [E, N], D, dt_bias [E]
+ * bc[0..N) and C_t at bc[N..2N) (row stride ld_bc, a multiple of 4 and
+ * >= 2N; bc 16-byte aligned; ld, ldy >= E).  A [E, N], D, dt_bias [E]
  * fp32 (A is the decay rate, not scaled).  h0 [E, N] fp32 shared initial
  * state or NULL (zero).  y [B*T, E] (row stride ldy) receives the ungated
  * output; h_out [B, E, N] fp32 the final state (may be NULL).

@@ -192,3 +192,12 @@ def test_stage_names_and_profile_read_without_recording():
         L.hymba_layer_profile(h, False)
     finally:
         L.hymba_layer_destroy(h)
+
+
+def test_scan_entry_checks_strides():
+    for ld, ld_bc, ldy, bc in [(4, 16, 8, FAKE), (8, 12, 8, FAKE), (8, 18, 8, FAKE), (8, 16, 4, FAKE),
+                               (8, 16, 8, FAKE + 8)]:
+        with pytest.raises(L.HymbaError) as e:
+            L.hymba_kernel_selective_scan(L.HYMBA_F16, FAKE, FAKE, ld, bc, ld_bc, FAKE, FAKE, FAKE, None, FAKE, ldy,
+                                          None, 1, 4, 8, 8, FAKE, 1 << 20, None)
+        assert e.value.status == L.HYMBA_ERR_INVALID_ARG
