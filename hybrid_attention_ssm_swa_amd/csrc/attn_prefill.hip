@@ -12,11 +12,11 @@
 //  * swa_meta_attn (MFMA): hd = 64, 16-bit operands (fp16 for the layer's
 //    activations, bf16 also instantiated) with v_mfma_f32_32x32x16_{f16,bf16}
 //    and fp32 accumulation.
-//    One workgroup = one (sequence, KV head) and a run of 32-query blocks; one
-//    wave per query head of the group (GQA: the K/V tile staged in LDS serves
-//    every head of the group).  The meta K and V^T tiles are loaded into LDS
-//    once per workgroup and stay resident for all its query blocks; window
-//    tiles of 64 keys stream through a double-buffered LDS stage.
+//    One workgroup = 4 waves = 128 consecutive queries of one query head (a
+//    32-query block per wave).  The K tiles and transposed V tiles of the keys
+//    those queries can see (meta, then the window span) stream through a
+//    double-buffered LDS stage loaded by all four waves; the heads of a GQA
+//    group reuse the same K/V through the L2 of the XCD their workgroups run on.
 //    Scores are computed transposed (S^T = K Q^T) so each lane owns one query
 //    column and 16 keys of a 32-key block: the softmax max needs one exchange
 //    with lane l^32, and the probabilities feed the P.V product as the B
@@ -35,9 +35,7 @@ constexpr int kQB = 32;          // queries per wave (one MFMA column block)
 constexpr int kKT = 64;          // keys per tile
 constexpr int kKStr = kHd + 8;   // LDS row stride (bf16) of K tiles: 144 B
 constexpr int kVStr = kKT + 4;   // LDS row stride (bf16) of V^T window tiles: 136 B
-constexpr int kMaxMeta = 128;    // resident meta keys (the pages' meta-token count)
-constexpr int kMetaVStr = kMaxMeta + 4;
-constexpr int kMaxWaves = 8;
+constexpr float kLazyLog2 = 8.f;   // rescale threshold of the online softmax (log2 units)
 
 struct __align__(16) U4 { uint32_t x, y, z, w; };
 
@@ -57,22 +55,17 @@ template <> struct Op<bf16_t> {
 template <typename ET>
 __device__ __forceinline__ typename Op<ET>::vec as_vec(U4 v) { return __builtin_bit_cast(typename Op<ET>::vec, v); }
 
-// 16-bit elements stored as raw 16-bit words
+// 16-bit elements stored as raw 16-bit words; a double-buffered stage of 64-key tiles
 struct AttnSmem {
-  uint16_t kw[2][kKT * kKStr];        // window K tiles  [key][dim]
-  uint16_t vw[2][kHd * kVStr];        // window V^T tiles [dim][key]
-  uint16_t km[kMaxMeta * kKStr];      // meta K          [key][dim]
-  uint16_t vm[kHd * kMetaVStr];       // meta V^T        [dim][key]
+  uint16_t kw[2][kKT * kKStr];        // K tiles   [key][dim]
+  uint16_t vw[2][kHd * kVStr];        // V^T tiles [dim][key]
 };
 
-// Cooperative load of a 64-key tile (K rows straight, V transposed) for the
-// whole workgroup: 128 work items, each owning 4 of the 512 16-byte K chunks
-// (64 rows x 8) and a 4-key x 8-dim block of V.  Rows beyond `nvalid` are
-// zero-filled.
-struct TileRegs {
-  U4 k[4];
-  U4 v[4];
-};
+// Cooperative load of a 64-key tile (K rows straight, V transposed) spread
+// over the workgroup's 256 threads, four 16-byte loads each: threads
+// [0, 128) own K chunks tid + 128 j (j < 4) of the tile's 512 (64 rows x 8
+// chunks); threads [128, 256) own a 4-key x 8-dim block of V.  Rows beyond
+// `nvalid` (>= 1) read a clamped, valid row and are zero-filled by value.
 
 __device__ __forceinline__ uint32_t u4_get(const U4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -88,50 +81,70 @@ __device__ __forceinline__ U4 masked_load(const void* p, bool keep) {
   return r;
 }
 
-template <typename ET>
-__device__ __forceinline__ void tile_fetch(TileRegs& r, const ET* __restrict__ kbase,
-                                           const ET* __restrict__ vbase, int64_t ld,
-                                           int nvalid, int item) {
-  // item in [0, 128): K chunks item + 128 j (j < 4) of 512 (64 rows x 8 chunks);
-  // V block: keys 4*(item/8) .. +3, dims 8*(item%8) .. +7
-  // rows >= nvalid (>= 1) read a clamped, valid row and are zeroed by value
+__device__ __forceinline__ void item_store(const U4 (&r)[4], uint16_t* ks, uint16_t* vs, int vstr, int key_off,
+                                           int item) {
+  if (item < 128) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = item + j * 128;
-    const int row = c >> 3, col = (c & 7) * 8;
-    r.k[j] = masked_load(kbase + (int64_t)min(row, nvalid - 1) * ld + col, row < nvalid);
-  }
-  const int key0 = (item >> 3) * 4, dim0 = (item & 7) * 8;
+    for (int j = 0; j < 4; ++j) {
+      const int c = item + j * 128;
+      const int row = c >> 3, col = (c & 7) * 8;
+      *reinterpret_cast<U4*>(ks + (key_off + row) * kKStr + col) = r[j];
+    }
+  } else {
+    // transpose 4 keys x 8 dims -> 8 rows (dims) of 4 consecutive keys
+    const int it = item - 128;
+    const int key0 = key_off + (it >> 3) * 4, dim0 = (it & 7) * 8;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = key0 + j;
-    r.v[j] = masked_load(vbase + (int64_t)min(row, nvalid - 1) * ld + dim0, row < nvalid);
+    for (int p = 0; p < 4; ++p) {
+      // dims dim0+2p (low halves) and dim0+2p+1 (high halves)
+      const uint32_t a = u4_get(r[0], p), b = u4_get(r[1], p);
+      const uint32_t c = u4_get(r[2], p), d = u4_get(r[3], p);
+      uint2 lo, hi;
+      lo.x = __builtin_amdgcn_perm(b, a, 0x05040100u);   // (a.lo, b.lo)
+      lo.y = __builtin_amdgcn_perm(d, c, 0x05040100u);
+      hi.x = __builtin_amdgcn_perm(b, a, 0x07060302u);   // (a.hi, b.hi)
+      hi.y = __builtin_amdgcn_perm(d, c, 0x07060302u);
+      *reinterpret_cast<uint2*>(vs + (dim0 + 2 * p) * vstr + key0) = lo;
+      *reinterpret_cast<uint2*>(vs + (dim0 + 2 * p + 1) * vstr + key0) = hi;
+    }
   }
 }
 
-__device__ __forceinline__ void tile_store(const TileRegs& r, uint16_t* ks, uint16_t* vs, int vstr,
-                                           int key_off, int item) {
+// The calling thread's item (tid < 256) of the tile whose first row is at
+// kbase / vbase (row stride ld elements, 32-bit offsets).  Full tiles load
+// without any clamping; only a tile with nvalid < 64 valid rows takes the
+// clamped, zero-filling path.
+struct TileRegs {
+  U4 r[4];
+};
+
+template <typename ET>
+__device__ __forceinline__ void tile_fetch(TileRegs& t, const ET* __restrict__ kbase,
+                                           const ET* __restrict__ vbase, int ld, int nvalid, int tid) {
+  const bool is_k = tid < 128;                       // waves 0-1: K chunks; waves 2-3: V blocks
+  const ET* base = is_k ? kbase : vbase;
+  const int it = is_k ? tid : tid - 128;
+  const int row0 = is_k ? (it >> 3) : (it >> 3) * 4;
+  const int rstep = is_k ? 16 : 1;
+  const int col = (it & 7) * 8;
+  if (nvalid >= kKT) {
+    const char* b = reinterpret_cast<const char*>(base);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = item + j * 128;
-    const int row = c >> 3, col = (c & 7) * 8;
-    *reinterpret_cast<U4*>(ks + (key_off + row) * kKStr + col) = r.k[j];
-  }
-  // transpose 4 keys x 8 dims -> 8 rows (dims) of 4 consecutive keys
-  const int key0 = key_off + (item >> 3) * 4, dim0 = (item & 7) * 8;
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t off = static_cast<uint32_t>(((row0 + rstep * j) * ld + col) * (int)sizeof(ET));
+      t.r[j] = *reinterpret_cast<const U4*>(b + off);
+    }
+  } else {
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    // dims dim0+2p (low halves) and dim0+2p+1 (high halves)
-    const uint32_t a = u4_get(r.v[0], p), b = u4_get(r.v[1], p);
-    const uint32_t c = u4_get(r.v[2], p), d = u4_get(r.v[3], p);
-    uint2 lo, hi;
-    lo.x = __builtin_amdgcn_perm(b, a, 0x05040100u);   // (a.lo, b.lo)
-    lo.y = __builtin_amdgcn_perm(d, c, 0x05040100u);
-    hi.x = __builtin_amdgcn_perm(b, a, 0x07060302u);   // (a.hi, b.hi)
-    hi.y = __builtin_amdgcn_perm(d, c, 0x07060302u);
-    *reinterpret_cast<uint2*>(vs + (dim0 + 2 * p) * vstr + key0) = lo;
-    *reinterpret_cast<uint2*>(vs + (dim0 + 2 * p + 1) * vstr + key0) = hi;
+    for (int j = 0; j < 4; ++j) {
+      const int row = row0 + rstep * j;
+      t.r[j] = masked_load(base + (int64_t)min(row, nvalid - 1) * ld + col, row < nvalid);
+    }
   }
+}
+
+__device__ __forceinline__ void tile_store(const TileRegs& t, uint16_t* ks, uint16_t* vs, int tid) {
+  item_store(t.r, ks, vs, kVStr, 0, tid);
 }
 
 struct WaveState {
@@ -140,16 +153,35 @@ struct WaveState {
   float l;            // partial row sum over this lane's keys
 };
 
+// x combined with the same register of lane l ^ 32 (v_permlane32_swap with
+// both operands x: the two results are the low half and the high half
+// broadcast to both halves, so any symmetric op of them is the xor-32 reduction).
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// max of three (one v_max3_f32; scores are never NaN)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // One 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
 // ks: [64][kKStr] K rows; vs: [64 dims][vstr] V^T; key0: first key index of
-// the tile in the mask's coordinates.  With kMask, key j is kept iff
+// the tile in the mask's coordinates.  With `mask`, key j is kept iff
 // lo_key <= j < hi_key and, for tq >= 0 (a real query tq), j <= tq and
 // (win <= 0 or j > tq - win).
-template <typename ET, bool kMask>
+template <typename ET>
 __device__ __forceinline__ void attend_tile(WaveState& st, const typename Op<ET>::vec (&qf)[4],
                                             const uint16_t* ks, const uint16_t* vs, int vstr,
                                             float sc, int lane, int key0, int lo_key, int hi_key,
-                                            int tq, int win) {
+                                            int tq, int win, bool mask) {
   const int col = lane & 31, half = lane >> 5;
   f32x16_t s[2];
 #pragma unroll
@@ -162,28 +194,43 @@ __device__ __forceinline__ void attend_tile(WaveState& st, const typename Op<ET>
       s[kb] = Op<ET>::mfma(a, qf[st4], s[kb]);
     }
   }
-  if (kMask) {
+  if (mask) {
     // key index of register r of block kb: key0 + 32 kb + 8 (r/4) + 4 half + r%4
+    int lo = lo_key, hi = hi_key;
+    if (tq >= 0) {
+      hi = min(hi, tq + 1);
+      if (win > 0) lo = max(lo, tq - win + 1);
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        bool vis = key >= lo_key && key < hi_key;          // tile bounds (meta count / T)
-        if (tq >= 0) vis = vis && key <= tq && (win <= 0 || key > tq - win);
-        if (!vis) s[kb][r] = -INFINITY;
+        if (key < lo || key >= hi) s[kb][r] = -INFINITY;   // exp2 gives exactly 0 whatever the running max
       }
   }
-  float mt = s[0][0];
+  float mt = max3f(s[0][0], s[0][1], s[0][2]);
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int r = 3; r < 15; r += 2) mt = max3f(mt, s[0][r], s[0][r + 1]);
+  mt = max3f(mt, s[0][15], s[1][0]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32));
-  const float mnew = fmaxf(st.m, mt);
-  const float alpha = fast_exp2((st.m - mnew) * sc);
-  st.m = mnew;
-  const float msc = mnew * sc;
+  for (int r = 1; r < 15; r += 2) mt = max3f(mt, s[1][r], s[1][r + 1]);
+  mt = fmaxf(mt, s[1][15]);
+  mt = max_xor32(mt);
+  // Lazy rescaling: the running max only moves (and the accumulators are rescaled) when some
+  // query of the wave sees a score more than 2^kLazyLog2 above it; otherwise the stale max is
+  // kept and probabilities may reach 2^kLazyLog2, exact in the 16-bit P and fp32 sums.
+  if (__builtin_amdgcn_ballot_w64((mt - st.m) * sc > kLazyLog2) != 0) {
+    const float mnew = fmaxf(st.m, mt);
+    const float alpha = fast_exp2((st.m - mnew) * sc);
+    st.m = mnew;
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc[db][r] *= alpha;
+  }
+  const float msc = st.m * sc;
   float psum = 0.f;
   typename Op<ET>::vec pf[4];
 #pragma unroll
@@ -204,11 +251,7 @@ __device__ __forceinline__ void attend_tile(WaveState& st, const typename Op<ET>
       pf[kb * 2 + hh] = as_vec<ET>(w);
     }
   }
-  st.l = fmaf(st.l, alpha, psum);
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st.acc[db][r] *= alpha;
+  st.l += psum;
   // O^T[dim][q] += sum_k V^T[dim][k] P^T[k][q]; PV k-step s covers tile keys
   // [16 s, 16 s + 16); k-index 8 h + j <-> key 16 s + 8 (j/4) + 4 h + j%4.
 #pragma unroll
@@ -224,124 +267,122 @@ __device__ __forceinline__ void attend_tile(WaveState& st, const typename Op<ET>
   }
 }
 
-// grid: (n_work, Hkv, B); block: 64 * max(2, heads per group) threads: one wave
-// per head of the group (a group of one gets a helper wave for the tile loads).
-// Work item x covers query blocks [x*qb_per_wg, (x+1)*qb_per_wg) (ordered so
-// the longest causal runs start first).
+// One workgroup = 4 waves = kQG consecutive queries (one 32-query block per
+// wave) of one query head.  The workgroup streams the key tiles its queries
+// can see -- the meta tiles, then the window span [q0 - W + 1, q0 + kQG) (all
+// earlier keys for a global layer) -- through a double-buffered LDS stage that
+// all four waves load and share; a wave skips tiles outside its own window.
+// Work items are numbered (sequence, KV head, query group, head of the group)
+// for SWA -- so consecutive items reuse one window of K/V -- and with the
+// longest query groups first for global layers; consecutive items go to the
+// same XCD (the dispatcher deals workgroups round-robin over the 8 XCDs), so
+// an XCD's L2 holds the K/V its workgroups share.
+constexpr int kQG = 4 * kQB;
+constexpr int kXcds = 8;
+
 template <typename ET>
-__global__ __launch_bounds__(512) void swa_meta_attn_kernel(AttnArgs<ET> a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void swa_meta_attn_kernel(AttnArgs<ET> a) {
   __shared__ AttnSmem sm;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int nthreads = blockDim.x;
-  const int g = blockIdx.y, b = blockIdx.z;
+  const int wave = tid >> 6, lane = tid & 63, col = lane & 31;
   const int group = a.n_heads / a.n_kv_heads;
-  const int h = g * group + wave;
+  const int nqg = static_cast<int>(ceil_div(a.T, kQG));
   const float sc = a.scale_log2;
-  const int n_items = 128;   // tile work items
 
-  // ---- resident meta tiles -------------------------------------------------
-  const int mpad = static_cast<int>(ceil_div(a.n_meta, kKT)) * kKT;
-  for (int t0 = 0; t0 < mpad; t0 += kKT) {
-    for (int it = tid; it < n_items; it += nthreads) {
-      TileRegs r;
-      tile_fetch(r, a.k_meta + (int64_t)t0 * a.ld_meta + g * kHd,
-                 a.v_meta + (int64_t)t0 * a.ld_meta + g * kHd, a.ld_meta, a.n_meta - t0, it);
-      tile_store(r, sm.km, sm.vm, kMetaVStr, t0, it);
-    }
+  // ---- work item: XCD-aware renumbering, then (b, g, qg, hh) ------------------
+  const int nwork = gridDim.x, L = blockIdx.x;
+  const int xcd = L % kXcds, j = L / kXcds, per = nwork / kXcds, extra = nwork % kXcds;
+  int work = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + j;
+  const int hh = work % group;
+  work /= group;
+  int b, g, qg;
+  if (a.window > 0) {
+    qg = work % nqg; work /= nqg;
+    g = work % a.n_kv_heads; b = work / a.n_kv_heads;
+  } else {
+    g = work % a.n_kv_heads; work /= a.n_kv_heads;
+    b = work % a.B; qg = nqg - 1 - work / a.B;
   }
-  __syncthreads();
+  const int h = g * group + hh;
+  const int q0 = qg * kQG;
+  const int qa = q0 + wave * kQB;               // this wave's first query
+  const bool wave_active = qa < a.T;
+  const int qlast = min(qa + kQB, a.T) - 1;     // this wave's last query
+  const int tq = min(qa + col, a.T - 1);
 
-  const int nqb = static_cast<int>(ceil_div(a.T, kQB));
-  const int work = gridDim.x - 1 - blockIdx.x;
-  const int qb0 = work * a.qb_per_wg;
-  const int qb1 = min(nqb, qb0 + a.qb_per_wg);
-  const int col = lane & 31;
-  const bool wave_active = wave < group;
-
+  // ---- key tiles: meta first, then the window span [lo, hi) ------------------
+  const int n_mt = static_cast<int>(ceil_div(a.n_meta, kKT));
+  const int lo = a.window > 0 ? max(0, q0 - a.window + 1) : 0;
+  const int hi = min(a.T, q0 + kQG);
+  const int n_tiles = n_mt + static_cast<int>(ceil_div(hi - lo, kKT));
   const ET* kseq = a.k + (int64_t)b * a.kv_seq_stride + g * kHd;
   const ET* vseq = a.v + (int64_t)b * a.kv_seq_stride + g * kHd;
+  const int ld_meta = static_cast<int>(a.ld_meta), ld_kv = static_cast<int>(a.ld_kv);
+  auto fetch = [&](TileRegs& r, int i) {
+    if (i < n_mt) {
+      const int64_t off = (int64_t)i * kKT * a.ld_meta + g * kHd;
+      tile_fetch(r, a.k_meta + off, a.v_meta + off, ld_meta, a.n_meta - i * kKT, tid);
+    } else {
+      const int t0 = lo + (i - n_mt) * kKT;
+      tile_fetch(r, kseq + (int64_t)t0 * a.ld_kv, vseq + (int64_t)t0 * a.ld_kv, ld_kv, hi - t0, tid);
+    }
+  };
 
-  for (int qb = qb0; qb < qb1; ++qb) {
-    const int q0 = qb * kQB;
-    const int tq = min(q0 + col, a.T - 1);
-    // Q^T fragments: k-step s holds dims 16 s + 8 (lane/32) .. +7 of query tq
-    typename Op<ET>::vec qf[4];
-    {
-      // a helper wave (no head of its own) reads the group's first head
-      const int hq = wave_active ? h : g * group;
-      const ET* qrow = a.q + ((int64_t)b * a.T + tq) * a.ld_q + hq * kHd + (lane >> 5) * 8;
+  // Q^T fragments: k-step s holds dims 16 s + 8 (lane/32) .. +7 of query tq
+  typename Op<ET>::vec qf[4];
+  {
+    const ET* qrow = a.q + ((int64_t)b * a.T + tq) * a.ld_q + h * kHd + (lane >> 5) * 8;
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) qf[s4] = as_vec<ET>(*reinterpret_cast<const U4*>(qrow + s4 * 16));
-    }
-    WaveState st;
-    st.acc[0] = f32x16_t{};
-    st.acc[1] = f32x16_t{};
-    st.m = -1e30f;
-    st.l = 0.f;
+    for (int s4 = 0; s4 < 4; ++s4) qf[s4] = as_vec<ET>(*reinterpret_cast<const U4*>(qrow + s4 * 16));
+  }
+  WaveState st;
+  st.acc[0] = f32x16_t{};
+  st.acc[1] = f32x16_t{};
+  st.m = -1e30f;
+  st.l = 0.f;
 
-    // meta keys: visible to every real query; mask only the padding tail
-    if (wave_active) {
-      for (int t0 = 0; t0 < mpad; t0 += kKT) {
-        if (t0 + kKT <= a.n_meta)
-          attend_tile<ET, false>(st, qf, sm.km + t0 * kKStr, sm.vm + t0, kMetaVStr, sc, lane, t0, 0,
-                                 a.n_meta, -1, 0);
-        else
-          attend_tile<ET, true>(st, qf, sm.km + t0 * kKStr, sm.vm + t0, kMetaVStr, sc, lane, t0, 0,
-                                a.n_meta, -1, 0);
-      }
+  TileRegs pre;
+  fetch(pre, 0);
+  for (int i = 0; i < n_tiles; ++i) {
+    const int buf = i & 1;
+    tile_store(pre, sm.kw[buf], sm.vw[buf], tid);
+    __syncthreads();
+    if (i + 1 < n_tiles) fetch(pre, i + 1);
+    if (!wave_active) continue;
+    int key0, lo_key, hi_key, tqm;
+    bool mask;
+    if (i < n_mt) {
+      // meta keys: visible to every real query; only the padding tail is masked
+      key0 = i * kKT; lo_key = 0; hi_key = a.n_meta; tqm = -1;
+      mask = key0 + kKT > a.n_meta;
+    } else {
+      const int t0 = lo + (i - n_mt) * kKT;
+      // skip tiles no query of this wave can see
+      if (t0 > qlast || (a.window > 0 && t0 + kKT - 1 <= qa - a.window)) continue;
+      key0 = t0; lo_key = t0; hi_key = hi; tqm = tq;
+      mask = !((t0 + kKT - 1 <= qa) && (a.window <= 0 || t0 > qlast - a.window) && (t0 + kKT <= hi));
     }
+    attend_tile<ET>(st, qf, sm.kw[buf], sm.vw[buf], kVStr, sc, lane, key0, lo_key, hi_key, tqm, a.window, mask);
+  }
 
-    // window keys [lo, hi)
-    const int qlast = min(q0 + kQB, a.T) - 1;
-    const int lo = a.window > 0 ? max(0, q0 - a.window + 1) : 0;
-    const int hi = qlast + 1;
-    const int ntiles = static_cast<int>(ceil_div(hi - lo, kKT));
-    TileRegs pre;
-    if (tid < n_items)
-      tile_fetch(pre, kseq + (int64_t)lo * a.ld_kv, vseq + (int64_t)lo * a.ld_kv, a.ld_kv,
-                 hi - lo, tid);
-    for (int i = 0; i < ntiles; ++i) {
-      const int buf = i & 1;
-      const int t0 = lo + i * kKT;
-      if (tid < n_items) tile_store(pre, sm.kw[buf], sm.vw[buf], kVStr, 0, tid);
-      __syncthreads();
-      if (i + 1 < ntiles && tid < n_items) {
-        const int t1 = t0 + kKT;
-        tile_fetch(pre, kseq + (int64_t)t1 * a.ld_kv, vseq + (int64_t)t1 * a.ld_kv, a.ld_kv,
-                   hi - t1, tid);
-      }
-      if (wave_active) {
-        // the tile needs a mask unless every key is visible to every query of the block
-        const bool full = (t0 + kKT - 1 <= q0) && (a.window <= 0 || t0 > qlast - a.window) &&
-                          (t0 + kKT <= hi);
-        if (full)
-          attend_tile<ET, false>(st, qf, sm.kw[buf], sm.vw[buf], kVStr, sc, lane, t0, t0, hi, tq, a.window);
-        else
-          attend_tile<ET, true>(st, qf, sm.kw[buf], sm.vw[buf], kVStr, sc, lane, t0, t0, hi, tq, a.window);
-      }
-    }
-
-    if (wave_active) {
-      const float ltot = st.l + __shfl_xor(st.l, 32);
-      const float inv = 1.f / ltot;
-      const int t = q0 + col;
-      if (t < a.T) {
-        ET* orow = a.o + ((int64_t)b * a.T + t) * a.ld_o + h * kHd;
-        const int half = lane >> 5;
+  if (wave_active) {
+    const float ltot = sum_xor32(st.l);
+    const float inv = 1.f / ltot;
+    const int t = qa + col;
+    if (t < a.T) {
+      ET* orow = a.o + ((int64_t)b * a.T + t) * a.ld_o + h * kHd;
+      const int half = lane >> 5;
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+      for (int db = 0; db < 2; ++db)
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int dim = db * 32 + 8 * r4 + 4 * half;
-            uint2 w;
-            w.x = Pair<ET>::pack(st.acc[db][r4 * 4 + 0] * inv, st.acc[db][r4 * 4 + 1] * inv);
-            w.y = Pair<ET>::pack(st.acc[db][r4 * 4 + 2] * inv, st.acc[db][r4 * 4 + 3] * inv);
-            *reinterpret_cast<uint2*>(orow + dim) = w;
-          }
-      }
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int dim = db * 32 + 8 * r4 + 4 * half;
+          uint2 w;
+          w.x = Pair<ET>::pack(st.acc[db][r4 * 4 + 0] * inv, st.acc[db][r4 * 4 + 1] * inv);
+          w.y = Pair<ET>::pack(st.acc[db][r4 * 4 + 2] * inv, st.acc[db][r4 * 4 + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + dim) = w;
+        }
     }
-    __syncthreads();   // window buffers are reused by the next query block
   }
 }
 
@@ -386,21 +427,11 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs<float> a) {
 
 
 template <typename ET>
-hipError_t launch_mfma(const AttnArgs<ET>& args, hipStream_t stream) {
-  AttnArgs<ET> a = args;
+hipError_t launch_mfma(const AttnArgs<ET>& a, hipStream_t stream) {
   const int group = a.n_heads / a.n_kv_heads;
-  const int nqb = static_cast<int>(ceil_div(a.T, kQB));
-  if (a.qb_per_wg <= 0) {
-    // enough workgroups to fill the chip, but long runs so the meta tiles stay useful
-    const int64_t per_seq_head = (int64_t)a.B * a.n_kv_heads;
-    int q = 4;
-    while (q > 1 && per_seq_head * ceil_div(nqb, q) < 2048) q >>= 1;
-    a.qb_per_wg = q;
-  }
-  const int nwork = static_cast<int>(ceil_div(nqb, a.qb_per_wg));
-  dim3 grid(nwork, a.n_kv_heads, a.B);
-  dim3 block(64 * (group < 2 ? 2 : group));
-  hipLaunchKernelGGL((swa_meta_attn_kernel<ET>), grid, block, 0, stream, a);
+  const int64_t nwork = (int64_t)a.B * a.n_kv_heads * group * ceil_div(a.T, kQG);
+  if (nwork > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((swa_meta_attn_kernel<ET>), dim3(static_cast<unsigned>(nwork)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -421,8 +452,7 @@ hipError_t launch_attn_prefill_f32(const AttnArgs<float>& a, hipStream_t stream)
 }
 
 bool attn_mfma_supported(int head_dim, int n_heads, int n_kv_heads, int n_meta) {
-  return head_dim == kHd && n_kv_heads > 0 && n_heads % n_kv_heads == 0 &&
-         n_heads / n_kv_heads <= kMaxWaves && n_meta <= kMaxMeta;
+  return head_dim == kHd && n_kv_heads > 0 && n_heads % n_kv_heads == 0 && n_meta >= 0;
 }
 
 }  // namespace hymba

@@ -136,9 +136,8 @@ int32_t check_cfg(const hymba_layer_cfg* c) {
   if (c->d_inner % 8 != 0) return fail(HYMBA_ERR_UNSUPPORTED, "d_inner must be a multiple of 8");
   if (c->d_model % 8 != 0) return fail(HYMBA_ERR_UNSUPPORTED, "d_model must be a multiple of 8");
   if (c->dtype == HYMBA_BF16) {
-    if (!attn_mfma_supported(c->head_dim, c->n_heads, c->n_kv_heads, c->n_meta))
-      return fail(HYMBA_ERR_UNSUPPORTED,
-                  "bf16 layers need head_dim 64, n_heads/n_kv_heads <= 8 and n_meta <= 128");
+    if (!attn_mfma_supported(c->head_dim, c->n_heads, c->n_kv_heads, c->n_meta) || c->n_heads / c->n_kv_heads > 8)
+      return fail(HYMBA_ERR_UNSUPPORTED, "bf16 layers need head_dim 64 and n_heads/n_kv_heads <= 8");
   } else {
     if (c->head_dim != 32 && c->head_dim != 64)
       return fail(HYMBA_ERR_UNSUPPORTED, "fp32 attention needs head_dim 32 or 64");
@@ -228,7 +227,7 @@ int32_t run_attention(const hymba_layer_cfg& c, const CT* q, int64_t ld_q, const
   a.k_meta = k_meta; a.v_meta = v_meta; a.ld_meta = (int64_t)c.n_kv_heads * c.head_dim; a.n_meta = n_meta;
   a.o = o; a.ld_o = ld_o;
   a.B = B; a.T = T_; a.n_heads = c.n_heads; a.n_kv_heads = c.n_kv_heads; a.head_dim = c.head_dim;
-  a.window = window; a.qb_per_wg = 0;
+  a.window = window;
   a.scale_log2 = kLog2e / std::sqrt(static_cast<float>(c.head_dim));
   if constexpr (sizeof(CT) == 2) {
     HIP_TRY(launch_attn_prefill_mfma(a, s), "attention launch");
@@ -728,6 +727,12 @@ int32_t hymba_kernel_attention(int32_t dtype, const void* q, int64_t ld_q, const
   if (dtype == HYMBA_F16 || dtype == HYMBA_BF16) {
     if (!attn_mfma_supported(head_dim, n_heads, n_kv_heads, n_meta))
       return fail(HYMBA_ERR_UNSUPPORTED, "16-bit attention shape not supported");
+    // 16-byte rows for the vector loads; row offsets within a 64-key tile fit 32 bits
+    const int64_t hq = (int64_t)n_heads * head_dim, hkv = (int64_t)n_kv_heads * head_dim;
+    if (ld_q < hq || ld_o < hq || ld_kv < hkv || ld_q % 8 || ld_o % 8 || ld_kv % 8 || kv_seq_stride % 8 ||
+        ld_kv >= (1 << 24) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        (n_meta > 0 && (!aligned(k_meta, 16) || !aligned(v_meta, 16))))
+      return fail(HYMBA_ERR_INVALID_ARG, "strides: rows >= heads * hd, multiples of 8 elements, 16-byte aligned");
     if (dtype == HYMBA_F16)
       return run_attention<half_t>(c, static_cast<const half_t*>(q), ld_q, static_cast<const half_t*>(k),
                                    static_cast<const half_t*>(v), ld_kv, kv_seq_stride,

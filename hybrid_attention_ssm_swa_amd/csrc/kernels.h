@@ -21,7 +21,7 @@ struct AttnArgs {
   const ET* k; const ET* v; int64_t ld_kv; int64_t kv_seq_stride;
   const ET* k_meta; const ET* v_meta; int64_t ld_meta; int n_meta;
   ET* o; int64_t ld_o;
-  int B, T, n_heads, n_kv_heads, head_dim, window, qb_per_wg;
+  int B, T, n_heads, n_kv_heads, head_dim, window;
   float scale_log2;   // log2(e) / sqrt(hd)
 };
 // MFMA kernel (hd = 64), fp16 or bf16 operands, fp32 accumulation.

@@ -78,7 +78,7 @@ typedef struct hymba_layer_cfg {
   int32_t head_dim;   /* hd: 64 for bf16; 32 or 64 for fp32                        */
   int32_t d_inner;    /* E: SSM channels = fused width (multiple of 8)             */
   int32_t d_state;    /* N: SSM state per channel (8 or 16)                        */
-  int32_t n_meta;     /* M meta tokens (0..128)                                    */
+  int32_t n_meta;     /* M meta tokens (>= 0)                                       */
   int32_t window;     /* > 0: sliding window of real keys incl. self; <= 0: global */
   int32_t own_kv;     /* 1: projects its own K/V (producer); 0: consumer           */
   int32_t dtype;      /* HYMBA_F32 or HYMBA_BF16                                   */

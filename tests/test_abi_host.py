@@ -69,7 +69,7 @@ def test_status_strings():
     (dict(d_state=12), L.HYMBA_ERR_UNSUPPORTED),
     (dict(head_dim=48), L.HYMBA_ERR_UNSUPPORTED),
     (dict(dtype=L.HYMBA_BF16, head_dim=32), L.HYMBA_ERR_UNSUPPORTED),
-    (dict(dtype=L.HYMBA_BF16, head_dim=64, n_meta=200), L.HYMBA_ERR_UNSUPPORTED),
+    (dict(dtype=L.HYMBA_BF16, head_dim=64, n_heads=18, n_kv_heads=2), L.HYMBA_ERR_UNSUPPORTED),
     (dict(d_inner=60), L.HYMBA_ERR_UNSUPPORTED),
 ])
 def test_create_rejects_bad_configs(kw, code):
@@ -78,6 +78,10 @@ def test_create_rejects_bad_configs(kw, code):
     with pytest.raises(L.HymbaError) as e:
         L.hymba_layer_create(cfg, _weights(), FAKE, 1 << 30)
     assert e.value.status == code
+
+
+def test_long_meta_prefix_is_accepted():
+    assert L.hymba_layer_persistent_bytes(_cfg(dtype=L.HYMBA_BF16, head_dim=64, n_meta=200)) > 0
 
 
 def test_create_checks_buffers():
@@ -201,3 +205,14 @@ def test_scan_entry_checks_strides():
             L.hymba_kernel_selective_scan(L.HYMBA_F16, FAKE, FAKE, ld, bc, ld_bc, FAKE, FAKE, FAKE, None, FAKE, ldy,
                                           None, 1, 4, 8, 8, FAKE, 1 << 20, None)
         assert e.value.status == L.HYMBA_ERR_INVALID_ARG
+
+
+def test_attention_entry_checks_strides():
+    ok = dict(ld_q=640, ld_kv=128, stride=128 * 40, q=FAKE, o=FAKE)
+    for bad in [dict(ld_q=636), dict(ld_kv=120), dict(ld_kv=130), dict(stride=128 * 40 + 4), dict(q=FAKE + 8),
+                dict(o=FAKE + 2)]:
+        a = dict(ok, **bad)
+        with pytest.raises(L.HymbaError) as e:
+            L.hymba_kernel_attention(L.HYMBA_F16, a["q"], a["ld_q"], FAKE, FAKE, a["ld_kv"], a["stride"], FAKE, FAKE,
+                                     4, a["o"], 640, 1, 40, 10, 2, 64, 16, None)
+        assert e.value.status == L.HYMBA_ERR_INVALID_ARG, bad

@@ -33,6 +33,7 @@ ATTN_CASES = [
     ("f16", 1, 200, 0, 4, 4, 64, 64),
     ("f16", 2, 130, 16, 8, 1, 64, 40),
     ("f16", 1, 2100, 128, 25, 5, 64, 1024),
+    ("f16", 2, 150, 200, 8, 2, 64, 50),
     ("bf16", 2, 300, 40, 10, 2, 64, 100),
     ("bf16", 1, 130, 128, 8, 1, 64, 0),
     ("f32", 2, 150, 16, 2, 2, 32, 32),
@@ -42,9 +43,20 @@ ATTN_CASES = [
 
 @pytest.mark.parametrize("dtype,B,T,M,Hq,Hkv,hd,W", ATTN_CASES)
 def test_attention_kernel(dtype, B, T, M, Hq, Hkv, hd, W):
-    announce(f"attention {dtype} B={B} T={T} M={M} H={Hq} Hkv={Hkv} hd={hd} W={W}")
+    _attention_case(dtype, B, T, M, Hq, Hkv, hd, W)
+
+
+@pytest.mark.parametrize("dtype,qs", [("f16", 4.0), ("bf16", 4.0), ("f16", 12.0)])
+def test_attention_kernel_peaked_scores(dtype, qs):
+    """Queries scaled so scores spread over tens of units: the running max moves by more than the
+    lazy-rescale threshold across tiles, and most probabilities underflow."""
+    _attention_case(dtype, 2, 700, 100, 10, 2, 64, 300, qs)
+
+
+def _attention_case(dtype, B, T, M, Hq, Hkv, hd, W, qs=1.0):
+    announce(f"attention {dtype} B={B} T={T} M={M} H={Hq} Hkv={Hkv} hd={hd} W={W} qscale={qs}")
     r = np.random.Generator(np.random.PCG64(100 + T + M + W))
-    q = _round(r.standard_normal((B, T, Hq, hd)).astype(np.float32), dtype)
+    q = _round(qs * r.standard_normal((B, T, Hq, hd)).astype(np.float32), dtype)
     k = _round(r.standard_normal((B, T, Hkv, hd)).astype(np.float32), dtype)
     v = _round(r.standard_normal((B, T, Hkv, hd)).astype(np.float32), dtype)
     km = _round(r.standard_normal((M, Hkv, hd)).astype(np.float32), dtype)
