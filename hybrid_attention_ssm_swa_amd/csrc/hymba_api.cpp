@@ -38,6 +38,10 @@ struct hymba_layer {
   half_t* w_o16 = nullptr;
   half_t* w_out16 = nullptr;
   bool prepared = false;
+  // second stream of a prefill (the SSM branch runs beside attention and W_O), created on first use
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  int side_device = -1;
   bool weights_ready = false;
   const hymba_layer* producer = nullptr;   // consumer: bound producer
   const hymba_layer* consumer = nullptr;   // producer: its bound consumer (pairs only)
@@ -274,17 +278,22 @@ int32_t in_projection(const hymba_layer& L, const void* x, int64_t rows, char* w
                  s);
 }
 
-// W_O, fused epilogue, output projection of `rows` rows; y_out in storage type.
+// W_O of `rows` rows: attention output O -> Ao.
 template <typename CT>
-int32_t tail(const hymba_layer& L, char* ws, const WsLayout& wl, int64_t rows, void* y_out, hipStream_t s) {
+int32_t w_o_projection(const hymba_layer& L, char* ws, const WsLayout& wl, int64_t rows, hipStream_t s) {
   const hymba_layer_cfg& c = L.cfg;
   const int64_t hq = (int64_t)c.n_heads * c.head_dim;
+  StageTimer st(L, ST_WO, s);
+  return project(L, ws + wl.O, hq, is_bf16(c) ? (const void*)L.w_o16 : L.w.w_o, hq, ws + wl.Ao, c.d_inner, rows,
+                 c.d_inner, hq, false, ws, wl, s);
+}
+
+// Fused epilogue and output projection of `rows` rows; y_out in storage type.
+template <typename CT>
+int32_t epilogue_and_out(const hymba_layer& L, char* ws, const WsLayout& wl, int64_t rows, void* y_out,
+                         hipStream_t s) {
+  const hymba_layer_cfg& c = L.cfg;
   const bool b16 = is_bf16(c);
-  {
-    StageTimer st(L, ST_WO, s);
-    STATUS_TRY(project(L, ws + wl.O, hq, b16 ? (const void*)L.w_o16 : L.w.w_o, hq, ws + wl.Ao, c.d_inner, rows,
-                       c.d_inner, hq, false, ws, wl, s));
-  }
   {
     StageTimer st(L, ST_EPI, s);
     EpiArgs<CT> e{};
@@ -312,6 +321,31 @@ int32_t tail(const hymba_layer& L, char* ws, const WsLayout& wl, int64_t rows, v
   StageTimer st(L, ST_OUT, s);
   return project(L, ws + wl.F, c.d_inner, L.w.w_out, c.d_inner, y_out, c.d_model, rows, c.d_model, c.d_inner,
                  false, ws, wl, s);
+}
+
+// W_O, fused epilogue, output projection on one stream.
+template <typename CT>
+int32_t tail(const hymba_layer& L, char* ws, const WsLayout& wl, int64_t rows, void* y_out, hipStream_t s) {
+  STATUS_TRY(w_o_projection<CT>(L, ws, wl, rows, s));
+  return epilogue_and_out<CT>(L, ws, wl, rows, y_out, s);
+}
+
+// The side stream and fork/join events of a layer on the current device.
+int32_t ensure_side_stream(hymba_layer& L) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  if (L.side && L.side_device == dev) return HYMBA_OK;
+  if (L.side) {
+    hipStreamDestroy(L.side);
+    hipEventDestroy(L.ev_fork);
+    hipEventDestroy(L.ev_join);
+    L.side = nullptr;
+  }
+  HIP_TRY(hipStreamCreateWithFlags(&L.side, hipStreamNonBlocking), "side stream create");
+  HIP_TRY(hipEventCreateWithFlags(&L.ev_fork, hipEventDisableTiming), "event create");
+  HIP_TRY(hipEventCreateWithFlags(&L.ev_join, hipEventDisableTiming), "event create");
+  L.side_device = dev;
+  return HYMBA_OK;
 }
 
 template <typename CT>
@@ -432,17 +466,25 @@ int32_t prefill_impl(hymba_layer& L, const void* x, int B, int T_, void* y, cons
   }
   const void *km, *vm;
   meta_kv_of(L, kv, &km, &vm);
+  // The SSM branch depends only on the projection: it runs on the layer's side stream beside
+  // attention and W_O, and the epilogue waits for both.
+  STATUS_TRY(ensure_side_stream(L));
+  HIP_TRY(hipEventRecord(L.ev_fork, s), "fork event");
+  HIP_TRY(hipStreamWaitEvent(L.side, L.ev_fork, 0), "fork wait");
+  {
+    StageTimer st(L, ST_SSM, L.side);
+    HIP_TRY(launch_selective_scan(scan_args<CT>(L, ws, wl, B, T_, L.h_meta, state_out), L.side), "scan launch");
+  }
+  HIP_TRY(hipEventRecord(L.ev_join, L.side), "join event");
   {
     StageTimer st(L, ST_ATTN, s);
     STATUS_TRY(run_attention<CT>(c, P, L.n_in, k, v, ld_kv, seq_stride, static_cast<const CT*>(km),
                                  static_cast<const CT*>(vm), c.n_meta, reinterpret_cast<CT*>(ws + wl.O),
                                  (int64_t)c.n_heads * c.head_dim, B, T_, c.window, s));
   }
-  {
-    StageTimer st(L, ST_SSM, s);
-    HIP_TRY(launch_selective_scan(scan_args<CT>(L, ws, wl, B, T_, L.h_meta, state_out), s), "scan launch");
-  }
-  return tail<CT>(L, ws, wl, rows, y, s);
+  STATUS_TRY(w_o_projection<CT>(L, ws, wl, rows, s));
+  HIP_TRY(hipStreamWaitEvent(s, L.ev_join, 0), "join wait");
+  return epilogue_and_out<CT>(L, ws, wl, rows, y, s);
 }
 
 template <typename CT>
@@ -548,6 +590,11 @@ int32_t hymba_layer_create(const hymba_layer_cfg* cfg, const hymba_layer_weights
 void hymba_layer_destroy(hymba_layer* L) {
   if (!L) return;
   for (hipEvent_t e : L->ev) hipEventDestroy(e);
+  if (L->side) {
+    hipStreamDestroy(L->side);
+    hipEventDestroy(L->ev_fork);
+    hipEventDestroy(L->ev_join);
+  }
   if (L->producer && L->producer->consumer == L) const_cast<hymba_layer*>(L->producer)->consumer = nullptr;
   if (L->consumer && L->consumer->producer == L) const_cast<hymba_layer*>(L->consumer)->producer = nullptr;
   delete L;

@@ -156,7 +156,11 @@ int32_t hymba_layer_prepare(hymba_layer* layer, const hymba_kv* kv, void* worksp
 
 /* Prefill of B sequences of T real tokens, continuing from the meta prefix.
  * x [B, T, d] -> y [B, T, d].  ssm_state_out [B, E, N] fp32 receives the final
- * SSM state (may be NULL).  kv as described above. */
+ * SSM state (may be NULL).  kv as described above.
+ * The SSM branch runs on a second stream owned by the layer (created on the
+ * first prefill on the current device, non-blocking, default priority),
+ * forked from and joined back into `stream` with events: to the caller all
+ * work is ordered on `stream`, and the pattern is legal under graph capture. */
 int32_t hymba_mixer_prefill(hymba_layer* layer, const void* x, int32_t B, int32_t T, void* y,
                             const hymba_kv* kv, float* ssm_state_out, void* workspace,
                             size_t workspace_bytes, void* stream);
