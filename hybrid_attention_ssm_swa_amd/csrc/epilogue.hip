@@ -6,9 +6,11 @@
 // outputs are normalised and scaled by learnable per-channel vectors because
 // the SSM output is consistently larger, then summed.
 //
-// One wave per token row; each lane keeps up to MAXC 16-byte chunks of Ao and
-// g in registers between the reduction and the write, so every input byte is
-// read from HBM once.  Rows wider than 64 * MAXC chunks re-read the tail.
+// One 256-thread workgroup per token row: each thread keeps up to MAXC
+// 16-byte chunks of Ao and g in registers between the two row reductions
+// (wave sums, then across the four waves through LDS) and the write, so every
+// input byte is read from HBM once and small register use keeps eight waves
+// per SIMD in flight.  Rows wider than 256 * MAXC chunks re-read the tail.
 #include "common.h"
 #include "kernels.h"
 
@@ -16,28 +18,36 @@ namespace hymba {
 
 namespace {
 
+// Sum over the 64 lanes: xor swizzles within each half, then the two halves.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x041F));   // xor 1
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x081F));   // xor 2
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));   // xor 4
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x201F));   // xor 8
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));   // xor 16
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <typename T, int MAXC>
-__global__ __launch_bounds__(256) void epilogue_kernel(EpiArgs<T> a) {
+constexpr int kEpiThreads = 256;
+
+template <typename T, typename FT, int MAXC>
+__global__ __launch_bounds__(kEpiThreads) void epilogue_kernel(EpiArgs<T, FT> a) {
   constexpr int V = Vec16<T>::n;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-  if (row >= a.rows) return;   // whole wave leaves; no workgroup barrier below
+  static_assert(Vec16<FT>::n == V, "output chunks must hold the same element count");
+  __shared__ float part[2][kEpiThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
   const T* ao = a.ao + row * a.ld_ao;
   const T* yy = a.y + row * a.ld_y;
   const T* zz = a.z + row * a.ld_z;
-  T* ff = a.f + row * a.ld_f;
+  FT* ff = a.f + row * a.ld_f;
   const int nch = a.E / V;
   float xa[MAXC][V], xg[MAXC][V];
   float ss1 = 0.f, ss2 = 0.f;
 #pragma unroll
   for (int k = 0; k < MAXC; ++k) {
-    const int ch = lane + 64 * k;
+    const int ch = tid + kEpiThreads * k;
     if (ch < nch) {
       float yv[V], zv[V];
       Vec16<T>::load(ao + ch * V, xa[k]);
@@ -51,7 +61,7 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EpiArgs<T> a) {
       }
     }
   }
-  for (int ch = lane + 64 * MAXC; ch < nch; ch += 64) {
+  for (int ch = tid + kEpiThreads * MAXC; ch < nch; ch += kEpiThreads) {
     float av[V], yv[V], zv[V];
     Vec16<T>::load(ao + ch * V, av);
     Vec16<T>::load(yy + ch * V, yv);
@@ -65,12 +75,24 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EpiArgs<T> a) {
   }
   ss1 = wave_sum(ss1);
   ss2 = wave_sum(ss2);
+  if (lane == 0) {
+    part[0][wave] = ss1;
+    part[1][wave] = ss2;
+  }
+  __syncthreads();
+  ss1 = 0.f;
+  ss2 = 0.f;
+#pragma unroll
+  for (int w = 0; w < kEpiThreads / 64; ++w) {
+    ss1 += part[0][w];
+    ss2 += part[1][w];
+  }
   const float inv_e = 1.f / static_cast<float>(a.E);
   const float r1 = 1.f / sqrtf(ss1 * inv_e + a.eps);
   const float r2 = 1.f / sqrtf(ss2 * inv_e + a.eps);
 #pragma unroll
   for (int k = 0; k < MAXC; ++k) {
-    const int ch = lane + 64 * k;
+    const int ch = tid + kEpiThreads * k;
     if (ch < nch) {
       float out[V];
 #pragma unroll
@@ -78,10 +100,10 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EpiArgs<T> a) {
         const int e = ch * V + j;
         out[j] = fmaf(a.beta1[e] * r1, xa[k][j], a.beta2[e] * r2 * xg[k][j]);
       }
-      Vec16<T>::store(ff + ch * V, out);
+      Vec16<FT>::store(ff + ch * V, out);
     }
   }
-  for (int ch = lane + 64 * MAXC; ch < nch; ch += 64) {
+  for (int ch = tid + kEpiThreads * MAXC; ch < nch; ch += kEpiThreads) {
     float av[V], yv[V], zv[V], out[V];
     Vec16<T>::load(ao + ch * V, av);
     Vec16<T>::load(yy + ch * V, yv);
@@ -91,21 +113,25 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EpiArgs<T> a) {
       const int e = ch * V + j;
       out[j] = fmaf(a.beta1[e] * r1, av[j], a.beta2[e] * r2 * (yv[j] * silu_f(zv[j])));
     }
-    Vec16<T>::store(ff + ch * V, out);
+    Vec16<FT>::store(ff + ch * V, out);
   }
 }
 
-template <typename T>
-hipError_t epi_dispatch(const EpiArgs<T>& a, hipStream_t s) {
+template <typename T, typename FT>
+hipError_t epi_dispatch(const EpiArgs<T, FT>& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
-  dim3 grid(static_cast<unsigned>(ceil_div(a.rows, 4))), block(256);
-  hipLaunchKernelGGL((epilogue_kernel<T, 8>), grid, block, 0, s, a);
+  dim3 grid(static_cast<unsigned>(a.rows)), block(kEpiThreads);
+  const int nch = a.E / Vec16<T>::n;
+  if (nch <= kEpiThreads)
+    hipLaunchKernelGGL((epilogue_kernel<T, FT, 1>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((epilogue_kernel<T, FT, 2>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_epilogue(const EpiArgs<float>& a, hipStream_t s) { return epi_dispatch(a, s); }
-hipError_t launch_epilogue(const EpiArgs<half_t>& a, hipStream_t s) { return epi_dispatch(a, s); }
+hipError_t launch_epilogue(const EpiArgs<half_t, bf16_t>& a, hipStream_t s) { return epi_dispatch(a, s); }
 
 }  // namespace hymba

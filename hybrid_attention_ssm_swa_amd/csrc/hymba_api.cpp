@@ -17,6 +17,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <new>
+#include <type_traits>
 #include <string>
 #include <vector>
 
@@ -36,7 +37,6 @@ struct hymba_layer {
   float* A2 = nullptr;         // [E, N] A * log2(e)
   half_t* w_in16 = nullptr;    // bf16 layers: fp16 copies of the weights
   half_t* w_o16 = nullptr;
-  half_t* w_out16 = nullptr;
   bool prepared = false;
   // second stream of a prefill (the SSM branch runs beside attention and W_O), created on first use
   hipStream_t side = nullptr;
@@ -152,7 +152,7 @@ int32_t check_cfg(const hymba_layer_cfg* c) {
 }
 
 struct PersistLayout {
-  size_t k_meta, v_meta, h_meta, y_meta, A2, w_in16, w_o16, w_out16, total;
+  size_t k_meta, v_meta, h_meta, y_meta, A2, w_in16, w_o16, total;
 };
 
 PersistLayout persist_layout(const hymba_layer_cfg& c) {
@@ -169,14 +169,13 @@ PersistLayout persist_layout(const hymba_layer_cfg& c) {
     const size_t hq = (size_t)c.n_heads * c.head_dim;
     p.w_in16 = off; off += align_up((size_t)n_in_of(c) * c.d_model * 2);
     p.w_o16 = off; off += align_up((size_t)c.d_inner * hq * 2);
-    p.w_out16 = off; off += align_up((size_t)c.d_model * c.d_inner * 2);
   }
   p.total = off;
   return p;
 }
 
 struct WsLayout {
-  size_t X16, P, bc32, O, Ao, Ys, F, Y32, gemm, part, total;
+  size_t X16, P, bc32, O, Ao, Ys, F, gemm, part, total;
   int64_t rows;
 };
 
@@ -195,7 +194,6 @@ WsLayout ws_layout(const hymba_layer& L, int64_t batch, int64_t seq) {
   w.Ao = off; off += align_up((size_t)rows * c.d_inner * as);
   w.Ys = off; off += align_up((size_t)rows * c.d_inner * as);
   w.F = off; off += align_up((size_t)rows * c.d_inner * as);
-  w.Y32 = off; off += b16 ? align_up((size_t)rows * c.d_model * 4) : 0;
   w.gemm = off; off += b16 ? kGemmWorkspaceBytes : 0;
   w.part = off;
   off += align_up((size_t)std::max<int64_t>(batch, 1) * c.n_heads * kDecodeMaxSplits * (c.head_dim + 2) * 4);
@@ -204,14 +202,16 @@ WsLayout ws_layout(const hymba_layer& L, int64_t batch, int64_t seq) {
 }
 
 // Y[rows, out] = X[rows, in] . W[out, in]^T.  fp32 layers: fp32 kernel.  bf16
-// layers: fp16 operands through hipBLASLt, output fp16 (out32 = false) or fp32.
+// layers: hipBLASLt with fp32 accumulation; fp16 operands and output for the
+// input projection and W_O (bf16_out = false), bf16 operands and output for
+// the output projection (bf16_out = true).
 int32_t project(const hymba_layer& L, const void* X, int64_t ldx, const void* W, int64_t ldw, void* Y,
-                int64_t ldy, int64_t rows, int64_t out, int64_t in, bool out32, char* ws, const WsLayout& wl,
+                int64_t ldy, int64_t rows, int64_t out, int64_t in, bool bf16_out, char* ws, const WsLayout& wl,
                 hipStream_t s) {
   if (is_bf16(L.cfg)) {
     const char* err = nullptr;
-    const int r = gemm_16(GT_F16, out32 ? GT_F32 : GT_F16, X, ldx, W, ldw, Y, ldy, rows, out, in, ws + wl.gemm,
-                          kGemmWorkspaceBytes, s, &err);
+    const GemmType t = bf16_out ? GT_BF16 : GT_F16;
+    const int r = gemm_16(t, t, X, ldx, W, ldw, Y, ldy, rows, out, in, ws + wl.gemm, kGemmWorkspaceBytes, s, &err);
     if (r != 0) return fail(r == -2 ? HYMBA_ERR_UNSUPPORTED : HYMBA_ERR_HIP, "projection GEMM: %s", err);
     return HYMBA_OK;
   }
@@ -295,32 +295,23 @@ int32_t epilogue_and_out(const hymba_layer& L, char* ws, const WsLayout& wl, int
   const hymba_layer_cfg& c = L.cfg;
   const bool b16 = is_bf16(c);
   {
+    // bf16 layers write F as bf16: the output projection then multiplies the layer's own bf16
+    // W_out and writes y in bf16 directly (one rounding of the fp32 accumulator)
+    typedef typename std::conditional<std::is_same<CT, float>::value, float, bf16_t>::type FT;
     StageTimer st(L, ST_EPI, s);
-    EpiArgs<CT> e{};
+    EpiArgs<CT, FT> e{};
     const CT* P = reinterpret_cast<const CT*>(ws + wl.P);
     e.ao = reinterpret_cast<const CT*>(ws + wl.Ao); e.ld_ao = c.d_inner;
     e.y = reinterpret_cast<const CT*>(ws + wl.Ys); e.ld_y = c.d_inner;
     e.z = P + L.off_z; e.ld_z = L.n_in;
     e.beta1 = L.w.beta1; e.beta2 = L.w.beta2;
-    e.f = reinterpret_cast<CT*>(ws + wl.F); e.ld_f = c.d_inner;
+    e.f = reinterpret_cast<FT*>(ws + wl.F); e.ld_f = c.d_inner;
     e.rows = rows; e.E = c.d_inner; e.eps = c.rms_eps;
     HIP_TRY(launch_epilogue(e, s), "epilogue launch");
   }
-  if (b16) {
-    float* y32 = reinterpret_cast<float*>(ws + wl.Y32);
-    {
-      StageTimer st(L, ST_OUT, s);
-      STATUS_TRY(project(L, ws + wl.F, c.d_inner, L.w_out16, c.d_inner, y32, c.d_model, rows, c.d_model,
-                         c.d_inner, true, ws, wl, s));
-    }
-    StageTimer st(L, ST_CVT, s);
-    HIP_TRY(launch_convert(y32, c.d_model, static_cast<bf16_t*>(y_out), c.d_model, rows, c.d_model, s),
-            "output conversion");
-    return HYMBA_OK;
-  }
   StageTimer st(L, ST_OUT, s);
   return project(L, ws + wl.F, c.d_inner, L.w.w_out, c.d_inner, y_out, c.d_model, rows, c.d_model, c.d_inner,
-                 false, ws, wl, s);
+                 b16, ws, wl, s);
 }
 
 // W_O, fused epilogue, output projection on one stream.
@@ -380,8 +371,6 @@ int32_t prepare_impl(hymba_layer& L, const hymba_kv* kv, char* ws, const WsLayou
                              c.d_model, s), "weight conversion");
       HIP_TRY(launch_convert(static_cast<const bf16_t*>(L.w.w_o), hq, L.w_o16, hq, c.d_inner, hq, s),
               "weight conversion");
-      HIP_TRY(launch_convert(static_cast<const bf16_t*>(L.w.w_out), c.d_inner, L.w_out16, c.d_inner, c.d_model,
-                             c.d_inner, s), "weight conversion");
     }
     L.weights_ready = true;
   }
@@ -573,7 +562,6 @@ int32_t hymba_layer_create(const hymba_layer_cfg* cfg, const hymba_layer_weights
   if (is_bf16(*cfg)) {
     L->w_in16 = reinterpret_cast<half_t*>(base + pl.w_in16);
     L->w_o16 = reinterpret_cast<half_t*>(base + pl.w_o16);
-    L->w_out16 = reinterpret_cast<half_t*>(base + pl.w_out16);
   }
   const int64_t q = (int64_t)cfg->n_heads * cfg->head_dim, kvw = (int64_t)cfg->n_kv_heads * cfg->head_dim;
   L->n_in = n_in_of(*cfg);
@@ -833,10 +821,15 @@ int32_t hymba_kernel_epilogue(int32_t dtype, const void* ao, int64_t ld_ao, cons
   if (!ao || !y || !z || !beta1 || !beta2 || !f) return fail(HYMBA_ERR_INVALID_ARG, "NULL pointer");
   if (rows < 0 || E < 1) return fail(HYMBA_ERR_INVALID_ARG, "bad dimensions");
   if (E % 8) return fail(HYMBA_ERR_UNSUPPORTED, "E must be a multiple of 8");
+  const int64_t vw = dtype == HYMBA_F32 ? 4 : 8;
+  if (ld_ao < E || ld_y < E || ld_z < E || ld_f < E || ld_ao % vw || ld_y % vw || ld_z % vw || ld_f % vw ||
+      !aligned(ao, 16) || !aligned(y, 16) || !aligned(z, 16) || !aligned(f, 16))
+    return fail(HYMBA_ERR_INVALID_ARG, "strides: >= E, whole 16-byte chunks, 16-byte aligned rows");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == HYMBA_F16) {
-    EpiArgs<half_t> a{static_cast<const half_t*>(ao), ld_ao, static_cast<const half_t*>(y), ld_y,
-                      static_cast<const half_t*>(z), ld_z, beta1, beta2, static_cast<half_t*>(f), ld_f, rows, E, eps};
+    EpiArgs<half_t, bf16_t> a{static_cast<const half_t*>(ao), ld_ao, static_cast<const half_t*>(y), ld_y,
+                              static_cast<const half_t*>(z), ld_z, beta1, beta2, static_cast<bf16_t*>(f), ld_f,
+                              rows, E, eps};
     HIP_TRY(launch_epilogue(a, s), "epilogue launch");
   } else if (dtype == HYMBA_F32) {
     EpiArgs<float> a{static_cast<const float*>(ao), ld_ao, static_cast<const float*>(y), ld_y,

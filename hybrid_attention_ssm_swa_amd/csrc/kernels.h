@@ -64,17 +64,19 @@ hipError_t launch_ssm_step(const StepArgs<float>& a, hipStream_t s);
 hipError_t launch_ssm_step(const StepArgs<half_t>& a, hipStream_t s);
 
 // ---- fused epilogue: F = beta1*rms(Ao) + beta2*rms(y*silu(z)) ------------------
-template <typename CT>
+// Inputs in the activation type CT; the fused output F in FT (bf16 layers
+// write F as bf16, the operand type of their output projection).
+template <typename CT, typename FT = CT>
 struct EpiArgs {
   const CT* ao; int64_t ld_ao;
   const CT* y; int64_t ld_y;
   const CT* z; int64_t ld_z;
   const float* beta1; const float* beta2;
-  CT* f; int64_t ld_f;
+  FT* f; int64_t ld_f;
   int64_t rows; int E; float eps;
 };
 hipError_t launch_epilogue(const EpiArgs<float>& a, hipStream_t s);
-hipError_t launch_epilogue(const EpiArgs<half_t>& a, hipStream_t s);
+hipError_t launch_epilogue(const EpiArgs<half_t, bf16_t>& a, hipStream_t s);
 
 // ---- K/V movement -------------------------------------------------------------
 // Source rows (b*T + t) with KV head g at column g*hd.  Writes, when non-null,

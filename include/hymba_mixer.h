@@ -62,10 +62,11 @@ extern "C" {
  *   HYMBA_F32:  x, y, weights and activations fp32.
  *   HYMBA_BF16: x, y and weight matrices bf16; activations (the shared
  *               projection, attention operands/outputs, the K/V exchanged
- *               through hymba_kv and kept in caches, SSM and fused outputs)
- *               fp16 with fp32 accumulation; SSM state and the vector
- *               parameters fp32.  fp16 keeps 11 significand bits where bf16
- *               keeps 8, at the same MFMA rate and the same bytes moved.
+ *               through hymba_kv and kept in caches, the SSM output) fp16
+ *               with fp32 accumulation; the fused output F bf16 (the
+ *               operand of the bf16 output projection); SSM state and the
+ *               vector parameters fp32.  fp16 keeps 11 significand bits where
+ *               bf16 keeps 8, at the same MFMA rate and the same bytes moved.
  * HYMBA_F16 names fp16 operands for the per-kernel entry points only. */
 #define HYMBA_F32 0
 #define HYMBA_BF16 1
@@ -235,8 +236,10 @@ int32_t hymba_kernel_selective_scan(int32_t dtype, const void* u, const void* dt
                                     float* h_out, int32_t B, int32_t T, int32_t E, int32_t N,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
-/* Fused epilogue over `rows` tokens: F = beta1*rms(ao) + beta2*rms(y*SiLU(z))
- * (dtype HYMBA_F32 or HYMBA_F16). */
+/* Fused epilogue over `rows` tokens: F = beta1*rms(ao) + beta2*rms(y*SiLU(z)).
+ * dtype HYMBA_F32: everything fp32.  HYMBA_F16: ao, y, z fp16 and F bf16 (as
+ * in bf16 layers, whose output projection takes F in bf16).  Row strides are
+ * >= E and multiples of 8 elements (4 for fp32); pointers 16-byte aligned. */
 int32_t hymba_kernel_epilogue(int32_t dtype, const void* ao, int64_t ld_ao, const void* y,
                               int64_t ld_y, const void* z, int64_t ld_z, const float* beta1,
                               const float* beta2, void* f, int64_t ld_f, int64_t rows, int32_t E,

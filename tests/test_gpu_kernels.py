@@ -132,7 +132,8 @@ def test_selective_scan_kernel(dtype, B, T, E, N, with_h0):
         check(f"h_T[b={b}]", gh[b], rh, dtype)
 
 
-@pytest.mark.parametrize("dtype,rows,E", [("f16", 37, 3200), ("f16", 5, 64), ("f16", 3, 8200), ("f32", 19, 136)])
+@pytest.mark.parametrize("dtype,rows,E", [("f16", 37, 3200), ("f16", 5, 64), ("f16", 3, 8200), ("f16", 4, 2048),
+                                          ("f16", 2, 4104), ("f32", 19, 136), ("f32", 3, 2056)])
 def test_epilogue_kernel(dtype, rows, E):
     announce(f"epilogue {dtype} rows={rows} E={E}")
     r = np.random.Generator(np.random.PCG64(300 + rows + E))
@@ -142,7 +143,9 @@ def test_epilogue_kernel(dtype, rows, E):
     b1 = r.uniform(0.5, 1.5, E).astype(np.float32)
     b2 = r.uniform(0.5, 1.5, E).astype(np.float32)
     dao, dy, dz = dev(ao, dtype), dev(y, dtype), dev(zbig, dtype)
-    f = torch.empty((rows, E), dtype=dao.dtype, device="cuda")
+    # 16-bit inputs (fp16 activations) give a bf16 F, the operand type of the bf16 output projection
+    fdt = torch.bfloat16 if dtype == "f16" else torch.float32
+    f = torch.empty((rows, E), dtype=fdt, device="cuda")
     t32 = lambda a: torch.from_numpy(a).cuda()
     db1, db2 = t32(b1), t32(b2)
     es = dz.element_size()
@@ -152,4 +155,4 @@ def test_epilogue_kernel(dtype, rows, E):
     torch.cuda.synchronize()
     z = zbig[:, 8:8 + E].astype(np.float64)
     ref = orc.fuse(ao.astype(np.float64), y.astype(np.float64) * orc.silu(z), b1, b2, 1e-6)
-    check_stored("F", host(f), ref, dtype)
+    check_stored("F", host(f), ref, "bf16" if dtype == "f16" else dtype)
