@@ -3,19 +3,25 @@
 // column-major product Y^T = W^T-op(A = W) x X: A = W with op T (K-contiguous),
 // B = X with op N, both K-contiguous ("TN"), the layout MFMA GEMMs prefer.
 // Plans (descriptors + algorithm) are cached per device and shape.  The
-// algorithm is the fastest of hipBLASLt's heuristic candidates, timed once on
-// the first call's own operands and stream (skipped while the stream is being
-// captured, or when the environment sets HYMBA_GEMM_TUNE=0: then the first
-// candidate is taken).
+// algorithm is the fastest of hipBLASLt's heuristic candidates -- for GEMMs of
+// more than ~50 GFLOP also of the library's other kernels with the same macro
+// tile as its top picks -- timed once on the first call's own operands and
+// stream (skipped while the stream is being captured, or when the environment
+// sets HYMBA_GEMM_TUNE=0: then the first heuristic candidate is taken).  Real
+// operands matter: these GEMMs run power-limited, and bit toggling in the
+// data moves the clock.
 #include "gemm_blaslt.h"
 
 #include <hipblaslt/hipblaslt.h>
+#include <hipblaslt/hipblaslt-ext.hpp>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <string>
 #include <tuple>
 #include <vector>
 
@@ -27,7 +33,6 @@ struct Plan {
   hipblasLtMatmulDesc_t desc = nullptr;
   hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
   hipblasLtMatmulAlgo_t algo;
-  size_t ws_needed = 0;
 };
 
 using Key = std::tuple<int, int, int, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, size_t>;
@@ -72,6 +77,50 @@ float time_candidate(hipblasLtHandle_t handle, const Plan& p, const hipblasLtMat
   hipEventDestroy(e0);
   hipEventDestroy(e1);
   return ms;
+}
+
+// Macro-tile tag ("MT256x256x64") of a kernel name, or "".
+std::string macro_tile(const std::string& name) {
+  const size_t a = name.find("_MT");
+  if (a == std::string::npos) return "";
+  const size_t b = name.find('_', a + 3);
+  return name.substr(a + 1, b == std::string::npos ? std::string::npos : b - a - 1);
+}
+
+// Appends up to 48 supported algorithms whose macro tile matches one of the top three heuristic
+// candidates' (hipBLASLt's heuristic ranks few of each tile's variants).
+void add_same_tile_algos(hipblasLtHandle_t handle, const Plan& p, GemmType in_type, GemmType out_type,
+                         hipblasLtMatmulHeuristicResult_t* res, int n, size_t ws_bytes,
+                         std::vector<hipblasLtMatmulAlgo_t>& cand) {
+  std::vector<std::string> tiles;
+  for (int i = 0; i < n && i < 3; ++i) {
+    const std::string t = macro_tile(hipblaslt_ext::getKernelNameFromAlgo(handle, res[i].algo));
+    if (!t.empty()) tiles.push_back(t);
+  }
+  if (tiles.empty()) return;
+  std::vector<hipblasLtMatmulHeuristicResult_t> all;
+  if (hipblaslt_ext::getAllAlgos(handle, hipblaslt_ext::GemmType::HIPBLASLT_GEMM, HIPBLAS_OP_T, HIPBLAS_OP_N,
+                                 dt_of(in_type), dt_of(in_type), dt_of(out_type), dt_of(out_type),
+                                 HIPBLAS_COMPUTE_32F, all) != HIPBLAS_STATUS_SUCCESS)
+    return;
+  const float alpha = 1.f, beta = 0.f;
+  int added = 0;
+  for (auto& r : all) {
+    if (added >= 48) break;
+    const std::string t = macro_tile(hipblaslt_ext::getKernelNameFromAlgo(handle, r.algo));
+    if (std::find(tiles.begin(), tiles.end(), t) == tiles.end()) continue;
+    const int idx = hipblaslt_ext::getIndexFromAlgo(r.algo);
+    bool dup = false;
+    for (auto& c : cand) dup = dup || hipblaslt_ext::getIndexFromAlgo(c) == idx;
+    if (dup) continue;
+    size_t need = 0;
+    if (hipblaslt_ext::matmulIsAlgoSupported(handle, p.desc, &alpha, p.la, p.lb, &beta, p.lc, p.lc, r.algo, need) !=
+            HIPBLAS_STATUS_SUCCESS ||
+        need > ws_bytes)
+      continue;
+    cand.push_back(r.algo);
+    ++added;
+  }
 }
 
 }  // namespace
@@ -123,23 +172,29 @@ int gemm_16(GemmType in_type, GemmType out_type, const void* X, int64_t ldx, con
         *err = "hipBLASLt found no algorithm for this GEMM shape";
         return -2;
       }
+      std::vector<hipblasLtMatmulAlgo_t> cand;
+      for (int i = 0; i < n; ++i)
+        if (res[i].workspaceSize <= ws_bytes) cand.push_back(res[i].algo);
+      if (cand.empty()) {
+        *err = "hipBLASLt found no algorithm within the workspace";
+        return -2;
+      }
       int best = 0;
       hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
       if (hipStreamIsCapturing(s, &cap) != hipSuccess) cap = hipStreamCaptureStatusActive;
-      if (n > 1 && cap == hipStreamCaptureStatusNone && env_flag("HYMBA_GEMM_TUNE", true)) {
+      if (cap == hipStreamCaptureStatusNone && env_flag("HYMBA_GEMM_TUNE", true)) {
+        if (2.0 * rows * out * in > 5e10) add_same_tile_algos(handle, p, in_type, out_type, res, n, ws_bytes, cand);
         const bool log = env_flag("HYMBA_GEMM_TUNE_LOG", false);
         float best_ms = -1.f;
-        for (int i = 0; i < n; ++i) {
-          if (res[i].workspaceSize > ws_bytes) continue;
-          const float ms = time_candidate(handle, p, res[i].algo, W, X, Y, ws, ws_bytes, s, 3);
+        for (size_t i = 0; cand.size() > 1 && i < cand.size(); ++i) {
+          const float ms = time_candidate(handle, p, cand[i], W, X, Y, ws, ws_bytes, s, 2);
           if (log)
-            std::fprintf(stderr, "[hymba gemm] rows %lld out %lld in %lld candidate %d: %.4f ms\n",
+            std::fprintf(stderr, "[hymba gemm] rows %lld out %lld in %lld candidate %zu: %.4f ms\n",
                          (long long)rows, (long long)out, (long long)in, i, ms);
-          if (ms > 0.f && (best_ms < 0.f || ms < best_ms)) { best_ms = ms; best = i; }
+          if (ms > 0.f && (best_ms < 0.f || ms < best_ms)) { best_ms = ms; best = static_cast<int>(i); }
         }
       }
-      p.algo = res[best].algo;
-      p.ws_needed = res[best].workspaceSize;
+      p.algo = cand[best];
       it = st.plans.emplace(key, p).first;
     }
     plan = it->second;
