@@ -52,37 +52,54 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs<T> a) {
 }
 
 constexpr int kThreads = 256;
-constexpr int kMaxKeysPerSplit = 512;
-constexpr int kMaxGroup = 8;
+constexpr int kDecPasses = 8;   // keys per thread and split
 
-// 8 consecutive elements -> floats
-template <typename T>
-__device__ __forceinline__ void load8(const T* p, float (&v)[8]) {
-  if constexpr (Vec16<T>::n == 8) {
-    Vec16<T>::load(p, v);
-  } else {
-    float a[4], b[4];
-    Vec16<T>::load(p, a);
-    Vec16<T>::load(p + 4, b);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
-  }
+// Sum over the LPK lanes of one key row (aligned groups of LPK <= 16 lanes):
+// quad swaps, then the half-row and row mirrors pair the partial sums of
+// neighbouring groups (all DPP, no LDS).
+template <int LPK>
+__device__ __forceinline__ float row_group_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  if (LPK > 2)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  if (LPK > 4)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  if (LPK > 8)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  return v;
 }
 
-// grid (splits, Hkv, B), 256 threads.  Phase 1: one thread per key computes the
-// group's scores (q broadcast from LDS).  Phase 2: per-head max / exp / sum.
-// Phase 3: threads = (key group, dim pair) accumulate P.V; key groups reduced
-// through LDS.  Writes per-split partials (acc, max, sum).
-template <typename T>
+// (m, l, acc) of two partial softmax sums over disjoint key sets, merged into the first.
+template <int EPC>
+__device__ __forceinline__ void merge_partial(float& m, float& l, float (&acc)[EPC], float m2, float l2,
+                                              const float (&acc2)[EPC]) {
+  const float mm = fmaxf(m, m2);
+  const float f1 = fast_exp2(m - mm), f2 = fast_exp2(m2 - mm);
+  l = l * f1 + l2 * f2;
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = acc[e] * f1 + acc2[e] * f2;
+  m = mm;
+}
+
+// grid (splits, Hkv, B), 256 threads.  A split covers a contiguous run of the
+// sequence's visible keys (meta keys, then the ring slots of real indices
+// lo..p).  LPK lanes share one key row (16 bytes each), so the workgroup
+// covers 256 / LPK keys per pass and at most kDecPasses passes; all of a
+// thread's K and V loads are issued first, then every thread runs an online
+// softmax (running max, sum, P.V over its 16 bytes of dims) for each of the G
+// query heads of the KV group.  The partials
+// of the key slots meet through lane shuffles, then across the four waves in
+// LDS; the split's (acc, max, sum) per head go to `part` for the combine.
+template <typename T, int G, int HD>
 __global__ __launch_bounds__(kThreads) void decode_attn_kernel(DecAttnArgs<T> a) {
-  __shared__ float qs[kMaxGroup][kDecodeMaxHd];
-  __shared__ float ps[kMaxGroup][kMaxKeysPerSplit];
-  __shared__ float red[kThreads / 64][kMaxGroup][kDecodeMaxHd];
-  __shared__ float stat[kMaxGroup][2];
+  constexpr int EPC = 16 / static_cast<int>(sizeof(T));   // elements per 16-byte chunk
+  constexpr int LPK = HD / EPC;                             // lanes per key row
+  constexpr int KPP = kThreads / LPK;                       // keys per pass
+  static_assert(LPK >= 2 && LPK <= 16, "key row must span 2..16 lanes");
+  __shared__ float red[kThreads / 64][G][HD + 2];
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int G = a.n_heads / a.n_kv_heads;
-  const int hd = a.head_dim;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = tid % LPK, slot = tid / LPK;
   const int C = a.cache_len;
   const int64_t p = a.pos[b];
   const int64_t weff = a.window > 0 ? a.window : C;
@@ -91,113 +108,124 @@ __global__ __launch_bounds__(kThreads) void decode_attn_kernel(DecAttnArgs<T> a)
   const int per = static_cast<int>(ceil_div(nkeys, a.splits));
   const int k0 = split * per;
   const int k1 = min(nkeys, k0 + per);
-  const int nk = max(0, k1 - k0);
 
-  for (int i = tid; i < G * hd; i += kThreads) {
-    const int hh = i / hd, d = i % hd;
-    qs[hh][d] = Elem<T>::load(a.q + (int64_t)b * a.ld_q + (g * G + hh) * hd + d) * a.scale_log2;
+  float qv[G][EPC];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    Vec16<T>::load(a.q + (int64_t)b * a.ld_q + (g * G + hh) * HD + c * EPC, qv[hh]);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) qv[hh][e] *= a.scale_log2;
   }
-  __syncthreads();
+  float m[G], l[G], acc[G][EPC];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    m[hh] = -1e30f;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[hh][e] = 0.f;
+  }
 
-  const T* kc = a.k_cache + ((int64_t)b * a.n_kv_heads + g) * C * hd;
-  const T* vc = a.v_cache + ((int64_t)b * a.n_kv_heads + g) * C * hd;
-  auto key_ptr = [&](const T* meta, const T* cache, int kk) -> const T* {
-    if (kk < a.n_meta) return meta + (int64_t)kk * a.ld_meta + g * hd;
-    const int64_t r = lo + (kk - a.n_meta);
-    return cache + (r % C) * hd;
-  };
-
-  // phase 1: scores (log2 units)
-  for (int j = tid; j < nk; j += kThreads) {
-    const T* kr = key_ptr(a.k_meta, kc, k0 + j);
-    float s[kMaxGroup];
+  const int64_t kvoff = ((int64_t)b * a.n_kv_heads + g) * C * HD + c * EPC;
+  const int64_t moff = (int64_t)g * HD + c * EPC;
+  // every key this thread handles (at most kDecPasses) is loaded before any is used, so a
+  // workgroup keeps its whole split of K and V in flight; ring slots are tracked incrementally
+  // from one 64-bit remainder
+  uint4 kr[kDecPasses], vr[kDecPasses];
+  {
+    int kk = k0 + slot;
+    int64_t rs = kk >= a.n_meta ? (lo + (kk - a.n_meta)) % C : 0;
+    const int step_mod = KPP % C;
 #pragma unroll
-    for (int hh = 0; hh < kMaxGroup; ++hh) s[hh] = 0.f;
-    for (int d0 = 0; d0 < hd; d0 += 8) {
-      float kv[8];
-      load8<T>(kr + d0, kv);
-#pragma unroll
-      for (int hh = 0; hh < kMaxGroup; ++hh) {
-        if (hh < G) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) s[hh] = fmaf(qs[hh][d0 + e], kv[e], s[hh]);
+    for (int i = 0; i < kDecPasses; ++i) {
+      if (kk < k1) {
+        if (kk < a.n_meta) {
+          const int64_t o = (int64_t)kk * a.ld_meta + moff;
+          kr[i] = *reinterpret_cast<const uint4*>(a.k_meta + o);
+          vr[i] = *reinterpret_cast<const uint4*>(a.v_meta + o);
+        } else {
+          const int64_t o = kvoff + rs * HD;
+          kr[i] = *reinterpret_cast<const uint4*>(a.k_cache + o);
+          vr[i] = *reinterpret_cast<const uint4*>(a.v_cache + o);
         }
       }
-    }
-#pragma unroll
-    for (int hh = 0; hh < kMaxGroup; ++hh)
-      if (hh < G) ps[hh][j] = s[hh];
-  }
-  __syncthreads();
-
-  // phase 2: per-head max, exp, sum (one wave per head, heads strided by 4)
-  const int wave = tid >> 6, lane = tid & 63;
-  for (int hh = wave; hh < G; hh += kThreads / 64) {
-    float m = -INFINITY;
-    for (int j = lane; j < nk; j += 64) m = fmaxf(m, ps[hh][j]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if (nk == 0) m = -1e30f;
-    float l = 0.f;
-    for (int j = lane; j < nk; j += 64) {
-      const float e = fast_exp2(ps[hh][j] - m);
-      ps[hh][j] = e;
-      l += e;
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
-    if (lane == 0) { stat[hh][0] = m; stat[hh][1] = l; }
-  }
-  __syncthreads();
-
-  // phase 3: O = P.V ; thread = (key group kg, dim pair dp)
-  const int npairs = hd / 2;
-  const int ngroups = kThreads / npairs;
-  const int dp = tid % npairs, kg = tid / npairs;
-  float acc[kMaxGroup][2];
-#pragma unroll
-  for (int hh = 0; hh < kMaxGroup; ++hh) { acc[hh][0] = 0.f; acc[hh][1] = 0.f; }
-  if (kg < ngroups) {
-    for (int j = kg; j < nk; j += ngroups) {
-      const T* vr = key_ptr(a.v_meta, vc, k0 + j);
-      const float v0 = Elem<T>::load(vr + 2 * dp), v1 = Elem<T>::load(vr + 2 * dp + 1);
-#pragma unroll
-      for (int hh = 0; hh < kMaxGroup; ++hh) {
-        if (hh < G) {
-          const float w = ps[hh][j];
-          acc[hh][0] = fmaf(w, v0, acc[hh][0]);
-          acc[hh][1] = fmaf(w, v1, acc[hh][1]);
+      const int next = kk + KPP;
+      if (next >= a.n_meta) {
+        if (kk >= a.n_meta) {
+          rs += step_mod;
+          if (rs >= C) rs -= C;
+        } else {
+          rs = (lo + (next - a.n_meta)) % C;
         }
       }
+      kk = next;
     }
   }
-  // reduce key groups: first within a wave (groups sharing a wave), then across waves
-  const int groups_per_wave = 64 / npairs;   // >= 1 since hd <= 128
 #pragma unroll
-  for (int hh = 0; hh < kMaxGroup; ++hh) {
-    if (hh < G) {
-      for (int off = npairs; off < 64; off <<= 1) {
-        acc[hh][0] += __shfl_xor(acc[hh][0], off);
-        acc[hh][1] += __shfl_xor(acc[hh][1], off);
+  for (int i = 0; i < kDecPasses; ++i) {
+    if (k0 + slot + i * KPP >= k1) break;   // uniform over the LPK lanes of a key row
+    float kf[EPC], vf[EPC];
+    Vec16<T>::load(reinterpret_cast<const T*>(&kr[i]), kf);
+    Vec16<T>::load(reinterpret_cast<const T*>(&vr[i]), vf);
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float sdot = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) sdot = fmaf(qv[hh][e], kf[e], sdot);
+      const float sc = row_group_sum<LPK>(sdot);
+      if (sc > m[hh]) {   // the running max moves: rescale this lane's sums
+        const float al = fast_exp2(m[hh] - sc);
+        m[hh] = sc;
+        l[hh] *= al;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[hh][e] *= al;
+      }
+      const float pr = fast_exp2(sc - m[hh]);
+      l[hh] += pr;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[hh][e] = fmaf(pr, vf[e], acc[hh][e]);
+    }
+  }
+
+  // merge the key slots of a wave (lanes c, c + LPK, ... ), then the four waves
+#pragma unroll
+  for (int off = LPK; off < 64; off <<= 1) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float acc2[EPC];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc2[e] = __shfl_xor(acc[hh][e], off);
+      const float m2 = __shfl_xor(m[hh], off), l2 = __shfl_xor(l[hh], off);
+      merge_partial<EPC>(m[hh], l[hh], acc[hh], m2, l2, acc2);
+    }
+  }
+  if (lane < LPK) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) red[wave][hh][c * EPC + e] = acc[hh][e];
+      if (c == 0) {
+        red[wave][hh][HD] = m[hh];
+        red[wave][hh][HD + 1] = l[hh];
       }
     }
   }
-  (void)groups_per_wave;
-  if (lane < npairs) {
-#pragma unroll
-    for (int hh = 0; hh < kMaxGroup; ++hh)
-      if (hh < G) { red[wave][hh][2 * dp] = acc[hh][0]; red[wave][hh][2 * dp + 1] = acc[hh][1]; }
-  }
   __syncthreads();
-  const int nwaves = kThreads / 64;
-  for (int i = tid; i < G * hd; i += kThreads) {
-    const int hh = i / hd, d = i % hd;
-    float s = 0.f;
-    for (int w = 0; w < nwaves; ++w) s += red[w][hh][d];
-    const int h = g * G + hh;
-    float* out = a.part + (((int64_t)b * a.n_heads + h) * a.splits + split) * (hd + 2);
-    out[d] = s;
-    if (d == 0) { out[hd] = stat[hh][0]; out[hd + 1] = stat[hh][1]; }
+  for (int i = tid; i < G * HD; i += kThreads) {
+    const int hh = i / HD, d = i % HD;
+    float mm = red[0][hh][HD];
+    for (int w = 1; w < kThreads / 64; ++w) mm = fmaxf(mm, red[w][hh][HD]);
+    float num = 0.f, den = 0.f;
+    for (int w = 0; w < kThreads / 64; ++w) {
+      const float f = fast_exp2(red[w][hh][HD] - mm);
+      num = fmaf(f, red[w][hh][d], num);
+      den = fmaf(f, red[w][hh][HD + 1], den);
+    }
+    float* out = a.part + (((int64_t)b * a.n_heads + g * G + hh) * a.splits + split) * (HD + 2);
+    out[d] = num;
+    if (d == 0) {
+      out[HD] = mm;
+      out[HD + 1] = den;
+    }
   }
 }
 
@@ -232,10 +260,29 @@ hipError_t kv_dispatch(const KvWriteArgs<T>& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T, int HD>
+hipError_t dec_dispatch_hd(const DecAttnArgs<T>& a, hipStream_t s) {
+  const dim3 grid(a.splits, a.n_kv_heads, a.B), block(kThreads);
+  switch (a.n_heads / a.n_kv_heads) {
+    case 1: hipLaunchKernelGGL((decode_attn_kernel<T, 1, HD>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_attn_kernel<T, 2, HD>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_attn_kernel<T, 3, HD>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_attn_kernel<T, 4, HD>), grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL((decode_attn_kernel<T, 5, HD>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((decode_attn_kernel<T, 6, HD>), grid, block, 0, s, a); break;
+    case 7: hipLaunchKernelGGL((decode_attn_kernel<T, 7, HD>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((decode_attn_kernel<T, 8, HD>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t dec_dispatch(const DecAttnArgs<T>& a, hipStream_t s) {
-  hipLaunchKernelGGL((decode_attn_kernel<T>), dim3(a.splits, a.n_kv_heads, a.B), dim3(kThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (a.head_dim == 64) e = dec_dispatch_hd<T, 64>(a, s);
+  else if (a.head_dim == 32) e = dec_dispatch_hd<T, 32>(a, s);
+  else return hipErrorInvalidValue;
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T>), dim3(a.B * a.n_heads), dim3(kDecodeMaxHd), 0, s, a);
   return hipGetLastError();
@@ -248,10 +295,13 @@ hipError_t launch_kv_write(const KvWriteArgs<half_t>& a, hipStream_t s) { return
 hipError_t launch_decode_attn(const DecAttnArgs<float>& a, hipStream_t s) { return dec_dispatch(a, s); }
 hipError_t launch_decode_attn(const DecAttnArgs<half_t>& a, hipStream_t s) { return dec_dispatch(a, s); }
 
-// Enough splits that every split holds at most kMaxKeysPerSplit keys and the
-// grid has ~2048 workgroups (8 per CU).
-int decode_attn_splits(int B, int n_kv_heads, int n_keys_max) {
-  int s = static_cast<int>(ceil_div(n_keys_max, kMaxKeysPerSplit));
+// Enough splits that a split holds at most (256 / lanes per key row) *
+// kDecPasses keys, and the grid has ~2048 workgroups (8 per CU) when keys allow.
+int decode_attn_splits(int B, int n_kv_heads, int n_keys_max, int head_dim, int elem_bytes) {
+  const int lpk = head_dim * elem_bytes / 16;
+  if (lpk < 2 || lpk > 16) return -1;
+  const int max_per_split = kThreads / lpk * kDecPasses;
+  int s = static_cast<int>(ceil_div(n_keys_max, max_per_split));
   if (s < 1) s = 1;
   const int64_t pairs = (int64_t)B * n_kv_heads;
   while (s < kDecodeMaxSplits && pairs * s < 2048 && ceil_div(n_keys_max, s * 2) >= 64) s *= 2;

@@ -495,7 +495,8 @@ int32_t decode_impl(hymba_layer& L, const void* x, const int64_t* pos, int B, vo
   const void *km, *vm;
   meta_kv_of(L, kv, &km, &vm);
   const int weff = c.window > 0 ? c.window : kv->cache_len;
-  const int splits = decode_attn_splits(B, c.n_kv_heads, c.n_meta + std::min(weff, kv->cache_len));
+  const int splits = decode_attn_splits(B, c.n_kv_heads, c.n_meta + std::min(weff, kv->cache_len), c.head_dim,
+                                        static_cast<int>(sizeof(CT)));
   if (splits < 1) return fail(HYMBA_ERR_UNSUPPORTED, "decode key range too long for the split-K kernel");
   {
     StageTimer st(L, ST_ATTN, s);

@@ -112,7 +112,7 @@ struct DecAttnArgs {
 };
 hipError_t launch_decode_attn(const DecAttnArgs<float>& a, hipStream_t s);
 hipError_t launch_decode_attn(const DecAttnArgs<half_t>& a, hipStream_t s);
-int decode_attn_splits(int B, int n_kv_heads, int n_keys_max);
+int decode_attn_splits(int B, int n_kv_heads, int n_keys_max, int head_dim, int elem_bytes);
 constexpr int kDecodeMaxSplits = 64;
 constexpr int kDecodeMaxHd = 128;
 
