@@ -61,9 +61,9 @@ def visible_keys(s, T):
 
 
 def conversion_bytes(s, R):
-    """bf16 layers: x bf16 -> fp16 (read 2 + write 2 B per element), the B/C columns fp16 -> fp32
-    (2 + 4), the output fp32 -> bf16 (4 + 2)."""
-    return float(R * s.d_model * 4 + R * 2 * s.d_state * 6 + R * s.d_model * 6)
+    """bf16 layers: x bf16 -> fp16 (read 2 + write 2 B per element) and the B/C columns
+    fp16 -> fp32 (2 + 4)."""
+    return float(R * s.d_model * 4 + R * 2 * s.d_state * 6)
 
 
 def prefill_work(s, B, T):
