@@ -15,6 +15,8 @@
 // this VALU work rather than by memory (the Griffin summary, hyeon-jae.tistory.com
 // section 1, notes diagonal RNN layers are memory bound on TPU; here the
 // per-state exp dominates).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -129,31 +131,36 @@ __global__ __launch_bounds__(64 * (N / NS)) void selective_scan_kernel(
     const int len = min(kTC, T_len - t0);
     const float* bcsf = reinterpret_cast<const float*>(&bcs[buf][0][0]);
     float part[kTC];
+    // full chunks take a branch-free copy of the step loop; only the last chunk checks len
+    auto steps = [&](auto full) {
 #pragma unroll
-    for (int s = 0; s < kTC; ++s) {
-      part[s] = 0.f;
-      if (s < len) {
-        const float2 d = dd[buf][s][lane];
-        float bb[NS], cb[NS];
+      for (int s = 0; s < kTC; ++s) {
+        part[s] = 0.f;
+        if (decltype(full)::value || s < len) {
+          const float2 d = dd[buf][s][lane];
+          float bb[NS], cb[NS];
 #pragma unroll
-        for (int q = 0; q < NS / VW; ++q) {
-          const BV vb = *reinterpret_cast<const BV*>(bcsf + s * 2 * N + n0 + VW * q);
-          const BV vc = *reinterpret_cast<const BV*>(bcsf + s * 2 * N + N + n0 + VW * q);
-          const float* pb = reinterpret_cast<const float*>(&vb);
-          const float* pc = reinterpret_cast<const float*>(&vc);
+          for (int q = 0; q < NS / VW; ++q) {
+            const BV vb = *reinterpret_cast<const BV*>(bcsf + s * 2 * N + n0 + VW * q);
+            const BV vc = *reinterpret_cast<const BV*>(bcsf + s * 2 * N + N + n0 + VW * q);
+            const float* pb = reinterpret_cast<const float*>(&vb);
+            const float* pc = reinterpret_cast<const float*>(&vc);
 #pragma unroll
-          for (int e = 0; e < VW; ++e) { bb[VW * q + e] = pb[e]; cb[VW * q + e] = pc[e]; }
+            for (int e = 0; e < VW; ++e) { bb[VW * q + e] = pb[e]; cb[VW * q + e] = pc[e]; }
+          }
+          float acc = 0.f;
+#pragma unroll
+          for (int n = 0; n < NS; ++n) {
+            const float dA = fast_exp2(d.x * a2[n]);
+            h[n] = fmaf(dA, h[n], d.y * bb[n]);
+            acc = fmaf(cb[n], h[n], acc);
+          }
+          part[s] = acc;
         }
-        float acc = 0.f;
-#pragma unroll
-        for (int n = 0; n < NS; ++n) {
-          const float dA = fast_exp2(d.x * a2[n]);
-          h[n] = fmaf(dA, h[n], d.y * bb[n]);
-          acc = fmaf(cb[n], h[n], acc);
-        }
-        part[s] = acc;
       }
-    }
+    };
+    if (len == kTC) steps(std::true_type{});
+    else steps(std::false_type{});
     if constexpr (WPC == 1) {
 #pragma unroll
       for (int s = 0; s < kTC; ++s)
