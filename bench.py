@@ -332,10 +332,10 @@ def _grid(r):
 
 def _label(rows):
     """Dispatches in issue order with their stage.  A GEMM takes its stage from the kernel issued
-    before it: after attention or the scan (which runs on a second stream beside attention) it is
-    W_O, after the epilogue the output projection, otherwise (after an input conversion or at the
-    start of a call) the input projection.  Consecutive GEMMs (one-off algorithm timing of a plan)
-    keep the label of the first."""
+    before it: after attention it is W_O, after the epilogue the output projection, otherwise
+    (after a conversion, the scan -- issued on a second stream between the two parts of the
+    projection -- or at the start of a call) the input projection.  Consecutive GEMMs (one-off
+    algorithm timing of a plan) keep the label of the first."""
     out, prev = [], None
     for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
         st = _kernel_stage(r["Kernel_Name"])
@@ -343,34 +343,35 @@ def _label(rows):
             if prev in ("in_proj", "w_o", "out_proj"):
                 st = prev
             else:
-                st = {"ssm": "w_o", "attention": "w_o", "epilogue": "out_proj"}.get(prev, "in_proj")
+                st = {"attention": "w_o", "epilogue": "out_proj"}.get(prev, "in_proj")
         out.append((st, r))
         prev = st
     return out
 
 
 def _main_groups(labelled, value, keep=10):
-    """Per stage, over its last `keep` dispatches (the timed loops; earlier ones include the
-    one-off meta-prefix pass and GEMM algorithm timing), the (kernel, grid) group with the most
-    dispatches: {stage: (name, grid, calls, mean)}.  The conversions of a bf16 call are two
-    kernels: their means are summed."""
+    """Per stage, over the dispatches of its last `keep` calls (the timed loops; earlier ones
+    include the one-off meta-prefix pass and GEMM algorithm timing): {stage: (name, grid, calls,
+    mean per call)}.  A stage that launches several kernels per call (the two parts of the input
+    projection, the conversions) sums their means."""
     per_stage = {}
     for st, r in labelled:
         per_stage.setdefault(st, []).append(r)
-    groups = {}
-    for st, rs in per_stage.items():
-        n_kinds = len({_grid(r) + r["Kernel_Name"] for r in rs[-keep:]}) if st == "convert" else 1
-        for r in rs[-keep * n_kinds:]:
-            groups.setdefault(st, {}).setdefault((r["Kernel_Name"], _grid(r)), []).append(value(r))
     best = {}
-    for st, g in groups.items():
-        (name, grid), vals = max(g.items(), key=lambda kv: (len(kv[1]), sum(kv[1])))
-        if st == "convert":
-            top = [v for v in g.values() if len(v) == len(vals)]
-            best[st] = ("convert_kernel (%d kinds)" % len(top), "several", len(vals),
-                        sum(sum(v) / len(v) for v in top))
-        else:
+    for st, rs in per_stage.items():
+        kinds = len({(r["Kernel_Name"], _grid(r)) for r in rs[-keep:]})
+        g = {}
+        for r in rs[-keep * kinds:]:
+            g.setdefault((r["Kernel_Name"], _grid(r)), []).append(value(r))
+        top_n = max(len(v) for v in g.values())
+        top = [(k, v) for k, v in g.items() if len(v) == top_n]
+        if len(top) == 1:
+            (name, grid), vals = top[0]
             best[st] = (name, grid, len(vals), sum(vals) / len(vals))
+        else:
+            name = top[0][0][0] if len({k[0] for k, _ in top}) == 1 else "%d kernels" % len(top)
+            best[st] = ("%s (%d launches per call)" % (name, len(top)), "several", top_n,
+                        sum(sum(v) / len(v) for _, v in top))
     return best
 
 

@@ -28,14 +28,15 @@ def test_prefill_work_stages():
 
 
 def _trace_rows():
-    seq = ["convert_kernel<a>", "Cijk_gemm", "convert_kernel<b>", "swa_meta_attn_kernel<h>",
-           "selective_scan_kernel<h,16,8>", "Cijk_gemm", "epilogue_kernel<h>", "Cijk_gemm", "convert_kernel<c>"]
+    seq = ["convert_kernel<a>", "Cijk_gemm_ssm", "convert_kernel<b>", "selective_scan_kernel<h,16,8>",
+           "Cijk_gemm_attn", "swa_meta_attn_kernel<h>", "Cijk_gemm", "epilogue_kernel<h>", "Cijk_gemm"]
     rows, d, t = [], 0, 0
     # one small meta pass, then three timed calls, then the copy probe
     for grid, calls in (("64", 1), ("4096", 3)):
         for _ in range(calls):
             for k in seq:
-                dur = {"Cijk_gemm": 100, "swa_meta_attn_kernel<h>": 50}.get(k, 10) * (1 if grid == "64" else 10)
+                dur = {"Cijk_gemm": 100, "Cijk_gemm_ssm": 60, "Cijk_gemm_attn": 40,
+                       "swa_meta_attn_kernel<h>": 50}.get(k, 10) * (1 if grid == "64" else 10)
                 rows.append({"Dispatch_Id": str(d), "Kernel_Name": k, "Grid_Size": grid,
                              "Start_Timestamp": str(t), "End_Timestamp": str(t + dur * 1000)})
                 d += 1
@@ -47,14 +48,15 @@ def _trace_rows():
 
 def test_dispatch_labels():
     lab = [st for st, _ in bench._label(_trace_rows())]
-    assert lab[:9] == ["convert", "in_proj", "convert", "attention", "ssm", "w_o", "epilogue", "out_proj",
-                       "convert"]
+    assert lab[:9] == ["convert", "in_proj", "convert", "ssm", "in_proj", "attention", "w_o", "epilogue",
+                       "out_proj"]
     assert lab[-1] == "copy_probe"
     g = bench._main_groups(bench._label(_trace_rows()),
                            lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    assert g["in_proj"][1:] == ("4096", 3, 1000.0)
+    assert g["in_proj"][1:] == ("several", 3, 1000.0)   # two projection GEMMs per call summed
+    assert g["w_o"][1:] == ("4096", 3, 1000.0)
     assert g["attention"][2:] == (3, 500.0)
-    assert g["convert"][2:] == (3, 300.0)      # three conversion kernels summed
+    assert g["convert"][2:] == (3, 200.0)      # two conversion kernels summed
 
 
 def _write(path, rows):
