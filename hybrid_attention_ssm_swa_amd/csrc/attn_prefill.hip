@@ -348,7 +348,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     tile_store(pre, sm.kw[buf], sm.vw[buf], tid);
     __syncthreads();
     if (i + 1 < n_tiles) fetch(pre, i + 1);
-    if (!wave_active) continue;
+    // Every wave runs every tile of the workgroup: a tile outside a wave's window (or a wave past
+    // the end of the sequence) is simply all masked and adds nothing.  Branching around it would
+    // split the loop-carried accumulators across paths and cost a 32-register copy per tile.
     int key0, lo_key, hi_key, tqm;
     bool mask;
     if (i < n_mt) {
@@ -357,8 +359,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       mask = key0 + kKT > a.n_meta;
     } else {
       const int t0 = lo + (i - n_mt) * kKT;
-      // skip tiles no query of this wave can see
-      if (t0 > qlast || (a.window > 0 && t0 + kKT - 1 <= qa - a.window)) continue;
       key0 = t0; lo_key = t0; hi_key = hi; tqm = tq;
       mask = !((t0 + kKT - 1 <= qa) && (a.window <= 0 || t0 > qlast - a.window) && (t0 + kKT <= hi));
     }
