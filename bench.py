@@ -236,14 +236,15 @@ def bench_prefill(cfg_id, steps, warmup):
     return out
 
 
-def bench_decode(cfg_id, steps, warmup):
+def bench_decode(cfg_id, steps, warmup, case=None):
+    """B=128 decode of a KV-sharing producer/consumer pair (the workload's ring cache), or, with
+    `case`, that decode case (e.g. a global layer over a full cache)."""
     import torch
     from hybrid_attention_ssm_swa_amd.layer import MixerLayer, make_kv, upload
-    from hymba_synth import config_by_id
     from hymba_synth.generate import make_config_case
-    cfg = config_by_id(cfg_id)
-    s, sc = cfg.shape, cfg.consumer_shape
-    case = make_config_case(cfg_id)
+    if case is None:
+        case = make_config_case(cfg_id)
+    s, sc = case.shape, case.consumer_shape
     dt = torch.bfloat16
     prod = MixerLayer(s, case.producer)
     cons = MixerLayer(sc, case.consumer)
@@ -268,7 +269,7 @@ def bench_decode(cfg_id, steps, warmup):
         cons.decode(xc, pos, kv, stc, yc)
 
     ms, ms_rec, (pst, cst) = timed([prod, cons], step, steps, warmup)
-    B, p, C = cfg.batch, cfg.seq, s.window
+    B, p, C = case.batch, int(case.pos[0]), case.k_cache.shape[2]
     ents = {}
     for role, lay_s, st in (("producer", s, pst), ("consumer", sc, cst)):
         work = decode_work(lay_s, B, p, C)
@@ -494,6 +495,13 @@ def main():
     if not args.main_only:
         workloads["decode_b128_pair"] = bench_decode(4, args.steps, args.warmup)
         log(f"[bench] decode: {workloads['decode_b128_pair']['tokens_per_s_per_layer']:.0f} tok/s/layer")
+        from hymba_synth import CONFIGS
+        from hymba_synth.generate import make_decode_case
+        g = CONFIGS[3].shape
+        workloads["global_decode_b8_full_cache"] = bench_decode(
+            3, args.steps, args.warmup, make_decode_case(g, g.with_(own_kv=False), 8, 8192, 1003, cache_len=8193))
+        log(f"[bench] global decode (B=8, 8193 keys + meta): "
+            f"{workloads['global_decode_b8_full_cache']['tokens_per_s_per_layer']:.0f} tok/s/layer")
         workloads["global_8k_prefill"] = bench_prefill(3, max(3, args.steps // 2), args.warmup)
         log(f"[bench] 8K global prefill: {workloads['global_8k_prefill']['tokens_per_s']:.0f} tok/s")
         workloads["ablation300m_prefill"] = bench_prefill(1, args.steps, args.warmup)

@@ -8,6 +8,8 @@
 // whole batch.  Decode is bound by reading the cache (Griffin summary,
 // hyeon-jae.tistory.com section 4: decode time is dominated by loading
 // parameters and cache).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs<T> a) {
 }
 
 constexpr int kThreads = 256;
-constexpr int kDecPasses = 8;   // keys per thread and split
+constexpr int kDecPasses = 8;   // keys per thread and load round
 
 // Sum over the LPK lanes of one key row (aligned groups of LPK <= 16 lanes):
 // quad swaps, then the half-row and row mirrors pair the partial sums of
@@ -84,10 +86,10 @@ __device__ __forceinline__ void merge_partial(float& m, float& l, float (&acc)[E
 // grid (splits, Hkv, B), 256 threads.  A split covers a contiguous run of the
 // sequence's visible keys (meta keys, then the ring slots of real indices
 // lo..p).  LPK lanes share one key row (16 bytes each), so the workgroup
-// covers 256 / LPK keys per pass and at most kDecPasses passes; all of a
-// thread's K and V loads are issued first, then every thread runs an online
-// softmax (running max, sum, P.V over its 16 bytes of dims) for each of the G
-// query heads of the KV group.  The partials
+// covers 256 / LPK keys per pass; passes go in rounds of kDecPasses whose K
+// and V loads are all issued first, then every thread runs an online softmax
+// (running max, sum, P.V over its 16 bytes of dims) for each of the G query
+// heads of the KV group.  The partials
 // of the key slots meet through lane shuffles, then across the four waves in
 // LDS; the split's (acc, max, sum) per head go to `part` for the combine.
 template <typename T, int G, int HD>
@@ -127,14 +129,15 @@ __global__ __launch_bounds__(kThreads) void decode_attn_kernel(DecAttnArgs<T> a)
 
   const int64_t kvoff = ((int64_t)b * a.n_kv_heads + g) * C * HD + c * EPC;
   const int64_t moff = (int64_t)g * HD + c * EPC;
-  // every key this thread handles (at most kDecPasses) is loaded before any is used, so a
-  // workgroup keeps its whole split of K and V in flight; ring slots are tracked incrementally
-  // from one 64-bit remainder
-  uint4 kr[kDecPasses], vr[kDecPasses];
-  {
-    int kk = k0 + slot;
-    int64_t rs = kk >= a.n_meta ? (lo + (kk - a.n_meta)) % C : 0;
-    const int step_mod = KPP % C;
+  // keys go in rounds of kDecPasses passes: every key of a round is loaded before any is used, so
+  // a workgroup keeps a round of its split's K and V in flight; ring slots are tracked
+  // incrementally from one 64-bit remainder
+  int kk = k0 + slot;
+  int64_t rs = kk >= a.n_meta ? (lo + (kk - a.n_meta)) % C : 0;
+  const int step_mod = KPP % C;
+  while (kk < k1) {   // uniform over the LPK lanes of a key row (they share kk)
+    uint4 kr[kDecPasses], vr[kDecPasses];
+    const int first = kk;
 #pragma unroll
     for (int i = 0; i < kDecPasses; ++i) {
       if (kk < k1) {
@@ -159,30 +162,30 @@ __global__ __launch_bounds__(kThreads) void decode_attn_kernel(DecAttnArgs<T> a)
       }
       kk = next;
     }
-  }
 #pragma unroll
-  for (int i = 0; i < kDecPasses; ++i) {
-    if (k0 + slot + i * KPP >= k1) break;   // uniform over the LPK lanes of a key row
-    float kf[EPC], vf[EPC];
-    Vec16<T>::load(reinterpret_cast<const T*>(&kr[i]), kf);
-    Vec16<T>::load(reinterpret_cast<const T*>(&vr[i]), vf);
+    for (int i = 0; i < kDecPasses; ++i) {
+      if (first + i * KPP >= k1) break;
+      float kf[EPC], vf[EPC];
+      Vec16<T>::load(reinterpret_cast<const T*>(&kr[i]), kf);
+      Vec16<T>::load(reinterpret_cast<const T*>(&vr[i]), vf);
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      float sdot = 0.f;
+      for (int hh = 0; hh < G; ++hh) {
+        float sdot = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) sdot = fmaf(qv[hh][e], kf[e], sdot);
-      const float sc = row_group_sum<LPK>(sdot);
-      if (sc > m[hh]) {   // the running max moves: rescale this lane's sums
-        const float al = fast_exp2(m[hh] - sc);
-        m[hh] = sc;
-        l[hh] *= al;
+        for (int e = 0; e < EPC; ++e) sdot = fmaf(qv[hh][e], kf[e], sdot);
+        const float sc = row_group_sum<LPK>(sdot);
+        if (sc > m[hh]) {   // the running max moves: rescale this lane's sums
+          const float al = fast_exp2(m[hh] - sc);
+          m[hh] = sc;
+          l[hh] *= al;
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[hh][e] *= al;
+          for (int e = 0; e < EPC; ++e) acc[hh][e] *= al;
+        }
+        const float pr = fast_exp2(sc - m[hh]);
+        l[hh] += pr;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[hh][e] = fmaf(pr, vf[e], acc[hh][e]);
       }
-      const float pr = fast_exp2(sc - m[hh]);
-      l[hh] += pr;
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[hh][e] = fmaf(pr, vf[e], acc[hh][e]);
     }
   }
 
@@ -295,17 +298,19 @@ hipError_t launch_kv_write(const KvWriteArgs<half_t>& a, hipStream_t s) { return
 hipError_t launch_decode_attn(const DecAttnArgs<float>& a, hipStream_t s) { return dec_dispatch(a, s); }
 hipError_t launch_decode_attn(const DecAttnArgs<half_t>& a, hipStream_t s) { return dec_dispatch(a, s); }
 
-// Enough splits that a split holds at most (256 / lanes per key row) *
-// kDecPasses keys, and the grid has ~2048 workgroups (8 per CU) when keys allow.
+// Splits per (sequence, KV head): enough for ~2048 workgroups (8 per CU), at
+// least one load round (256 / lanes per key row * kDecPasses keys) per split
+// when the key range allows, never fewer than 64 keys per split, at most
+// kDecodeMaxSplits.  Longer splits run several rounds.
 int decode_attn_splits(int B, int n_kv_heads, int n_keys_max, int head_dim, int elem_bytes) {
   const int lpk = head_dim * elem_bytes / 16;
-  if (lpk < 2 || lpk > 16) return -1;
-  const int max_per_split = kThreads / lpk * kDecPasses;
-  int s = static_cast<int>(ceil_div(n_keys_max, max_per_split));
-  if (s < 1) s = 1;
+  if (lpk < 2 || lpk > 16 || B < 1 || n_kv_heads < 1) return -1;
+  const int64_t per_round = (int64_t)(kThreads / lpk) * kDecPasses;
   const int64_t pairs = (int64_t)B * n_kv_heads;
-  while (s < kDecodeMaxSplits && pairs * s < 2048 && ceil_div(n_keys_max, s * 2) >= 64) s *= 2;
-  return s > kDecodeMaxSplits ? -1 : s;
+  int64_t s = std::max<int64_t>(ceil_div(n_keys_max, per_round), ceil_div(2048, pairs));
+  s = std::min<int64_t>(s, std::max<int64_t>(1, ceil_div(n_keys_max, 64)));
+  s = std::min<int64_t>(s, kDecodeMaxSplits);
+  return static_cast<int>(std::max<int64_t>(s, 1));
 }
 
 }  // namespace hymba

@@ -153,6 +153,20 @@ def test_config4_decode_full_size():
     assert np.array_equal(vc[:, :, other], f16(case.v_cache[:, :, other]))
 
 
+def test_global_decode_full_cache():
+    """Global-attention decode at the 1.5B global layer's shape: 8 sequences at position 8192 over a
+    full cache (every earlier real token plus the meta prefix), producer/consumer pair."""
+    announce("global decode B=8, pos 8192, full cache")
+    s = CONFIGS[3].shape
+    case = make_decode_case(s, s.with_(own_kv=False), 8, 8192, seed=77, cache_len=8193)
+    _, _, yp, yc, stp, stc, kc, _ = _decode_pair_gpu(case)
+    ref = _decode_pair_oracle(case, range(case.batch))
+    check_stored("producer y", yp, np.stack([ref[b][0].Y for b in ref]), "bf16")
+    check_stored("consumer y", yc, np.stack([ref[b][1].Y for b in ref]), "bf16")
+    check("consumer state", stc, np.stack([ref[b][1].h for b in ref]), "bf16")
+    check_stored("written K slot", kc[:, :, 8192], np.stack([ref[b][0].k_cache[:, 8192] for b in ref]), "f16")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_decode_small_mixed_positions(dtype):
     """Positions differ per sequence: before the window fills, at the wrap, far beyond."""
