@@ -25,6 +25,7 @@ class LayerShape:
     own_kv: bool         # True: the layer projects its own K/V; False: K/V come from the previous layer
     dtype: str           # "f32" or "bf16" (storage); state and accumulation are fp32 in both
     rms_eps: float = 1e-6
+    rope_base: float = 0.0   # > 0: rotary position encoding of q and k with this base; 0: none
 
     @property
     def q_width(self) -> int:

@@ -47,6 +47,14 @@ same way by the GPU path):
   D11 decode index p counts real tokens; K/V of real token r live in cache
       slot r mod C.
   D12 a KV consumer uses its producer's K/V for every position, meta included.
+  D17 rotary position encoding (when rope_base > 0): the pages (Hymba summary
+      section 2.5 "Hymba Model Family" on the 8K-context stage; Griffin summary
+      section 2.3 "Temporal-mixing blocks") name RoPE and a changeable base but
+      print no formula, so the RoFormer
+      definition is used: consecutive pairs (x[2i], x[2i+1]) of every q and k
+      head vector are rotated by the angle pos * base^(-2i/hd); the meta rows
+      sit at positions 0..M-1 and real token t at M + t; K is rotated before it
+      is cached or handed to a consumer, which uses it as given (D12).
 
 Parity status: the attention mask, GQA grouping, scan, gate/norm/fusion and
 KV-sharing are pinned by closed forms, library routines and brute force in
@@ -103,6 +111,23 @@ def split_projection(P, s):
 
 
 # --- attention [H] sections 2.2-2.3, [G] section 2.3 ------------------------------
+
+def rope(x, positions, base):
+    """Rotary position encoding of head vectors x [L, heads, hd] at positions [L] (reading D17):
+    each consecutive pair (x[..., 2i], x[..., 2i+1]) turns by positions * base**(-2i/hd).
+    base <= 0 leaves x unchanged."""
+    x = np.asarray(x, F64)
+    if not base or base <= 0:
+        return x
+    hd = x.shape[-1]
+    theta = float(base) ** (-2.0 * np.arange(hd // 2) / hd)
+    ang = np.asarray(positions, F64)[:, None] * theta[None, :]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    out = np.empty_like(x)
+    out[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+    out[..., 1::2] = x[..., 0::2] * s + x[..., 1::2] * c
+    return out
+
 
 def visible(i, j, n_meta, window):
     """Key position j is visible to query position i (positions count meta rows first).
@@ -203,7 +228,7 @@ def meta_kv(p):
     s = p.shape
     P = np.asarray(p.meta, F64) @ np.asarray(p.w_in, F64).T
     parts = split_projection(P, s)
-    k = parts["k"].reshape(s.n_meta, s.n_kv_heads, s.head_dim)
+    k = rope(parts["k"].reshape(s.n_meta, s.n_kv_heads, s.head_dim), np.arange(s.n_meta), s.rope_base)
     v = parts["v"].reshape(s.n_meta, s.n_kv_heads, s.head_dim)
     return k, v
 
@@ -221,9 +246,9 @@ def layer_forward(p, x, k_meta=None, v_meta=None, k=None, v=None, h_init=None):
     xt = np.concatenate([np.asarray(p.meta, F64), np.asarray(x, F64)], axis=0)
     P = xt @ np.asarray(p.w_in, F64).T
     parts = split_projection(P, s)
-    Q = parts["q"].reshape(L, s.n_heads, s.head_dim)
+    Q = rope(parts["q"].reshape(L, s.n_heads, s.head_dim), np.arange(L), s.rope_base)
     if s.own_kv:
-        K = parts["k"].reshape(L, s.n_kv_heads, s.head_dim)
+        K = rope(parts["k"].reshape(L, s.n_kv_heads, s.head_dim), np.arange(L), s.rope_base)
         V = parts["v"].reshape(L, s.n_kv_heads, s.head_dim)
     else:
         K = np.concatenate([np.asarray(k_meta, F64), np.asarray(k, F64)], axis=0)
@@ -273,7 +298,7 @@ def decode_step(p, x, pos, k_cache, v_cache, h, k_meta, v_meta):
     kc = np.array(k_cache, F64, copy=True)
     vc = np.array(v_cache, F64, copy=True)
     if s.own_kv:
-        kc[:, pos % C, :] = parts["k"].reshape(s.n_kv_heads, s.head_dim)
+        kc[:, pos % C, :] = rope(parts["k"].reshape(1, s.n_kv_heads, s.head_dim), [M + pos], s.rope_base)[0]
         vc[:, pos % C, :] = parts["v"].reshape(s.n_kv_heads, s.head_dim)
     lo = max(0, pos - s.window + 1) if s.window > 0 else 0
     if s.window <= 0:
@@ -281,7 +306,7 @@ def decode_step(p, x, pos, k_cache, v_cache, h, k_meta, v_meta):
     reals = np.arange(lo, pos + 1)
     Kk = np.concatenate([np.asarray(k_meta, F64), kc[:, reals % C, :].transpose(1, 0, 2)], axis=0)
     Vv = np.concatenate([np.asarray(v_meta, F64), vc[:, reals % C, :].transpose(1, 0, 2)], axis=0)
-    q = parts["q"].reshape(s.n_heads, s.head_dim)
+    q = rope(parts["q"].reshape(1, s.n_heads, s.head_dim), [M + pos], s.rope_base)[0]
     group = s.n_heads // s.n_kv_heads
     O = np.empty((s.n_heads, s.head_dim), F64)
     for hh in range(s.n_heads):

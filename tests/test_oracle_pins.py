@@ -431,3 +431,60 @@ def test_prefill_case_shapes_and_split():
         assert ("k" in parts) == own
         outs = orc.prefill_batch(case)
         assert outs[1].Y.shape == (5, s.d_model)
+
+
+# --- rotary position encoding (reading D17) --------------------------------------------
+
+def test_rope_two_dims_is_a_plane_rotation():
+    """hd = 2: the single pair turns by the position itself (base**0 = 1), counter-clockwise."""
+    for p in (0.0, 1.0, 3.0, 1000.0):
+        out = orc.rope(np.array([[[1.0, 0.0]], [[0.0, 1.0]]]), [p, p], 10000.0)
+        assert np.allclose(out[0, 0], [math.cos(p), math.sin(p)], atol=1e-12)
+        assert np.allclose(out[1, 0], [-math.sin(p), math.cos(p)], atol=1e-12)
+
+
+def test_rope_pairs_and_frequencies():
+    """hd = 4: dims (0, 1) turn at frequency 1, dims (2, 3) at base**-0.5; no mixing across pairs."""
+    base, p = 100.0, 2.5
+    e = np.eye(4)[:, None, :]                      # four unit vectors, one head each
+    out = orc.rope(e, [p] * 4, base)
+    w1 = base ** -0.5
+    assert np.allclose(out[0, 0], [math.cos(p), math.sin(p), 0, 0], atol=1e-12)
+    assert np.allclose(out[2, 0], [0, 0, math.cos(p * w1), math.sin(p * w1)], atol=1e-12)
+    assert np.allclose(out[3, 0], [0, 0, -math.sin(p * w1), math.cos(p * w1)], atol=1e-12)
+
+
+def test_rope_scores_depend_only_on_relative_position():
+    r = np.random.Generator(np.random.PCG64(5))
+    q = r.standard_normal((1, 3, 16))
+    k = r.standard_normal((1, 3, 16))
+    def score(i, j):
+        return np.sum(orc.rope(q, [i], 500.0) * orc.rope(k, [j], 500.0), axis=-1)
+    assert np.allclose(score(7, 3), score(107, 103), atol=1e-10)
+    assert np.allclose(score(0, 0), np.sum(q * k, axis=-1), atol=1e-12)   # no offset: plain dot
+    assert not np.allclose(score(7, 3), score(7, 4))
+    # rotations keep every vector's norm
+    assert np.allclose(np.linalg.norm(orc.rope(q, [12345], 500.0), axis=-1), np.linalg.norm(q, axis=-1))
+
+
+def test_rope_prefill_then_decode_uses_the_same_positions():
+    """With RoPE, decode at real index T (position M + T) continues prefill(T) exactly as row T of
+    prefill(T+1): meta at positions 0..M-1, real token t at M + t, K rotated before caching."""
+    s = SMALL.with_(window=5, rope_base=50.0)
+    case = make_prefill_case(s, 1, 12, seed=91)
+    T = 11
+    full = orc.layer_forward(case.params, case.x[0])
+    pre = orc.layer_forward(case.params, case.x[0, :T])
+    C = 5
+    kc = np.zeros((s.n_kv_heads, C, s.head_dim))
+    vc = np.zeros_like(kc)
+    for t in range(T - C, T):
+        kc[:, t % C] = pre.K[s.n_meta + t]
+        vc[:, t % C] = pre.V[s.n_meta + t]
+    km, vm = orc.meta_kv(case.params)
+    assert np.allclose(km, full.K[:s.n_meta], atol=1e-12)
+    d = orc.decode_step(case.params, case.x[0, T], T, kc, vc, pre.h_final, km, vm)
+    assert np.allclose(d.Y, full.Y[T], rtol=1e-10, atol=1e-12)
+    # and RoPE changes the result (the base is not silently ignored)
+    plain = orc.layer_forward(make_prefill_case(s.with_(rope_base=0.0), 1, 12, seed=91).params, case.x[0])
+    assert not np.allclose(plain.Y, full.Y)
