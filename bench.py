@@ -38,7 +38,7 @@ PEAK_F32_VEC = 157.3e12    # fp32 vector FLOP/s (packed); non-packed lane-op rat
 N_CU, CLK = 256, 2.4e9
 PEAK_VALU_LANE_OPS = N_CU * 64 * CLK        # non-packed fp32 lane-ops/s (39.3 T)
 
-STAGES = ["in_proj", "kv_write", "attention", "w_o", "ssm", "epilogue", "out_proj", "convert"]
+STAGES = ["in_proj", "kv_write", "attention", "w_o", "ssm", "epilogue", "out_proj", "convert", "rope"]
 # in a prefill the scan runs on a second stream beside attention and W_O: their durations include
 # the contention, so the headline roofline is taken over the kernels that run alone
 CONCURRENT = {"ssm": "attention, w_o", "attention": "ssm", "w_o": "ssm"}
@@ -82,6 +82,9 @@ def prefill_work(s, B, T):
     }
     if s.dtype == "bf16":
         w["convert"] = ("hbm", conversion_bytes(s, R))
+    if getattr(s, "rope_base", 0.0) > 0:
+        # q (and a producer's k) columns read and written once
+        w["rope"] = ("hbm", float(R * (hq + (s.n_kv_heads * s.head_dim if s.own_kv else 0)) * es * 2))
     if s.own_kv:
         w["kv_write"] = ("hbm", float(R * s.n_kv_heads * s.head_dim * es * 2 * 2))
     return w
@@ -193,13 +196,13 @@ def timed(layers, fn, steps, warmup):
     return ms, ms_rec, [L.hymba_layer_profile_read(lay.handle) for lay in layers]
 
 
-def bench_prefill(cfg_id, steps, warmup):
+def bench_prefill(cfg_id, steps, warmup, rope_base=0.0):
     import torch
     from hybrid_attention_ssm_swa_amd.layer import MixerLayer, make_kv, upload
     from hymba_synth import config_by_id
     from hymba_synth.generate import make_config_case
     cfg = config_by_id(cfg_id)
-    s = cfg.shape
+    s = cfg.shape.with_(rope_base=rope_base)
     t = time.time()
     case = make_config_case(cfg_id)
     log(f"[bench] config {cfg_id} ({cfg.name}) inputs generated in {time.time() - t:.1f}s")
@@ -504,6 +507,8 @@ def main():
             f"{workloads['global_decode_b8_full_cache']['tokens_per_s_per_layer']:.0f} tok/s/layer")
         workloads["global_8k_prefill"] = bench_prefill(3, max(3, args.steps // 2), args.warmup)
         log(f"[bench] 8K global prefill: {workloads['global_8k_prefill']['tokens_per_s']:.0f} tok/s")
+        workloads["rope_swa_8k_prefill"] = bench_prefill(2, args.steps, args.warmup, rope_base=10000.0)
+        log(f"[bench] 8K SWA prefill with RoPE (base 1e4): {workloads['rope_swa_8k_prefill']['tokens_per_s']:.0f} tok/s")
         workloads["ablation300m_prefill"] = bench_prefill(1, args.steps, args.warmup)
         log(f"[bench] 300M SWA prefill: {workloads['ablation300m_prefill']['tokens_per_s']:.0f} tok/s")
 

@@ -33,7 +33,7 @@ EXPORTED = [
     "hymba_kernel_selective_scan", "hymba_kernel_epilogue",
     "hymba_layer_profile", "hymba_layer_profile_read", "hymba_stage_name",
 ]
-HYMBA_N_STAGES = 8
+HYMBA_N_STAGES = 9
 
 
 class HymbaError(RuntimeError):
@@ -46,7 +46,8 @@ class hymba_layer_cfg(ctypes.Structure):
     _fields_ = [("d_model", c_int32), ("n_heads", c_int32), ("n_kv_heads", c_int32),
                 ("head_dim", c_int32), ("d_inner", c_int32), ("d_state", c_int32),
                 ("n_meta", c_int32), ("window", c_int32), ("own_kv", c_int32),
-                ("dtype", c_int32), ("rms_eps", c_float)]
+                ("dtype", c_int32), ("rms_eps", c_float),
+                ("rope_base", c_float)]
 
 
 class hymba_layer_weights(ctypes.Structure):

@@ -23,6 +23,7 @@ SOURCES = [
     "gemm_blaslt.cpp",
     "attn_prefill.hip",
     "scan.hip",
+    "rope.hip",
     "epilogue.hip",
     "decode.hip",
     "gemm_f32.hip",

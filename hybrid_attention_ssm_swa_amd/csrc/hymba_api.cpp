@@ -106,9 +106,10 @@ struct StageTimer {
     if (pair >= 0) hipEventRecord(L.ev[2 * pair + 1], s);
   }
 };
-enum { ST_IN_PROJ = 0, ST_KV = 1, ST_ATTN = 2, ST_WO = 3, ST_SSM = 4, ST_EPI = 5, ST_OUT = 6, ST_CVT = 7 };
-const char* kStageNames[HYMBA_N_STAGES] = {"in_proj", "kv_write", "attention", "w_o",
-                                           "ssm",     "epilogue", "out_proj",  "convert"};
+enum { ST_IN_PROJ = 0, ST_KV = 1, ST_ATTN = 2, ST_WO = 3, ST_SSM = 4, ST_EPI = 5, ST_OUT = 6, ST_CVT = 7,
+       ST_ROPE = 8 };
+const char* kStageNames[HYMBA_N_STAGES] = {"in_proj", "kv_write", "attention", "w_o", "ssm",
+                                           "epilogue", "out_proj", "convert", "rope"};
 
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -135,6 +136,10 @@ int32_t check_cfg(const hymba_layer_cfg* c) {
   if (c->own_kv != 0 && c->own_kv != 1) return fail(HYMBA_ERR_INVALID_ARG, "own_kv must be 0 or 1");
   if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps))
     return fail(HYMBA_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
+  if (!(c->rope_base >= 0.f) || !std::isfinite(c->rope_base))
+    return fail(HYMBA_ERR_INVALID_ARG, "rope_base must be finite and >= 0");
+  if (c->rope_base > 0.f && (c->head_dim % 8 != 0 || c->head_dim / 2 > kRopeMaxPairs))
+    return fail(HYMBA_ERR_UNSUPPORTED, "rotary encoding needs head_dim a multiple of 8, at most 128");
   if (c->d_state != 8 && c->d_state != 16)
     return fail(HYMBA_ERR_UNSUPPORTED, "d_state must be 8 or 16 (got %d)", c->d_state);
   if (c->d_inner % 8 != 0) return fail(HYMBA_ERR_UNSUPPORTED, "d_inner must be a multiple of 8");
@@ -278,6 +283,25 @@ int32_t in_projection(const hymba_layer& L, const void* x, int64_t rows, char* w
                  s);
 }
 
+// Rotary encoding of the q (and, for a producer, k) columns of `rows` projection rows in place:
+// row r sits at position first + pos[r] (decode) or first + r % T.
+template <typename CT>
+int32_t apply_rope(const hymba_layer& L, char* ws, const WsLayout& wl, int64_t rows, int64_t T, int64_t first,
+                   const int64_t* pos, hipStream_t s) {
+  const hymba_layer_cfg& c = L.cfg;
+  if (!(c.rope_base > 0.f)) return HYMBA_OK;
+  StageTimer st(L, ST_ROPE, s);
+  RopeArgs<CT> a{};
+  a.p = reinterpret_cast<CT*>(ws + wl.P); a.ld = L.n_in;
+  a.rows = rows; a.T = T;
+  a.n_q_heads = c.n_heads; a.k_off = L.off_k; a.n_k_heads = c.own_kv ? c.n_kv_heads : 0; a.head_dim = c.head_dim;
+  a.first = first; a.pos = pos;
+  for (int i = 0; i < c.head_dim / 2; ++i)
+    a.theta[i] = std::pow(static_cast<double>(c.rope_base), -2.0 * i / c.head_dim);
+  HIP_TRY(launch_rope(a, s), "rotary encoding launch");
+  return HYMBA_OK;
+}
+
 // W_O of `rows` rows: attention output O -> Ao.
 template <typename CT>
 int32_t w_o_projection(const hymba_layer& L, char* ws, const WsLayout& wl, int64_t rows, hipStream_t s) {
@@ -389,6 +413,7 @@ int32_t prepare_impl(hymba_layer& L, const hymba_kv* kv, char* ws, const WsLayou
     return HYMBA_OK;
   }
   STATUS_TRY(in_projection<CT>(L, L.w.meta, M, ws, wl, s));
+  STATUS_TRY(apply_rope<CT>(L, ws, wl, M, M, 0, nullptr, s));   // meta rows at positions 0..M-1
   const CT* P = reinterpret_cast<const CT*>(ws + wl.P);
   const int64_t kvw = (int64_t)c.n_kv_heads * c.head_dim;
   const CT *kk, *vv;
@@ -434,6 +459,7 @@ int32_t prefill_impl(hymba_layer& L, const void* x, int B, int T_, void* y, cons
   const int64_t rows = (int64_t)B * T_;
   const int64_t kvw = (int64_t)c.n_kv_heads * c.head_dim;
   STATUS_TRY(in_projection<CT>(L, x, rows, ws, wl, s));
+  STATUS_TRY(apply_rope<CT>(L, ws, wl, rows, T_, c.n_meta, nullptr, s));   // real token t at M + t
   const CT* P = reinterpret_cast<const CT*>(ws + wl.P);
   const CT *k, *v;
   int64_t ld_kv, seq_stride;
@@ -482,6 +508,7 @@ int32_t decode_impl(hymba_layer& L, const void* x, const int64_t* pos, int B, vo
   if (L.profiling) ++L.prof_calls;
   const hymba_layer_cfg& c = L.cfg;
   STATUS_TRY(in_projection<CT>(L, x, B, ws, wl, s));
+  STATUS_TRY(apply_rope<CT>(L, ws, wl, B, 1, c.n_meta, pos, s));   // the new token at M + pos[b]
   const CT* P = reinterpret_cast<const CT*>(ws + wl.P);
   if (c.own_kv) {
     StageTimer st(L, ST_KV, s);
@@ -605,6 +632,8 @@ int32_t hymba_kv_share_bind(hymba_layer* consumer, const hymba_layer* producer) 
     return fail(HYMBA_ERR_BIND, "producer and consumer differ in n_kv_heads, head_dim, n_meta or dtype");
   if ((c.window > 0) != (p.window > 0) || (c.window > 0 && c.window != p.window))
     return fail(HYMBA_ERR_BIND, "producer and consumer must have the same attention window");
+  if (c.rope_base != p.rope_base)
+    return fail(HYMBA_ERR_BIND, "producer and consumer must use the same rotary encoding base");
   if (producer->consumer && producer->consumer != consumer)
     return fail(HYMBA_ERR_BIND, "the producer already has a consumer (K/V are shared by pairs)");
   if (consumer->producer && consumer->producer != producer)

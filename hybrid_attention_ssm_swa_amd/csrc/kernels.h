@@ -116,6 +116,22 @@ int decode_attn_splits(int B, int n_kv_heads, int n_keys_max, int head_dim, int 
 constexpr int kDecodeMaxSplits = 64;
 constexpr int kDecodeMaxHd = 128;
 
+// ---- rotary position encoding of the projection's q and k columns, in place ----------
+// Row r (of `rows`) holds q heads at columns [0, n_q_heads * hd) and k heads at
+// [k_off, k_off + n_k_heads * hd); its position is first + pos[r] (pos != null,
+// decode) or first + r % T.  theta[i] = base^(-2i/hd) for the pairs of a head.
+constexpr int kRopeMaxPairs = 64;
+template <typename CT>
+struct RopeArgs {
+  CT* p; int64_t ld;
+  int64_t rows; int64_t T;
+  int n_q_heads; int64_t k_off; int n_k_heads; int head_dim;
+  int64_t first; const int64_t* pos;
+  double theta[kRopeMaxPairs];
+};
+hipError_t launch_rope(const RopeArgs<float>& a, hipStream_t s);
+hipError_t launch_rope(const RopeArgs<half_t>& a, hipStream_t s);
+
 // ---- fp32 GEMM: Y[rows, out] = X[rows, in] . W[out, in]^T ----------------------
 hipError_t launch_gemm_f32(const float* X, int64_t ldx, const float* W, int64_t ldw, float* Y,
                            int64_t ldy, int64_t rows, int out, int in, hipStream_t s);

@@ -46,7 +46,8 @@ class MixerLayer:
     """One hybrid-head mixer layer on the current GPU.
 
     `shape` has the fields of a layer configuration (d_model, n_heads, head_dim,
-    n_kv_heads, d_inner, d_state, n_meta, window, own_kv, dtype, rms_eps);
+    n_kv_heads, d_inner, d_state, n_meta, window, own_kv, dtype, rms_eps and,
+    optionally, rope_base);
     `params` has meta, w_in, w_o, w_out, A, D, dt_bias, beta1, beta2 arrays.
     """
 
@@ -71,6 +72,7 @@ class MixerLayer:
         cfg.n_meta, cfg.window, cfg.own_kv = shape.n_meta, shape.window, int(shape.own_kv)
         cfg.dtype = L.HYMBA_BF16 if shape.dtype == "bf16" else L.HYMBA_F32
         cfg.rms_eps = shape.rms_eps
+        cfg.rope_base = getattr(shape, "rope_base", 0.0)
         self.cfg = cfg
         w = L.hymba_layer_weights()
         w.w_in, w.w_o, w.w_out, w.meta = _ptr(self.w_in), _ptr(self.w_o), _ptr(self.w_out), _ptr(self.meta)

@@ -84,6 +84,12 @@ typedef struct hymba_layer_cfg {
   int32_t own_kv;     /* 1: projects its own K/V (producer); 0: consumer           */
   int32_t dtype;      /* HYMBA_F32 or HYMBA_BF16                                   */
   float rms_eps;      /* epsilon inside the RMS norm's square root (e.g. 1e-6)     */
+  float rope_base;    /* > 0: rotary position encoding of q and k (RoFormer pairs
+                         (2i, 2i+1) turned by pos * base^(-2i/hd); meta rows at
+                         positions 0..M-1, real token t at M + t; K is rotated
+                         before it is cached or handed on), the base the Hymba
+                         summary's section 2.5 says the 8K stage changes;
+                         0: no position encoding                              */
 } hymba_layer_cfg;
 
 /* Device pointers.  Matrices in the storage dtype; vectors fp32. */
@@ -194,6 +200,7 @@ const char* hymba_status_string(int32_t status);
  *   0 shared input projection GEMM   1 K/V write            2 attention
  *   3 W_O projection GEMM            4 SSM (scan / step)    5 fused epilogue
  *   6 output projection GEMM         7 storage/activation type conversions
+ *   8 rotary encoding of q and k (layers with rope_base > 0)
  * hymba_layer_profile(layer, 0) stops recording and keeps what was recorded.
  * hymba_layer_profile_read waits for the last recorded event and writes, per
  * stage, the summed interval time divided by the number of recorded calls
@@ -202,7 +209,7 @@ const char* hymba_status_string(int32_t status);
  * that the read fails with HYMBA_ERR_WORKSPACE (stage_ms zeroed).  The first
  * enable creates the events (HYMBA_ERR_HIP on failure); nothing else touches
  * the device.                                                               */
-#define HYMBA_N_STAGES 8
+#define HYMBA_N_STAGES 9
 int32_t hymba_layer_profile(hymba_layer* layer, int32_t enable);
 int32_t hymba_layer_profile_read(hymba_layer* layer, float* stage_ms, int32_t n);
 const char* hymba_stage_name(int32_t stage);

@@ -26,7 +26,7 @@ def _declared_functions():
 
 def _cfg(**kw):
     base = dict(d_model=64, n_heads=4, n_kv_heads=2, head_dim=32, d_inner=64, d_state=8, n_meta=4,
-                window=8, own_kv=1, dtype=L.HYMBA_F32, rms_eps=1e-6)
+                window=8, own_kv=1, dtype=L.HYMBA_F32, rms_eps=1e-6, rope_base=0.0)
     base.update(kw)
     c = L.hymba_layer_cfg()
     for k, v in base.items():
@@ -71,6 +71,8 @@ def test_status_strings():
     (dict(dtype=L.HYMBA_BF16, head_dim=32), L.HYMBA_ERR_UNSUPPORTED),
     (dict(dtype=L.HYMBA_BF16, head_dim=64, n_heads=18, n_kv_heads=2), L.HYMBA_ERR_UNSUPPORTED),
     (dict(d_inner=60), L.HYMBA_ERR_UNSUPPORTED),
+    (dict(rope_base=-1.0), L.HYMBA_ERR_INVALID_ARG),
+    (dict(rope_base=float("inf")), L.HYMBA_ERR_INVALID_ARG),
 ])
 def test_create_rejects_bad_configs(kw, code):
     cfg = _cfg(**kw)
@@ -116,6 +118,11 @@ def test_bind_rules():
         assert e.value.status == L.HYMBA_ERR_BIND
         L.hymba_kv_share_bind(cons, None)             # unbind frees the producer
         L.hymba_kv_share_bind(cons2, prod)
+        other_rope = _create(_cfg(own_kv=0, rope_base=500.0))
+        with pytest.raises(L.HymbaError) as e:
+            L.hymba_kv_share_bind(other_rope, prod)
+        assert e.value.status == L.HYMBA_ERR_BIND
+        L.hymba_layer_destroy(other_rope)
         wrong_window = _create(_cfg(own_kv=0, window=0))
         with pytest.raises(L.HymbaError) as e:
             L.hymba_kv_share_bind(wrong_window, prod)
@@ -188,7 +195,7 @@ def test_kernel_entry_points_validate():
 
 def test_stage_names_and_profile_read_without_recording():
     names = [L.hymba_stage_name(i) for i in range(L.HYMBA_N_STAGES)]
-    assert names == ["in_proj", "kv_write", "attention", "w_o", "ssm", "epilogue", "out_proj", "convert"]
+    assert names == ["in_proj", "kv_write", "attention", "w_o", "ssm", "epilogue", "out_proj", "convert", "rope"]
     assert L.hymba_stage_name(L.HYMBA_N_STAGES) == "unknown"
     h = _create(_cfg())
     try:

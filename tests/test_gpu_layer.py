@@ -58,6 +58,9 @@ SMALL_BF16 = LayerShape(d_model=256, n_heads=8, head_dim=64, n_kv_heads=2, d_inn
     (SMALL_BF16, 2, 1),
     (SMALL_BF16.with_(n_kv_heads=8, n_meta=64), 1, 130),
     (CONFIGS[0].shape.with_(window=5, n_meta=3), 2, 41),
+    (SMALL_BF16.with_(rope_base=10000.0), 2, 150),
+    (SMALL_BF16.with_(rope_base=500.0, window=0, n_meta=40), 1, 130),
+    (CONFIGS[0].shape.with_(rope_base=100.0), 1, 60),
 ])
 def test_small_layer_prefill(shape, B, T):
     announce(f"small prefill {shape} B={B} T={T}")
@@ -67,7 +70,7 @@ def test_small_layer_prefill(shape, B, T):
 
 def test_meta_prefix_outputs():
     """The prepared meta prefix (K/V, SSM state, meta-row outputs) equals the oracle's meta rows."""
-    for shape in (SMALL_BF16, CONFIGS[0].shape):
+    for shape in (SMALL_BF16, CONFIGS[0].shape, SMALL_BF16.with_(rope_base=1000.0)):
         announce(f"meta prefix {shape.dtype}")
         case = make_prefill_case(shape, 1, 8, seed=11)
         layer = MixerLayer(shape, case.params)
@@ -167,12 +170,12 @@ def test_global_decode_full_cache():
     check_stored("written K slot", kc[:, :, 8192], np.stack([ref[b][0].k_cache[:, 8192] for b in ref]), "f16")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_decode_small_mixed_positions(dtype):
+@pytest.mark.parametrize("dtype,rope", [("bf16", 0.0), ("f32", 0.0), ("bf16", 10000.0), ("f32", 300.0)])
+def test_decode_small_mixed_positions(dtype, rope):
     """Positions differ per sequence: before the window fills, at the wrap, far beyond."""
-    announce(f"decode small {dtype}")
+    announce(f"decode small {dtype} rope {rope}")
     base = SMALL_BF16 if dtype == "bf16" else CONFIGS[0].shape.with_(n_meta=6)
-    s = base.with_(window=16)
+    s = base.with_(window=16, rope_base=rope)
     case = make_decode_case(s, s.with_(own_kv=False), 6, 0, seed=21, cache_len=16)
     case.pos = np.array([0, 3, 15, 16, 17, 1000], dtype=np.int64)
     _, _, yp, yc, stp, stc, _, _ = _decode_pair_gpu(case)
@@ -182,11 +185,12 @@ def test_decode_small_mixed_positions(dtype):
     check("consumer state", stc, np.stack([ref[b][1].h for b in ref]), dtype)
 
 
-def test_kv_share_bound_equals_handed():
+@pytest.mark.parametrize("rope", [0.0, 10000.0])
+def test_kv_share_bound_equals_handed(rope):
     """A consumer bound to its producer gives exactly the output of an unbound consumer handed the
     producer's K/V (spec check on the GPU path), and both match the oracle."""
-    announce("kv share bound vs handed")
-    s = SMALL_BF16
+    announce(f"kv share bound vs handed, rope {rope}")
+    s = SMALL_BF16.with_(rope_base=rope)
     r = np.random.Generator(np.random.PCG64(31))
     from hymba_synth import make_layer_params
     prod_p = make_layer_params(r, s)
@@ -216,12 +220,13 @@ def test_kv_share_bound_equals_handed():
         check_stored(f"consumer Y[b={b}]", y_bound[b], ref.Y, "bf16")
 
 
-@pytest.mark.parametrize("window,T", [(16, 40), (16, 9), (0, 33)])
-def test_prefill_then_decode_continues(window, T):
+@pytest.mark.parametrize("window,T,rope", [(16, 40, 0.0), (16, 9, 0.0), (0, 33, 0.0), (16, 40, 10000.0),
+                                           (0, 33, 700.0)])
+def test_prefill_then_decode_continues(window, T, rope):
     """prefill(T) leaves the cache and state that decode(T) continues from:
     its output equals row T of prefill(T+1) (GPU) and the oracle."""
-    announce(f"prefill->decode window={window} T={T}")
-    s = SMALL_BF16.with_(window=window)
+    announce(f"prefill->decode window={window} T={T} rope={rope}")
+    s = SMALL_BF16.with_(window=window, rope_base=rope)
     case = make_prefill_case(s, 2, T + 1, seed=41)
     layer = MixerLayer(s, case.params)
     C = window if window > 0 else T + 8
