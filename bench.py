@@ -289,6 +289,65 @@ def bench_decode(cfg_id, steps, warmup, case=None):
     return out
 
 
+def griffin_work(shape, B, T):
+    """Algorithmic work of the Griffin block's stages (prefill of B x T, or decode with T = 1)."""
+    es = 2 if shape.dtype == "bf16" else 4
+    rows, D, R = B * T, shape.d_model, shape.d_rnn
+    if T == 1:   # decode: the GEMMs stream their weights
+        gemm = lambda o, i: ("hbm", float(o * i * es + rows * (o + i) * es))   # noqa: E731
+        w = {"in_proj": gemm(2 * R, D), "gate_proj": gemm(2 * R, R), "out_proj": gemm(D, R)}
+    else:
+        w = {"in_proj": ("mfma", 2.0 * rows * D * 2 * R), "gate_proj": ("mfma", 2.0 * rows * R * 2 * R),
+             "out_proj": ("mfma", 2.0 * rows * R * D)}
+    # conv: u read, xc written (+ the conv state); RG-LRU: both gates, xc and v read, y written
+    w["conv"] = ("hbm", float(rows * R * es * 2 + B * 3 * R * 4 * 2))
+    w["rglru"] = ("hbm", float(rows * R * es * 5 + B * R * 4 * 2))
+    return w
+
+
+def bench_griffin(steps, warmup, B=16, T=8192, decode_batch=128):
+    """The Griffin recurrent block at d_model 1536, d_rnn 2048 (bf16): an 8K prefill of B
+    sequences and a decode step of `decode_batch` sequences."""
+    import torch
+    from hybrid_attention_ssm_swa_amd import _lib as L
+    from hybrid_attention_ssm_swa_amd.griffin import GriffinBlock
+    from hybrid_attention_ssm_swa_amd.layer import upload
+    from hymba_synth.griffin import GRIFFIN_8K, make_griffin_case
+    shape = GRIFFIN_8K
+    case = make_griffin_case(shape, B, T, seed=2024)
+    blk = GriffinBlock(shape, case.params)
+    x = upload(case.x, torch.bfloat16, "cuda")
+    del case
+    y = torch.empty_like(x)
+    conv, h = blk.new_state(B)
+    fn = lambda i: blk.prefill(x, conv_state_out=conv, h_out=h, y=y)   # noqa: E731
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    ms = _time_loop(fn, steps)
+    stage = [0.0] * L.GRIFFIN_N_STAGES
+    reps = max(3, steps // 2)
+    for _ in range(reps):
+        _, st = blk.prefill(x, conv_state_out=conv, h_out=h, y=y, timed=True)
+        stage = [a + b / reps for a, b in zip(stage, st)]
+    work = griffin_work(shape, B, T)
+    ents = [roofline_entry(n, work[n][0], work[n][1], stage[k]) for k, n in enumerate(L.GRIFFIN_STAGES)]
+    del x, y
+    torch.cuda.empty_cache()
+    # decode: one token for each of decode_batch sequences, states in place (two sets alternated)
+    xd = torch.randn(decode_batch, shape.d_model, device="cuda").to(torch.bfloat16)
+    yd = torch.empty_like(xd)
+    sets = [blk.new_state(decode_batch) for _ in range(2)]
+    fd = lambda i: blk.decode(xd, *sets[i % 2], y_t=yd)   # noqa: E731
+    for _ in range(warmup):
+        fd(0)
+    torch.cuda.synchronize()
+    ms_d = _time_loop(fd, steps)
+    return {"tokens_per_s": B * T / (ms * 1e-3), "ms_per_step": ms, "batch": B, "seq": T,
+            "stage_ms": dict(zip(L.GRIFFIN_STAGES, stage)), "kernels": ents,
+            "decode": {"batch": decode_batch, "ms_per_step": ms_d, "tokens_per_s": decode_batch / (ms_d * 1e-3)}}
+
+
 # --- rocprofv3 summaries (run on the host after the profiled runs) ----------------------------
 
 COPY_PROBE_BYTES = 1 << 30      # the plain copy kernel (torch.neg over fp32) reads and writes this much
@@ -511,6 +570,9 @@ def main():
         log(f"[bench] 8K SWA prefill with RoPE (base 1e4): {workloads['rope_swa_8k_prefill']['tokens_per_s']:.0f} tok/s")
         workloads["ablation300m_prefill"] = bench_prefill(1, args.steps, args.warmup)
         log(f"[bench] 300M SWA prefill: {workloads['ablation300m_prefill']['tokens_per_s']:.0f} tok/s")
+        workloads["griffin_block_8k"] = bench_griffin(args.steps, args.warmup)
+        log(f"[bench] Griffin block 8K prefill: {workloads['griffin_block_8k']['tokens_per_s']:.0f} tok/s; "
+            f"decode B=128: {workloads['griffin_block_8k']['decode']['tokens_per_s']:.0f} tok/s")
 
     kernels = [k for k in main_run["kernels"] if k["bound"] != "alu" and "concurrent_with" not in k]
     dominant = max(kernels, key=lambda k: k["ms"])

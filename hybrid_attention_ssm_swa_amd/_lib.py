@@ -32,8 +32,12 @@ EXPORTED = [
     "hymba_last_error", "hymba_status_string", "hymba_kernel_attention",
     "hymba_kernel_selective_scan", "hymba_kernel_epilogue",
     "hymba_layer_profile", "hymba_layer_profile_read", "hymba_stage_name",
+    "griffin_block_persistent_bytes", "griffin_block_prepare", "griffin_workspace_bytes",
+    "griffin_block_prefill", "griffin_block_decode",
 ]
 HYMBA_N_STAGES = 9
+GRIFFIN_N_STAGES = 5
+GRIFFIN_STAGES = ["in_proj", "conv", "gate_proj", "rglru", "out_proj"]
 
 
 class HymbaError(RuntimeError):
@@ -54,6 +58,15 @@ class hymba_layer_weights(ctypes.Structure):
     _fields_ = [("w_in", c_void_p), ("w_o", c_void_p), ("w_out", c_void_p), ("meta", c_void_p),
                 ("A", c_void_p), ("D", c_void_p), ("dt_bias", c_void_p), ("beta1", c_void_p),
                 ("beta2", c_void_p)]
+
+
+class griffin_block_cfg(ctypes.Structure):
+    _fields_ = [("d_model", c_int32), ("d_rnn", c_int32), ("dtype", c_int32), ("c", c_float)]
+
+
+class griffin_block_weights(ctypes.Structure):
+    _fields_ = [("w_in", c_void_p), ("conv_w", c_void_p), ("w_gate", c_void_p), ("lam", c_void_p),
+                ("w_out", c_void_p)]
 
 
 class hymba_kv(ctypes.Structure):
@@ -97,6 +110,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hymba_layer_profile": (c_int32, [P, c_int32]),
         "hymba_layer_profile_read": (c_int32, [P, POINTER(c_float), c_int32]),
         "hymba_stage_name": (c_char_p, [c_int32]),
+        "griffin_block_persistent_bytes": (c_size_t, [POINTER(griffin_block_cfg)]),
+        "griffin_block_prepare": (c_int32, [POINTER(griffin_block_cfg), POINTER(griffin_block_weights), P,
+                                            c_size_t, P]),
+        "griffin_workspace_bytes": (c_size_t, [POINTER(griffin_block_cfg), c_int32, c_int32]),
+        "griffin_block_prefill": (c_int32, [POINTER(griffin_block_cfg), POINTER(griffin_block_weights), P, P,
+                                            c_int32, c_int32, P, P, P, P, P, P, c_size_t, P, POINTER(c_float)]),
+        "griffin_block_decode": (c_int32, [POINTER(griffin_block_cfg), POINTER(griffin_block_weights), P, P,
+                                           c_int32, P, P, P, P, c_size_t, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -213,3 +234,34 @@ def hymba_layer_profile_read(layer: int):
 
 def hymba_stage_name(stage: int) -> str:
     return load_library().hymba_stage_name(stage).decode()
+
+
+def griffin_block_persistent_bytes(cfg: griffin_block_cfg) -> int:
+    return load_library().griffin_block_persistent_bytes(ctypes.byref(cfg))
+
+
+def griffin_block_prepare(cfg: griffin_block_cfg, weights: griffin_block_weights, persistent, persistent_bytes: int,
+                          stream) -> None:
+    _check(load_library().griffin_block_prepare(ctypes.byref(cfg), ctypes.byref(weights), persistent,
+                                                persistent_bytes, stream))
+
+
+def griffin_workspace_bytes(cfg: griffin_block_cfg, batch: int, seq: int) -> int:
+    return load_library().griffin_workspace_bytes(ctypes.byref(cfg), batch, seq)
+
+
+def griffin_block_prefill(cfg: griffin_block_cfg, weights: griffin_block_weights, persistent, x: int, B: int, T: int,
+                          y: int, conv_state, h, conv_state_out, h_out, workspace: int, workspace_bytes: int,
+                          stream, timed: bool = False):
+    """With timed=True the call returns the milliseconds of each of GRIFFIN_STAGES (and waits for the work)."""
+    ms = (c_float * GRIFFIN_N_STAGES)() if timed else None
+    _check(load_library().griffin_block_prefill(ctypes.byref(cfg), ctypes.byref(weights), persistent, x, B, T, y,
+                                                conv_state, h, conv_state_out, h_out, workspace, workspace_bytes,
+                                                stream, ms))
+    return [float(v) for v in ms] if timed else None
+
+
+def griffin_block_decode(cfg: griffin_block_cfg, weights: griffin_block_weights, persistent, x_t: int, B: int,
+                         y_t: int, conv_state: int, h: int, workspace: int, workspace_bytes: int, stream) -> None:
+    _check(load_library().griffin_block_decode(ctypes.byref(cfg), ctypes.byref(weights), persistent, x_t, B, y_t,
+                                               conv_state, h, workspace, workspace_bytes, stream))

@@ -28,6 +28,8 @@ SOURCES = [
     "decode.hip",
     "gemm_f32.hip",
     "convert.hip",
+    "griffin.hip",
+    "griffin_api.cpp",
 ]
 
 ARCH = "gfx950"

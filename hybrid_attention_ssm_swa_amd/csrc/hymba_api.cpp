@@ -21,6 +21,7 @@
 #include <string>
 #include <vector>
 
+#include "errors.h"
 #include "gemm_blaslt.h"
 #include "kernels.h"
 
@@ -59,10 +60,10 @@ struct hymba_layer {
 };
 
 namespace {
-
 thread_local std::string g_err;
+}  // namespace
 
-int32_t fail(int32_t code, const char* fmt, ...) {
+int32_t hymba::set_error(int32_t code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -71,6 +72,10 @@ int32_t fail(int32_t code, const char* fmt, ...) {
   g_err = buf;
   return code;
 }
+
+namespace {
+
+constexpr auto fail = hymba::set_error;
 
 int32_t hip_fail(hipError_t e, const char* what) {
   return fail(HYMBA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));

@@ -146,6 +146,38 @@ hipError_t launch_convert(const float* src, int64_t ld_src, bf16_t* dst, int64_t
 hipError_t launch_convert(const half_t* src, int64_t ld_src, bf16_t* dst, int64_t ld_dst, int64_t rows,
                           int64_t cols, hipStream_t s);
 
+// ---- Griffin recurrent block: causal width-4 conv and the RG-LRU recurrence ------
+// conv: xc[row, r] = sum_k w[k, r] u[row - k, r] within a sequence; inputs before t = 0 come
+// from hist [B, 3, R] fp32 (oldest first; null: zeros); state_out [B, 3, R] (null: none) gets
+// the last three inputs (may alias hist only when seq == 1).
+template <typename T>
+struct GriffinConvArgs {
+  const T* u; int64_t ld_u;
+  const float* w;
+  const float* hist; float* state_out;
+  T* xc; int64_t ld_xc;
+  int B; int seq; int R;
+};
+hipError_t launch_griffin_conv(const GriffinConvArgs<float>& a, hipStream_t s);
+hipError_t launch_griffin_conv(const GriffinConvArgs<half_t>& a, hipStream_t s);
+
+// RG-LRU + GeLU branch: g [rows, 2R] holds the gate pre-activations (W_a xc | W_x xc); time is cut
+// into S segments of L steps; summ holds B * (S + 1) * R records (sum of log a, end state).
+template <typename T>
+struct RglruArgs {
+  const T* g; int64_t ld_g;
+  const T* xc; int64_t ld_xc;
+  const T* v; int64_t ld_v;
+  T* y; int64_t ldy;
+  const float* lam; float c;
+  const float* h0; float* h_out;
+  float2* summ;
+  int B; int seq; int R; int S; int L;
+};
+hipError_t launch_rglru(const RglruArgs<float>& a, hipStream_t s);
+hipError_t launch_rglru(const RglruArgs<half_t>& a, hipStream_t s);
+void rglru_plan(int B, int T, int R, int* S, int* L);
+
 // ---- misc ----------------------------------------------------------------------
 hipError_t launch_scale_copy(const float* src, float* dst, int64_t n, float scale, hipStream_t s);
 hipError_t launch_fill(float* dst, int64_t n, float value, hipStream_t s);

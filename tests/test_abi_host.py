@@ -11,7 +11,7 @@ import hybrid_attention_ssm_swa_amd as H
 from hybrid_attention_ssm_swa_amd import _lib as L
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "hymba_mixer.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in ("hymba_mixer.h", "griffin_block.h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="library not built")
 
@@ -19,9 +19,11 @@ FAKE = 1 << 20   # an aligned, never-dereferenced stand-in for device pointers
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(hymba_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b((?:hymba|griffin)_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def _cfg(**kw):
@@ -223,3 +225,94 @@ def test_attention_entry_checks_strides():
             L.hymba_kernel_attention(L.HYMBA_F16, a["q"], a["ld_q"], FAKE, FAKE, a["ld_kv"], a["stride"], FAKE, FAKE,
                                      4, a["o"], 640, 1, 40, 10, 2, 64, 16, None)
         assert e.value.status == L.HYMBA_ERR_INVALID_ARG, bad
+
+
+# --- the Griffin block's entry points -------------------------------------------------
+
+def _gcfg(**kw):
+    base = dict(d_model=64, d_rnn=96, dtype=L.HYMBA_F32, c=8.0)
+    base.update(kw)
+    c = L.griffin_block_cfg()
+    for k, v in base.items():
+        setattr(c, k, v)
+    return c
+
+
+def _gweights():
+    w = L.griffin_block_weights()
+    for f, _ in w._fields_:
+        setattr(w, f, FAKE)
+    return w
+
+
+def test_griffin_workspace_grows_with_the_call():
+    c = _gcfg()
+    a, b = L.griffin_workspace_bytes(c, 1, 100), L.griffin_workspace_bytes(c, 4, 100)
+    assert 0 < a < b and a % 256 == 0
+    assert L.griffin_workspace_bytes(_gcfg(dtype=L.HYMBA_BF16), 1, 100) > 64 << 20   # + GEMM workspace
+    assert L.griffin_workspace_bytes(c, 0, 5) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_model=0), L.HYMBA_ERR_INVALID_ARG),
+    (dict(dtype=5), L.HYMBA_ERR_INVALID_ARG),
+    (dict(c=0.0), L.HYMBA_ERR_INVALID_ARG),
+    (dict(c=float("nan")), L.HYMBA_ERR_INVALID_ARG),
+    (dict(d_rnn=100), L.HYMBA_ERR_UNSUPPORTED),
+])
+def test_griffin_rejects_bad_configs(kw, code):
+    c = _gcfg(**kw)
+    assert L.griffin_workspace_bytes(c, 1, 8) == 0
+    with pytest.raises(L.HymbaError) as e:
+        L.griffin_block_prefill(c, _gweights(), FAKE, FAKE, 1, 8, FAKE, None, None, None, None, FAKE, 1 << 40, None)
+    assert e.value.status == code
+
+
+def test_griffin_call_checks():
+    c, w = _gcfg(), _gweights()
+    big = 1 << 40
+    # empty calls return before touching anything
+    L.griffin_block_prefill(c, w, None, None, 0, 8, None, None, None, None, None, None, 0, None)
+    cases = [
+        (dict(ws_bytes=16), L.HYMBA_ERR_WORKSPACE),
+        (dict(ws=FAKE + 16), L.HYMBA_ERR_INVALID_ARG),
+        (dict(x=FAKE + 2), L.HYMBA_ERR_INVALID_ARG),
+        (dict(y=None), L.HYMBA_ERR_INVALID_ARG),
+        (dict(state=FAKE, state_out=FAKE), L.HYMBA_ERR_INVALID_ARG),   # aliasing needs seq == 1
+        (dict(B=70000), L.HYMBA_ERR_UNSUPPORTED),
+    ]
+    cases_bf16 = [(dict(pers=None), L.HYMBA_ERR_INVALID_ARG), (dict(pers=FAKE + 128), L.HYMBA_ERR_INVALID_ARG)]
+    for kw, code in cases:
+        a = dict(x=FAKE, y=FAKE, ws=FAKE, ws_bytes=big, state=None, state_out=None, B=2, pers=None)
+        a.update(kw)
+        with pytest.raises(L.HymbaError) as e:
+            L.griffin_block_prefill(c, w, a["pers"], a["x"], a["B"], 8, a["y"], a["state"], None, a["state_out"],
+                                    None, a["ws"], a["ws_bytes"], None)
+        assert e.value.status == code, (kw, L.hymba_last_error())
+    nw = _gweights()
+    nw.lam = None
+    with pytest.raises(L.HymbaError) as e:
+        L.griffin_block_prefill(c, nw, None, FAKE, 1, 8, FAKE, None, None, None, None, FAKE, big, None)
+    assert e.value.status == L.HYMBA_ERR_INVALID_ARG
+    with pytest.raises(L.HymbaError) as e:
+        L.griffin_block_decode(c, w, None, FAKE, 1, FAKE, None, FAKE, FAKE, big, None)
+    assert e.value.status == L.HYMBA_ERR_INVALID_ARG
+    cb = _gcfg(dtype=L.HYMBA_BF16)
+    for kw, code in cases_bf16:
+        with pytest.raises(L.HymbaError) as e:
+            L.griffin_block_prefill(cb, w, kw["pers"], FAKE, 1, 8, FAKE, None, None, None, None, FAKE, big, None)
+        assert e.value.status == code
+
+
+def test_griffin_persistent_buffer():
+    assert L.griffin_block_persistent_bytes(_gcfg()) == 0
+    c = _gcfg(dtype=L.HYMBA_BF16)
+    n = L.griffin_block_persistent_bytes(c)
+    assert n >= 2 * (2 * 96 * 64 + 2 * 96 * 96 + 64 * 96) and n % 256 == 0
+    L.griffin_block_prepare(_gcfg(), _gweights(), None, 0, None)    # fp32: nothing to do
+    with pytest.raises(L.HymbaError) as e:
+        L.griffin_block_prepare(c, _gweights(), FAKE, n - 1, None)
+    assert e.value.status == L.HYMBA_ERR_WORKSPACE
+    with pytest.raises(L.HymbaError) as e:
+        L.griffin_block_prepare(c, _gweights(), FAKE + 16, n, None)
+    assert e.value.status == L.HYMBA_ERR_INVALID_ARG
