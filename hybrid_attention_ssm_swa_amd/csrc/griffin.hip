@@ -3,15 +3,12 @@
 // the RG-LRU recurrence merged with the GeLU branch.
 //
 // The RG-LRU state is one number per channel, so channels alone (B * R) give
-// too few independent lanes to fill the chip; time is cut into S segments and
-// h_t = a_t h_(t-1) + b_t runs as a chunked scan with carry propagation.
-// Pass 1 runs segments 0 .. S-2 from zero and records (sum of log a_t, end
-// state); record 0 holds the handed state h0.  Pass 2 folds the records before
-// its segment into the start state (h = exp(sum log a) h + h_end), reruns the
-// segment and writes y_t = h_t GeLU(v_t).  A segment's decay is kept as a sum
-// of logs, so it neither under- nor overflows however long the segment.
-// Lane = channel: a wave's loads of one time step cover 64 consecutive
-// channels of a row (one 128-byte line for fp16 activations).
+// few independent lanes; the recurrence h_t = a_t h_(t-1) + b_t therefore
+// also runs in parallel over time inside a workgroup (the waves take
+// consecutive steps of a tile and combine their (decay product, state)
+// summaries), each coefficient computed once.  A lane takes two adjacent
+// channels: a wave's loads of one time step cover 128 consecutive channels of
+// a row (256 bytes of fp16 activations).
 #include <algorithm>
 
 #include "common.h"
@@ -22,182 +19,301 @@ namespace hymba {
 namespace {
 
 constexpr int kConvTaps = 4;
+constexpr int kConvSteps = 16;  // time steps per conv thread (the taps stay in registers)
 constexpr int kStepChunk = 8;   // time steps whose loads are issued together
 
-// thread per (row, 16-byte chunk of R)
+// 16 loaded bytes -> floats
+template <typename T> struct Unpack;
+template <> struct Unpack<float> {
+  static constexpr int n = 4;
+  __device__ static __forceinline__ void run(const uint4 x, float (&v)[4]) {
+    v[0] = __uint_as_float(x.x); v[1] = __uint_as_float(x.y); v[2] = __uint_as_float(x.z); v[3] = __uint_as_float(x.w);
+  }
+};
+template <> struct Unpack<half_t> {
+  static constexpr int n = 8;
+  __device__ static __forceinline__ void run(const uint4 x, float (&v)[8]) {
+    v[0] = f16lo(x.x); v[1] = f16hi(x.x); v[2] = f16lo(x.y); v[3] = f16hi(x.y);
+    v[4] = f16lo(x.z); v[5] = f16hi(x.z); v[6] = f16lo(x.w); v[7] = f16hi(x.w);
+  }
+};
+
+template <int V>
+__device__ __forceinline__ void load_f32(const float* p, float (&v)[V]) {
+#pragma unroll
+  for (int e = 0; e < V; e += 4) {
+    const float4 q = *reinterpret_cast<const float4*>(p + e);
+    v[e] = q.x; v[e + 1] = q.y; v[e + 2] = q.z; v[e + 3] = q.w;
+  }
+}
+template <int V>
+__device__ __forceinline__ void store_f32(float* p, const float (&v)[V]) {
+#pragma unroll
+  for (int e = 0; e < V; e += 4) *reinterpret_cast<float4*>(p + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+}
+
+// Thread per (sequence, kConvSteps time steps, 16-byte chunk of R); consecutive threads take
+// consecutive chunks of a row, so a wave's loads cover 1 KB of one row.  Each input row is read
+// once per thread and slides through a three-row register window.
 template <typename T>
 __global__ __launch_bounds__(256) void griffin_conv_kernel(GriffinConvArgs<T> a) {
-  constexpr int V = Vec16<T>::n;
+  constexpr int V = Unpack<T>::n;
   constexpr int H = kConvTaps - 1;
   const int cpr = a.R / V;
+  const int tiles = static_cast<int>(ceil_div(a.seq, kConvSteps));
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)a.B * a.seq * cpr) return;
+  if (i >= (int64_t)a.B * tiles * cpr) return;
   const int r0 = static_cast<int>(i % cpr) * V;
-  const int64_t row = i / cpr;
-  const int t = static_cast<int>(row % a.seq);
-  const int64_t b = row / a.seq;
-  // input at time tt (>= -H) of this sequence and chunk
-  auto input = [&](int tt, float (&u)[V]) {
+  const int64_t rest = i / cpr;
+  const int t0 = static_cast<int>(rest % tiles) * kConvSteps;
+  const int64_t b = rest / tiles;
+  const int t1 = min(a.seq, t0 + kConvSteps);
+  const T* __restrict__ u = a.u + b * a.seq * a.ld_u + r0;
+  T* __restrict__ xc = a.xc + b * a.seq * a.ld_xc + r0;
+  float w[kConvTaps][V];
+#pragma unroll
+  for (int k = 0; k < kConvTaps; ++k) load_f32<V>(a.w + k * a.R + r0, w[k]);
+  float win[H][V];   // inputs at t-3, t-2, t-1
+#pragma unroll
+  for (int j = 0; j < H; ++j) {
+    const int tt = t0 - H + j;
     if (tt >= 0) {
-      Vec16<T>::load(a.u + (b * a.seq + tt) * a.ld_u + r0, u);
+      Unpack<T>::run(*reinterpret_cast<const uint4*>(u + (int64_t)tt * a.ld_u), win[j]);
     } else if (a.hist) {
-      Vec16<float>::load(a.hist + (b * H + (H + tt)) * a.R + r0, *reinterpret_cast<float(*)[4]>(&u[0]));
-      if constexpr (V == 8)
-        Vec16<float>::load(a.hist + (b * H + (H + tt)) * a.R + r0 + 4, *reinterpret_cast<float(*)[4]>(&u[4]));
+      load_f32<V>(a.hist + (b * H + (H + tt)) * a.R + r0, win[j]);
     } else {
 #pragma unroll
-      for (int e = 0; e < V; ++e) u[e] = 0.f;
+      for (int e = 0; e < V; ++e) win[j][e] = 0.f;
+    }
+  }
+  auto step = [&](const uint4 raw, int t) {
+    float x[V];
+    Unpack<T>::run(raw, x);
+    float acc[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e)
+      acc[e] = fmaf(w[0][e], x[e], fmaf(w[1][e], win[2][e], fmaf(w[2][e], win[1][e], w[3][e] * win[0][e])));
+    Vec16<T>::store(xc + (int64_t)t * a.ld_xc, acc);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      win[0][e] = win[1][e];
+      win[1][e] = win[2][e];
+      win[2][e] = x[e];
     }
   };
-  float acc[V] = {};
+  if (t1 - t0 == kConvSteps) {
+    uint4 raw[kConvSteps];
 #pragma unroll
-  for (int k = 0; k < kConvTaps; ++k) {
-    float u[V];
-    input(t - k, u);
-    float w[V];
-    Vec16<float>::load(a.w + k * a.R + r0, *reinterpret_cast<float(*)[4]>(&w[0]));
-    if constexpr (V == 8) Vec16<float>::load(a.w + k * a.R + r0 + 4, *reinterpret_cast<float(*)[4]>(&w[4]));
+    for (int j = 0; j < kConvSteps; ++j) raw[j] = *reinterpret_cast<const uint4*>(u + (int64_t)(t0 + j) * a.ld_u);
 #pragma unroll
-    for (int e = 0; e < V; ++e) acc[e] = fmaf(w[e], u[e], acc[e]);
+    for (int j = 0; j < kConvSteps; ++j) step(raw[j], t0 + j);
+  } else {
+    for (int t = t0; t < t1; ++t) step(*reinterpret_cast<const uint4*>(u + (int64_t)t * a.ld_u), t);
   }
-  Vec16<T>::store(a.xc + row * a.ld_xc + r0, acc);
-  if (a.state_out && t == a.seq - 1) {
-    // the last H inputs, oldest first; all are read before any is written (state_out may alias
-    // hist only when seq == 1, and then only this thread touches this chunk of the state)
-    float sv[H][V];
+  // the last tile leaves the last H inputs in the window (read before anything is written: the
+  // state may alias hist only when seq == 1, a single tile)
+  if (a.state_out && t1 == a.seq) {
 #pragma unroll
-    for (int j = 0; j < H; ++j) input(a.seq - H + j, sv[j]);
-#pragma unroll
-    for (int j = 0; j < H; ++j) {
-      float* sp = a.state_out + (b * H + j) * a.R + r0;
-      Vec16<float>::store(sp, *reinterpret_cast<const float(*)[4]>(&sv[j][0]));
-      if constexpr (V == 8) Vec16<float>::store(sp + 4, *reinterpret_cast<const float(*)[4]>(&sv[j][4]));
-    }
+    for (int j = 0; j < H; ++j) store_f32<V>(a.state_out + (b * H + j) * a.R + r0, win[j]);
   }
 }
 
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __expf(-x)); }
+// Fast transcendental pieces on the hardware exp2 / reciprocal / square root, accurate to a few
+// 1e-7 (well inside the fp32 parity bar):
+__device__ __forceinline__ float rcp_f(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float exp_f(float x) { return fast_exp2(x * kLog2e); }
+__device__ __forceinline__ float sigmoid_f(float x) { return rcp_f(1.f + exp_f(-x)); }
+
+// 1 - e^z for z <= 0 without cancellation near 0: the Taylor series of -expm1 to z^6 for
+// |z| < 1/4 (relative truncation error below |z|^6 / 5040 < 5e-8), else 1 - e^z.
+__device__ __forceinline__ float one_minus_exp(float z) {
+  if (z > -0.25f) {
+    float p = fmaf(z, 1.f / 720.f, 1.f / 120.f);
+    p = fmaf(z, p, 1.f / 24.f);
+    p = fmaf(z, p, 1.f / 6.f);
+    p = fmaf(z, p, 0.5f);
+    p = fmaf(z, p, 1.f);
+    return -z * p;
+  }
+  return 1.f - exp_f(z);
+}
+
+// GeLU(v) = v Phi(v) = v (1 + erf(v / sqrt 2)) / 2, erf by the rational approximation of
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26 (|error| <= 1.5e-7).
+__device__ __forceinline__ float gelu_f(float v) {
+  const float x = fabsf(v) * 0.70710678118654752f;
+  const float t = rcp_f(fmaf(0.3275911f, x, 1.f));
+  float p = fmaf(t, 1.061405429f, -1.453152027f);
+  p = fmaf(t, p, 1.421413741f);
+  p = fmaf(t, p, -0.284496736f);
+  p = fmaf(t, p, 0.254829592f);
+  const float erf_abs = fmaf(-p * t, exp_f(-x * x), 1.f);
+  return 0.5f * v * (1.f + copysignf(erf_abs, v));
+}
 
 // c softplus(-Lambda) = -c log sigmoid(Lambda)
 __device__ __forceinline__ float decay_scale(float lam, float c) {
   return c * (fmaxf(-lam, 0.f) + log1pf(__expf(-fabsf(lam))));
 }
 
-// One segment [t0, t1) of channel r of sequence b: advances h (and the log-decay sum) and, with
-// kOut, writes y_t = h_t GeLU(v_t).
-template <typename T, bool kOut>
-__device__ __forceinline__ void run_segment(const RglruArgs<T>& a, int64_t row0, int t0, int t1, int r,
-                                            float c_sp, float& h, float& lsum) {
-  const T* __restrict__ g = a.g + row0 * a.ld_g + r;
-  const T* __restrict__ xc = a.xc + row0 * a.ld_xc + r;
-  const T* __restrict__ v = a.v + row0 * a.ld_v + r;
-  T* __restrict__ y = a.y + row0 * a.ldy + r;
-  auto step = [&](float rho, float iota, float x, float vv, int64_t t) {
-    const float la = -c_sp * sigmoid_f(rho);                 // log a_t = c r_t log sigmoid(Lambda)
-    const float bt = sqrtf(-expm1f(2.f * la)) * sigmoid_f(iota) * x;
-    h = fmaf(__expf(la), h, bt);
-    if constexpr (kOut) {
-      Elem<T>::store(y + t * a.ldy, h * (0.5f * vv * (1.f + erff(vv * 0.70710678118654752f))));
-    } else {
-      lsum += la;
+// Two consecutive elements: one 4-byte load for fp16, 8 bytes for fp32, kept packed until used.
+template <typename T> struct Pair2;
+template <> struct Pair2<half_t> {
+  using Raw = uint32_t;
+  __device__ static __forceinline__ Raw load(const half_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+  __device__ static __forceinline__ void unpack(Raw w, float (&v)[2]) { v[0] = f16lo(w); v[1] = f16hi(w); }
+  __device__ static __forceinline__ void store(half_t* p, const float (&v)[2]) {
+    *reinterpret_cast<uint32_t*>(p) = pack_f16x2(v[0], v[1]);
+  }
+};
+template <> struct Pair2<float> {
+  using Raw = float2;
+  __device__ static __forceinline__ Raw load(const float* p) { return *reinterpret_cast<const float2*>(p); }
+  __device__ static __forceinline__ void unpack(Raw w, float (&v)[2]) { v[0] = w.x; v[1] = w.y; }
+  __device__ static __forceinline__ void store(float* p, const float (&v)[2]) {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  }
+};
+
+constexpr int kVpl = 2;        // channels per lane
+constexpr int kWaveSteps = 8;  // time steps per wave and tile
+constexpr int kMaxWaves = 8;
+
+// RG-LRU + GeLU branch in one pass.  Workgroup = kW waves on 128 channels of one sequence, for
+// the whole sequence; time runs in tiles of kW * 8 steps, wave w taking steps [8w, 8w + 8) of a
+// tile.  A wave loads its steps (the next tile's loads are issued before the current tile is
+// processed), computes a_t and b_t = sqrt(1 - a_t^2) i_t xc_t once, keeps them in registers and
+// folds them into its summary (prod a_t, h from zero).  After one barrier every wave folds the
+// summaries of the waves before it into the tile's carry-in (its start state) and all of them
+// into the next tile's carry, reruns its steps from registers and writes y_t = h_t GeLU(v_t).
+// The summaries are double-buffered in LDS by tile parity: a buffer is rewritten two tiles later,
+// after a barrier every wave passes only once it has read it.
+template <typename T, int kW>
+__global__ __launch_bounds__(64 * kW) void rglru_kernel(RglruArgs<T> a) {
+  using P = Pair2<T>;
+  using Raw = typename P::Raw;
+  __shared__ float2 sm[2][kW][64][kVpl];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = (blockIdx.x * 64 + lane) * kVpl;
+  const int64_t b = blockIdx.y;
+  const bool on = r < a.R;
+  const int rr = on ? r : 0;   // inactive lanes of a partial last group stay in the barriers
+  float c_sp[kVpl], carry[kVpl];
+#pragma unroll
+  for (int e = 0; e < kVpl; ++e) {
+    c_sp[e] = decay_scale(a.lam[rr + e], a.c);
+    carry[e] = (on && a.h0) ? a.h0[b * a.R + r + e] : 0.f;
+  }
+  const int64_t row0 = b * a.seq;
+  const T* __restrict__ g = a.g + row0 * a.ld_g + rr;
+  const T* __restrict__ xc = a.xc + row0 * a.ld_xc + rr;
+  const T* __restrict__ v = a.v + row0 * a.ld_v + rr;
+  T* __restrict__ y = a.y + row0 * a.ldy + rr;
+  constexpr int kTile = kW * kWaveSteps;
+  const int tiles = static_cast<int>(ceil_div(a.seq, kTile));
+  struct Raws { Raw rho[kWaveSteps], iota[kWaveSteps], x[kWaveSteps], v[kWaveSteps]; };
+  auto fetch = [&](int tile, Raws& q) {
+    const int t0 = tile * kTile + w * kWaveSteps;
+#pragma unroll
+    for (int j = 0; j < kWaveSteps; ++j) {
+      const int64_t t = t0 + j;
+      if (on && t < a.seq) {
+        q.rho[j] = P::load(g + t * a.ld_g);
+        q.iota[j] = P::load(g + t * a.ld_g + a.R);
+        q.x[j] = P::load(xc + t * a.ld_xc);
+        q.v[j] = P::load(v + t * a.ld_v);
+      }
     }
   };
-  int t = t0;
-  for (; t + kStepChunk <= t1; t += kStepChunk) {
-    float rho[kStepChunk], iota[kStepChunk], x[kStepChunk], vv[kStepChunk];
+  Raws nxt;
+  fetch(0, nxt);
+  for (int tile = 0; tile < tiles; ++tile) {
+    const Raws cur = nxt;
+    if (tile + 1 < tiles) fetch(tile + 1, nxt);
+    const int t0 = tile * kTile + w * kWaveSteps;
+    float at[kWaveSteps][kVpl], bt[kWaveSteps][kVpl];
+    float A[kVpl], H[kVpl];
 #pragma unroll
-    for (int j = 0; j < kStepChunk; ++j) {
-      rho[j] = Elem<T>::load(g + (t + j) * a.ld_g);
-      iota[j] = Elem<T>::load(g + (t + j) * a.ld_g + a.R);
-      x[j] = Elem<T>::load(xc + (t + j) * a.ld_xc);
-      if constexpr (kOut) vv[j] = Elem<T>::load(v + (t + j) * a.ld_v);
-      else vv[j] = 0.f;
+    for (int e = 0; e < kVpl; ++e) { A[e] = 1.f; H[e] = 0.f; }
+#pragma unroll
+    for (int j = 0; j < kWaveSteps; ++j) {
+      float rho[kVpl], iota[kVpl], x[kVpl];
+      P::unpack(cur.rho[j], rho);
+      P::unpack(cur.iota[j], iota);
+      P::unpack(cur.x[j], x);
+      const bool valid = on && t0 + j < a.seq;
+#pragma unroll
+      for (int e = 0; e < kVpl; ++e) {
+        const float la = -c_sp[e] * sigmoid_f(rho[e]);   // log a_t = c r_t log sigmoid(Lambda)
+        at[j][e] = valid ? exp_f(la) : 1.f;
+        bt[j][e] = valid ? __builtin_amdgcn_sqrtf(one_minus_exp(2.f * la)) * sigmoid_f(iota[e]) * x[e] : 0.f;
+        H[e] = fmaf(at[j][e], H[e], bt[j][e]);
+        A[e] *= at[j][e];
+      }
+    }
+    const int p = tile & 1;
+#pragma unroll
+    for (int e = 0; e < kVpl; ++e) sm[p][w][lane][e] = make_float2(A[e], H[e]);
+    __syncthreads();
+    float h[kVpl];
+#pragma unroll
+    for (int e = 0; e < kVpl; ++e) h[e] = carry[e];
+#pragma unroll
+    for (int u = 0; u < kW; ++u) {
+      float2 q[kVpl];
+#pragma unroll
+      for (int e = 0; e < kVpl; ++e) q[e] = sm[p][u][lane][e];
+      if (u == w) {
+#pragma unroll
+        for (int e = 0; e < kVpl; ++e) h[e] = carry[e];   // the start state of this wave's steps
+      }
+#pragma unroll
+      for (int e = 0; e < kVpl; ++e) carry[e] = fmaf(q[e].x, carry[e], q[e].y);
     }
 #pragma unroll
-    for (int j = 0; j < kStepChunk; ++j) step(rho[j], iota[j], x[j], vv[j], t + j);
-  }
-  for (; t < t1; ++t)
-    step(Elem<T>::load(g + (int64_t)t * a.ld_g), Elem<T>::load(g + (int64_t)t * a.ld_g + a.R),
-         Elem<T>::load(xc + (int64_t)t * a.ld_xc), kOut ? Elem<T>::load(v + (int64_t)t * a.ld_v) : 0.f, t);
-}
-
-// grid (ceil(R / 64), S - 1, B): segments 0 .. S-2; record seg + 1; segment 0 also writes record 0
-template <typename T>
-__global__ __launch_bounds__(64) void rglru_summary_kernel(RglruArgs<T> a) {
-  const int r = blockIdx.x * 64 + threadIdx.x;
-  const int seg = blockIdx.y, b = blockIdx.z;
-  if (r >= a.R) return;
-  float2* rec = a.summ + (int64_t)b * (a.S + 1) * a.R + r;
-  if (seg == 0) rec[0] = make_float2(0.f, a.h0 ? a.h0[(int64_t)b * a.R + r] : 0.f);
-  const int t0 = seg * a.L, t1 = min(a.seq, t0 + a.L);
-  float h = 0.f, lsum = 0.f;
-  run_segment<T, false>(a, (int64_t)b * a.seq, t0, t1, r, decay_scale(a.lam[r], a.c), h, lsum);
-  rec[(int64_t)(seg + 1) * a.R] = make_float2(lsum, h);
-}
-
-// grid (ceil(R / 64), S, B)
-template <typename T>
-__global__ __launch_bounds__(64) void rglru_output_kernel(RglruArgs<T> a) {
-  const int r = blockIdx.x * 64 + threadIdx.x;
-  const int seg = blockIdx.y, b = blockIdx.z;
-  if (r >= a.R) return;
-  float h;
-  if (a.S == 1) {
-    h = a.h0 ? a.h0[(int64_t)b * a.R + r] : 0.f;
-  } else {   // h0 comes through record 0, so h_out may alias h0
-    const float2* rec = a.summ + (int64_t)b * (a.S + 1) * a.R + r;
-    h = 0.f;
-    for (int s = 0; s <= seg; ++s) {
-      const float2 q = rec[(int64_t)s * a.R];
-      h = fmaf(__expf(q.x), h, q.y);
+    for (int j = 0; j < kWaveSteps; ++j) {
+      float vv[kVpl], out[kVpl];
+      P::unpack(cur.v[j], vv);
+#pragma unroll
+      for (int e = 0; e < kVpl; ++e) {
+        h[e] = fmaf(at[j][e], h[e], bt[j][e]);
+        out[e] = h[e] * gelu_f(vv[e]);
+      }
+      if (on && t0 + j < a.seq) P::store(y + (int64_t)(t0 + j) * a.ldy, out);
     }
   }
-  const int t0 = seg * a.L, t1 = min(a.seq, t0 + a.L);
-  float unused = 0.f;
-  run_segment<T, true>(a, (int64_t)b * a.seq, t0, t1, r, decay_scale(a.lam[r], a.c), h, unused);
-  if (a.h_out && seg == a.S - 1) a.h_out[(int64_t)b * a.R + r] = h;
+  if (on && w == 0 && a.h_out) {
+#pragma unroll
+    for (int e = 0; e < kVpl; ++e) a.h_out[b * a.R + r + e] = carry[e];
+  }
 }
 
 template <typename T>
 hipError_t conv_dispatch(const GriffinConvArgs<T>& a, hipStream_t s) {
-  constexpr int V = Vec16<T>::n;
+  constexpr int V = Unpack<T>::n;
   if (a.R % V) return hipErrorInvalidValue;
-  const int64_t n = (int64_t)a.B * a.seq * (a.R / V);
+  const int64_t n = (int64_t)a.B * ceil_div(a.seq, kConvSteps) * (a.R / V);
   if (n <= 0) return hipSuccess;
   if (ceil_div(n, 256) > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL((griffin_conv_kernel<T>), dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
+// waves per workgroup: enough for the sequence, at most kMaxWaves
 template <typename T>
 hipError_t rglru_dispatch(const RglruArgs<T>& a, hipStream_t s) {
   if (a.B <= 0 || a.seq <= 0) return hipSuccess;
-  if (a.S < 1 || a.L < 1 || (int64_t)(a.S - 1) * a.L >= a.seq || (int64_t)a.S * a.L < a.seq)
-    return hipErrorInvalidValue;   // every segment non-empty, together covering the sequence
-  const unsigned gx = static_cast<unsigned>(ceil_div(a.R, 64));
-  if (a.S > 1) {
-    hipLaunchKernelGGL((rglru_summary_kernel<T>), dim3(gx, a.S - 1, a.B), dim3(64), 0, s, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL((rglru_output_kernel<T>), dim3(gx, a.S, a.B), dim3(64), 0, s, a);
+  if (a.R % kVpl || a.B > 65535) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(ceil_div(a.R, 64 * kVpl)), a.B);
+  const int64_t need = ceil_div(a.seq, kWaveSteps);
+  if (need >= 8) hipLaunchKernelGGL((rglru_kernel<T, 8>), grid, dim3(64 * 8), 0, s, a);
+  else if (need >= 4) hipLaunchKernelGGL((rglru_kernel<T, 4>), grid, dim3(64 * 4), 0, s, a);
+  else if (need >= 2) hipLaunchKernelGGL((rglru_kernel<T, 2>), grid, dim3(64 * 2), 0, s, a);
+  else hipLaunchKernelGGL((rglru_kernel<T, 1>), grid, dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
-
-// Segments of a B x T x R recurrence: about 8 waves per SIMD of the chip, segments of at least
-// 64 steps; every segment non-empty.
-void rglru_plan(int B, int T, int R, int* S, int* L) {
-  int64_t s = 1;
-  if (T > 0 && B > 0) {
-    const int64_t waves_per_seg = (int64_t)B * ceil_div(R, 64);
-    s = std::max<int64_t>(1, std::min<int64_t>(ceil_div(8192, waves_per_seg), T / 64));
-  }
-  const int64_t l = std::max<int64_t>(1, ceil_div(T, s));
-  *L = static_cast<int>(l);
-  *S = static_cast<int>(std::max<int64_t>(1, ceil_div(T, l)));
-}
 
 hipError_t launch_griffin_conv(const GriffinConvArgs<float>& a, hipStream_t s) { return conv_dispatch(a, s); }
 hipError_t launch_griffin_conv(const GriffinConvArgs<half_t>& a, hipStream_t s) { return conv_dispatch(a, s); }

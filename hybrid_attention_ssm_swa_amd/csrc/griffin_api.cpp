@@ -50,22 +50,19 @@ int32_t check_cfg(const griffin_block_cfg* c) {
 }
 
 struct Ws {
-  size_t x16 = 0, uv = 0, xc = 0, g = 0, hy = 0, summ = 0, gemm = 0, total = 0;
-  int S = 1, L = 1;
+  size_t x16 = 0, uv = 0, xc = 0, g = 0, hy = 0, gemm = 0, total = 0;
 };
 
-// x16 (bf16 blocks: x in fp16, later y in fp16) | uv | xc | g | hy | segment records | GEMM workspace
+// x16 (bf16 blocks: x in fp16, later y in fp16) | uv | xc | g | hy | GEMM workspace
 Ws layout(const griffin_block_cfg& c, int B, int T) {
   Ws w;
   const size_t rows = static_cast<size_t>(B) * T, R = c.d_rnn, D = c.d_model, e = elem(c);
-  rglru_plan(B, T, c.d_rnn, &w.S, &w.L);
   size_t o = 0;
   w.x16 = o;  o += is_bf16(c) ? align_up(rows * D * 2) : 0;
   w.uv = o;   o += align_up(rows * 2 * R * e);
   w.xc = o;   o += align_up(rows * R * e);
   w.g = o;    o += align_up(rows * 2 * R * e);
   w.hy = o;   o += align_up(rows * R * e);
-  w.summ = o; o += align_up(static_cast<size_t>(B) * (w.S + 1) * R * sizeof(float2));
   w.gemm = o; o += is_bf16(c) ? kGemmWorkspaceBytes : 0;
   w.total = o;
   return w;
@@ -149,8 +146,7 @@ int32_t run(const griffin_block_cfg& c, const griffin_block_weights& w, const vo
   G_STATUS_TRY(tm.mark(GS_CONV, s));
   G_STATUS_TRY(project(c, xc, W_gate, g, rows, 2 * R, R, ws, wl, s));
   G_STATUS_TRY(tm.mark(GS_GATE, s));
-  RglruArgs<ET> ra{g, 2 * R, xc, R, uv + R, 2 * R, hy, R, w.lam, c.c, h, h_out,
-                   reinterpret_cast<float2*>(ws + wl.summ), B, T, c.d_rnn, wl.S, wl.L};
+  RglruArgs<ET> ra{g, 2 * R, xc, R, uv + R, 2 * R, hy, R, w.lam, c.c, h, h_out, B, T, c.d_rnn};
   G_HIP_TRY(launch_rglru(ra, s), "RG-LRU launch");
   G_STATUS_TRY(tm.mark(GS_RGLRU, s));
   G_STATUS_TRY(project(c, hy, W_out, Y, rows, D, R, ws, wl, s));

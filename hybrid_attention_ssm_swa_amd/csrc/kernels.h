@@ -161,8 +161,8 @@ struct GriffinConvArgs {
 hipError_t launch_griffin_conv(const GriffinConvArgs<float>& a, hipStream_t s);
 hipError_t launch_griffin_conv(const GriffinConvArgs<half_t>& a, hipStream_t s);
 
-// RG-LRU + GeLU branch: g [rows, 2R] holds the gate pre-activations (W_a xc | W_x xc); time is cut
-// into S segments of L steps; summ holds B * (S + 1) * R records (sum of log a, end state).
+// RG-LRU + GeLU branch: g [rows, 2R] holds the gate pre-activations (W_a xc | W_x xc); y = h GeLU(v);
+// h0 [B, R] (null: zeros) -> h_out [B, R] (null: none; may alias h0).  R even, B <= 65535.
 template <typename T>
 struct RglruArgs {
   const T* g; int64_t ld_g;
@@ -171,12 +171,10 @@ struct RglruArgs {
   T* y; int64_t ldy;
   const float* lam; float c;
   const float* h0; float* h_out;
-  float2* summ;
-  int B; int seq; int R; int S; int L;
+  int B; int seq; int R;
 };
 hipError_t launch_rglru(const RglruArgs<float>& a, hipStream_t s);
 hipError_t launch_rglru(const RglruArgs<half_t>& a, hipStream_t s);
-void rglru_plan(int B, int T, int R, int* S, int* L);
 
 // ---- misc ----------------------------------------------------------------------
 hipError_t launch_scale_copy(const float* src, float* dst, int64_t n, float scale, hipStream_t s);
