@@ -85,6 +85,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run hybrid_attention_ssm_swa_amd/build.py "
                            "(or __graft_entry__.build()) first")
+    # PyTorch ships its own HIP runtime: load it first so that the library binds to the same
+    # runtime as the tensors and streams it is handed (a second runtime sees no device).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P = c_void_p
     sig = {

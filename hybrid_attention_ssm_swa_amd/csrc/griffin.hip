@@ -10,6 +10,7 @@
 // channels: a wave's loads of one time step cover 128 consecutive channels of
 // a row (256 bytes of fp16 activations).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -124,18 +125,17 @@ __device__ __forceinline__ float rcp_f(float x) { return __builtin_amdgcn_rcpf(x
 __device__ __forceinline__ float exp_f(float x) { return fast_exp2(x * kLog2e); }
 __device__ __forceinline__ float sigmoid_f(float x) { return rcp_f(1.f + exp_f(-x)); }
 
-// 1 - e^z for z <= 0 without cancellation near 0: the Taylor series of -expm1 to z^6 for
-// |z| < 1/4 (relative truncation error below |z|^6 / 5040 < 5e-8), else 1 - e^z.
-__device__ __forceinline__ float one_minus_exp(float z) {
-  if (z > -0.25f) {
-    float p = fmaf(z, 1.f / 720.f, 1.f / 120.f);
-    p = fmaf(z, p, 1.f / 24.f);
-    p = fmaf(z, p, 1.f / 6.f);
-    p = fmaf(z, p, 0.5f);
-    p = fmaf(z, p, 1.f);
-    return -z * p;
-  }
-  return 1.f - exp_f(z);
+// 1 - a^2 for a = e^la (la <= 0) without cancellation near a = 1: with z = 2 la, the Taylor
+// series of -expm1(z) to z^6 for |z| < 1/4 (relative truncation error below |z|^6 / 5040 < 5e-8),
+// else 1 - a a (then 1 - a^2 > 0.22 and the rounding of a costs at most a few 1e-7 relative).
+__device__ __forceinline__ float one_minus_sq(float a, float la) {
+  const float z = 2.f * la;
+  float p = fmaf(z, 1.f / 720.f, 1.f / 120.f);
+  p = fmaf(z, p, 1.f / 24.f);
+  p = fmaf(z, p, 1.f / 6.f);
+  p = fmaf(z, p, 0.5f);
+  p = fmaf(z, p, 1.f);
+  return z > -0.25f ? -z * p : fmaf(-a, a, 1.f);
 }
 
 // GeLU(v) = v Phi(v) = v (1 + erf(v / sqrt 2)) / 2, erf by the rational approximation of
@@ -156,22 +156,43 @@ __device__ __forceinline__ float decay_scale(float lam, float c) {
   return c * (fmaxf(-lam, 0.f) + log1pf(__expf(-fabsf(lam))));
 }
 
+// Raw buffer access (gfx9 buffer resource: base, stride 0, byte range; loads past the range return
+// 0, stores past it are dropped).  The row offset goes in a scalar register, the lane's column
+// offset in a vector register, so an access costs no vector address arithmetic.
+constexpr int kBufferFlags = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufferFlags);
+}
+
 // Two consecutive elements: one 4-byte load for fp16, 8 bytes for fp32, kept packed until used.
 template <typename T> struct Pair2;
 template <> struct Pair2<half_t> {
   using Raw = uint32_t;
-  __device__ static __forceinline__ Raw load(const half_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+  __device__ static __forceinline__ Raw load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
+  }
   __device__ static __forceinline__ void unpack(Raw w, float (&v)[2]) { v[0] = f16lo(w); v[1] = f16hi(w); }
-  __device__ static __forceinline__ void store(half_t* p, const float (&v)[2]) {
-    *reinterpret_cast<uint32_t*>(p) = pack_f16x2(v[0], v[1]);
+  __device__ static __forceinline__ void store(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                                               const float (&v)[2]) {
+    __builtin_amdgcn_raw_buffer_store_b32(pack_f16x2(v[0], v[1]), rs, voff, soff, 0);
   }
 };
 template <> struct Pair2<float> {
-  using Raw = float2;
-  __device__ static __forceinline__ Raw load(const float* p) { return *reinterpret_cast<const float2*>(p); }
-  __device__ static __forceinline__ void unpack(Raw w, float (&v)[2]) { v[0] = w.x; v[1] = w.y; }
-  __device__ static __forceinline__ void store(float* p, const float (&v)[2]) {
-    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  using Raw = uint2;
+  __device__ static __forceinline__ Raw load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
+    const auto w = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
+    return make_uint2(w[0], w[1]);
+  }
+  __device__ static __forceinline__ void unpack(Raw w, float (&v)[2]) {
+    v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
+  }
+  __device__ static __forceinline__ void store(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                                               const float (&v)[2]) {
+    using U2 = unsigned __attribute__((ext_vector_type(2)));
+    U2 w;
+    w[0] = __float_as_uint(v[0]);
+    w[1] = __float_as_uint(v[1]);
+    __builtin_amdgcn_raw_buffer_store_b64(w, rs, voff, soff, 0);
   }
 };
 
@@ -193,7 +214,8 @@ __global__ __launch_bounds__(64 * kW) void rglru_kernel(RglruArgs<T> a) {
   using P = Pair2<T>;
   using Raw = typename P::Raw;
   __shared__ float2 sm[2][kW][64][kVpl];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // the wave index is wave-uniform: readfirstlane tells the compiler (scalar buffer offsets)
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = (blockIdx.x * 64 + lane) * kVpl;
   const int64_t b = blockIdx.y;
   const bool on = r < a.R;
@@ -204,35 +226,33 @@ __global__ __launch_bounds__(64 * kW) void rglru_kernel(RglruArgs<T> a) {
     c_sp[e] = decay_scale(a.lam[rr + e], a.c);
     carry[e] = (on && a.h0) ? a.h0[b * a.R + r + e] : 0.f;
   }
+  // one buffer resource per tensor and sequence; byte offsets: row in a scalar, column per lane
   const int64_t row0 = b * a.seq;
-  const T* __restrict__ g = a.g + row0 * a.ld_g + rr;
-  const T* __restrict__ xc = a.xc + row0 * a.ld_xc + rr;
-  const T* __restrict__ v = a.v + row0 * a.ld_v + rr;
-  T* __restrict__ y = a.y + row0 * a.ldy + rr;
+  constexpr uint32_t es = sizeof(T);
+  const auto rs_g = buffer_rsrc(a.g + row0 * a.ld_g, static_cast<uint32_t>(a.seq * a.ld_g * es));
+  const auto rs_x = buffer_rsrc(a.xc + row0 * a.ld_xc, static_cast<uint32_t>(a.seq * a.ld_xc * es));
+  const auto rs_v = buffer_rsrc(a.v + row0 * a.ld_v, static_cast<uint32_t>(a.seq * a.ld_v * es));
+  const auto rs_y = buffer_rsrc(a.y + row0 * a.ldy, static_cast<uint32_t>(a.seq * a.ldy * es));
+  const uint32_t col = static_cast<uint32_t>(rr) * es, col_i = static_cast<uint32_t>(rr + a.R) * es;
   constexpr int kTile = kW * kWaveSteps;
   const int tiles = static_cast<int>(ceil_div(a.seq, kTile));
   struct Raws { Raw rho[kWaveSteps], iota[kWaveSteps], x[kWaveSteps], v[kWaveSteps]; };
+  // steps past the sequence read zeros (outside the buffer range) and are masked below
   auto fetch = [&](int tile, Raws& q) {
     const int t0 = tile * kTile + w * kWaveSteps;
 #pragma unroll
     for (int j = 0; j < kWaveSteps; ++j) {
-      const int64_t t = t0 + j;
-      if (on && t < a.seq) {
-        q.rho[j] = P::load(g + t * a.ld_g);
-        q.iota[j] = P::load(g + t * a.ld_g + a.R);
-        q.x[j] = P::load(xc + t * a.ld_xc);
-        q.v[j] = P::load(v + t * a.ld_v);
-      }
+      const uint32_t t = static_cast<uint32_t>(t0 + j);
+      q.rho[j] = P::load(rs_g, col, t * static_cast<uint32_t>(a.ld_g) * es);
+      q.iota[j] = P::load(rs_g, col_i, t * static_cast<uint32_t>(a.ld_g) * es);
+      q.x[j] = P::load(rs_x, col, t * static_cast<uint32_t>(a.ld_xc) * es);
+      q.v[j] = P::load(rs_v, col, t * static_cast<uint32_t>(a.ld_v) * es);
     }
   };
-  Raws nxt;
-  fetch(0, nxt);
-  for (int tile = 0; tile < tiles; ++tile) {
-    const Raws cur = nxt;
-    if (tile + 1 < tiles) fetch(tile + 1, nxt);
-    const int t0 = tile * kTile + w * kWaveSteps;
-    float at[kWaveSteps][kVpl], bt[kWaveSteps][kVpl];
-    float A[kVpl], H[kVpl];
+  auto is_full = [&](int tile) { return on && tile * kTile + (w + 1) * kWaveSteps <= a.seq; };
+  float at[kWaveSteps][kVpl], bt[kWaveSteps][kVpl];
+  // a_t, b_t of the slice and its summary (prod a_t, h from zero)
+  auto coeffs = [&](auto full, const Raws& cur, int t0, float (&A)[kVpl], float (&H)[kVpl]) {
 #pragma unroll
     for (int e = 0; e < kVpl; ++e) { A[e] = 1.f; H[e] = 0.f; }
 #pragma unroll
@@ -241,16 +261,46 @@ __global__ __launch_bounds__(64 * kW) void rglru_kernel(RglruArgs<T> a) {
       P::unpack(cur.rho[j], rho);
       P::unpack(cur.iota[j], iota);
       P::unpack(cur.x[j], x);
-      const bool valid = on && t0 + j < a.seq;
+      const bool valid = decltype(full)::value || (on && t0 + j < a.seq);
 #pragma unroll
       for (int e = 0; e < kVpl; ++e) {
         const float la = -c_sp[e] * sigmoid_f(rho[e]);   // log a_t = c r_t log sigmoid(Lambda)
-        at[j][e] = valid ? exp_f(la) : 1.f;
-        bt[j][e] = valid ? __builtin_amdgcn_sqrtf(one_minus_exp(2.f * la)) * sigmoid_f(iota[e]) * x[e] : 0.f;
+        const float ae = exp_f(la);
+        const float be = __builtin_amdgcn_sqrtf(one_minus_sq(ae, la)) * sigmoid_f(iota[e]) * x[e];
+        at[j][e] = valid ? ae : 1.f;
+        bt[j][e] = valid ? be : 0.f;
         H[e] = fmaf(at[j][e], H[e], bt[j][e]);
         A[e] *= at[j][e];
       }
     }
+  };
+  // rerun of the slice from its start state h, writing y_t = h_t GeLU(v_t)
+  auto outputs = [&](auto full, const Raws& cur, int t0, float (&h)[kVpl]) {
+#pragma unroll
+    for (int j = 0; j < kWaveSteps; ++j) {
+      float vv[kVpl], out[kVpl];
+      P::unpack(cur.v[j], vv);
+#pragma unroll
+      for (int e = 0; e < kVpl; ++e) {
+        h[e] = fmaf(at[j][e], h[e], bt[j][e]);
+        out[e] = h[e] * gelu_f(vv[e]);
+      }
+      if (decltype(full)::value || (on && t0 + j < a.seq))
+        P::store(rs_y, col, static_cast<uint32_t>(t0 + j) * static_cast<uint32_t>(a.ldy) * es, out);
+    }
+  };
+  using Full = std::true_type;
+  using Part = std::false_type;
+  Raws nxt;
+  fetch(0, nxt);
+  for (int tile = 0; tile < tiles; ++tile) {
+    const Raws cur = nxt;
+    if (tile + 1 < tiles) fetch(tile + 1, nxt);
+    const int t0 = tile * kTile + w * kWaveSteps;
+    const bool full = is_full(tile);
+    float A[kVpl], H[kVpl];
+    if (full) coeffs(Full{}, cur, t0, A, H);
+    else coeffs(Part{}, cur, t0, A, H);
     const int p = tile & 1;
 #pragma unroll
     for (int e = 0; e < kVpl; ++e) sm[p][w][lane][e] = make_float2(A[e], H[e]);
@@ -270,17 +320,8 @@ __global__ __launch_bounds__(64 * kW) void rglru_kernel(RglruArgs<T> a) {
 #pragma unroll
       for (int e = 0; e < kVpl; ++e) carry[e] = fmaf(q[e].x, carry[e], q[e].y);
     }
-#pragma unroll
-    for (int j = 0; j < kWaveSteps; ++j) {
-      float vv[kVpl], out[kVpl];
-      P::unpack(cur.v[j], vv);
-#pragma unroll
-      for (int e = 0; e < kVpl; ++e) {
-        h[e] = fmaf(at[j][e], h[e], bt[j][e]);
-        out[e] = h[e] * gelu_f(vv[e]);
-      }
-      if (on && t0 + j < a.seq) P::store(y + (int64_t)(t0 + j) * a.ldy, out);
-    }
+    if (full) outputs(Full{}, cur, t0, h);
+    else outputs(Part{}, cur, t0, h);
   }
   if (on && w == 0 && a.h_out) {
 #pragma unroll
@@ -304,6 +345,9 @@ template <typename T>
 hipError_t rglru_dispatch(const RglruArgs<T>& a, hipStream_t s) {
   if (a.B <= 0 || a.seq <= 0) return hipSuccess;
   if (a.R % kVpl || a.B > 65535) return hipErrorInvalidValue;
+  // one sequence of each tensor must fit a buffer's 31-bit byte range
+  const int64_t ld = std::max(std::max(a.ld_g, a.ld_xc), std::max(a.ld_v, a.ldy));
+  if ((int64_t)a.seq * ld * (int64_t)sizeof(T) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(ceil_div(a.R, 64 * kVpl)), a.B);
   const int64_t need = ceil_div(a.seq, kWaveSteps);
   if (need >= 8) hipLaunchKernelGGL((rglru_kernel<T, 8>), grid, dim3(64 * 8), 0, s, a);

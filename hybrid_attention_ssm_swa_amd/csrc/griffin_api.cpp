@@ -197,6 +197,8 @@ int32_t check_call(const griffin_block_cfg* cfg, const griffin_block_weights* w,
   if (static_cast<int64_t>(B) * T > (int64_t(1) << 31) / 2)
     return set_error(HYMBA_ERR_UNSUPPORTED, "batch * seq beyond 2^30 rows");
   if (B == 0 || T == 0) { *need = 0; return HYMBA_OK; }
+  if (static_cast<int64_t>(T) * 2 * cfg->d_rnn * static_cast<int64_t>(elem(*cfg)) >= (int64_t(1) << 31))
+    return set_error(HYMBA_ERR_UNSUPPORTED, "one sequence's gate activations (seq x 2 d_rnn) must stay below 2 GiB");
   if (!x || !y || !ws) return set_error(HYMBA_ERR_INVALID_ARG, "x, y and workspace must be non-NULL");
   if (!aligned16(x) || !aligned16(y)) return set_error(HYMBA_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(ws) % kAlign)

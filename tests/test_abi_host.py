@@ -280,13 +280,14 @@ def test_griffin_call_checks():
         (dict(y=None), L.HYMBA_ERR_INVALID_ARG),
         (dict(state=FAKE, state_out=FAKE), L.HYMBA_ERR_INVALID_ARG),   # aliasing needs seq == 1
         (dict(B=70000), L.HYMBA_ERR_UNSUPPORTED),
+        (dict(B=1, T=3_000_000), L.HYMBA_ERR_UNSUPPORTED),    # 3e6 x 192 x 4 B > 2 GiB per sequence
     ]
     cases_bf16 = [(dict(pers=None), L.HYMBA_ERR_INVALID_ARG), (dict(pers=FAKE + 128), L.HYMBA_ERR_INVALID_ARG)]
     for kw, code in cases:
-        a = dict(x=FAKE, y=FAKE, ws=FAKE, ws_bytes=big, state=None, state_out=None, B=2, pers=None)
+        a = dict(x=FAKE, y=FAKE, ws=FAKE, ws_bytes=big, state=None, state_out=None, B=2, T=8, pers=None)
         a.update(kw)
         with pytest.raises(L.HymbaError) as e:
-            L.griffin_block_prefill(c, w, a["pers"], a["x"], a["B"], 8, a["y"], a["state"], None, a["state_out"],
+            L.griffin_block_prefill(c, w, a["pers"], a["x"], a["B"], a["T"], a["y"], a["state"], None, a["state_out"],
                                     None, a["ws"], a["ws_bytes"], None)
         assert e.value.status == code, (kw, L.hymba_last_error())
     nw = _gweights()
