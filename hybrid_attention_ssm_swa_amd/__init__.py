@@ -3,7 +3,8 @@
 The computation lives in libhymba_mixer.so (HIP kernels + hipBLASLt GEMMs
 behind a C ABI, include/hymba_mixer.h).  This package is its Python binding:
 ``_lib`` mirrors the C functions by name; ``layer.MixerLayer`` manages device
-memory (torch) around one layer.  Importing works without the library; the
+memory (torch) around one layer, ``griffin.GriffinBlock`` around one Griffin
+recurrent block.  Importing works without the library; the
 first call loads it and raises if it has not been built.
 """
 from ._lib import (  # noqa: F401
@@ -12,6 +13,9 @@ from ._lib import (  # noqa: F401
     hymba_layer_persistent_bytes, hymba_layer_create, hymba_layer_destroy, hymba_kv_share_bind,
     hymba_mixer_workspace_bytes, hymba_layer_prepare, hymba_mixer_prefill, hymba_mixer_decode,
     hymba_layer_meta_outputs, hymba_last_error, hymba_status_string,
-    hymba_kernel_attention, hymba_kernel_selective_scan, hymba_kernel_epilogue,
+    hymba_kernel_attention, hymba_kernel_selective_scan, hymba_kernel_epilogue, hymba_kernel_gemm_rows,
+    hymba_kernel_gemm_rows_workspace,
     hymba_layer_profile, hymba_layer_profile_read, hymba_stage_name, HYMBA_N_STAGES,
+    griffin_block_cfg, griffin_block_weights, griffin_block_persistent_bytes, griffin_block_prepare,
+    griffin_workspace_bytes, griffin_block_prefill, griffin_block_decode, GRIFFIN_N_STAGES,
 )

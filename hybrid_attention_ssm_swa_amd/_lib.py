@@ -30,7 +30,8 @@ EXPORTED = [
     "hymba_kv_share_bind", "hymba_mixer_workspace_bytes", "hymba_layer_prepare",
     "hymba_mixer_prefill", "hymba_mixer_decode", "hymba_layer_meta_outputs",
     "hymba_last_error", "hymba_status_string", "hymba_kernel_attention",
-    "hymba_kernel_selective_scan", "hymba_kernel_epilogue",
+    "hymba_kernel_selective_scan", "hymba_kernel_epilogue", "hymba_kernel_gemm_rows",
+    "hymba_kernel_gemm_rows_workspace",
     "hymba_layer_profile", "hymba_layer_profile_read", "hymba_stage_name",
     "griffin_block_persistent_bytes", "griffin_block_prepare", "griffin_workspace_bytes",
     "griffin_block_prefill", "griffin_block_decode",
@@ -113,6 +114,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                   c_int32, c_int32, c_int32, c_int32, P, c_size_t, P]),
         "hymba_kernel_epilogue": (c_int32, [c_int32, P, c_int64, P, c_int64, P, c_int64, P, P, P, c_int64,
                                             c_int64, c_int32, c_float, P]),
+        "hymba_kernel_gemm_rows": (c_int32, [c_int32, c_int32, c_int32, P, c_int64, P, c_int64, P, c_int64, P,
+                                             c_int64, c_int32, c_int32, c_int32, c_int32, c_int32, P, c_size_t, P]),
+        "hymba_kernel_gemm_rows_workspace": (c_size_t, [c_int32, c_int32, c_int32]),
         "hymba_layer_profile": (c_int32, [P, c_int32]),
         "hymba_layer_profile_read": (c_int32, [P, POINTER(c_float), c_int32]),
         "hymba_stage_name": (c_char_p, [c_int32]),
@@ -224,6 +228,16 @@ def hymba_kernel_epilogue(dtype, ao, ld_ao, y, ld_y, z, ld_z, beta1, beta2, f, l
                           stream) -> None:
     _check(load_library().hymba_kernel_epilogue(dtype, ao, ld_ao, y, ld_y, z, ld_z, beta1, beta2, f, ld_f,
                                                 rows, E, eps, stream))
+
+
+def hymba_kernel_gemm_rows(w_dtype, x_dtype, y_dtype, w, ldw, x, ldx, y, ldy, y32, ldy32, c0, c1, M, N, K,
+                           workspace, workspace_bytes, stream) -> None:
+    _check(load_library().hymba_kernel_gemm_rows(w_dtype, x_dtype, y_dtype, w, ldw, x, ldx, y, ldy, y32, ldy32,
+                                                 c0, c1, M, N, K, workspace, workspace_bytes, stream))
+
+
+def hymba_kernel_gemm_rows_workspace(M: int, N: int, K: int) -> int:
+    return load_library().hymba_kernel_gemm_rows_workspace(M, N, K)
 
 
 def hymba_layer_profile(layer: int, enable: bool) -> None:

@@ -27,6 +27,7 @@ SOURCES = [
     "epilogue.hip",
     "decode.hip",
     "gemm_f32.hip",
+    "gemm_skinny.hip",
     "convert.hip",
     "griffin.hip",
     "griffin_api.cpp",

@@ -156,9 +156,10 @@ __device__ __forceinline__ float decay_scale(float lam, float c) {
   return c * (fmaxf(-lam, 0.f) + log1pf(__expf(-fabsf(lam))));
 }
 
-// Raw buffer access (gfx9 buffer resource: base, stride 0, byte range; loads past the range return
-// 0, stores past it are dropped).  The row offset goes in a scalar register, the lane's column
-// offset in a vector register, so an access costs no vector address arithmetic.
+// Raw buffer access (gfx9 buffer resource: base, stride 0, byte range).  The row offset goes in a
+// scalar register, the lane's column offset in a vector register, so an access costs no vector
+// address arithmetic.  The hardware range check covers only the vector offset, so the callers
+// keep every row offset inside the buffer themselves.
 constexpr int kBufferFlags = 0x00020000;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufferFlags);
@@ -237,12 +238,12 @@ __global__ __launch_bounds__(64 * kW) void rglru_kernel(RglruArgs<T> a) {
   constexpr int kTile = kW * kWaveSteps;
   const int tiles = static_cast<int>(ceil_div(a.seq, kTile));
   struct Raws { Raw rho[kWaveSteps], iota[kWaveSteps], x[kWaveSteps], v[kWaveSteps]; };
-  // steps past the sequence read zeros (outside the buffer range) and are masked below
+  // steps past the sequence re-read its last row (a scalar clamp) and are masked below
   auto fetch = [&](int tile, Raws& q) {
     const int t0 = tile * kTile + w * kWaveSteps;
 #pragma unroll
     for (int j = 0; j < kWaveSteps; ++j) {
-      const uint32_t t = static_cast<uint32_t>(t0 + j);
+      const uint32_t t = static_cast<uint32_t>(min(t0 + j, a.seq - 1));
       q.rho[j] = P::load(rs_g, col, t * static_cast<uint32_t>(a.ld_g) * es);
       q.iota[j] = P::load(rs_g, col_i, t * static_cast<uint32_t>(a.ld_g) * es);
       q.x[j] = P::load(rs_x, col, t * static_cast<uint32_t>(a.ld_xc) * es);

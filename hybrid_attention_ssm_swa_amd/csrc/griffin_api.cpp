@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -38,6 +39,13 @@ bool is_bf16(const griffin_block_cfg& c) { return c.dtype == HYMBA_BF16; }
 size_t elem(const griffin_block_cfg& c) { return is_bf16(c) ? 2 : 4; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// few rows: all three projections on the weight-streaming kernel (x read in bf16, y written in
+// bf16 by it); else the library GEMMs with the x and y conversions
+bool few_rows(const griffin_block_cfg& c, int64_t rows) {
+  const int64_t R = c.d_rnn, D = c.d_model;
+  return skinny_fits(rows, 2 * R, D) && skinny_fits(rows, 2 * R, R) && skinny_fits(rows, D, R);
+}
+
 int32_t check_cfg(const griffin_block_cfg* c) {
   if (!c) return set_error(HYMBA_ERR_INVALID_ARG, "cfg is NULL");
   if (c->d_model <= 0 || c->d_rnn <= 0) return set_error(HYMBA_ERR_INVALID_ARG, "d_model and d_rnn must be positive");
@@ -50,7 +58,7 @@ int32_t check_cfg(const griffin_block_cfg* c) {
 }
 
 struct Ws {
-  size_t x16 = 0, uv = 0, xc = 0, g = 0, hy = 0, gemm = 0, total = 0;
+  size_t x16 = 0, uv = 0, xc = 0, g = 0, hy = 0, gemm = 0, skp = 0, total = 0;
 };
 
 // x16 (bf16 blocks: x in fp16, later y in fp16) | uv | xc | g | hy | GEMM workspace
@@ -64,6 +72,13 @@ Ws layout(const griffin_block_cfg& c, int B, int T) {
   w.g = o;    o += align_up(rows * 2 * R * e);
   w.hy = o;   o += align_up(rows * R * e);
   w.gemm = o; o += is_bf16(c) ? kGemmWorkspaceBytes : 0;
+  // fp32 partial sums of the few-row GEMMs (split K)
+  w.skp = o;
+  if (is_bf16(c) && few_rows(c, static_cast<int64_t>(rows))) {
+    const int M = static_cast<int>(rows), Ri = static_cast<int>(R), Di = static_cast<int>(D);
+    o += align_up(std::max({skinny_plan(M, 2 * Ri, Di).part_bytes, skinny_plan(M, 2 * Ri, Ri).part_bytes,
+                            skinny_plan(M, Di, Ri).part_bytes}));
+  }
   w.total = o;
   return w;
 }
@@ -85,9 +100,26 @@ Persist persist_layout(const griffin_block_cfg& c) {
   return p;
 }
 
-// Y[rows, out] = X[rows, in] . W[out, in]^T
+// Y[rows, out] = X[rows, in] . W[out, in]^T; bf16 blocks: fp16 X and W, output fp16 (or bf16 with
+// bf16_out, few rows only)
 int32_t project(const griffin_block_cfg& c, const void* X, const void* W, void* Y, int64_t rows, int64_t out,
-                int64_t in, char* ws, const Ws& wl, hipStream_t s) {
+                int64_t in, char* ws, const Ws& wl, hipStream_t s, bool bf16_out = false) {
+  if (is_bf16(c) && few_rows(c, rows)) {   // few rows (decode): the weight-streaming kernel
+    hipError_t e;
+    if (bf16_out) {
+      SkinnyArgs<half_t, half_t, bf16_t> a{static_cast<const half_t*>(W), in, static_cast<const half_t*>(X), in,
+                                           static_cast<bf16_t*>(Y), out, nullptr, 0, 0, 0, static_cast<int>(rows),
+                                           static_cast<int>(out), static_cast<int>(in)};
+      e = launch_skinny_gemm(a, reinterpret_cast<float*>(ws + wl.skp), wl.total - wl.skp, s);
+    } else {
+      SkinnyArgs<half_t, half_t, half_t> a{static_cast<const half_t*>(W), in, static_cast<const half_t*>(X), in,
+                                           static_cast<half_t*>(Y), out, nullptr, 0, 0, 0, static_cast<int>(rows),
+                                           static_cast<int>(out), static_cast<int>(in)};
+      e = launch_skinny_gemm(a, reinterpret_cast<float*>(ws + wl.skp), wl.total - wl.skp, s);
+    }
+    G_HIP_TRY(e, "Griffin projection (few rows) launch");
+    return HYMBA_OK;
+  }
   if (is_bf16(c)) {
     const char* err = nullptr;
     const int r = gemm_16(GT_F16, GT_F16, X, in, W, in, Y, out, rows, out, in, ws + wl.gemm, kGemmWorkspaceBytes,
@@ -133,13 +165,15 @@ struct Timer {   // stage events of a measured call
 template <typename ET>
 int32_t run(const griffin_block_cfg& c, const griffin_block_weights& w, const void* W_in, const void* W_gate,
             const void* W_out, const void* X, int B, int T, void* Y, const float* conv_state, const float* h,
-            float* conv_state_out, float* h_out, char* ws, const Ws& wl, hipStream_t s, Timer& tm) {
+            float* conv_state_out, float* h_out, char* ws, const Ws& wl, hipStream_t s, Timer& tm,
+            bool projected = false) {
   const int64_t rows = static_cast<int64_t>(B) * T, R = c.d_rnn, D = c.d_model;
   ET* uv = reinterpret_cast<ET*>(ws + wl.uv);
   ET* xc = reinterpret_cast<ET*>(ws + wl.xc);
   ET* g = reinterpret_cast<ET*>(ws + wl.g);
   ET* hy = reinterpret_cast<ET*>(ws + wl.hy);
-  G_STATUS_TRY(project(c, X, W_in, uv, rows, 2 * R, D, ws, wl, s));
+  // projected: the input projection has run already (uv written) and Y takes the block's bf16 y
+  if (!projected) G_STATUS_TRY(project(c, X, W_in, uv, rows, 2 * R, D, ws, wl, s));
   G_STATUS_TRY(tm.mark(GS_IN, s));
   GriffinConvArgs<ET> ca{uv, 2 * R, w.conv_w, conv_state, conv_state_out, xc, R, B, T, c.d_rnn};
   G_HIP_TRY(launch_griffin_conv(ca, s), "Griffin conv launch");
@@ -149,7 +183,7 @@ int32_t run(const griffin_block_cfg& c, const griffin_block_weights& w, const vo
   RglruArgs<ET> ra{g, 2 * R, xc, R, uv + R, 2 * R, hy, R, w.lam, c.c, h, h_out, B, T, c.d_rnn};
   G_HIP_TRY(launch_rglru(ra, s), "RG-LRU launch");
   G_STATUS_TRY(tm.mark(GS_RGLRU, s));
-  G_STATUS_TRY(project(c, hy, W_out, Y, rows, D, R, ws, wl, s));
+  G_STATUS_TRY(project(c, hy, W_out, Y, rows, D, R, ws, wl, s, projected));
   return HYMBA_OK;
 }
 
@@ -159,7 +193,20 @@ int32_t forward(const griffin_block_cfg& c, const griffin_block_weights& w, cons
   Timer tm;
   if (stage_ms) G_STATUS_TRY(tm.start(s));
   const int64_t rows = static_cast<int64_t>(B) * T, D = c.d_model;
-  if (is_bf16(c)) {
+  if (is_bf16(c) && few_rows(c, rows)) {
+    // few rows: the input projection reads x in bf16 and the output projection writes y in bf16
+    const Persist pl = persist_layout(c);
+    const char* pw = static_cast<const char*>(persistent);
+    const int64_t R = c.d_rnn;
+    half_t* uv = reinterpret_cast<half_t*>(ws + wl.uv);
+    SkinnyArgs<half_t, bf16_t, half_t> in{reinterpret_cast<const half_t*>(pw + pl.w_in), D,
+                                          static_cast<const bf16_t*>(x), D, uv, 2 * R, nullptr, 0, 0, 0,
+                                          static_cast<int>(rows), static_cast<int>(2 * R), static_cast<int>(D)};
+    G_HIP_TRY(launch_skinny_gemm(in, reinterpret_cast<float*>(ws + wl.skp), wl.total - wl.skp, s),
+              "Griffin input projection (few rows) launch");
+    G_STATUS_TRY(run<half_t>(c, w, nullptr, pw + pl.w_gate, pw + pl.w_out, nullptr, B, T, y, conv_state, h,
+                             conv_state_out, h_out, ws, wl, s, tm, true));
+  } else if (is_bf16(c)) {
     const Persist pl = persist_layout(c);
     const char* pw = static_cast<const char*>(persistent);
     half_t* x16 = reinterpret_cast<half_t*>(ws + wl.x16);

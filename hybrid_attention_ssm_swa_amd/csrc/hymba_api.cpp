@@ -185,9 +185,21 @@ PersistLayout persist_layout(const hymba_layer_cfg& c) {
 }
 
 struct WsLayout {
-  size_t X16, P, bc32, O, Ao, Ys, F, gemm, part, total;
+  size_t X16, P, bc32, O, Ao, Ys, F, gemm, part, skp, total;
   int64_t rows;
 };
+
+// fp32 partial sums of the few-row GEMMs (split K) of `rows` rows: the largest of the three
+// projections, 0 when they go through hipBLASLt
+size_t skinny_part_bytes(const hymba_layer& L, int64_t rows) {
+  const hymba_layer_cfg& c = L.cfg;
+  if (!is_bf16(c) || rows <= 0 || rows > kSkinnyMaxRows) return 0;
+  const int M = static_cast<int>(rows), hq = c.n_heads * c.head_dim;
+  size_t b = 0;
+  for (auto nk : {std::pair<int, int>(static_cast<int>(L.n_in), c.d_model), {c.d_inner, hq}, {c.d_model, c.d_inner}})
+    if (skinny_fits(M, nk.first, nk.second)) b = std::max(b, skinny_plan(M, nk.first, nk.second).part_bytes);
+  return b;
+}
 
 WsLayout ws_layout(const hymba_layer& L, int64_t batch, int64_t seq) {
   const hymba_layer_cfg& c = L.cfg;
@@ -207,6 +219,8 @@ WsLayout ws_layout(const hymba_layer& L, int64_t batch, int64_t seq) {
   w.gemm = off; off += b16 ? kGemmWorkspaceBytes : 0;
   w.part = off;
   off += align_up((size_t)std::max<int64_t>(batch, 1) * c.n_heads * kDecodeMaxSplits * (c.head_dim + 2) * 4);
+  w.skp = off;
+  off += align_up(std::max(skinny_part_bytes(L, batch * seq), skinny_part_bytes(L, c.n_meta)));
   w.total = off;
   return w;
 }
@@ -218,6 +232,22 @@ WsLayout ws_layout(const hymba_layer& L, int64_t batch, int64_t seq) {
 int32_t project(const hymba_layer& L, const void* X, int64_t ldx, const void* W, int64_t ldw, void* Y,
                 int64_t ldy, int64_t rows, int64_t out, int64_t in, bool bf16_out, char* ws, const WsLayout& wl,
                 hipStream_t s) {
+  if (is_bf16(L.cfg) && skinny_fits(rows, out, in)) {   // few rows (decode): the weight-streaming kernel
+    hipError_t e;
+    if (bf16_out) {
+      SkinnyArgs<bf16_t, bf16_t, bf16_t> a{static_cast<const bf16_t*>(W), ldw, static_cast<const bf16_t*>(X), ldx,
+                                           static_cast<bf16_t*>(Y), ldy, nullptr, 0, 0, 0, static_cast<int>(rows),
+                                           static_cast<int>(out), static_cast<int>(in)};
+      e = launch_skinny_gemm(a, reinterpret_cast<float*>(ws + wl.skp), wl.total - wl.skp, s);
+    } else {
+      SkinnyArgs<half_t, half_t, half_t> a{static_cast<const half_t*>(W), ldw, static_cast<const half_t*>(X), ldx,
+                                           static_cast<half_t*>(Y), ldy, nullptr, 0, 0, 0, static_cast<int>(rows),
+                                           static_cast<int>(out), static_cast<int>(in)};
+      e = launch_skinny_gemm(a, reinterpret_cast<float*>(ws + wl.skp), wl.total - wl.skp, s);
+    }
+    HIP_TRY(e, "projection (few rows) launch");
+    return HYMBA_OK;
+  }
   if (is_bf16(L.cfg)) {
     const char* err = nullptr;
     const GemmType t = bf16_out ? GT_BF16 : GT_F16;
@@ -264,6 +294,19 @@ template <typename CT>
 int32_t in_projection(const hymba_layer& L, const void* x, int64_t rows, char* ws, const WsLayout& wl,
                       hipStream_t s) {
   const hymba_layer_cfg& c = L.cfg;
+  if (is_bf16(c) && skinny_fits(rows, L.n_in, c.d_model)) {
+    // few rows: one weight-streaming GEMM reads x in bf16 (converted to fp16 in registers) and
+    // writes P in fp16 plus the B/C columns in fp32 for the scan
+    StageTimer st(L, ST_IN_PROJ, s);
+    SkinnyArgs<half_t, bf16_t, half_t> a{L.w_in16, c.d_model, static_cast<const bf16_t*>(x), c.d_model,
+                                         reinterpret_cast<half_t*>(ws + wl.P), L.n_in,
+                                         reinterpret_cast<float*>(ws + wl.bc32), 2 * c.d_state,
+                                         static_cast<int>(L.off_b), static_cast<int>(L.off_b + 2 * c.d_state),
+                                         static_cast<int>(rows), static_cast<int>(L.n_in), c.d_model};
+    HIP_TRY(launch_skinny_gemm(a, reinterpret_cast<float*>(ws + wl.skp), wl.total - wl.skp, s),
+            "input projection (few rows) launch");
+    return HYMBA_OK;
+  }
   if (is_bf16(c)) {
     half_t* x16 = reinterpret_cast<half_t*>(ws + wl.X16);
     {
@@ -873,6 +916,55 @@ int32_t hymba_kernel_epilogue(int32_t dtype, const void* ao, int64_t ld_ao, cons
   } else {
     return fail(HYMBA_ERR_INVALID_ARG, "epilogue dtype must be HYMBA_F32 or HYMBA_F16");
   }
+  return HYMBA_OK;
+}
+
+size_t hymba_kernel_gemm_rows_workspace(int32_t M, int32_t N, int32_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return skinny_plan(M, N, K).part_bytes;
+}
+
+int32_t hymba_kernel_gemm_rows(int32_t w_dtype, int32_t x_dtype, int32_t y_dtype, const void* w, int64_t ldw,
+                               const void* x, int64_t ldx, void* y, int64_t ldy, float* y32, int64_t ldy32,
+                               int32_t c0, int32_t c1, int32_t M, int32_t N, int32_t K, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (!w || !x || !y) return fail(HYMBA_ERR_INVALID_ARG, "NULL pointer");
+  if (M < 0 || N < 1 || K < 1) return fail(HYMBA_ERR_INVALID_ARG, "bad dimensions");
+  if (N % 4 || K % 8) return fail(HYMBA_ERR_UNSUPPORTED, "N must be a multiple of 4 and K of 8");
+  if (ldw < K || ldx < K || ldy < N || ldw % 8 || ldx % 8 || ldy % 4 || !aligned(w, 16) || !aligned(x, 16) ||
+      !aligned(y, 16))
+    return fail(HYMBA_ERR_INVALID_ARG, "strides: ldw, ldx >= K, multiples of 8; ldy >= N, a multiple of 4; "
+                                       "16-byte aligned pointers");
+  if (y32 && (c0 < 0 || c1 > N || c0 > c1 || c0 % 4 || c1 % 4 || ldy32 < c1 - c0 || ldy32 % 4 || !aligned(y32, 16)))
+    return fail(HYMBA_ERR_INVALID_ARG, "y32: 0 <= c0 <= c1 <= N multiples of 4, ldy32 >= c1 - c0 (of 4), aligned");
+  if (M == 0) return HYMBA_OK;
+  const size_t need = skinny_plan(M, N, K).part_bytes;
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(HYMBA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  if (need && !aligned(workspace, 16)) return fail(HYMBA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  float* part = static_cast<float*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (w_dtype == HYMBA_F16 && x_dtype == HYMBA_F16 && y_dtype == HYMBA_F16) {
+    SkinnyArgs<half_t, half_t, half_t> a{static_cast<const half_t*>(w), ldw, static_cast<const half_t*>(x), ldx,
+                                         static_cast<half_t*>(y), ldy, y32, ldy32, c0, c1, M, N, K};
+    e = launch_skinny_gemm(a, part, workspace_bytes, s);
+  } else if (w_dtype == HYMBA_F16 && x_dtype == HYMBA_BF16 && y_dtype == HYMBA_F16) {
+    SkinnyArgs<half_t, bf16_t, half_t> a{static_cast<const half_t*>(w), ldw, static_cast<const bf16_t*>(x), ldx,
+                                         static_cast<half_t*>(y), ldy, y32, ldy32, c0, c1, M, N, K};
+    e = launch_skinny_gemm(a, part, workspace_bytes, s);
+  } else if (w_dtype == HYMBA_F16 && x_dtype == HYMBA_F16 && y_dtype == HYMBA_BF16) {
+    SkinnyArgs<half_t, half_t, bf16_t> a{static_cast<const half_t*>(w), ldw, static_cast<const half_t*>(x), ldx,
+                                         static_cast<bf16_t*>(y), ldy, y32, ldy32, c0, c1, M, N, K};
+    e = launch_skinny_gemm(a, part, workspace_bytes, s);
+  } else if (w_dtype == HYMBA_BF16 && x_dtype == HYMBA_BF16 && y_dtype == HYMBA_BF16) {
+    SkinnyArgs<bf16_t, bf16_t, bf16_t> a{static_cast<const bf16_t*>(w), ldw, static_cast<const bf16_t*>(x), ldx,
+                                         static_cast<bf16_t*>(y), ldy, y32, ldy32, c0, c1, M, N, K};
+    e = launch_skinny_gemm(a, part, workspace_bytes, s);
+  } else {
+    return fail(HYMBA_ERR_UNSUPPORTED, "unsupported (w, x, y) type combination");
+  }
+  HIP_TRY(e, "few-row GEMM launch");
   return HYMBA_OK;
 }
 

@@ -176,6 +176,38 @@ struct RglruArgs {
 hipError_t launch_rglru(const RglruArgs<float>& a, hipStream_t s);
 hipError_t launch_rglru(const RglruArgs<half_t>& a, hipStream_t s);
 
+// ---- weight-streaming GEMM for few rows: Y[M, N] = X[M, K] . W[N, K]^T -------------
+// 16-bit W and X (X converted to W's type in registers), fp32 accumulation, output OT; the
+// output columns [c0, c1) are also written in fp32 to y32[m, c - c0] when y32 is set.
+// N % 4 == 0, K % 8 == 0, 16-byte aligned rows (ldw, ldx multiples of 8; ldy, ldy32, c0, c1 of 4).
+template <typename WT, typename XT, typename OT>
+struct SkinnyArgs {
+  const WT* w; int64_t ldw;
+  const XT* x; int64_t ldx;
+  OT* y; int64_t ldy;
+  float* y32; int64_t ldy32; int c0; int c1;
+  int M; int N; int K;
+};
+// Split of K over workgroups; with S > 1 the launch needs part_bytes of fp32 workspace.
+struct SkinnyPlan { int kC = 8; int S = 1; size_t part_bytes = 0; };
+SkinnyPlan skinny_plan(int M, int N, int K);
+hipError_t launch_skinny_gemm(const SkinnyArgs<half_t, half_t, half_t>& a, float* part, size_t part_bytes,
+                              hipStream_t s);
+hipError_t launch_skinny_gemm(const SkinnyArgs<half_t, bf16_t, half_t>& a, float* part, size_t part_bytes,
+                              hipStream_t s);
+hipError_t launch_skinny_gemm(const SkinnyArgs<half_t, half_t, bf16_t>& a, float* part, size_t part_bytes,
+                              hipStream_t s);
+hipError_t launch_skinny_gemm(const SkinnyArgs<bf16_t, bf16_t, bf16_t>& a, float* part, size_t part_bytes,
+                              hipStream_t s);
+constexpr int kSkinnyMaxRows = 256;   // the callers use it up to this many rows
+// ... and for weights up to this size: a larger weight (the 1.5B layer's 36 MB input
+// projection) reaches more CUs through the library GEMM than through this kernel, whose
+// 64-feature workgroups each re-read X and whose K splits add fp32 partial sums
+constexpr int64_t kSkinnyMaxWeightBytes = int64_t(24) << 20;
+inline bool skinny_fits(int64_t rows, int64_t n, int64_t k) {
+  return rows > 0 && rows <= kSkinnyMaxRows && n * k * 2 <= kSkinnyMaxWeightBytes;
+}
+
 // ---- misc ----------------------------------------------------------------------
 hipError_t launch_scale_copy(const float* src, float* dst, int64_t n, float scale, hipStream_t s);
 hipError_t launch_fill(float* dst, int64_t n, float value, hipStream_t s);

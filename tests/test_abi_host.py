@@ -317,3 +317,33 @@ def test_griffin_persistent_buffer():
     with pytest.raises(L.HymbaError) as e:
         L.griffin_block_prepare(c, _gweights(), FAKE + 16, n, None)
     assert e.value.status == L.HYMBA_ERR_INVALID_ARG
+
+
+def test_gemm_rows_rejects_bad_arguments():
+    """Validated before any device work (fake aligned pointers)."""
+    args = dict(w=FAKE, ldw=8, x=FAKE, ldx=8, y=FAKE, ldy=8, y32=None, ldy32=0, c0=0, c1=0, M=1, N=8, K=8,
+                ws=None, ws_bytes=0)
+    cases = [
+        (dict(types=(L.HYMBA_F32, L.HYMBA_F16, L.HYMBA_F16)), L.HYMBA_ERR_UNSUPPORTED),
+        (dict(N=6), L.HYMBA_ERR_UNSUPPORTED),
+        (dict(K=12, ldw=16, ldx=16), L.HYMBA_ERR_UNSUPPORTED),
+        (dict(ldx=4), L.HYMBA_ERR_INVALID_ARG),
+        (dict(x=FAKE + 8), L.HYMBA_ERR_INVALID_ARG),
+        (dict(y32=FAKE, ldy32=4, c0=0, c1=8), L.HYMBA_ERR_INVALID_ARG),   # ldy32 < c1 - c0
+        (dict(y=None), L.HYMBA_ERR_INVALID_ARG),
+        (dict(M=128, N=1600, K=3200, ldw=3200, ldx=3200, ldy=1600), L.HYMBA_ERR_WORKSPACE),   # split K
+    ]
+    for kw, code in cases:
+        a = dict(args, types=(L.HYMBA_F16, L.HYMBA_F16, L.HYMBA_F16))
+        a.update(kw)
+        with pytest.raises(L.HymbaError) as e:
+            L.hymba_kernel_gemm_rows(*a["types"], a["w"], a["ldw"], a["x"], a["ldx"], a["y"], a["ldy"], a["y32"],
+                                     a["ldy32"], a["c0"], a["c1"], a["M"], a["N"], a["K"], a["ws"], a["ws_bytes"],
+                                     None)
+        assert e.value.status == code, (kw, L.hymba_last_error())
+    # zero rows: nothing to do
+    L.hymba_kernel_gemm_rows(L.HYMBA_F16, L.HYMBA_F16, L.HYMBA_F16, FAKE, 8, FAKE, 8, FAKE, 8, None, 0, 0, 0,
+                             0, 8, 8, None, 0, None)
+    # the split of K: one workgroup per CU or more, partial sums only when K is split
+    assert L.hymba_kernel_gemm_rows_workspace(128, 1600, 3200) == 13 * 128 * 1600 * 4
+    assert L.hymba_kernel_gemm_rows_workspace(128, 16384, 512) == 0
