@@ -23,6 +23,7 @@
 //    operand without any cross-lane movement.
 //  * attn_f32: fp32 storage, one thread per (query, head), online softmax on
 //    the VALU; used for the fp32 workload and small head dims.
+#include "attn_tile.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -30,242 +31,7 @@ namespace hymba {
 
 namespace {
 
-constexpr int kHd = 64;          // head dim of the MFMA kernel
-constexpr int kQB = 32;          // queries per wave (one MFMA column block)
-constexpr int kKT = 64;          // keys per tile
-constexpr int kKStr = kHd + 8;   // LDS row stride (bf16) of K tiles: 144 B
-constexpr int kVStr = kKT + 4;   // LDS row stride (bf16) of V^T window tiles: 136 B
-constexpr float kLazyLog2 = 8.f;   // rescale threshold of the online softmax (log2 units)
-
-struct __align__(16) U4 { uint32_t x, y, z, w; };
-
-template <typename ET> struct Op;
-template <> struct Op<half_t> {
-  typedef f16x8_t vec;
-  __device__ static __forceinline__ f32x16_t mfma(vec a, vec b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
-};
-template <> struct Op<bf16_t> {
-  typedef bf16x8_t vec;
-  __device__ static __forceinline__ f32x16_t mfma(vec a, vec b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-};
-template <typename ET>
-__device__ __forceinline__ typename Op<ET>::vec as_vec(U4 v) { return __builtin_bit_cast(typename Op<ET>::vec, v); }
-
-// 16-bit elements stored as raw 16-bit words; a double-buffered stage of 64-key tiles
-struct AttnSmem {
-  uint16_t kw[2][kKT * kKStr];        // K tiles   [key][dim]
-  uint16_t vw[2][kHd * kVStr];        // V^T tiles [dim][key]
-};
-
-// Cooperative load of a 64-key tile (K rows straight, V transposed) spread
-// over the workgroup's 256 threads, four 16-byte loads each: threads
-// [0, 128) own K chunks tid + 128 j (j < 4) of the tile's 512 (64 rows x 8
-// chunks); threads [128, 256) own a 4-key x 8-dim block of V.  Rows beyond
-// `nvalid` (>= 1) read a clamped, valid row and are zero-filled by value.
-
-__device__ __forceinline__ uint32_t u4_get(const U4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
-__device__ __forceinline__ U4 masked_load(const void* p, bool keep) {
-  const U4 x = *reinterpret_cast<const U4*>(p);
-  U4 r;
-  r.x = keep ? x.x : 0u;
-  r.y = keep ? x.y : 0u;
-  r.z = keep ? x.z : 0u;
-  r.w = keep ? x.w : 0u;
-  return r;
-}
-
-__device__ __forceinline__ void item_store(const U4 (&r)[4], uint16_t* ks, uint16_t* vs, int vstr, int key_off,
-                                           int item) {
-  if (item < 128) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = item + j * 128;
-      const int row = c >> 3, col = (c & 7) * 8;
-      *reinterpret_cast<U4*>(ks + (key_off + row) * kKStr + col) = r[j];
-    }
-  } else {
-    // transpose 4 keys x 8 dims -> 8 rows (dims) of 4 consecutive keys
-    const int it = item - 128;
-    const int key0 = key_off + (it >> 3) * 4, dim0 = (it & 7) * 8;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      // dims dim0+2p (low halves) and dim0+2p+1 (high halves)
-      const uint32_t a = u4_get(r[0], p), b = u4_get(r[1], p);
-      const uint32_t c = u4_get(r[2], p), d = u4_get(r[3], p);
-      uint2 lo, hi;
-      lo.x = __builtin_amdgcn_perm(b, a, 0x05040100u);   // (a.lo, b.lo)
-      lo.y = __builtin_amdgcn_perm(d, c, 0x05040100u);
-      hi.x = __builtin_amdgcn_perm(b, a, 0x07060302u);   // (a.hi, b.hi)
-      hi.y = __builtin_amdgcn_perm(d, c, 0x07060302u);
-      *reinterpret_cast<uint2*>(vs + (dim0 + 2 * p) * vstr + key0) = lo;
-      *reinterpret_cast<uint2*>(vs + (dim0 + 2 * p + 1) * vstr + key0) = hi;
-    }
-  }
-}
-
-// The calling thread's item (tid < 256) of the tile whose first row is at
-// kbase / vbase (row stride ld elements, 32-bit offsets).  Full tiles load
-// without any clamping; only a tile with nvalid < 64 valid rows takes the
-// clamped, zero-filling path.
-struct TileRegs {
-  U4 r[4];
-};
-
-template <typename ET>
-__device__ __forceinline__ void tile_fetch(TileRegs& t, const ET* __restrict__ kbase,
-                                           const ET* __restrict__ vbase, int ld, int nvalid, int tid) {
-  const bool is_k = tid < 128;                       // waves 0-1: K chunks; waves 2-3: V blocks
-  const ET* base = is_k ? kbase : vbase;
-  const int it = is_k ? tid : tid - 128;
-  const int row0 = is_k ? (it >> 3) : (it >> 3) * 4;
-  const int rstep = is_k ? 16 : 1;
-  const int col = (it & 7) * 8;
-  if (nvalid >= kKT) {
-    const char* b = reinterpret_cast<const char*>(base);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t off = static_cast<uint32_t>(((row0 + rstep * j) * ld + col) * (int)sizeof(ET));
-      t.r[j] = *reinterpret_cast<const U4*>(b + off);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = row0 + rstep * j;
-      t.r[j] = masked_load(base + (int64_t)min(row, nvalid - 1) * ld + col, row < nvalid);
-    }
-  }
-}
-
-__device__ __forceinline__ void tile_store(const TileRegs& t, uint16_t* ks, uint16_t* vs, int tid) {
-  item_store(t.r, ks, vs, kVStr, 0, tid);
-}
-
-struct WaveState {
-  f32x16_t acc[2];    // O^T blocks: dims [0,32) and [32,64), column = query
-  float m;            // running max (raw score units)
-  float l;            // partial row sum over this lane's keys
-};
-
-// x combined with the same register of lane l ^ 32 (v_permlane32_swap with
-// both operands x: the two results are the low half and the high half
-// broadcast to both halves, so any symmetric op of them is the xor-32 reduction).
-__device__ __forceinline__ float max_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// max of three (one v_max3_f32; scores are never NaN)
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-// One 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-// ks: [64][kKStr] K rows; vs: [64 dims][vstr] V^T; key0: first key index of
-// the tile in the mask's coordinates.  With `mask`, key j is kept iff
-// lo_key <= j < hi_key and, for tq >= 0 (a real query tq), j <= tq and
-// (win <= 0 or j > tq - win).
-template <typename ET>
-__device__ __forceinline__ void attend_tile(WaveState& st, const typename Op<ET>::vec (&qf)[4],
-                                            const uint16_t* ks, const uint16_t* vs, int vstr,
-                                            float sc, int lane, int key0, int lo_key, int hi_key,
-                                            int tq, int win, bool mask) {
-  const int col = lane & 31, half = lane >> 5;
-  f32x16_t s[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    s[kb] = f32x16_t{};
-    const uint16_t* krow = ks + (kb * 32 + col) * kKStr + half * 8;
-#pragma unroll
-    for (int st4 = 0; st4 < 4; ++st4) {
-      const auto a = as_vec<ET>(*reinterpret_cast<const U4*>(krow + st4 * 16));
-      s[kb] = Op<ET>::mfma(a, qf[st4], s[kb]);
-    }
-  }
-  if (mask) {
-    // key index of register r of block kb: key0 + 32 kb + 8 (r/4) + 4 half + r%4
-    int lo = lo_key, hi = hi_key;
-    if (tq >= 0) {
-      hi = min(hi, tq + 1);
-      if (win > 0) lo = max(lo, tq - win + 1);
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (key < lo || key >= hi) s[kb][r] = -INFINITY;   // exp2 gives exactly 0 whatever the running max
-      }
-  }
-  float mt = max3f(s[0][0], s[0][1], s[0][2]);
-#pragma unroll
-  for (int r = 3; r < 15; r += 2) mt = max3f(mt, s[0][r], s[0][r + 1]);
-  mt = max3f(mt, s[0][15], s[1][0]);
-#pragma unroll
-  for (int r = 1; r < 15; r += 2) mt = max3f(mt, s[1][r], s[1][r + 1]);
-  mt = fmaxf(mt, s[1][15]);
-  mt = max_xor32(mt);
-  // Lazy rescaling: the running max only moves (and the accumulators are rescaled) when some
-  // query of the wave sees a score more than 2^kLazyLog2 above it; otherwise the stale max is
-  // kept and probabilities may reach 2^kLazyLog2, exact in the 16-bit P and fp32 sums.
-  if (__builtin_amdgcn_ballot_w64((mt - st.m) * sc > kLazyLog2) != 0) {
-    const float mnew = fmaxf(st.m, mt);
-    const float alpha = fast_exp2((st.m - mnew) * sc);
-    st.m = mnew;
-    st.l *= alpha;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.acc[db][r] *= alpha;
-  }
-  const float msc = st.m * sc;
-  float psum = 0.f;
-  typename Op<ET>::vec pf[4];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      float p[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        p[j] = fast_exp2(fmaf(s[kb][hh * 8 + j], sc, -msc));
-        psum += p[j];
-      }
-      U4 w;
-      w.x = Pair<ET>::pack(p[0], p[1]);
-      w.y = Pair<ET>::pack(p[2], p[3]);
-      w.z = Pair<ET>::pack(p[4], p[5]);
-      w.w = Pair<ET>::pack(p[6], p[7]);
-      pf[kb * 2 + hh] = as_vec<ET>(w);
-    }
-  }
-  st.l += psum;
-  // O^T[dim][q] += sum_k V^T[dim][k] P^T[k][q]; PV k-step s covers tile keys
-  // [16 s, 16 s + 16); k-index 8 h + j <-> key 16 s + 8 (j/4) + 4 h + j%4.
-#pragma unroll
-  for (int db = 0; db < 2; ++db) {
-    const uint16_t* vrow = vs + (db * 32 + col) * vstr + 4 * half;
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 16 * s4);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 * s4 + 8);
-      U4 w = {lo.x, lo.y, hi.x, hi.y};
-      st.acc[db] = Op<ET>::mfma(as_vec<ET>(w), pf[s4], st.acc[db]);
-    }
-  }
-}
+using namespace attn;
 
 // One workgroup = 4 waves = kQG consecutive queries (one 32-query block per
 // wave) of one query head.  The workgroup streams the key tiles its queries

@@ -9,7 +9,9 @@
 // hyeon-jae.tistory.com section 4: decode time is dominated by loading
 // parameters and cache).
 #include <algorithm>
+#include <type_traits>
 
+#include "attn_tile.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -232,6 +234,104 @@ __global__ __launch_bounds__(kThreads) void decode_attn_kernel(DecAttnArgs<T> a)
   }
 }
 
+// MFMA decode attention (fp16 K/V, head dim 64): one wave per (split, KV head, sequence).  The
+// G query heads of the KV group are the query columns of the prefill kernel's tile step
+// (v_mfma_f32_32x32x16_f16, S^T = K Q^T; columns G..31 carry zero queries and are dropped).  The
+// wave walks its split's keys in 64-key tiles: the next tile's K rows and V blocks are loaded
+// into registers while the current one, staged in LDS (K rows straight, V transposed), goes
+// through the online softmax.  The split's (acc, max, sum) per head go to `part` as in the VALU
+// kernel, and the same combine kernel merges the splits.
+template <int G>
+__global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecAttnArgs<half_t> a) {
+  using namespace attn;
+  static_assert(G >= 1 && G <= kQB, "query heads of a KV group must fit one column block");
+  __shared__ __align__(16) uint16_t ks[kKT * kKStr];
+  __shared__ __align__(16) uint16_t vs[kHd * kVStr];
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x, col = lane & 31, half = lane >> 5;
+  const int C = a.cache_len;
+  const int64_t p = a.pos[b];
+  const int64_t weff = a.window > 0 ? a.window : C;
+  const int64_t lo = p - weff + 1 > 0 ? p - weff + 1 : 0;
+  const int nkeys = a.n_meta + static_cast<int>(p - lo + 1 > 0 ? p - lo + 1 : 0);
+  const int per = static_cast<int>(ceil_div(nkeys, a.splits));
+  const int k0 = split * per;
+  const int k1 = min(nkeys, k0 + per);
+  const int lo_mod = static_cast<int>(lo % C);   // ring slot of the first window key
+
+  // Q^T as the B operand: column col = head g G + col, k-step s = dims [16 s + 8 half, +8)
+  Op<half_t>::vec qf[4];
+  {
+    const half_t* qrow = a.q + (int64_t)b * a.ld_q + (int64_t)(g * G + min(col, G - 1)) * kHd + 8 * half;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      U4 v = *reinterpret_cast<const U4*>(qrow + s4 * 16);
+      if (col >= G) v = U4{0u, 0u, 0u, 0u};
+      qf[s4] = as_vec<half_t>(v);
+    }
+  }
+  WaveState st;
+  st.acc[0] = f32x16_t{};
+  st.acc[1] = f32x16_t{};
+  st.m = -1e30f;
+  st.l = 0.f;
+
+  // key kk of the sequence -> its K (and V) row: a meta row, or ring slot lo + kk - M (mod C)
+  const int64_t ring = ((int64_t)b * a.n_kv_heads + g) * C;
+  auto row_off = [&](int kk) -> int64_t {
+    if (kk < a.n_meta) return -1 - ((int64_t)kk * a.ld_meta + (int64_t)g * kHd);   // negative: meta
+    int slot = lo_mod + (kk - a.n_meta);
+    if (slot >= C) slot -= C;
+    return (ring + slot) * kHd;
+  };
+  // a lane's 16 loads of the tile starting at key t0 with nvalid keys: items lane and lane + 64
+  // of the K chunks (4 rows 16 apart each) and of the V blocks (4 consecutive keys x 8 dims);
+  // rows past nvalid read the last valid row (their scores are masked)
+  auto fetch = [&](int t0, int nvalid, U4 (&kr)[2][4], U4 (&vr)[2][4]) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int item = lane + 64 * it;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int krow = (item >> 3) + 16 * j, kcol = (item & 7) * 8;
+        const int64_t ko = row_off(t0 + min(krow, nvalid - 1));
+        kr[it][j] = *reinterpret_cast<const U4*>((ko < 0 ? a.k_meta + (-1 - ko) : a.k_cache + ko) + kcol);
+        const int vrow = (item >> 3) * 4 + j, vcol = (item & 7) * 8;
+        const int64_t vo = row_off(t0 + min(vrow, nvalid - 1));
+        vr[it][j] = *reinterpret_cast<const U4*>((vo < 0 ? a.v_meta + (-1 - vo) : a.v_cache + vo) + vcol);
+      }
+    }
+  };
+  U4 kr[2][4], vr[2][4];
+  if (k0 < k1) fetch(k0, min(kKT, k1 - k0), kr, vr);
+  for (int t0 = k0; t0 < k1; t0 += kKT) {
+    const int nvalid = min(kKT, k1 - t0);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      item_store(kr[it], ks, vs, kVStr, 0, lane + 64 * it);         // K chunks
+      item_store(vr[it], ks, vs, kVStr, 0, 128 + lane + 64 * it);   // V blocks, transposed
+    }
+    __syncthreads();
+    if (t0 + kKT < k1) fetch(t0 + kKT, min(kKT, k1 - t0 - kKT), kr, vr);   // next tile in flight
+    attend_tile<half_t>(st, qf, ks, vs, kVStr, a.scale_log2, lane, 0, 0, nvalid, -1, 0, nvalid < kKT);
+    __syncthreads();
+  }
+
+  // this split's partials of heads g G + col (col < G): acc over the lane's 32 dims, max (log2
+  // units) and the sum over both halves of the column
+  const float ltot = sum_xor32(st.l);
+  if (col >= G) return;
+  float* out = a.part + (((int64_t)b * a.n_heads + g * G + col) * a.splits + split) * (kHd + 2);
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) out[db * 32 + 8 * (r >> 2) + 4 * half + (r & 3)] = st.acc[db][r];
+  if (half == 0) {
+    out[kHd] = st.m * a.scale_log2;
+    out[kHd + 1] = ltot;
+  }
+}
+
 // grid B * H, block hd threads: merge the split partials of one (sequence, head).
 template <typename T>
 __global__ __launch_bounds__(kDecodeMaxHd) void decode_combine_kernel(DecAttnArgs<T> a) {
@@ -280,9 +380,33 @@ hipError_t dec_dispatch_hd(const DecAttnArgs<T>& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t dec_dispatch_mfma(const DecAttnArgs<half_t>& a, hipStream_t s) {
+  const dim3 grid(a.splits, a.n_kv_heads, a.B), block(64);
+  switch (a.n_heads / a.n_kv_heads) {
+    case 1: hipLaunchKernelGGL((decode_attn_mfma_kernel<1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_attn_mfma_kernel<2>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_attn_mfma_kernel<3>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_attn_mfma_kernel<4>), grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL((decode_attn_mfma_kernel<5>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((decode_attn_mfma_kernel<6>), grid, block, 0, s, a); break;
+    case 7: hipLaunchKernelGGL((decode_attn_mfma_kernel<7>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((decode_attn_mfma_kernel<8>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t dec_dispatch(const DecAttnArgs<T>& a, hipStream_t s) {
   hipError_t e;
+  if constexpr (std::is_same<T, half_t>::value) {
+    if (a.head_dim == 64) {
+      e = dec_dispatch_mfma(a, s);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((decode_combine_kernel<T>), dim3(a.B * a.n_heads), dim3(kDecodeMaxHd), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   if (a.head_dim == 64) e = dec_dispatch_hd<T, 64>(a, s);
   else if (a.head_dim == 32) e = dec_dispatch_hd<T, 32>(a, s);
   else return hipErrorInvalidValue;
