@@ -494,6 +494,44 @@ def summarize_rocprof(trace_dir, bench_json, fetch_dir, write_dir, command, out_
     print("\n".join(lines))
 
 
+def summarize_griffin(trace_dir, bench_json, command, out_txt):
+    """Per-stage kernel medians of the Griffin block's 8K prefill from a rocprofv3 kernel trace:
+    each 8K conv dispatch anchors one call, whose neighbours in dispatch order are the x
+    conversion and input GEMM before it and the gate GEMM, RG-LRU, output GEMM and y conversion
+    after it."""
+    lines = [f"# rocprofv3 summary: {command['title']}", "# profiled command (repository root, one MI355X):",
+             f"#   {command['trace']}", "# summarized on the host with:", f"#   {command['summary']}", ""]
+    rows = sorted(_csv_rows(trace_dir, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3   # noqa: E731
+    conv = [i for i, r in enumerate(rows) if "griffin_conv_kernel" in r["Kernel_Name"]]
+    big = max((int(rows[i]["Grid_Size_X"]) if "Grid_Size_X" in rows[i] else 0) for i in conv) if conv else 0
+    anchors = [i for i in conv if int(rows[i].get("Grid_Size_X", 0)) == big and 2 <= i < len(rows) - 4]
+    order = [("convert x", -2), ("in_proj", -1), ("conv", 0), ("gate_proj", 1), ("rglru", 2), ("out_proj", 3),
+             ("convert y", 4)]
+    # the median over calls: the first call also tunes the GEMM plans (extra candidate kernels)
+    lines.append(f"{'stage':<10} {'calls':>5} {'median_us':>10}  grid            kernel")
+    total = 0.0
+    for stage, off in order:
+        sel = [rows[i + off] for i in anchors]
+        if not sel:
+            continue
+        ds = sorted(dur(r) for r in sel)
+        med = ds[len(ds) // 2] if len(ds) % 2 else 0.5 * (ds[len(ds) // 2 - 1] + ds[len(ds) // 2])
+        total += med
+        lines.append(f"{stage:<10} {len(sel):>5} {med:>10.1f}  {_grid(sel[-1]):<15} {sel[-1]['Kernel_Name'][:90]}")
+    lines.append(f"{'sum':<10} {'':>5} {total:>10.1f}")
+    if bench_json and os.path.exists(bench_json):
+        txt = [l for l in open(bench_json).read().splitlines() if l.startswith("{")]
+        if txt:
+            b = json.loads(txt[-1])
+            lines += ["", "## the profiled run's event timings (ms per call)",
+                      "  " + ", ".join(f"{k} {v:.3f}" for k, v in b["stage_ms"].items()),
+                      f"  prefill {b['ms_per_step']:.3f} ms/step, {b['tokens_per_s'] / 1e6:.2f} M tokens/s; "
+                      f"decode B=128 {b['decode']['ms_per_step'] * 1e3:.1f} us/step"]
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # --- CPU baseline: the fp64 oracle on a bounded sample ---------------------------------------
 
 def cpu_baseline(budget_s=12.0, max_seqs=3):
@@ -530,7 +568,18 @@ def main():
     ap.add_argument("--pmc-fetch", help="with --summarize-rocprof: rocprofv3 --pmc FETCH_SIZE output dir")
     ap.add_argument("--pmc-write", help="with --summarize-rocprof: rocprofv3 --pmc WRITE_SIZE output dir")
     ap.add_argument("--profile-cmd", help="with --summarize-rocprof: the profiled command, for the header")
+    ap.add_argument("--griffin-only", action="store_true",
+                    help="time only the Griffin block (8K prefill and B=128 decode); prints its JSON record")
+    ap.add_argument("--summarize-griffin", metavar="TRACE_DIR",
+                    help="host only: write profiles/kernels_griffin8k_prefill.txt from a kernel trace and exit")
     args = ap.parse_args()
+    if args.summarize_griffin:
+        cmd = {"title": "Griffin recurrent block, 8K prefill (B=16 x 8192, d 1536, d_rnn 2048, bf16)",
+               "trace": args.profile_cmd or "(not given)",
+               "summary": "python3 " + shlex.join(os.path.relpath(a) if os.path.exists(a) else a for a in sys.argv)}
+        summarize_griffin(args.summarize_griffin, args.bench_json, cmd,
+                          os.path.join(ROOT, "profiles", "kernels_griffin8k_prefill.txt"))
+        return
     if args.summarize_rocprof:
         cmd = {"title": "1.5B-shaped SWA mixer layer, 8K prefill (B=16 x 8192 + 128 meta), K/V handed in",
                "trace": args.profile_cmd or "(not given)",
@@ -551,6 +600,9 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+    if args.griffin_only:
+        print(json.dumps(bench_griffin(args.steps, args.warmup)), flush=True)
+        return
     main_run = bench_prefill(2, args.steps, args.warmup)
     log(f"[bench] 8K SWA prefill: {main_run['tokens_per_s']:.0f} tok/s, {main_run['ms_per_step']:.3f} ms/step")
     workloads = {}

@@ -91,3 +91,32 @@ def test_summary_traffic_scaling(tmp_path):
     assert t["attention"]["bytes_per_launch"] == pytest.approx(100 * 1024 * 0.5 + 50 * 1024)
     assert t["attention"]["source_sha256"] == bench.source_sha("attention")
     assert "in_proj" in open(out_txt).read()
+
+
+def test_griffin_summary_attribution(tmp_path):
+    """Each 8K conv dispatch anchors one prefill call; its neighbours in dispatch order are the
+    x conversion and input GEMM, then the gate GEMM, RG-LRU, output GEMM and y conversion."""
+    seq = [("convert_kernel<bf16,f16>", 100), ("Cijk_in", 1300), ("griffin_conv_kernel<h>", 180),
+           ("Cijk_gate", 1500), ("rglru_kernel<h,8>", 660), ("Cijk_out", 700), ("convert_kernel<f16,bf16>", 110)]
+    rows, t, d = [], 0, 0
+    for call in range(3):
+        for name, us in seq:
+            grid = "2097152" if "conv" in name and "griffin" in name else "4096"
+            rows.append({"Dispatch_Id": str(d), "Kernel_Name": name, "Grid_Size_X": grid, "Grid_Size_Y": "1",
+                         "Grid_Size_Z": "1", "Start_Timestamp": str(t), "End_Timestamp": str(t + us * 1000)})
+            t += us * 1000 + 10
+            d += 1
+    # a decode call afterwards: a small conv grid that must not be picked
+    for name, us in seq:
+        grid = "256" if "griffin_conv" in name else "64"
+        rows.append({"Dispatch_Id": str(d), "Kernel_Name": name, "Grid_Size_X": grid, "Grid_Size_Y": "1",
+                     "Grid_Size_Z": "1", "Start_Timestamp": str(t), "End_Timestamp": str(t + 5000)})
+        t += 5010
+        d += 1
+    _write(str(tmp_path / "tr" / "h" / "1_kernel_trace.csv"), rows)
+    out = str(tmp_path / "g.txt")
+    bench.summarize_griffin(str(tmp_path / "tr"), None, {"title": "t", "trace": "x", "summary": "y"}, out)
+    txt = open(out).read()
+    got = {l.split()[0]: float(l.split()[2]) for l in txt.splitlines()
+           if l.split() and l.split()[0] in ("in_proj", "conv", "gate_proj", "rglru", "out_proj")}
+    assert got == {"in_proj": 1300.0, "conv": 180.0, "gate_proj": 1500.0, "rglru": 660.0, "out_proj": 700.0}
