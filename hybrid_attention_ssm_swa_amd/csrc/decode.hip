@@ -234,9 +234,108 @@ __global__ __launch_bounds__(kThreads) void decode_attn_kernel(DecAttnArgs<T> a)
   }
 }
 
+// ---- the decode tile step on 16 query columns (v_mfma_f32_16x16x32_f16) ------------------
+// A GQA group has at most 8 query heads, so 16 columns waste half as much softmax work as the
+// prefill step's 32.  16x16x32 layouts: A lane l = row l%16, k [8(l/16), +8); B lane l =
+// column l%16, the same k; C lane l = column l%16, rows 4(l/16) + 0..3.
+struct WaveState16 {
+  f32x4_t acc[4];   // O^T: dims 16 db + 4 (lane/16) + r of column lane%16
+  float m;          // running max (raw score units)
+  float l;          // partial sum over this lane's keys
+};
+
+__device__ __forceinline__ f32x4_t mfma16(attn::U4 a, attn::U4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
+                                                0, 0);
+}
+// x combined with the same register of lane l ^ 16 (v_permlane16_swap with both operands x)
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One 64-key tile (K rows ks [64][kKStr], V^T vs [64 dims][kVStr]) for 16 query columns: S^T =
+// K Q^T in four 16-key blocks, online softmax (lazy rescale as in the prefill step), O^T +=
+// V^T P^T in two 32-key steps.  Keys from nvalid on are masked.  The lane's scores s[kb][r] are
+// keys 16 kb + 4 q + r (q = lane/16); as the B operand of PV step m they fill k-slots 8 q + j =
+// keys 32 m + 4 q + j (j < 4) and 32 m + 16 + 4 q + j - 4 (j >= 4), and the V^T reads follow the
+// same order, so P needs no cross-lane movement.
+__device__ __forceinline__ void attend_tile16(WaveState16& st, const attn::U4 (&qf)[2], const uint16_t* ks,
+                                              const uint16_t* vs, float sc, int lane, int nvalid) {
+  using namespace attn;
+  const int col = lane & 15, q = lane >> 4;
+  f32x4_t s[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    s[kb] = f32x4_t{};
+    const uint16_t* krow = ks + (16 * kb + col) * kKStr + 8 * q;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) s[kb] = mfma16(*reinterpret_cast<const U4*>(krow + 32 * h), qf[h], s[kb]);
+  }
+  if (nvalid < kKT) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (16 * kb + 4 * q + r >= nvalid) s[kb][r] = -INFINITY;
+  }
+  float mt = max3f(s[0][0], s[0][1], s[0][2]);
+  mt = max3f(mt, s[0][3], s[1][0]);
+  mt = max3f(mt, s[1][1], s[1][2]);
+  mt = max3f(mt, s[1][3], s[2][0]);
+  mt = max3f(mt, s[2][1], s[2][2]);
+  mt = max3f(mt, s[2][3], s[3][0]);
+  mt = max3f(mt, s[3][1], s[3][2]);
+  mt = fmaxf(mt, s[3][3]);
+  mt = max_xor32(max_xor16(mt));   // the column's max over its four lanes
+  if (__builtin_amdgcn_ballot_w64((mt - st.m) * sc > kLazyLog2) != 0) {
+    const float mnew = fmaxf(st.m, mt);
+    const float alpha = fast_exp2((st.m - mnew) * sc);
+    st.m = mnew;
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st.acc[db][r] *= alpha;
+  }
+  const float msc = st.m * sc;
+  float psum = 0.f;
+  U4 pf[2];
+#pragma unroll
+  for (int m2 = 0; m2 < 2; ++m2) {
+    float p[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = fast_exp2(fmaf(s[2 * m2][r], sc, -msc));
+      p[4 + r] = fast_exp2(fmaf(s[2 * m2 + 1][r], sc, -msc));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) psum += p[j];
+    pf[m2].x = pack_f16x2(p[0], p[1]);
+    pf[m2].y = pack_f16x2(p[2], p[3]);
+    pf[m2].z = pack_f16x2(p[4], p[5]);
+    pf[m2].w = pack_f16x2(p[6], p[7]);
+  }
+  st.l += psum;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const uint16_t* vrow = vs + (16 * db + col) * kVStr + 4 * q;
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2) {
+      const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 32 * m2);
+      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 32 * m2 + 16);
+      st.acc[db] = mfma16(U4{lo.x, lo.y, hi.x, hi.y}, pf[m2], st.acc[db]);
+    }
+  }
+}
+
 // MFMA decode attention (fp16 K/V, head dim 64): one wave per (split, KV head, sequence).  The
-// G query heads of the KV group are the query columns of the prefill kernel's tile step
-// (v_mfma_f32_32x32x16_f16, S^T = K Q^T; columns G..31 carry zero queries and are dropped).  The
+// G query heads of the KV group are the query columns of a 16-column tile step
+// (v_mfma_f32_16x16x32_f16, S^T = K Q^T; columns G..15 carry zero queries and are dropped).  The
 // wave walks its split's keys in 64-key tiles: the next tile's K rows and V blocks are loaded
 // into registers while the current one, staged in LDS (K rows straight, V transposed), goes
 // through the online softmax.  The split's (acc, max, sum) per head go to `part` as in the VALU
@@ -244,11 +343,11 @@ __global__ __launch_bounds__(kThreads) void decode_attn_kernel(DecAttnArgs<T> a)
 template <int G>
 __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecAttnArgs<half_t> a) {
   using namespace attn;
-  static_assert(G >= 1 && G <= kQB, "query heads of a KV group must fit one column block");
+  static_assert(G >= 1 && G <= 16, "query heads of a KV group must fit 16 columns");
   __shared__ __align__(16) uint16_t ks[kKT * kKStr];
   __shared__ __align__(16) uint16_t vs[kHd * kVStr];
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x, col = lane & 31, half = lane >> 5;
+  const int lane = threadIdx.x;
   const int C = a.cache_len;
   const int64_t p = a.pos[b];
   const int64_t weff = a.window > 0 ? a.window : C;
@@ -259,20 +358,20 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecAttnArgs<half_t
   const int k1 = min(nkeys, k0 + per);
   const int lo_mod = static_cast<int>(lo % C);   // ring slot of the first window key
 
-  // Q^T as the B operand: column col = head g G + col, k-step s = dims [16 s + 8 half, +8)
-  Op<half_t>::vec qf[4];
+  // Q^T as the B operand: column c16 = head g G + c16, k-step h = dims [32 h + 8 q, +8)
+  const int c16 = lane & 15, q = lane >> 4;
+  U4 qf[2];
   {
-    const half_t* qrow = a.q + (int64_t)b * a.ld_q + (int64_t)(g * G + min(col, G - 1)) * kHd + 8 * half;
+    const half_t* qrow = a.q + (int64_t)b * a.ld_q + (int64_t)(g * G + min(c16, G - 1)) * kHd + 8 * q;
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      U4 v = *reinterpret_cast<const U4*>(qrow + s4 * 16);
-      if (col >= G) v = U4{0u, 0u, 0u, 0u};
-      qf[s4] = as_vec<half_t>(v);
+    for (int h = 0; h < 2; ++h) {
+      const U4 v = *reinterpret_cast<const U4*>(qrow + 32 * h);
+      qf[h] = c16 < G ? v : U4{0u, 0u, 0u, 0u};
     }
   }
-  WaveState st;
-  st.acc[0] = f32x16_t{};
-  st.acc[1] = f32x16_t{};
+  WaveState16 st;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) st.acc[db] = f32x4_t{};
   st.m = -1e30f;
   st.l = 0.f;
 
@@ -313,20 +412,20 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecAttnArgs<half_t
     }
     __syncthreads();
     if (t0 + kKT < k1) fetch(t0 + kKT, min(kKT, k1 - t0 - kKT), kr, vr);   // next tile in flight
-    attend_tile<half_t>(st, qf, ks, vs, kVStr, a.scale_log2, lane, 0, 0, nvalid, -1, 0, nvalid < kKT);
+    attend_tile16(st, qf, ks, vs, a.scale_log2, lane, nvalid);
     __syncthreads();
   }
 
-  // this split's partials of heads g G + col (col < G): acc over the lane's 32 dims, max (log2
-  // units) and the sum over both halves of the column
-  const float ltot = sum_xor32(st.l);
-  if (col >= G) return;
-  float* out = a.part + (((int64_t)b * a.n_heads + g * G + col) * a.splits + split) * (kHd + 2);
+  // this split's partials of heads g G + c16 (c16 < G): acc over the lane's 16 dims, max (log2
+  // units) and the sum over the column's four lanes
+  const float ltot = sum_xor32(sum_xor16(st.l));
+  if (c16 >= G) return;
+  float* out = a.part + (((int64_t)b * a.n_heads + g * G + c16) * a.splits + split) * (kHd + 2);
 #pragma unroll
-  for (int db = 0; db < 2; ++db)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) out[db * 32 + 8 * (r >> 2) + 4 * half + (r & 3)] = st.acc[db][r];
-  if (half == 0) {
+    for (int r = 0; r < 4; ++r) out[16 * db + 4 * q + r] = st.acc[db][r];
+  if (q == 0) {
     out[kHd] = st.m * a.scale_log2;
     out[kHd + 1] = ltot;
   }
