@@ -188,8 +188,9 @@ struct SkinnyArgs {
   float* y32; int64_t ldy32; int c0; int c1;
   int M; int N; int K;
 };
-// Split of K over workgroups; with S > 1 the launch needs part_bytes of fp32 workspace.
-struct SkinnyPlan { int kC = 8; int S = 1; size_t part_bytes = 0; };
+// Launch plan: feature tile F (64 or 32); part_bytes of workspace (none with the current kernel,
+// which never splits K across workgroups).
+struct SkinnyPlan { int F = 64; size_t part_bytes = 0; };
 SkinnyPlan skinny_plan(int M, int N, int K);
 hipError_t launch_skinny_gemm(const SkinnyArgs<half_t, half_t, half_t>& a, float* part, size_t part_bytes,
                               hipStream_t s);
@@ -201,8 +202,8 @@ hipError_t launch_skinny_gemm(const SkinnyArgs<bf16_t, bf16_t, bf16_t>& a, float
                               hipStream_t s);
 constexpr int kSkinnyMaxRows = 256;   // the callers use it up to this many rows
 // ... and for weights up to this size: a larger weight (the 1.5B layer's 36 MB input
-// projection) reaches more CUs through the library GEMM than through this kernel, whose
-// 64-feature workgroups each re-read X and whose K splits add fp32 partial sums
+// projection) goes through the library GEMM, about twice as fast there as through this
+// kernel, whose 32-row workgroups each re-read W's tile from L2 and X once per feature tile
 constexpr int64_t kSkinnyMaxWeightBytes = int64_t(24) << 20;
 inline bool skinny_fits(int64_t rows, int64_t n, int64_t k) {
   return rows > 0 && rows <= kSkinnyMaxRows && n * k * 2 <= kSkinnyMaxWeightBytes;

@@ -331,7 +331,6 @@ def test_gemm_rows_rejects_bad_arguments():
         (dict(x=FAKE + 8), L.HYMBA_ERR_INVALID_ARG),
         (dict(y32=FAKE, ldy32=4, c0=0, c1=8), L.HYMBA_ERR_INVALID_ARG),   # ldy32 < c1 - c0
         (dict(y=None), L.HYMBA_ERR_INVALID_ARG),
-        (dict(M=128, N=1600, K=3200, ldw=3200, ldx=3200, ldy=1600), L.HYMBA_ERR_WORKSPACE),   # split K
     ]
     for kw, code in cases:
         a = dict(args, types=(L.HYMBA_F16, L.HYMBA_F16, L.HYMBA_F16))
@@ -344,6 +343,7 @@ def test_gemm_rows_rejects_bad_arguments():
     # zero rows: nothing to do
     L.hymba_kernel_gemm_rows(L.HYMBA_F16, L.HYMBA_F16, L.HYMBA_F16, FAKE, 8, FAKE, 8, FAKE, 8, None, 0, 0, 0,
                              0, 8, 8, None, 0, None)
-    # the split of K: one workgroup per CU or more, partial sums only when K is split
-    assert L.hymba_kernel_gemm_rows_workspace(128, 1600, 3200) == 13 * 128 * 1600 * 4
+    # K is never split across workgroups: no workspace at any shape
+    assert L.hymba_kernel_gemm_rows_workspace(128, 1600, 3200) == 0
+    assert L.hymba_kernel_gemm_rows_workspace(300, 1600, 3200) == 0
     assert L.hymba_kernel_gemm_rows_workspace(128, 16384, 512) == 0

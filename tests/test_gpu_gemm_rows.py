@@ -4,8 +4,9 @@ the layers use for up to 256 rows) with an fp64 matmul of the same 16-bit operan
 Bound per element: the output type's own rounding u*|ref| plus the worst-case fp32
 accumulation error K * 2^-24 * (|x| |w|^T) (products of 16-bit values are exact in fp32).
 Shapes: the decode projections of the 1.5B layer (128 rows), and ragged ones: rows not a
-multiple of 32 or spanning two 128-row blocks, features not a multiple of 64, K not a
-multiple of 64, padded strides, and the fp32 copy of a column range.
+multiple of 32, features not a multiple of 32 or 64, K not a multiple of 64 or of the 512-k
+phase, K walks of 1 to 10 phases (up to 8 unrolled, more in a loop), padded strides, and the
+fp32 copy of a column range.
 """
 import numpy as np
 import pytest
@@ -36,6 +37,8 @@ def _mat(rng, rows, cols, ld, dt):
     ((L.HYMBA_F16, L.HYMBA_BF16, L.HYMBA_F16), 200, 100, 72, 16, (0, 100)),
     ((L.HYMBA_BF16, L.HYMBA_BF16, L.HYMBA_BF16), 1, 4, 8, 0, None),
     ((L.HYMBA_F16, L.HYMBA_F16, L.HYMBA_BF16), 256, 260, 136, 8, None),
+    ((L.HYMBA_F16, L.HYMBA_F16, L.HYMBA_F16), 40, 68, 4616, 8, None),         # K walk of 10 phases: the loop
+    ((L.HYMBA_F16, L.HYMBA_BF16, L.HYMBA_F16), 33, 132, 4096, 0, (64, 132)),  # 8 phases, the longest unrolled
 ])
 def test_gemm_rows_matches_fp64(types, M, N, K, pad, cols):
     wt, xt, yt = types
