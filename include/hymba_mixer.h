@@ -256,7 +256,7 @@ int32_t hymba_kernel_epilogue(int32_t dtype, const void* ao, int64_t ld_ao, cons
  * rows (decode batches): y[M, N] = x[M, K] . w[N, K]^T with fp32 accumulation
  * ([H] §2.1 Eq. 3: the shared input projection, W_O and the output
  * projection).  Types (w, x, y): (HYMBA_F16, HYMBA_F16, HYMBA_F16),
- * (HYMBA_F16, HYMBA_BF16, HYMBA_F16) (x converted to fp16 in registers),
+ * (HYMBA_F16, HYMBA_BF16, HYMBA_F16) (x converted to fp16 on its way in),
  * (HYMBA_F16, HYMBA_F16, HYMBA_BF16) and (HYMBA_BF16, HYMBA_BF16, HYMBA_BF16).
  * Row-major, 16-byte aligned pointers; ldw, ldx multiples of 8 and >= K; ldy
  * a multiple of 4 and >= N; N % 4 == 0, K % 8 == 0; M >= 0 (any number of
@@ -264,15 +264,17 @@ int32_t hymba_kernel_epilogue(int32_t dtype, const void* ao, int64_t ld_ao, cons
  * multiple of 4) or NULL: also receives the columns [c0, c1) of y
  * (multiples of 4) as y32[m, c - c0].  workspace: device memory of at least
  * hymba_kernel_gemm_rows_workspace(M, N, K) bytes, 16-byte aligned (may be
- * NULL when that is 0). */
+ * NULL when that is 0, which it is for every shape with the current kernel).
+ * Deterministic: the sum over K is taken in a fixed order. */
 int32_t hymba_kernel_gemm_rows(int32_t w_dtype, int32_t x_dtype, int32_t y_dtype, const void* w,
                                int64_t ldw, const void* x, int64_t ldx, void* y, int64_t ldy,
                                float* y32, int64_t ldy32, int32_t c0, int32_t c1, int32_t M,
                                int32_t N, int32_t K, void* workspace, size_t workspace_bytes,
                                void* stream);
 
-/* Workspace bytes hymba_kernel_gemm_rows needs for [M, N, K] (fp32 partial sums when K is split
- * over workgroups; 0 when it is not). */
+/* Workspace bytes hymba_kernel_gemm_rows needs for [M, N, K]: 0, since the kernel
+ * never splits K across workgroups (kept so that callers size it the same way if
+ * a later kernel does). */
 size_t hymba_kernel_gemm_rows_workspace(int32_t M, int32_t N, int32_t K);
 
 #ifdef __cplusplus
