@@ -387,6 +387,30 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecAttnArgs<half_t
   // of the K chunks (4 rows 16 apart each) and of the V blocks (4 consecutive keys x 8 dims);
   // rows past nvalid read the last valid row (their scores are masked)
   auto fetch = [&](int t0, int nvalid, U4 (&kr)[2][4], U4 (&vr)[2][4]) {
+    // A full tile wholly in the meta rows, or wholly in one unwrapped stretch of the ring, is a
+    // strided block: one base for the tile and 32-bit row offsets.  Other tiles (the one across
+    // the meta/window boundary, the one across the ring's wrap, a partial last tile) take the
+    // per-row mapping.
+    const int meta_rows = min(max(a.n_meta - t0, 0), kKT);
+    int s0 = lo_mod + (t0 + meta_rows - a.n_meta);   // ring slot of the tile's first window key
+    if (s0 >= C) s0 -= C;
+    if (nvalid == kKT && (meta_rows == kKT || (meta_rows == 0 && s0 + kKT <= C))) {   // uniform
+      const bool meta = meta_rows == kKT;
+      const half_t* kb = meta ? a.k_meta + (int64_t)t0 * a.ld_meta + g * kHd : a.k_cache + (ring + s0) * kHd;
+      const half_t* vb = meta ? a.v_meta + (int64_t)t0 * a.ld_meta + g * kHd : a.v_cache + (ring + s0) * kHd;
+      const int stride = meta ? static_cast<int>(a.ld_meta) : kHd;
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int item = lane + 64 * it;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = (item & 7) * 8;
+          kr[it][j] = *reinterpret_cast<const U4*>(kb + ((item >> 3) + 16 * j) * stride + col);
+          vr[it][j] = *reinterpret_cast<const U4*>(vb + ((item >> 3) * 4 + j) * stride + col);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int item = lane + 64 * it;
@@ -401,19 +425,34 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecAttnArgs<half_t
       }
     }
   };
-  U4 kr[2][4], vr[2][4];
-  if (k0 < k1) fetch(k0, min(kKT, k1 - k0), kr, vr);
-  for (int t0 = k0; t0 < k1; t0 += kKT) {
-    const int nvalid = min(kKT, k1 - t0);
+  auto stage = [&](const U4 (&kr)[2][4], const U4 (&vr)[2][4]) {
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       item_store(kr[it], ks, vs, kVStr, 0, lane + 64 * it);         // K chunks
       item_store(vr[it], ks, vs, kVStr, 0, 128 + lane + 64 * it);   // V blocks, transposed
     }
     __syncthreads();
-    if (t0 + kKT < k1) fetch(t0 + kKT, min(kKT, k1 - t0 - kKT), kr, vr);   // next tile in flight
-    attend_tile16(st, qf, ks, vs, a.scale_log2, lane, nvalid);
+  };
+  U4 kr[2][4], vr[2][4];
+  if (k1 - k0 > kKT && k1 - k0 <= 2 * kKT) {
+    // two tiles (the usual split length): both in flight from the start, straight-line code
+    U4 kr2[2][4], vr2[2][4];
+    fetch(k0, kKT, kr, vr);
+    fetch(k0 + kKT, k1 - k0 - kKT, kr2, vr2);
+    stage(kr, vr);
+    attend_tile16(st, qf, ks, vs, a.scale_log2, lane, kKT);
     __syncthreads();
+    stage(kr2, vr2);
+    attend_tile16(st, qf, ks, vs, a.scale_log2, lane, k1 - k0 - kKT);
+  } else {
+    if (k0 < k1) fetch(k0, min(kKT, k1 - k0), kr, vr);
+    for (int t0 = k0; t0 < k1; t0 += kKT) {
+      const int nvalid = min(kKT, k1 - t0);
+      stage(kr, vr);
+      if (t0 + kKT < k1) fetch(t0 + kKT, min(kKT, k1 - t0 - kKT), kr, vr);   // next tile in flight
+      attend_tile16(st, qf, ks, vs, a.scale_log2, lane, nvalid);
+      __syncthreads();
+    }
   }
 
   // this split's partials of heads g G + c16 (c16 < G): acc over the lane's 16 dims, max (log2
