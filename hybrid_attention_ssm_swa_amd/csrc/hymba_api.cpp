@@ -291,16 +291,18 @@ void meta_kv_of(const hymba_layer& L, const hymba_kv* kv, const void** km, const
 
 // Shared projection of `rows` rows of x (storage type) into P (activation type).
 template <typename CT>
+// bc32: also write the B/C columns in fp32 (the prefill scan reads them so; the decode step
+// reads them from P).
 int32_t in_projection(const hymba_layer& L, const void* x, int64_t rows, char* ws, const WsLayout& wl,
-                      hipStream_t s) {
+                      bool bc32, hipStream_t s) {
   const hymba_layer_cfg& c = L.cfg;
   if (is_bf16(c) && skinny_fits(rows, L.n_in, c.d_model)) {
-    // few rows: one weight-streaming GEMM reads x in bf16 (converted to fp16 in registers) and
-    // writes P in fp16 plus the B/C columns in fp32 for the scan
+    // few rows: one weight-streaming GEMM reads x in bf16 (converted to fp16 on the way in) and
+    // writes P in fp16, plus the B/C columns in fp32 for the scan
     StageTimer st(L, ST_IN_PROJ, s);
     SkinnyArgs<half_t, bf16_t, half_t> a{L.w_in16, c.d_model, static_cast<const bf16_t*>(x), c.d_model,
                                          reinterpret_cast<half_t*>(ws + wl.P), L.n_in,
-                                         reinterpret_cast<float*>(ws + wl.bc32), 2 * c.d_state,
+                                         bc32 ? reinterpret_cast<float*>(ws + wl.bc32) : nullptr, 2 * c.d_state,
                                          static_cast<int>(L.off_b), static_cast<int>(L.off_b + 2 * c.d_state),
                                          static_cast<int>(rows), static_cast<int>(L.n_in), c.d_model};
     HIP_TRY(launch_skinny_gemm(a, reinterpret_cast<float*>(ws + wl.skp), wl.total - wl.skp, s),
@@ -319,6 +321,7 @@ int32_t in_projection(const hymba_layer& L, const void* x, int64_t rows, char* w
       STATUS_TRY(project(L, x16, c.d_model, L.w_in16, c.d_model, ws + wl.P, L.n_in, rows, L.n_in, c.d_model,
                          false, ws, wl, s));
     }
+    if (!bc32) return HYMBA_OK;
     // B/C columns as fp32 for the scan
     StageTimer st(L, ST_CVT, s);
     HIP_TRY(launch_convert(reinterpret_cast<const half_t*>(ws + wl.P) + L.off_b, L.n_in,
@@ -460,7 +463,7 @@ int32_t prepare_impl(hymba_layer& L, const hymba_kv* kv, char* ws, const WsLayou
     L.prep_kmeta = km; L.prep_vmeta = vm;
     return HYMBA_OK;
   }
-  STATUS_TRY(in_projection<CT>(L, L.w.meta, M, ws, wl, s));
+  STATUS_TRY(in_projection<CT>(L, L.w.meta, M, ws, wl, true, s));
   STATUS_TRY(apply_rope<CT>(L, ws, wl, M, M, 0, nullptr, s));   // meta rows at positions 0..M-1
   const CT* P = reinterpret_cast<const CT*>(ws + wl.P);
   const int64_t kvw = (int64_t)c.n_kv_heads * c.head_dim;
@@ -506,7 +509,7 @@ int32_t prefill_impl(hymba_layer& L, const void* x, int B, int T_, void* y, cons
   const hymba_layer_cfg& c = L.cfg;
   const int64_t rows = (int64_t)B * T_;
   const int64_t kvw = (int64_t)c.n_kv_heads * c.head_dim;
-  STATUS_TRY(in_projection<CT>(L, x, rows, ws, wl, s));
+  STATUS_TRY(in_projection<CT>(L, x, rows, ws, wl, true, s));
   STATUS_TRY(apply_rope<CT>(L, ws, wl, rows, T_, c.n_meta, nullptr, s));   // real token t at M + t
   const CT* P = reinterpret_cast<const CT*>(ws + wl.P);
   const CT *k, *v;
@@ -555,7 +558,7 @@ int32_t decode_impl(hymba_layer& L, const void* x, const int64_t* pos, int B, vo
                     float* state, char* ws, const WsLayout& wl, hipStream_t s) {
   if (L.profiling) ++L.prof_calls;
   const hymba_layer_cfg& c = L.cfg;
-  STATUS_TRY(in_projection<CT>(L, x, B, ws, wl, s));
+  STATUS_TRY(in_projection<CT>(L, x, B, ws, wl, false, s));
   STATUS_TRY(apply_rope<CT>(L, ws, wl, B, 1, c.n_meta, pos, s));   // the new token at M + pos[b]
   const CT* P = reinterpret_cast<const CT*>(ws + wl.P);
   if (c.own_kv) {
