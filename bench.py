@@ -532,6 +532,34 @@ def summarize_griffin(trace_dir, bench_json, command, out_txt):
     print("\n".join(lines))
 
 
+def summarize_decode(trace_dir, bench_json, command, out_txt):
+    """Per-kernel medians of the 128-sequence decode pair from a rocprofv3 kernel trace, by kernel
+    name and grid (each decode kernel has its own name or grid; the GEMM library's kernels are
+    listed by their own names), ordered by total time."""
+    lines = [f"# rocprofv3 summary: {command['title']}", "# profiled command (repository root, one MI355X):",
+             f"#   {command['trace']}", "# summarized on the host with:", f"#   {command['summary']}", ""]
+    rows = _csv_rows(trace_dir, "kernel_trace.csv")
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3   # noqa: E731
+    groups = {}
+    for r in rows:
+        groups.setdefault((r["Kernel_Name"], _grid(r)), []).append(dur(r))
+    lines.append(f"{'calls':>5} {'median_us':>10} {'total_us':>10}  grid            kernel")
+    for (name, grid), ds in sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:16]:
+        ds = sorted(ds)
+        lines.append(f"{len(ds):>5} {ds[len(ds) // 2]:>10.2f} {sum(ds):>10.0f}  {grid:<15} {name[:90]}")
+    if bench_json and os.path.exists(bench_json):
+        txt = [l for l in open(bench_json).read().splitlines() if l.startswith("{")]
+        if txt:
+            b = json.loads(txt[-1])
+            lines += ["", "## the profiled run's event timings (ms per layer call)",
+                      "  producer: " + ", ".join(f"{k} {v:.4f}" for k, v in b["producer_stage_ms"].items() if v),
+                      "  consumer: " + ", ".join(f"{k} {v:.4f}" for k, v in b["consumer_stage_ms"].items() if v),
+                      f"  {b['ms_per_pair_step'] * 1e3:.1f} us per pair step, "
+                      f"{b['tokens_per_s_per_layer'] / 1e6:.3f} M tokens/s per layer"]
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # --- CPU baseline: the fp64 oracle on a bounded sample ---------------------------------------
 
 def cpu_baseline(budget_s=12.0, max_seqs=3):
@@ -572,7 +600,19 @@ def main():
                     help="time only the Griffin block (8K prefill and B=128 decode); prints its JSON record")
     ap.add_argument("--summarize-griffin", metavar="TRACE_DIR",
                     help="host only: write profiles/kernels_griffin8k_prefill.txt from a kernel trace and exit")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the 128-sequence decode pair; prints its JSON record")
+    ap.add_argument("--summarize-decode", metavar="TRACE_DIR",
+                    help="host only: write profiles/kernels_decode_b128.txt from a kernel trace and exit")
     args = ap.parse_args()
+    if args.summarize_decode:
+        cmd = {"title": "KV-sharing producer/consumer pair of 1.5B-shaped SWA layers, decode of 128 sequences "
+                        "at position 8192 (1024-slot ring + 128 meta keys), bf16",
+               "trace": args.profile_cmd or "(not given)",
+               "summary": "python3 " + shlex.join(os.path.relpath(a) if os.path.exists(a) else a for a in sys.argv)}
+        summarize_decode(args.summarize_decode, args.bench_json, cmd,
+                         os.path.join(ROOT, "profiles", "kernels_decode_b128.txt"))
+        return
     if args.summarize_griffin:
         cmd = {"title": "Griffin recurrent block, 8K prefill (B=16 x 8192, d 1536, d_rnn 2048, bf16)",
                "trace": args.profile_cmd or "(not given)",
@@ -602,6 +642,9 @@ def main():
         copy_probe()
     if args.griffin_only:
         print(json.dumps(bench_griffin(args.steps, args.warmup)), flush=True)
+        return
+    if args.decode_only:
+        print(json.dumps(bench_decode(4, args.steps, args.warmup)), flush=True)
         return
     main_run = bench_prefill(2, args.steps, args.warmup)
     log(f"[bench] 8K SWA prefill: {main_run['tokens_per_s']:.0f} tok/s, {main_run['ms_per_step']:.3f} ms/step")

@@ -120,3 +120,23 @@ def test_griffin_summary_attribution(tmp_path):
     got = {l.split()[0]: float(l.split()[2]) for l in txt.splitlines()
            if l.split() and l.split()[0] in ("in_proj", "conv", "gate_proj", "rglru", "out_proj")}
     assert got == {"in_proj": 1300.0, "conv": 180.0, "gate_proj": 1500.0, "rglru": 660.0, "out_proj": 700.0}
+
+
+def test_decode_summary_groups_by_kernel_and_grid(tmp_path):
+    """Kernels with the same name but different grids (the two projections' GEMMs) stay apart;
+    the median of each group is reported and groups are ordered by total time."""
+    rows, t, d = [], 0, 0
+    for call in range(5):
+        for name, grid, us in [("decode_attn_mfma_kernel<5>", "320", 33 + call), ("rows_gemm_kernel", "1024", 11),
+                               ("rows_gemm_kernel", "2048", 12), ("ssm_step_kernel", "4096", 13)]:
+            rows.append({"Dispatch_Id": str(d), "Kernel_Name": name, "Grid_Size_X": grid, "Grid_Size_Y": "1",
+                         "Grid_Size_Z": "1", "Start_Timestamp": str(t), "End_Timestamp": str(t + us * 1000)})
+            t += us * 1000 + 10
+            d += 1
+    _write(str(tmp_path / "tr" / "h" / "1_kernel_trace.csv"), rows)
+    out = str(tmp_path / "d.txt")
+    bench.summarize_decode(str(tmp_path / "tr"), None, {"title": "t", "trace": "x", "summary": "y"}, out)
+    body = [l.split() for l in open(out).read().splitlines() if l and l[0] == " " or (l and l[0].isdigit())]
+    got = [(r[-1], r[3], int(r[0]), float(r[1])) for r in body if len(r) >= 5]
+    assert got == [("decode_attn_mfma_kernel<5>", "320x1x1", 5, 35.0), ("ssm_step_kernel", "4096x1x1", 5, 13.0),
+                   ("rows_gemm_kernel", "2048x1x1", 5, 12.0), ("rows_gemm_kernel", "1024x1x1", 5, 11.0)]
