@@ -301,26 +301,17 @@ hipError_t rows_dispatch(const SkinnyArgs<WT, XT, OT>& a, hipStream_t s) {
 }  // namespace
 
 // Feature tile: 64 when that gives at least 128 workgroups, else 32 (twice the workgroups, X
-// read twice as often).  No workspace.
+// read twice as often).
 SkinnyPlan skinny_plan(int M, int N, int K) {
   (void)K;
   SkinnyPlan p;
   p.F = ceil_div(N, 64) * ceil_div(M, kRwR) >= 128 ? 64 : 32;
-  p.part_bytes = 0;
   return p;
 }
 
-hipError_t launch_skinny_gemm(const SkinnyArgs<half_t, half_t, half_t>& a, float* part, size_t bytes, hipStream_t s) {
-  (void)part; (void)bytes; return rows_dispatch(a, s);
-}
-hipError_t launch_skinny_gemm(const SkinnyArgs<half_t, bf16_t, half_t>& a, float* part, size_t bytes, hipStream_t s) {
-  (void)part; (void)bytes; return rows_dispatch(a, s);
-}
-hipError_t launch_skinny_gemm(const SkinnyArgs<half_t, half_t, bf16_t>& a, float* part, size_t bytes, hipStream_t s) {
-  (void)part; (void)bytes; return rows_dispatch(a, s);
-}
-hipError_t launch_skinny_gemm(const SkinnyArgs<bf16_t, bf16_t, bf16_t>& a, float* part, size_t bytes, hipStream_t s) {
-  (void)part; (void)bytes; return rows_dispatch(a, s);
-}
+hipError_t launch_skinny_gemm(const SkinnyArgs<half_t, half_t, half_t>& a, hipStream_t s) { return rows_dispatch(a, s); }
+hipError_t launch_skinny_gemm(const SkinnyArgs<half_t, bf16_t, half_t>& a, hipStream_t s) { return rows_dispatch(a, s); }
+hipError_t launch_skinny_gemm(const SkinnyArgs<half_t, half_t, bf16_t>& a, hipStream_t s) { return rows_dispatch(a, s); }
+hipError_t launch_skinny_gemm(const SkinnyArgs<bf16_t, bf16_t, bf16_t>& a, hipStream_t s) { return rows_dispatch(a, s); }
 
 }  // namespace hymba

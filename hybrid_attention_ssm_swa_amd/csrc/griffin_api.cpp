@@ -58,7 +58,7 @@ int32_t check_cfg(const griffin_block_cfg* c) {
 }
 
 struct Ws {
-  size_t x16 = 0, uv = 0, xc = 0, g = 0, hy = 0, gemm = 0, skp = 0, total = 0;
+  size_t x16 = 0, uv = 0, xc = 0, g = 0, hy = 0, gemm = 0, total = 0;
 };
 
 // x16 (bf16 blocks: x in fp16, later y in fp16) | uv | xc | g | hy | GEMM workspace
@@ -72,13 +72,6 @@ Ws layout(const griffin_block_cfg& c, int B, int T) {
   w.g = o;    o += align_up(rows * 2 * R * e);
   w.hy = o;   o += align_up(rows * R * e);
   w.gemm = o; o += is_bf16(c) ? kGemmWorkspaceBytes : 0;
-  // fp32 partial sums of the few-row GEMMs (split K)
-  w.skp = o;
-  if (is_bf16(c) && few_rows(c, static_cast<int64_t>(rows))) {
-    const int M = static_cast<int>(rows), Ri = static_cast<int>(R), Di = static_cast<int>(D);
-    o += align_up(std::max({skinny_plan(M, 2 * Ri, Di).part_bytes, skinny_plan(M, 2 * Ri, Ri).part_bytes,
-                            skinny_plan(M, Di, Ri).part_bytes}));
-  }
   w.total = o;
   return w;
 }
@@ -110,12 +103,12 @@ int32_t project(const griffin_block_cfg& c, const void* X, const void* W, void* 
       SkinnyArgs<half_t, half_t, bf16_t> a{static_cast<const half_t*>(W), in, static_cast<const half_t*>(X), in,
                                            static_cast<bf16_t*>(Y), out, nullptr, 0, 0, 0, static_cast<int>(rows),
                                            static_cast<int>(out), static_cast<int>(in)};
-      e = launch_skinny_gemm(a, reinterpret_cast<float*>(ws + wl.skp), wl.total - wl.skp, s);
+      e = launch_skinny_gemm(a, s);
     } else {
       SkinnyArgs<half_t, half_t, half_t> a{static_cast<const half_t*>(W), in, static_cast<const half_t*>(X), in,
                                            static_cast<half_t*>(Y), out, nullptr, 0, 0, 0, static_cast<int>(rows),
                                            static_cast<int>(out), static_cast<int>(in)};
-      e = launch_skinny_gemm(a, reinterpret_cast<float*>(ws + wl.skp), wl.total - wl.skp, s);
+      e = launch_skinny_gemm(a, s);
     }
     G_HIP_TRY(e, "Griffin projection (few rows) launch");
     return HYMBA_OK;
@@ -202,7 +195,7 @@ int32_t forward(const griffin_block_cfg& c, const griffin_block_weights& w, cons
     SkinnyArgs<half_t, bf16_t, half_t> in{reinterpret_cast<const half_t*>(pw + pl.w_in), D,
                                           static_cast<const bf16_t*>(x), D, uv, 2 * R, nullptr, 0, 0, 0,
                                           static_cast<int>(rows), static_cast<int>(2 * R), static_cast<int>(D)};
-    G_HIP_TRY(launch_skinny_gemm(in, reinterpret_cast<float*>(ws + wl.skp), wl.total - wl.skp, s),
+    G_HIP_TRY(launch_skinny_gemm(in, s),
               "Griffin input projection (few rows) launch");
     G_STATUS_TRY(run<half_t>(c, w, nullptr, pw + pl.w_gate, pw + pl.w_out, nullptr, B, T, y, conv_state, h,
                              conv_state_out, h_out, ws, wl, s, tm, true));

@@ -185,21 +185,9 @@ PersistLayout persist_layout(const hymba_layer_cfg& c) {
 }
 
 struct WsLayout {
-  size_t X16, P, bc32, O, Ao, Ys, F, gemm, part, skp, total;
+  size_t X16, P, bc32, O, Ao, Ys, F, gemm, part, total;
   int64_t rows;
 };
-
-// fp32 partial sums of the few-row GEMMs (split K) of `rows` rows: the largest of the three
-// projections, 0 when they go through hipBLASLt
-size_t skinny_part_bytes(const hymba_layer& L, int64_t rows) {
-  const hymba_layer_cfg& c = L.cfg;
-  if (!is_bf16(c) || rows <= 0 || rows > kSkinnyMaxRows) return 0;
-  const int M = static_cast<int>(rows), hq = c.n_heads * c.head_dim;
-  size_t b = 0;
-  for (auto nk : {std::pair<int, int>(static_cast<int>(L.n_in), c.d_model), {c.d_inner, hq}, {c.d_model, c.d_inner}})
-    if (skinny_fits(M, nk.first, nk.second)) b = std::max(b, skinny_plan(M, nk.first, nk.second).part_bytes);
-  return b;
-}
 
 WsLayout ws_layout(const hymba_layer& L, int64_t batch, int64_t seq) {
   const hymba_layer_cfg& c = L.cfg;
@@ -219,8 +207,6 @@ WsLayout ws_layout(const hymba_layer& L, int64_t batch, int64_t seq) {
   w.gemm = off; off += b16 ? kGemmWorkspaceBytes : 0;
   w.part = off;
   off += align_up((size_t)std::max<int64_t>(batch, 1) * c.n_heads * kDecodeMaxSplits * (c.head_dim + 2) * 4);
-  w.skp = off;
-  off += align_up(std::max(skinny_part_bytes(L, batch * seq), skinny_part_bytes(L, c.n_meta)));
   w.total = off;
   return w;
 }
@@ -238,12 +224,12 @@ int32_t project(const hymba_layer& L, const void* X, int64_t ldx, const void* W,
       SkinnyArgs<bf16_t, bf16_t, bf16_t> a{static_cast<const bf16_t*>(W), ldw, static_cast<const bf16_t*>(X), ldx,
                                            static_cast<bf16_t*>(Y), ldy, nullptr, 0, 0, 0, static_cast<int>(rows),
                                            static_cast<int>(out), static_cast<int>(in)};
-      e = launch_skinny_gemm(a, reinterpret_cast<float*>(ws + wl.skp), wl.total - wl.skp, s);
+      e = launch_skinny_gemm(a, s);
     } else {
       SkinnyArgs<half_t, half_t, half_t> a{static_cast<const half_t*>(W), ldw, static_cast<const half_t*>(X), ldx,
                                            static_cast<half_t*>(Y), ldy, nullptr, 0, 0, 0, static_cast<int>(rows),
                                            static_cast<int>(out), static_cast<int>(in)};
-      e = launch_skinny_gemm(a, reinterpret_cast<float*>(ws + wl.skp), wl.total - wl.skp, s);
+      e = launch_skinny_gemm(a, s);
     }
     HIP_TRY(e, "projection (few rows) launch");
     return HYMBA_OK;
@@ -305,7 +291,7 @@ int32_t in_projection(const hymba_layer& L, const void* x, int64_t rows, char* w
                                          bc32 ? reinterpret_cast<float*>(ws + wl.bc32) : nullptr, 2 * c.d_state,
                                          static_cast<int>(L.off_b), static_cast<int>(L.off_b + 2 * c.d_state),
                                          static_cast<int>(rows), static_cast<int>(L.n_in), c.d_model};
-    HIP_TRY(launch_skinny_gemm(a, reinterpret_cast<float*>(ws + wl.skp), wl.total - wl.skp, s),
+    HIP_TRY(launch_skinny_gemm(a, s),
             "input projection (few rows) launch");
     return HYMBA_OK;
   }
@@ -923,8 +909,8 @@ int32_t hymba_kernel_epilogue(int32_t dtype, const void* ao, int64_t ld_ao, cons
 }
 
 size_t hymba_kernel_gemm_rows_workspace(int32_t M, int32_t N, int32_t K) {
-  if (M <= 0 || N <= 0 || K <= 0) return 0;
-  return skinny_plan(M, N, K).part_bytes;
+  (void)M; (void)N; (void)K;
+  return 0;   // the kernel never splits K across workgroups
 }
 
 int32_t hymba_kernel_gemm_rows(int32_t w_dtype, int32_t x_dtype, int32_t y_dtype, const void* w, int64_t ldw,
@@ -941,29 +927,25 @@ int32_t hymba_kernel_gemm_rows(int32_t w_dtype, int32_t x_dtype, int32_t y_dtype
   if (y32 && (c0 < 0 || c1 > N || c0 > c1 || c0 % 4 || c1 % 4 || ldy32 < c1 - c0 || ldy32 % 4 || !aligned(y32, 16)))
     return fail(HYMBA_ERR_INVALID_ARG, "y32: 0 <= c0 <= c1 <= N multiples of 4, ldy32 >= c1 - c0 (of 4), aligned");
   if (M == 0) return HYMBA_OK;
-  const size_t need = skinny_plan(M, N, K).part_bytes;
-  if (workspace_bytes < need || (need && !workspace))
-    return fail(HYMBA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-  if (need && !aligned(workspace, 16)) return fail(HYMBA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  float* part = static_cast<float*>(workspace);
+  (void)workspace; (void)workspace_bytes;   // none needed (hymba_kernel_gemm_rows_workspace is 0)
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (w_dtype == HYMBA_F16 && x_dtype == HYMBA_F16 && y_dtype == HYMBA_F16) {
     SkinnyArgs<half_t, half_t, half_t> a{static_cast<const half_t*>(w), ldw, static_cast<const half_t*>(x), ldx,
                                          static_cast<half_t*>(y), ldy, y32, ldy32, c0, c1, M, N, K};
-    e = launch_skinny_gemm(a, part, workspace_bytes, s);
+    e = launch_skinny_gemm(a, s);
   } else if (w_dtype == HYMBA_F16 && x_dtype == HYMBA_BF16 && y_dtype == HYMBA_F16) {
     SkinnyArgs<half_t, bf16_t, half_t> a{static_cast<const half_t*>(w), ldw, static_cast<const bf16_t*>(x), ldx,
                                          static_cast<half_t*>(y), ldy, y32, ldy32, c0, c1, M, N, K};
-    e = launch_skinny_gemm(a, part, workspace_bytes, s);
+    e = launch_skinny_gemm(a, s);
   } else if (w_dtype == HYMBA_F16 && x_dtype == HYMBA_F16 && y_dtype == HYMBA_BF16) {
     SkinnyArgs<half_t, half_t, bf16_t> a{static_cast<const half_t*>(w), ldw, static_cast<const half_t*>(x), ldx,
                                          static_cast<bf16_t*>(y), ldy, y32, ldy32, c0, c1, M, N, K};
-    e = launch_skinny_gemm(a, part, workspace_bytes, s);
+    e = launch_skinny_gemm(a, s);
   } else if (w_dtype == HYMBA_BF16 && x_dtype == HYMBA_BF16 && y_dtype == HYMBA_BF16) {
     SkinnyArgs<bf16_t, bf16_t, bf16_t> a{static_cast<const bf16_t*>(w), ldw, static_cast<const bf16_t*>(x), ldx,
                                          static_cast<bf16_t*>(y), ldy, y32, ldy32, c0, c1, M, N, K};
-    e = launch_skinny_gemm(a, part, workspace_bytes, s);
+    e = launch_skinny_gemm(a, s);
   } else {
     return fail(HYMBA_ERR_UNSUPPORTED, "unsupported (w, x, y) type combination");
   }

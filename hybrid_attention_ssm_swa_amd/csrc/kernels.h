@@ -188,18 +188,14 @@ struct SkinnyArgs {
   float* y32; int64_t ldy32; int c0; int c1;
   int M; int N; int K;
 };
-// Launch plan: feature tile F (64 or 32); part_bytes of workspace (none with the current kernel,
-// which never splits K across workgroups).
-struct SkinnyPlan { int F = 64; size_t part_bytes = 0; };
+// Launch plan: feature tile F (64 or 32).  The kernel needs no workspace: K is never split
+// across workgroups.
+struct SkinnyPlan { int F = 64; };
 SkinnyPlan skinny_plan(int M, int N, int K);
-hipError_t launch_skinny_gemm(const SkinnyArgs<half_t, half_t, half_t>& a, float* part, size_t part_bytes,
-                              hipStream_t s);
-hipError_t launch_skinny_gemm(const SkinnyArgs<half_t, bf16_t, half_t>& a, float* part, size_t part_bytes,
-                              hipStream_t s);
-hipError_t launch_skinny_gemm(const SkinnyArgs<half_t, half_t, bf16_t>& a, float* part, size_t part_bytes,
-                              hipStream_t s);
-hipError_t launch_skinny_gemm(const SkinnyArgs<bf16_t, bf16_t, bf16_t>& a, float* part, size_t part_bytes,
-                              hipStream_t s);
+hipError_t launch_skinny_gemm(const SkinnyArgs<half_t, half_t, half_t>& a, hipStream_t s);
+hipError_t launch_skinny_gemm(const SkinnyArgs<half_t, bf16_t, half_t>& a, hipStream_t s);
+hipError_t launch_skinny_gemm(const SkinnyArgs<half_t, half_t, bf16_t>& a, hipStream_t s);
+hipError_t launch_skinny_gemm(const SkinnyArgs<bf16_t, bf16_t, bf16_t>& a, hipStream_t s);
 constexpr int kSkinnyMaxRows = 256;   // the callers use it up to this many rows
 // ... and for weights up to this size: a larger weight (the 1.5B layer's 36 MB input
 // projection) goes through the library GEMM, about twice as fast there as through this
