@@ -726,6 +726,7 @@ int32_t hymba_mixer_decode(hymba_layer* L, const void* x_t, const int64_t* pos, 
   if (!x_t || !y_t || !pos || !ssm_state || !ws)
     return fail(HYMBA_ERR_INVALID_ARG, "x_t, pos, y_t, ssm_state and workspace must be non-NULL");
   if (B < 1) return fail(HYMBA_ERR_INVALID_ARG, "B must be >= 1");
+  if (B > 65535) return fail(HYMBA_ERR_UNSUPPORTED, "a decode step takes at most 65535 sequences (got %d)", B);
   if (!kv || !kv->k_cache || !kv->v_cache) return fail(HYMBA_ERR_INVALID_ARG, "decode needs kv->k_cache and kv->v_cache");
   const hymba_layer_cfg& c = L->cfg;
   if (kv->cache_len < 1) return fail(HYMBA_ERR_INVALID_ARG, "cache_len must be >= 1");

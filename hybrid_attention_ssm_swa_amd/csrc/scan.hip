@@ -195,17 +195,16 @@ __global__ __launch_bounds__(64 * (N / NS)) void selective_scan_kernel(
 
 // Decode: one token per sequence.  N/4 consecutive lanes share a channel, each
 // owning 4 states (one 16-byte state load and store); y is reduced across them.
+// grid (ceil(E * N/4 / 256), B): no division by a runtime size in the index math.
 template <typename T, int N>
 __global__ __launch_bounds__(256) void ssm_step_kernel(StepArgs<T> a) {
   constexpr int LPC = N / 4;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)a.B * a.E * LPC;
-  const bool active = gid < total;
-  const int64_t g2 = active ? gid : total - 1;
-  const int q = static_cast<int>(g2 % LPC);
-  const int64_t ch = g2 / LPC;
-  const int c = static_cast<int>(ch % a.E);
-  const int64_t b = ch / a.E;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;   // lane within the sequence
+  const bool active = i < a.E * LPC;
+  const int i2 = active ? i : a.E * LPC - 1;
+  const int q = i2 % LPC, c = i2 / LPC;
+  const int64_t b = blockIdx.y;
+  const int64_t ch = b * a.E + c;
   const T* row = a.bc + b * a.ld;
   const float uv = Elem<T>::load(a.u + b * a.ld + c);
   const float dv = Elem<T>::load(a.dt + b * a.ld + c);
@@ -270,8 +269,9 @@ hipError_t scan_dispatch(const ScanArgs<T>& a, hipStream_t s) {
 
 template <typename T>
 hipError_t step_dispatch(const StepArgs<T>& a, hipStream_t s) {
-  const int64_t lanes = (int64_t)a.B * a.E * (a.N / 4);
-  dim3 grid(static_cast<unsigned>(ceil_div(lanes, 256))), block(256);
+  if (a.B <= 0) return hipSuccess;
+  if (a.B > 65535 || (int64_t)a.E * (a.N / 4) >= INT32_MAX) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(ceil_div((int64_t)a.E * (a.N / 4), 256)), static_cast<unsigned>(a.B)), block(256);
   switch (a.N) {
     case 8: hipLaunchKernelGGL((ssm_step_kernel<T, 8>), grid, block, 0, s, a); break;
     case 16: hipLaunchKernelGGL((ssm_step_kernel<T, 16>), grid, block, 0, s, a); break;

@@ -176,7 +176,8 @@ int32_t hymba_mixer_prefill(hymba_layer* layer, const void* x, int32_t B, int32_
  * pos[b] (device int64 [B]).  ssm_state [B, E, N] fp32 holds the state after
  * token pos-1 and is updated in place.  A producer writes its new K/V into
  * slot pos mod cache_len before attending; the consumer of the pair must be
- * called after it with the same kv. */
+ * called after it with the same kv.  1 <= B <= 65535 (HYMBA_ERR_UNSUPPORTED
+ * above: the sequence index is a launch grid dimension). */
 int32_t hymba_mixer_decode(hymba_layer* layer, const void* x_t, const int64_t* pos, int32_t B,
                            void* y_t, const hymba_kv* kv, float* ssm_state, void* workspace,
                            size_t workspace_bytes, void* stream);

@@ -169,6 +169,9 @@ def test_hot_calls_validate_before_device_work():
         with pytest.raises(L.HymbaError) as e:     # no cache at all
             L.hymba_mixer_decode(h, FAKE, FAKE, 1, FAKE, None, FAKE, FAKE, 1 << 30, None)
         assert e.value.status == L.HYMBA_ERR_INVALID_ARG
+        with pytest.raises(L.HymbaError) as e:     # more sequences than a launch grid dimension holds
+            L.hymba_mixer_decode(h, FAKE, FAKE, 65536, FAKE, kv, FAKE, FAKE, 1 << 30, None)
+        assert e.value.status == L.HYMBA_ERR_UNSUPPORTED
         with pytest.raises(L.HymbaError) as e:
             L.hymba_layer_meta_outputs(h)          # not prepared yet
         assert e.value.status == L.HYMBA_ERR_INVALID_ARG
