@@ -1,6 +1,8 @@
 // Tile machinery of the MFMA attention kernels (prefill and decode): 64-key
-// tiles of K rows and transposed V in LDS, and one wave's online-softmax step
-// over a tile for 32 query columns with v_mfma_f32_32x32x16_{f16,bf16}.
+// tiles of K and V rows in LDS, and one wave's online-softmax step over a tile
+// for 32 query columns with v_mfma_f32_32x32x16_{f16,bf16}.  V is stored as it
+// comes (key rows) and read back transposed by ds_read_b64_tr_b16 as the A
+// operand of the P.V product.
 //
 // Scores are computed transposed (S^T = K Q^T) so each lane owns one query
 // column and 16 keys of a 32-key block: the softmax max needs one exchange
@@ -16,8 +18,13 @@ namespace attn {
 constexpr int kHd = 64;          // head dim of the MFMA kernel
 constexpr int kQB = 32;          // queries per wave (one MFMA column block)
 constexpr int kKT = 64;          // keys per tile
-constexpr int kKStr = kHd + 8;   // LDS row stride (bf16) of K tiles: 144 B
-constexpr int kVStr = kKT + 4;   // LDS row stride (bf16) of V^T window tiles: 136 B
+constexpr int kKStr = kHd + 8;   // LDS row stride (16-bit words) of K tiles: 144 B
+// LDS row strides of V tiles, chosen so that the transposed reads hit 64 distinct banks:
+// with 32x32 fragments a read's two 16-lane groups take 4 rows at dims d and d + 16
+// (row stride 192 B: rows fall 48 banks apart), with 16x16 fragments its groups take
+// 8 consecutive rows at the same dims (160 B: 40 banks apart).
+constexpr int kVStr = kHd + 32;      // 192 B, the prefill tile step (32x32 fragments)
+constexpr int kVStr16 = kHd + 16;    // 160 B, the decode tile step (16x16 fragments)
 constexpr float kLazyLog2 = 8.f;   // rescale threshold of the online softmax (log2 units)
 
 struct __align__(16) U4 { uint32_t x, y, z, w; };
@@ -40,15 +47,15 @@ __device__ __forceinline__ typename Op<ET>::vec as_vec(U4 v) { return __builtin_
 
 // 16-bit elements stored as raw 16-bit words; a double-buffered stage of 64-key tiles
 struct AttnSmem {
-  uint16_t kw[2][kKT * kKStr];        // K tiles   [key][dim]
-  uint16_t vw[2][kHd * kVStr];        // V^T tiles [dim][key]
+  uint16_t kw[2][kKT * kKStr];        // K tiles [key][dim]
+  uint16_t vw[2][kKT * kVStr];        // V tiles [key][dim]
 };
 
-// Cooperative load of a 64-key tile (K rows straight, V transposed) spread
-// over the workgroup's 256 threads, four 16-byte loads each: threads
-// [0, 128) own K chunks tid + 128 j (j < 4) of the tile's 512 (64 rows x 8
-// chunks); threads [128, 256) own a 4-key x 8-dim block of V.  Rows beyond
-// `nvalid` (>= 1) read a clamped, valid row and are zero-filled by value.
+// Cooperative load of a 64-key tile spread over the workgroup's 256 threads,
+// four 16-byte loads each: threads [0, 128) own K chunks tid + 128 j (j < 4)
+// of the tile's 512 (64 rows x 8 chunks), threads [128, 256) the same chunks
+// of V.  Rows beyond `nvalid` (>= 1) read a clamped, valid row and are
+// zero-filled by value.
 
 __device__ __forceinline__ uint32_t u4_get(const U4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -64,33 +71,31 @@ __device__ __forceinline__ U4 masked_load(const void* p, bool keep) {
   return r;
 }
 
+// chunks it + 128 j (j < 4) of a tile: row (it >> 3) + 16 j, dims 8 (it & 7) + 0..7.  Stored
+// field by field: a plain struct copy from the fetch registers to LDS stays a memory-to-memory
+// copy that the compiler routes through scratch.
+__device__ __forceinline__ void chunk_store(const U4 (&r)[4], uint16_t* base, int str, int it) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    *reinterpret_cast<uint4*>(base + ((it >> 3) + 16 * j) * str + (it & 7) * 8) =
+        make_uint4(r[j].x, r[j].y, r[j].z, r[j].w);
+}
+
+// item < 128: K chunks into ks; item >= 128: the same chunks of V into vs (a branch, not a
+// pointer select: the item is wave-uniform in K/V at every call)
 __device__ __forceinline__ void item_store(const U4 (&r)[4], uint16_t* ks, uint16_t* vs, int vstr, int key_off,
                                            int item) {
-  if (item < 128) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = item + j * 128;
-      const int row = c >> 3, col = (c & 7) * 8;
-      *reinterpret_cast<U4*>(ks + (key_off + row) * kKStr + col) = r[j];
-    }
-  } else {
-    // transpose 4 keys x 8 dims -> 8 rows (dims) of 4 consecutive keys
-    const int it = item - 128;
-    const int key0 = key_off + (it >> 3) * 4, dim0 = (it & 7) * 8;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      // dims dim0+2p (low halves) and dim0+2p+1 (high halves)
-      const uint32_t a = u4_get(r[0], p), b = u4_get(r[1], p);
-      const uint32_t c = u4_get(r[2], p), d = u4_get(r[3], p);
-      uint2 lo, hi;
-      lo.x = __builtin_amdgcn_perm(b, a, 0x05040100u);   // (a.lo, b.lo)
-      lo.y = __builtin_amdgcn_perm(d, c, 0x05040100u);
-      hi.x = __builtin_amdgcn_perm(b, a, 0x07060302u);   // (a.hi, b.hi)
-      hi.y = __builtin_amdgcn_perm(d, c, 0x07060302u);
-      *reinterpret_cast<uint2*>(vs + (dim0 + 2 * p) * vstr + key0) = lo;
-      *reinterpret_cast<uint2*>(vs + (dim0 + 2 * p + 1) * vstr + key0) = hi;
-    }
-  }
+  if (item < 128) chunk_store(r, ks + key_off * kKStr, kKStr, item);
+  else chunk_store(r, vs + key_off * vstr, vstr, item - 128);
+}
+
+// 4 keys x 1 dim of a V tile [key][dim] (row stride vstr) per lane, transposed by the LDS: the
+// 16 lanes of a group read 4 rows x 16 dims (lane j: row j / 4, dims 4 (j % 4) + 0..3 from p)
+// and lane i receives dim i of the 4 rows, keys in order.
+__device__ __forceinline__ uint2 v_tr4(const uint16_t* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                       (__attribute__((address_space(3))) v4s*)(const_cast<uint16_t*>(p))));
 }
 
 // The calling thread's item (tid < 256) of the tile whose first row is at
@@ -104,11 +109,11 @@ struct TileRegs {
 template <typename ET>
 __device__ __forceinline__ void tile_fetch(TileRegs& t, const ET* __restrict__ kbase,
                                            const ET* __restrict__ vbase, int ld, int nvalid, int tid) {
-  const bool is_k = tid < 128;                       // waves 0-1: K chunks; waves 2-3: V blocks
+  const bool is_k = tid < 128;                       // waves 0-1: K chunks; waves 2-3: V chunks
   const ET* base = is_k ? kbase : vbase;
-  const int it = is_k ? tid : tid - 128;
-  const int row0 = is_k ? (it >> 3) : (it >> 3) * 4;
-  const int rstep = is_k ? 16 : 1;
+  const int it = tid & 127;
+  const int row0 = it >> 3;
+  constexpr int rstep = 16;
   const int col = (it & 7) * 8;
   if (nvalid >= kKT) {
     const char* b = reinterpret_cast<const char*>(base);
@@ -156,7 +161,7 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 }
 
 // One 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-// ks: [64][kKStr] K rows; vs: [64 dims][vstr] V^T; key0: first key index of
+// ks: [64][kKStr] K rows; vs: [64][vstr] V rows; key0: first key index of
 // the tile in the mask's coordinates.  With `mask`, key j is kept iff
 // lo_key <= j < hi_key and, for tq >= 0 (a real query tq), j <= tq and
 // (win <= 0 or j > tq - win).
@@ -236,14 +241,17 @@ __device__ __forceinline__ void attend_tile(WaveState& st, const typename Op<ET>
   }
   st.l += psum;
   // O^T[dim][q] += sum_k V^T[dim][k] P^T[k][q]; PV k-step s covers tile keys
-  // [16 s, 16 s + 16); k-index 8 h + j <-> key 16 s + 8 (j/4) + 4 h + j%4.
+  // [16 s, 16 s + 16); k-index 8 h + j <-> key 16 s + 8 (j/4) + 4 h + j%4.  The A
+  // fragment (lane l: dim 32 db + l % 32) comes from two transposed reads of 4 keys:
+  // lane group g = l / 16 reads rows 16 s + 4 h (+ 8) + (l % 16) / 4 at dims
+  // 32 db + 16 (g % 2) + 4 (l % 4).
+  const uint16_t* vlane = vs + (4 * half + ((lane & 15) >> 2)) * vstr + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
   for (int db = 0; db < 2; ++db) {
-    const uint16_t* vrow = vs + (db * 32 + col) * vstr + 4 * half;
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 16 * s4);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 * s4 + 8);
+      const uint2 lo = v_tr4(vlane + 16 * s4 * vstr + 32 * db);
+      const uint2 hi = v_tr4(vlane + (16 * s4 + 8) * vstr + 32 * db);
       U4 w = {lo.x, lo.y, hi.x, hi.y};
       st.acc[db] = Op<ET>::mfma(as_vec<ET>(w), pf[s4], st.acc[db]);
     }

@@ -258,7 +258,7 @@ __device__ __forceinline__ float sum_xor16(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One 64-key tile (K rows ks [64][kKStr], V^T vs [64 dims][kVStr]) for 16 query columns: S^T =
+// One 64-key tile (K rows ks [64][kKStr], V rows vs [64][kVStr16]) for 16 query columns: S^T =
 // K Q^T in four 16-key blocks, online softmax (lazy rescale as in the prefill step), O^T +=
 // V^T P^T in two 32-key steps.  Keys from nvalid on are masked.  The lane's scores s[kb][r] are
 // keys 16 kb + 4 q + r (q = lane/16); as the B operand of PV step m they fill k-slots 8 q + j =
@@ -321,13 +321,16 @@ __device__ __forceinline__ void attend_tile16(WaveState16& st, const attn::U4 (&
     pf[m2].w = pack_f16x2(p[6], p[7]);
   }
   st.l += psum;
+  // A fragment (lane l: dim 16 db + l % 16, keys 32 m + 4 q + 0..3 and 32 m + 16 + 4 q + 0..3) from
+  // two transposed reads: lane group q reads rows 32 m + 4 q (+ 16) + (l % 16) / 4, dims
+  // 16 db + 4 (l % 4).
+  const uint16_t* vlane = vs + (4 * q + ((lane & 15) >> 2)) * kVStr16 + 4 * (lane & 3);
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
-    const uint16_t* vrow = vs + (16 * db + col) * kVStr + 4 * q;
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2) {
-      const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 32 * m2);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 32 * m2 + 16);
+      const uint2 lo = v_tr4(vlane + 32 * m2 * kVStr16 + 16 * db);
+      const uint2 hi = v_tr4(vlane + (32 * m2 + 16) * kVStr16 + 16 * db);
       st.acc[db] = mfma16(U4{lo.x, lo.y, hi.x, hi.y}, pf[m2], st.acc[db]);
     }
   }
@@ -345,7 +348,7 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecAttnArgs<half_t
   using namespace attn;
   static_assert(G >= 1 && G <= 16, "query heads of a KV group must fit 16 columns");
   __shared__ __align__(16) uint16_t ks[kKT * kKStr];
-  __shared__ __align__(16) uint16_t vs[kHd * kVStr];
+  __shared__ __align__(16) uint16_t vs[kKT * kVStr16];
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
   const int C = a.cache_len;
@@ -384,7 +387,7 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecAttnArgs<half_t
     return (ring + slot) * kHd;
   };
   // a lane's 16 loads of the tile starting at key t0 with nvalid keys: items lane and lane + 64
-  // of the K chunks (4 rows 16 apart each) and of the V blocks (4 consecutive keys x 8 dims);
+  // of the K chunks and of the V chunks (each 4 rows 16 apart);
   // rows past nvalid read the last valid row (their scores are masked)
   auto fetch = [&](int t0, int nvalid, U4 (&kr)[2][4], U4 (&vr)[2][4]) {
     // A full tile wholly in the meta rows, or wholly in one unwrapped stretch of the ring, is a
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecAttnArgs<half_t
         for (int j = 0; j < 4; ++j) {
           const int col = (item & 7) * 8;
           kr[it][j] = *reinterpret_cast<const U4*>(kb + ((item >> 3) + 16 * j) * stride + col);
-          vr[it][j] = *reinterpret_cast<const U4*>(vb + ((item >> 3) * 4 + j) * stride + col);
+          vr[it][j] = *reinterpret_cast<const U4*>(vb + ((item >> 3) + 16 * j) * stride + col);
         }
       }
       return;
@@ -419,7 +422,7 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecAttnArgs<half_t
         const int krow = (item >> 3) + 16 * j, kcol = (item & 7) * 8;
         const int64_t ko = row_off(t0 + min(krow, nvalid - 1));
         kr[it][j] = *reinterpret_cast<const U4*>((ko < 0 ? a.k_meta + (-1 - ko) : a.k_cache + ko) + kcol);
-        const int vrow = (item >> 3) * 4 + j, vcol = (item & 7) * 8;
+        const int vrow = (item >> 3) + 16 * j, vcol = (item & 7) * 8;
         const int64_t vo = row_off(t0 + min(vrow, nvalid - 1));
         vr[it][j] = *reinterpret_cast<const U4*>((vo < 0 ? a.v_meta + (-1 - vo) : a.v_cache + vo) + vcol);
       }
@@ -428,8 +431,8 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecAttnArgs<half_t
   auto stage = [&](const U4 (&kr)[2][4], const U4 (&vr)[2][4]) {
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-      item_store(kr[it], ks, vs, kVStr, 0, lane + 64 * it);         // K chunks
-      item_store(vr[it], ks, vs, kVStr, 0, 128 + lane + 64 * it);   // V blocks, transposed
+      chunk_store(kr[it], ks, kKStr, lane + 64 * it);     // K chunks
+      chunk_store(vr[it], vs, kVStr16, lane + 64 * it);   // V chunks
     }
     __syncthreads();
   };
