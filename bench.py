@@ -134,15 +134,19 @@ def scan_alu_entry(s, B, T, ms):
 
 # --- traffic measured by rocprofv3 counters (optional, committed under profiles/) ---------
 
-# source whose change invalidates a stage's recorded counters (GEMMs: the plan selection code)
-KERNEL_SOURCES = {"attention": "attn_prefill.hip", "ssm": "scan.hip", "epilogue": "epilogue.hip",
-                  "in_proj": "gemm_blaslt.cpp", "w_o": "gemm_blaslt.cpp", "out_proj": "gemm_blaslt.cpp",
-                  "convert": "convert.hip", "kv_write": "decode.hip"}
+# sources whose change invalidates a stage's recorded counters: the kernel file and the tile
+# headers it includes (GEMMs: the plan selection code)
+KERNEL_SOURCES = {"attention": ("attn_prefill.hip", "attn_tile.h"), "ssm": ("scan.hip",),
+                  "epilogue": ("epilogue.hip",), "in_proj": ("gemm_blaslt.cpp",), "w_o": ("gemm_blaslt.cpp",),
+                  "out_proj": ("gemm_blaslt.cpp",), "convert": ("convert.hip",),
+                  "kv_write": ("decode.hip", "attn_tile.h")}
 
 
 def source_sha(stage):
-    src = KERNEL_SOURCES[stage]
-    return hashlib.sha256(open(os.path.join(ROOT, "hybrid_attention_ssm_swa_amd", "csrc", src), "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for src in KERNEL_SOURCES[stage]:
+        h.update(open(os.path.join(ROOT, "hybrid_attention_ssm_swa_amd", "csrc", src), "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(stage):
