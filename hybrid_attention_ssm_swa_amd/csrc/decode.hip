@@ -474,24 +474,76 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecAttnArgs<half_t
 }
 
 // grid B * H, block hd threads: merge the split partials of one (sequence, head).
+// One block per (sequence, head): thread t takes dim t % hd of the splits g, g + G, ... (group
+// g = t / hd of G = blockDim / hd, about one group per 8 splits), merged online (running max, rescaled sums) eight splits at a
+// time with all their loads issued first; the groups then meet in LDS in group order.  A split
+// with no keys carries a max of -inf or a huge negative one, and weight 0.
+constexpr int kCombineThreads = 256;   // at most; a multiple of every supported head dim
 template <typename T>
-__global__ __launch_bounds__(kDecodeMaxHd) void decode_combine_kernel(DecAttnArgs<T> a) {
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecAttnArgs<T> a) {
+  __shared__ float3 red[kCombineThreads];
   const int bh = blockIdx.x;
-  const int d = threadIdx.x;
-  const int hd = a.head_dim;
-  if (d >= hd) return;
+  const int hd = a.head_dim, G = blockDim.x / hd;
+  const int d = threadIdx.x % hd, g = threadIdx.x / hd;
   const float* part = a.part + (int64_t)bh * a.splits * (hd + 2);
-  float m = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) m = fmaxf(m, part[s * (hd + 2) + hd]);
-  float num = 0.f, den = 0.f;
-  for (int s = 0; s < a.splits; ++s) {
-    const float* ps = part + s * (hd + 2);
-    const float w = fast_exp2(ps[hd] - m);
-    num = fmaf(w, ps[d], num);
-    den = fmaf(w, ps[hd + 1], den);
+  float M = -INFINITY, num = 0.f, den = 0.f;
+  auto merge = [&](float mb, float (&mv)[8], float (&ov)[8], float (&lv)[8], int n) {
+    const float mn = fmaxf(M, mb);
+    if (mn == -INFINITY) return;
+    const float sc = M == mn ? 1.f : fast_exp2(M - mn);
+    num *= sc;
+    den *= sc;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < n) {
+        const float w = fast_exp2(mv[j] - mn);   // mv = -inf gives 0
+        num = fmaf(w, ov[j], num);
+        den = fmaf(w, lv[j], den);
+      }
+    }
+    M = mn;
+  };
+  for (int s0 = g; s0 < a.splits; s0 += 8 * G) {
+    float mv[8], ov[8], lv[8];
+    float mb = -INFINITY;
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int s = s0 + j * G;
+      mv[j] = -INFINITY; ov[j] = 0.f; lv[j] = 0.f;
+      if (s < a.splits) {
+        const float* ps = part + (int64_t)s * (hd + 2);
+        mv[j] = ps[hd];
+        ov[j] = ps[d];
+        lv[j] = ps[hd + 1];
+        n = j + 1;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mb = fmaxf(mb, mv[j]);
+    merge(mb, mv, ov, lv, n);
+  }
+  red[threadIdx.x] = make_float3(M, num, den);
+  __syncthreads();
+  if (g != 0) return;
+  for (int k = 1; k < G; ++k) {
+    const float3 o = red[k * hd + d];
+    const float mn = fmaxf(M, o.x);
+    if (mn == -INFINITY) continue;
+    const float s1 = M == mn ? 1.f : fast_exp2(M - mn), s2 = o.x == mn ? 1.f : fast_exp2(o.x - mn);
+    num = num * s1 + o.y * s2;
+    den = den * s1 + o.z * s2;
+    M = mn;
   }
   const int b = bh / a.n_heads, h = bh % a.n_heads;
   Elem<T>::store(a.o + (int64_t)b * a.ld_o + h * hd + d, num / den);
+}
+
+// groups of head_dim threads: about one per 8 splits, at most kCombineThreads threads
+template <typename T>
+unsigned combine_threads(const DecAttnArgs<T>& a) {
+  const int gmax = kCombineThreads / a.head_dim;
+  return static_cast<unsigned>(a.head_dim * std::min(gmax, std::max(1, (a.splits + 7) / 8)));
 }
 
 template <typename T>
@@ -544,7 +596,7 @@ hipError_t dec_dispatch(const DecAttnArgs<T>& a, hipStream_t s) {
     if (a.head_dim == 64) {
       e = dec_dispatch_mfma(a, s);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((decode_combine_kernel<T>), dim3(a.B * a.n_heads), dim3(kDecodeMaxHd), 0, s, a);
+      hipLaunchKernelGGL((decode_combine_kernel<T>), dim3(a.B * a.n_heads), dim3(combine_threads(a)), 0, s, a);
       return hipGetLastError();
     }
   }
@@ -552,7 +604,7 @@ hipError_t dec_dispatch(const DecAttnArgs<T>& a, hipStream_t s) {
   else if (a.head_dim == 32) e = dec_dispatch_hd<T, 32>(a, s);
   else return hipErrorInvalidValue;
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<T>), dim3(a.B * a.n_heads), dim3(kDecodeMaxHd), 0, s, a);
+  hipLaunchKernelGGL((decode_combine_kernel<T>), dim3(a.B * a.n_heads), dim3(combine_threads(a)), 0, s, a);
   return hipGetLastError();
 }
 
