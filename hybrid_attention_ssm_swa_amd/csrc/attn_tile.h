@@ -19,11 +19,12 @@ constexpr int kHd = 64;          // head dim of the MFMA kernel
 constexpr int kQB = 32;          // queries per wave (one MFMA column block)
 constexpr int kKT = 64;          // keys per tile
 constexpr int kKStr = kHd + 8;   // LDS row stride (16-bit words) of K tiles: 144 B
-// LDS row strides of V tiles, chosen so that the transposed reads hit 64 distinct banks:
-// with 32x32 fragments a read's two 16-lane groups take 4 rows at dims d and d + 16
-// (row stride 192 B: rows fall 48 banks apart), with 16x16 fragments its groups take
-// 8 consecutive rows at the same dims (160 B: 40 banks apart).
-constexpr int kVStr = kHd + 32;      // 192 B, the prefill tile step (32x32 fragments)
+// LDS row strides of V tiles.  With 32x32 fragments a transposed read's two 16-lane groups
+// take 4 rows at dims d and d + 16; a 192 B stride would make that conflict-free, but the
+// prefill stage then needs 43 KB instead of 37 KB per workgroup, and the kernel measured
+// faster with K's 144 B stride and some 2-way conflicts.  With 16x16 fragments (decode) a
+// read's groups take 8 consecutive rows at the same dims: 160 B puts them 40 banks apart.
+constexpr int kVStr = kKStr;         // 144 B, the prefill tile step (32x32 fragments)
 constexpr int kVStr16 = kHd + 16;    // 160 B, the decode tile step (16x16 fragments)
 constexpr float kLazyLog2 = 8.f;   // rescale threshold of the online softmax (log2 units)
 
