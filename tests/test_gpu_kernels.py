@@ -133,7 +133,9 @@ def test_selective_scan_kernel(dtype, B, T, E, N, with_h0):
 
 
 @pytest.mark.parametrize("dtype,rows,E", [("f16", 37, 3200), ("f16", 5, 64), ("f16", 3, 8200), ("f16", 4, 2048),
-                                          ("f16", 2, 4104), ("f32", 19, 136), ("f32", 3, 2056)])
+                                          ("f16", 2, 4104), ("f32", 19, 136), ("f32", 3, 2056),
+                                          # thousands of rows (workgroups over the whole grid)
+                                          ("f16", 4099, 3200), ("f32", 9003, 136)])
 def test_epilogue_kernel(dtype, rows, E):
     announce(f"epilogue {dtype} rows={rows} E={E}")
     r = np.random.Generator(np.random.PCG64(300 + rows + E))
