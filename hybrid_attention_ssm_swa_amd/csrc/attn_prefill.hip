@@ -94,18 +94,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     }
   };
 
-  // Q^T fragments: k-step s holds dims 16 s + 8 (lane/32) .. +7 of query tq
+  // Q^T fragments: k-step s holds dims 16 s + 8 (lane/32) .. +7 of query tq (fp16: prescaled
+  // by log2(e)/sqrt(hd), so that scores come out in log2 units)
   typename Op<ET>::vec qf[4];
   {
     const ET* qrow = a.q + ((int64_t)b * a.T + tq) * a.ld_q + h * kHd + (lane >> 5) * 8;
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) qf[s4] = as_vec<ET>(*reinterpret_cast<const U4*>(qrow + s4 * 16));
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const U4 r = *reinterpret_cast<const U4*>(qrow + s4 * 16);
+      if constexpr (!Op<ET>::kLog2Scores) {
+        qf[s4] = as_vec<ET>(r);
+        continue;
+      }
+      U4 w;
+      w.x = Pair<ET>::pack(Pair<ET>::lo(r.x) * sc, Pair<ET>::hi(r.x) * sc);
+      w.y = Pair<ET>::pack(Pair<ET>::lo(r.y) * sc, Pair<ET>::hi(r.y) * sc);
+      w.z = Pair<ET>::pack(Pair<ET>::lo(r.z) * sc, Pair<ET>::hi(r.z) * sc);
+      w.w = Pair<ET>::pack(Pair<ET>::lo(r.w) * sc, Pair<ET>::hi(r.w) * sc);
+      qf[s4] = as_vec<ET>(w);
+    }
   }
   WaveState st;
   st.acc[0] = f32x16_t{};
   st.acc[1] = f32x16_t{};
-  st.m = -1e30f;
+  st.m = -INFINITY;
   st.l = 0.f;
+  st.bias = (lane >> 5) ? 0u : Pair<ET>::pack(INFINITY, 0.f);
 
   TileRegs pre;
   fetch(pre, 0);
@@ -128,7 +142,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       key0 = t0; lo_key = t0; hi_key = hi; tqm = tq;
       mask = !((t0 + kKT - 1 <= qa) && (a.window <= 0 || t0 > qlast - a.window) && (t0 + kKT <= hi));
     }
-    attend_tile<ET>(st, qf, sm.kw[buf], sm.vw[buf], kVStr, sc, lane, key0, lo_key, hi_key, tqm, a.window, mask);
+    attend_tile<ET>(st, qf, sm.kw[buf], sm.vw[buf], kVStr, sc, lane, key0, lo_key, hi_key, tqm, a.window, mask, i == 0);
   }
 
   if (wave_active) {

@@ -10,6 +10,8 @@
 // without any cross-lane movement.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace hymba {
@@ -26,21 +28,41 @@ constexpr int kKStr = kHd + 8;   // LDS row stride (16-bit words) of K tiles: 14
 // read's groups take 8 consecutive rows at the same dims: 160 B puts them 40 banks apart.
 constexpr int kVStr = kKStr;         // 144 B, the prefill tile step (32x32 fragments)
 constexpr int kVStr16 = kHd + 16;    // 160 B, the decode tile step (16x16 fragments)
-constexpr float kLazyLog2 = 8.f;   // rescale threshold of the online softmax (log2 units)
+constexpr float kLazyLog2 = 8.f;   // rescale threshold of the decode tile's online softmax (log2 units)
 
 struct __align__(16) U4 { uint32_t x, y, z, w; };
 
 template <typename ET> struct Op;
 template <> struct Op<half_t> {
   typedef f16x8_t vec;
+  typedef f16x4_t vec4;
+  // Q is prescaled by log2(e)/sqrt(hd) and rounded to fp16 once (a relative error of at most
+  // 2^-11 per product, that of the 16-bit P itself), so scores arrive in log2 units
+  static constexpr bool kLog2Scores = true;
   __device__ static __forceinline__ f32x16_t mfma(vec a, vec b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x16_t mfma8(vec4 a, vec4 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x8f16(a, b, c, 0, 0, 0);
+  }
+  // c + the two 16-bit values of w (v_dot2c_f32_f16 against (1, 1): exact products, fp32 sum)
+  __device__ static __forceinline__ float add_pair(uint32_t w, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), f16x2_t{1, 1}, c, false);
   }
 };
 template <> struct Op<bf16_t> {
   typedef bf16x8_t vec;
+  typedef s16x4_t vec4;
+  // bf16 would round a prescaled Q to 2^-8: scores stay raw and the scale is applied in fp32
+  static constexpr bool kLog2Scores = false;
   __device__ static __forceinline__ f32x16_t mfma(vec a, vec b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x16_t mfma8(vec4 a, vec4 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ float add_pair(uint32_t w, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), bf16x2_t{1, 1}, c, false);
   }
 };
 template <typename ET>
@@ -136,10 +158,25 @@ __device__ __forceinline__ void tile_store(const TileRegs& t, uint16_t* ks, uint
   item_store(t.r, ks, vs, kVStr, 0, tid);
 }
 
+// Online-softmax state of one wave (32 query columns).  Each query keeps a
+// reference max m (in score units: log2 units where Q is prescaled, raw
+// otherwise) that its 16-bit type represents exactly; the score chain of a
+// tile starts with one 32x32x8 MFMA step that adds -m to every score (A = all
+// ones, B = -m in the first k slot of the query's lane < 32), so
+// probabilities come out of exp2 with no per-score subtraction and no
+// per-tile max.  The reference only moves when a tile would give some lane of
+// the wave a probability sum above kGrowSum: that tile's scores are then
+// recomputed without the bias, the tile max is taken, and the accumulators
+// are rescaled.  Every probability of an accepted tile is therefore at most
+// kGrowSum, far below the 16-bit P's overflow.  The first tile always takes
+// that path.
+constexpr float kGrowSum = 4096.f;
+
 struct WaveState {
   f32x16_t acc[2];    // O^T blocks: dims [0,32) and [32,64), column = query
-  float m;            // running max (raw score units)
-  float l;            // partial row sum over this lane's keys
+  float m;            // reference max of the lane's query, score units (-inf until a key is visible)
+  float l;            // partial row sum over this lane's keys, relative to m
+  uint32_t bias;      // 16-bit pair (-m, 0) in lanes < 32, zero in lanes >= 32
 };
 
 // x combined with the same register of lane l ^ 32 (v_permlane32_swap with
@@ -161,84 +198,110 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return r;
 }
 
-// One 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-// ks: [64][kKStr] K rows; vs: [64][vstr] V rows; key0: first key index of
-// the tile in the mask's coordinates.  With `mask`, key j is kept iff
-// lo_key <= j < hi_key and, for tq >= 0 (a real query tq), j <= tq and
-// (win <= 0 or j > tq - win).
+// Mask of a tile: key j is kept iff lo_key <= j < hi_key and, for tq >= 0 (a
+// real query tq), j <= tq and (win <= 0 or j > tq - win).  Register r of block
+// kb holds key key0 + 32 kb + 8 (r/4) + 4 half + r%4.
+__device__ __forceinline__ void mask_tile(f32x16_t (&s)[2], int half, int key0, int lo_key, int hi_key, int tq,
+                                          int win) {
+  int lo = lo_key, hi = hi_key;
+  if (tq >= 0) {
+    hi = min(hi, tq + 1);
+    if (win > 0) lo = max(lo, tq - win + 1);
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (key < lo || key >= hi) s[kb][r] = -INFINITY;   // exp2 gives exactly 0
+    }
+}
+
+// One 64-key tile: S^T = K Q^T (minus the reference), online softmax,
+// O^T += V^T P^T.  ks: [64][kKStr] K rows; vs: [64][vstr] V rows; key0: first
+// key index of the tile in the mask's coordinates; sc: log2(e)/sqrt(hd), applied
+// here unless Q was prescaled; `first`: the wave's first tile.
 template <typename ET>
 __device__ __forceinline__ void attend_tile(WaveState& st, const typename Op<ET>::vec (&qf)[4],
-                                            const uint16_t* ks, const uint16_t* vs, int vstr,
-                                            float sc, int lane, int key0, int lo_key, int hi_key,
-                                            int tq, int win, bool mask) {
+                                            const uint16_t* ks, const uint16_t* vs, int vstr, float sc, int lane,
+                                            int key0, int lo_key, int hi_key, int tq, int win, bool mask,
+                                            bool first) {
+  typedef typename Op<ET>::vec4 V4;
   const int col = lane & 31, half = lane >> 5;
+  const uint32_t one2 = Pair<ET>::pack(1.f, 1.f);
+  const V4 ones = __builtin_bit_cast(V4, make_uint2(one2, one2));
   f32x16_t s[2];
+  auto scores = [&](auto biased) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    s[kb] = f32x16_t{};
-    const uint16_t* krow = ks + (kb * 32 + col) * kKStr + half * 8;
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint16_t* krow = ks + (kb * 32 + col) * kKStr + half * 8;
+      f32x16_t c = f32x16_t{};
+      if constexpr (decltype(biased)::value) c = Op<ET>::mfma8(ones, __builtin_bit_cast(V4, make_uint2(st.bias, 0u)), c);
 #pragma unroll
-    for (int st4 = 0; st4 < 4; ++st4) {
-      const auto a = as_vec<ET>(*reinterpret_cast<const U4*>(krow + st4 * 16));
-      s[kb] = Op<ET>::mfma(a, qf[st4], s[kb]);
+      for (int st4 = 0; st4 < 4; ++st4) {
+        const auto a = as_vec<ET>(*reinterpret_cast<const U4*>(krow + st4 * 16));
+        c = Op<ET>::mfma(a, qf[st4], c);
+      }
+      s[kb] = c;
     }
-  }
-  if (mask) {
-    // key index of register r of block kb: key0 + 32 kb + 8 (r/4) + 4 half + r%4
-    int lo = lo_key, hi = hi_key;
-    if (tq >= 0) {
-      hi = min(hi, tq + 1);
-      if (win > 0) lo = max(lo, tq - win + 1);
-    }
+    if (mask) mask_tile(s, half, key0, lo_key, hi_key, tq, win);
+  };
+  // P^T as 16-bit pairs (B fragments of the P.V steps) and this lane's sum of them
+  U4 pw[4];
+  float psum;
+  auto probs = [&](float sub) {
+    psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (key < lo || key >= hi) s[kb][r] = -INFINITY;   // exp2 gives exactly 0 whatever the running max
+      for (int hh = 0; hh < 2; ++hh) {
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if constexpr (Op<ET>::kLog2Scores) p[j] = fast_exp2(s[kb][hh * 8 + j] - sub);
+          else p[j] = fast_exp2((s[kb][hh * 8 + j] - sub) * sc);
+        }
+        U4 w;
+        w.x = Pair<ET>::pack(p[0], p[1]);
+        w.y = Pair<ET>::pack(p[2], p[3]);
+        w.z = Pair<ET>::pack(p[4], p[5]);
+        w.w = Pair<ET>::pack(p[6], p[7]);
+        psum = Op<ET>::add_pair(w.x, psum);
+        psum = Op<ET>::add_pair(w.y, psum);
+        psum = Op<ET>::add_pair(w.z, psum);
+        psum = Op<ET>::add_pair(w.w, psum);
+        pw[kb * 2 + hh] = w;
       }
+  };
+  bool slow = first;
+  if (!first) {
+    scores(std::true_type{});
+    probs(0.f);
+    slow = __builtin_amdgcn_ballot_w64(psum > kGrowSum) != 0;
   }
-  float mt = max3f(s[0][0], s[0][1], s[0][2]);
+  if (slow) {
+    scores(std::false_type{});
+    float mt = max3f(s[0][0], s[0][1], s[0][2]);
 #pragma unroll
-  for (int r = 3; r < 15; r += 2) mt = max3f(mt, s[0][r], s[0][r + 1]);
-  mt = max3f(mt, s[0][15], s[1][0]);
+    for (int r = 3; r < 15; r += 2) mt = max3f(mt, s[0][r], s[0][r + 1]);
+    mt = max3f(mt, s[0][15], s[1][0]);
 #pragma unroll
-  for (int r = 1; r < 15; r += 2) mt = max3f(mt, s[1][r], s[1][r + 1]);
-  mt = fmaxf(mt, s[1][15]);
-  mt = max_xor32(mt);
-  // Lazy rescaling: the running max only moves (and the accumulators are rescaled) when some
-  // query of the wave sees a score more than 2^kLazyLog2 above it; otherwise the stale max is
-  // kept and probabilities may reach 2^kLazyLog2, exact in the 16-bit P and fp32 sums.
-  if (__builtin_amdgcn_ballot_w64((mt - st.m) * sc > kLazyLog2) != 0) {
-    const float mnew = fmaxf(st.m, mt);
-    const float alpha = fast_exp2((st.m - mnew) * sc);
-    st.m = mnew;
+    for (int r = 1; r < 15; r += 2) mt = max3f(mt, s[1][r], s[1][r + 1]);
+    mt = fmaxf(mt, s[1][15]);
+    mt = max_xor32(mt);
+    // the new reference: the larger of the old one and the tile max, rounded to the 16-bit type
+    float mnew = fmaxf(st.m, mt);
+    if (mnew != -INFINITY) mnew = Pair<ET>::lo(Pair<ET>::pack(fminf(mnew, 6.0e4f), 0.f));
+    const bool none = mnew == -INFINITY;              // no visible key yet: nothing to rescale
+    const float alpha = none ? 1.f : fast_exp2(Op<ET>::kLog2Scores ? st.m - mnew : (st.m - mnew) * sc);
     st.l *= alpha;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.acc[db][r] *= alpha;
-  }
-  const float msc = st.m * sc;
-  float psum = 0.f;
-  typename Op<ET>::vec pf[4];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      float p[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        p[j] = fast_exp2(fmaf(s[kb][hh * 8 + j], sc, -msc));
-        psum += p[j];
-      }
-      U4 w;
-      w.x = Pair<ET>::pack(p[0], p[1]);
-      w.y = Pair<ET>::pack(p[2], p[3]);
-      w.z = Pair<ET>::pack(p[4], p[5]);
-      w.w = Pair<ET>::pack(p[6], p[7]);
-      pf[kb * 2 + hh] = as_vec<ET>(w);
-    }
+    st.m = mnew;
+    st.bias = half ? 0u : Pair<ET>::pack(-mnew, 0.f);
+    probs(none ? 0.f : mnew);
   }
   st.l += psum;
   // O^T[dim][q] += sum_k V^T[dim][k] P^T[k][q]; PV k-step s covers tile keys
@@ -254,7 +317,7 @@ __device__ __forceinline__ void attend_tile(WaveState& st, const typename Op<ET>
       const uint2 lo = v_tr4(vlane + 16 * s4 * vstr + 32 * db);
       const uint2 hi = v_tr4(vlane + (16 * s4 + 8) * vstr + 32 * db);
       U4 w = {lo.x, lo.y, hi.x, hi.y};
-      st.acc[db] = Op<ET>::mfma(as_vec<ET>(w), pf[s4], st.acc[db]);
+      st.acc[db] = Op<ET>::mfma(as_vec<ET>(w), as_vec<ET>(pw[s4]), st.acc[db]);
     }
   }
 }
