@@ -94,25 +94,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     }
   };
 
-  // Q^T fragments: k-step s holds dims 16 s + 8 (lane/32) .. +7 of query tq (fp16: prescaled
-  // by log2(e)/sqrt(hd), so that scores come out in log2 units)
+  // Q^T fragments: k-step s holds dims 16 s + 8 (lane/32) .. +7 of query tq
   typename Op<ET>::vec qf[4];
   {
     const ET* qrow = a.q + ((int64_t)b * a.T + tq) * a.ld_q + h * kHd + (lane >> 5) * 8;
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const U4 r = *reinterpret_cast<const U4*>(qrow + s4 * 16);
-      if constexpr (!Op<ET>::kLog2Scores) {
-        qf[s4] = as_vec<ET>(r);
-        continue;
-      }
-      U4 w;
-      w.x = Pair<ET>::pack(Pair<ET>::lo(r.x) * sc, Pair<ET>::hi(r.x) * sc);
-      w.y = Pair<ET>::pack(Pair<ET>::lo(r.y) * sc, Pair<ET>::hi(r.y) * sc);
-      w.z = Pair<ET>::pack(Pair<ET>::lo(r.z) * sc, Pair<ET>::hi(r.z) * sc);
-      w.w = Pair<ET>::pack(Pair<ET>::lo(r.w) * sc, Pair<ET>::hi(r.w) * sc);
-      qf[s4] = as_vec<ET>(w);
-    }
+    for (int s4 = 0; s4 < 4; ++s4) qf[s4] = as_vec<ET>(*reinterpret_cast<const U4*>(qrow + s4 * 16));
   }
   WaveState st;
   st.acc[0] = f32x16_t{};

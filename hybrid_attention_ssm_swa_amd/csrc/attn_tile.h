@@ -36,9 +36,6 @@ template <typename ET> struct Op;
 template <> struct Op<half_t> {
   typedef f16x8_t vec;
   typedef f16x4_t vec4;
-  // Q is prescaled by log2(e)/sqrt(hd) and rounded to fp16 once (a relative error of at most
-  // 2^-11 per product, that of the 16-bit P itself), so scores arrive in log2 units
-  static constexpr bool kLog2Scores = true;
   __device__ static __forceinline__ f32x16_t mfma(vec a, vec b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
@@ -53,8 +50,6 @@ template <> struct Op<half_t> {
 template <> struct Op<bf16_t> {
   typedef bf16x8_t vec;
   typedef s16x4_t vec4;
-  // bf16 would round a prescaled Q to 2^-8: scores stay raw and the scale is applied in fp32
-  static constexpr bool kLog2Scores = false;
   __device__ static __forceinline__ f32x16_t mfma(vec a, vec b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
@@ -159,22 +154,21 @@ __device__ __forceinline__ void tile_store(const TileRegs& t, uint16_t* ks, uint
 }
 
 // Online-softmax state of one wave (32 query columns).  Each query keeps a
-// reference max m (in score units: log2 units where Q is prescaled, raw
-// otherwise) that its 16-bit type represents exactly; the score chain of a
-// tile starts with one 32x32x8 MFMA step that adds -m to every score (A = all
-// ones, B = -m in the first k slot of the query's lane < 32), so
-// probabilities come out of exp2 with no per-score subtraction and no
-// per-tile max.  The reference only moves when a tile would give some lane of
-// the wave a probability sum above kGrowSum: that tile's scores are then
-// recomputed without the bias, the tile max is taken, and the accumulators
-// are rescaled.  Every probability of an accepted tile is therefore at most
-// kGrowSum, far below the 16-bit P's overflow.  The first tile always takes
-// that path.
+// reference max m (raw score units) that its 16-bit type represents exactly.
+// The score chain of a tile starts with one 32x32x8 MFMA step that adds -m to
+// every score (A = all ones, B = -m in the first k slot of the query's lane
+// < 32), so a probability costs one multiply by the scale and one exp2, with
+// no subtraction and no per-tile max.  The reference only moves when a tile
+// would give some lane of the wave a probability sum above kGrowSum: that
+// tile's scores are then recomputed without the bias, the tile max is taken,
+// and the accumulators are rescaled.  Every probability of an accepted tile is
+// therefore at most kGrowSum, far below the 16-bit P's overflow.  The first
+// tile always takes that path.
 constexpr float kGrowSum = 4096.f;
 
 struct WaveState {
   f32x16_t acc[2];    // O^T blocks: dims [0,32) and [32,64), column = query
-  float m;            // reference max of the lane's query, score units (-inf until a key is visible)
+  float m;            // reference max of the lane's query, raw score units (-inf until a key is visible)
   float l;            // partial row sum over this lane's keys, relative to m
   uint32_t bias;      // 16-bit pair (-m, 0) in lanes < 32, zero in lanes >= 32
 };
@@ -191,12 +185,10 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// max of three (one v_max3_f32; scores are never NaN)
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
+// max of three.  Plain fmaxf, which the compiler turns into v_max3_f32 after quieting inputs it
+// cannot prove canonical: an inline-asm v_max3_f32 would be invisible to the hazard recognizer,
+// which then inserts no wait states between an MFMA writing the scores and the asm reading them.
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
 // Mask of a tile: key j is kept iff lo_key <= j < hi_key and, for tq >= 0 (a
 // real query tq), j <= tq and (win <= 0 or j > tq - win).  Register r of block
@@ -220,7 +212,7 @@ __device__ __forceinline__ void mask_tile(f32x16_t (&s)[2], int half, int key0, 
 // One 64-key tile: S^T = K Q^T (minus the reference), online softmax,
 // O^T += V^T P^T.  ks: [64][kKStr] K rows; vs: [64][vstr] V rows; key0: first
 // key index of the tile in the mask's coordinates; sc: log2(e)/sqrt(hd), applied
-// here unless Q was prescaled; `first`: the wave's first tile.
+// in fp32 to the biased scores (P = 2^(sc (s - m))); `first`: the wave's first tile.
 template <typename ET>
 __device__ __forceinline__ void attend_tile(WaveState& st, const typename Op<ET>::vec (&qf)[4],
                                             const uint16_t* ks, const uint16_t* vs, int vstr, float sc, int lane,
@@ -257,10 +249,7 @@ __device__ __forceinline__ void attend_tile(WaveState& st, const typename Op<ET>
       for (int hh = 0; hh < 2; ++hh) {
         float p[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if constexpr (Op<ET>::kLog2Scores) p[j] = fast_exp2(s[kb][hh * 8 + j] - sub);
-          else p[j] = fast_exp2((s[kb][hh * 8 + j] - sub) * sc);
-        }
+        for (int j = 0; j < 8; ++j) p[j] = fast_exp2((s[kb][hh * 8 + j] - sub) * sc);
         U4 w;
         w.x = Pair<ET>::pack(p[0], p[1]);
         w.y = Pair<ET>::pack(p[2], p[3]);
@@ -293,7 +282,7 @@ __device__ __forceinline__ void attend_tile(WaveState& st, const typename Op<ET>
     float mnew = fmaxf(st.m, mt);
     if (mnew != -INFINITY) mnew = Pair<ET>::lo(Pair<ET>::pack(fminf(mnew, 6.0e4f), 0.f));
     const bool none = mnew == -INFINITY;              // no visible key yet: nothing to rescale
-    const float alpha = none ? 1.f : fast_exp2(Op<ET>::kLog2Scores ? st.m - mnew : (st.m - mnew) * sc);
+    const float alpha = none ? 1.f : fast_exp2((st.m - mnew) * sc);
     st.l *= alpha;
 #pragma unroll
     for (int db = 0; db < 2; ++db)

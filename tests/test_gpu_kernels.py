@@ -46,7 +46,7 @@ def test_attention_kernel(dtype, B, T, M, Hq, Hkv, hd, W):
     _attention_case(dtype, B, T, M, Hq, Hkv, hd, W)
 
 
-@pytest.mark.parametrize("dtype,qs", [("f16", 4.0), ("bf16", 4.0), ("f16", 12.0)])
+@pytest.mark.parametrize("dtype,qs", [("f16", 4.0), ("bf16", 4.0), ("f16", 12.0), ("f16", 24.0), ("bf16", 24.0)])
 def test_attention_kernel_peaked_scores(dtype, qs):
     """Queries scaled so scores spread over tens of units: the running max moves by more than the
     lazy-rescale threshold across tiles, and most probabilities underflow."""
