@@ -116,8 +116,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     __syncthreads();
     if (i + 1 < n_tiles) fetch(pre, i + 1);
     // Every wave runs every tile of the workgroup: a tile outside a wave's window (or a wave past
-    // the end of the sequence) is simply all masked and adds nothing.  Branching around it would
-    // split the loop-carried accumulators across paths and cost a 32-register copy per tile.
+    // the end of the sequence) is simply all masked and adds nothing.  Branching around it splits
+    // the loop-carried accumulators across paths and costs a 32-register copy per tile.
     int key0, lo_key, hi_key, tqm;
     bool mask;
     if (i < n_mt) {

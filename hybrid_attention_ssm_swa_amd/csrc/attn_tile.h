@@ -192,7 +192,9 @@ __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf
 
 // Mask of a tile: key j is kept iff lo_key <= j < hi_key and, for tq >= 0 (a
 // real query tq), j <= tq and (win <= 0 or j > tq - win).  Register r of block
-// kb holds key key0 + 32 kb + 8 (r/4) + 4 half + r%4.
+// kb holds key key0 + 4 half + off with off = 32 kb + 8 (r/4) + r%4 (< 64); the
+// lane's visible offsets form one range [a, b), kept as a 64-bit mask, so each
+// score costs a bit extract and a bit select.
 __device__ __forceinline__ void mask_tile(f32x16_t (&s)[2], int half, int key0, int lo_key, int hi_key, int tq,
                                           int win) {
   int lo = lo_key, hi = hi_key;
@@ -200,13 +202,21 @@ __device__ __forceinline__ void mask_tile(f32x16_t (&s)[2], int half, int key0, 
     hi = min(hi, tq + 1);
     if (win > 0) lo = max(lo, tq - win + 1);
   }
+  const int base = key0 + 4 * half;
+  const int a = min(max(lo - base, 0), 64), b = min(max(hi - base, 0), 64);
+  const uint64_t below_b = b >= 64 ? ~0ull : (1ull << b) - 1;
+  const uint64_t below_a = a >= 64 ? ~0ull : (1ull << a) - 1;
+  const uint64_t keep = below_b & ~below_a;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < 2; ++kb) {
+    const uint32_t word = static_cast<uint32_t>(keep >> (32 * kb));
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-      if (key < lo || key >= hi) s[kb][r] = -INFINITY;   // exp2 gives exactly 0
+      const int bit = 8 * (r >> 2) + (r & 3);
+      const uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(word << (31 - bit)) >> 31);
+      s[kb][r] = __uint_as_float((__float_as_uint(s[kb][r]) & m) | (0xff800000u & ~m));   // -inf: exp2 gives 0
     }
+  }
 }
 
 // One 64-key tile: S^T = K Q^T (minus the reference), online softmax,
