@@ -252,6 +252,7 @@ __device__ __forceinline__ void attend_tile(WaveState& st, const typename Op<ET>
   U4 pw[4];
   float psum;
   auto probs = [&](float sub) {
+    const float off = -sub * sc;   // P = 2^(sc (s - sub)) as one FMA per score (one multiply for sub = 0)
     psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -259,7 +260,7 @@ __device__ __forceinline__ void attend_tile(WaveState& st, const typename Op<ET>
       for (int hh = 0; hh < 2; ++hh) {
         float p[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = fast_exp2((s[kb][hh * 8 + j] - sub) * sc);
+        for (int j = 0; j < 8; ++j) p[j] = fast_exp2(fmaf(s[kb][hh * 8 + j], sc, off));
         U4 w;
         w.x = Pair<ET>::pack(p[0], p[1]);
         w.y = Pair<ET>::pack(p[2], p[3]);
@@ -292,12 +293,14 @@ __device__ __forceinline__ void attend_tile(WaveState& st, const typename Op<ET>
     float mnew = fmaxf(st.m, mt);
     if (mnew != -INFINITY) mnew = Pair<ET>::lo(Pair<ET>::pack(fminf(mnew, 6.0e4f), 0.f));
     const bool none = mnew == -INFINITY;              // no visible key yet: nothing to rescale
-    const float alpha = none ? 1.f : fast_exp2((st.m - mnew) * sc);
-    st.l *= alpha;
+    if (!first) {   // the first tile has nothing accumulated yet
+      const float alpha = none ? 1.f : fast_exp2((st.m - mnew) * sc);
+      st.l *= alpha;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+      for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st.acc[db][r] *= alpha;
+        for (int r = 0; r < 16; ++r) st.acc[db][r] *= alpha;
+    }
     st.m = mnew;
     st.bias = half ? 0u : Pair<ET>::pack(-mnew, 0.f);
     probs(none ? 0.f : mnew);
