@@ -107,6 +107,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   st.m = -INFINITY;
   st.l = 0.f;
   st.bias = (lane >> 5) ? 0u : Pair<ET>::pack(INFINITY, 0.f);
+  st.exact = false;
 
   TileRegs pre;
   fetch(pre, 0);

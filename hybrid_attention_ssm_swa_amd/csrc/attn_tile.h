@@ -163,14 +163,18 @@ __device__ __forceinline__ void tile_store(const TileRegs& t, uint16_t* ks, uint
 // tile's scores are then recomputed without the bias, the tile max is taken,
 // and the accumulators are rescaled.  Every probability of an accepted tile is
 // therefore at most kGrowSum, far below the 16-bit P's overflow.  The first
-// tile always takes that path.
+// tile always takes that path, and so does every tile of a wave in which some
+// query's max has left the 16-bit range (|m| > kRefMax, only reachable with
+// fp16): that wave keeps m in fp32 and subtracts it per score from then on.
 constexpr float kGrowSum = 4096.f;
+constexpr float kRefMax = 6.0e4f;   // largest reference magnitude kept as a 16-bit value
 
 struct WaveState {
   f32x16_t acc[2];    // O^T blocks: dims [0,32) and [32,64), column = query
   float m;            // reference max of the lane's query, raw score units (-inf until a key is visible)
   float l;            // partial row sum over this lane's keys, relative to m
   uint32_t bias;      // 16-bit pair (-m, 0) in lanes < 32, zero in lanes >= 32
+  bool exact;         // wave-uniform: some query's max left the 16-bit range, m is plain fp32
 };
 
 // x combined with the same register of lane l ^ 32 (v_permlane32_swap with
@@ -273,8 +277,8 @@ __device__ __forceinline__ void attend_tile(WaveState& st, const typename Op<ET>
         pw[kb * 2 + hh] = w;
       }
   };
-  bool slow = first;
-  if (!first) {
+  bool slow = first || __builtin_amdgcn_readfirstlane(st.exact);
+  if (!slow) {
     scores(std::true_type{});
     probs(0.f);
     slow = __builtin_amdgcn_ballot_w64(psum > kGrowSum) != 0;
@@ -290,8 +294,10 @@ __device__ __forceinline__ void attend_tile(WaveState& st, const typename Op<ET>
     mt = fmaxf(mt, s[1][15]);
     mt = max_xor32(mt);
     // the new reference: the larger of the old one and the tile max, rounded to the 16-bit type
+    // unless some query's max is out of its range (then fp32, for the rest of the wave's tiles)
     float mnew = fmaxf(st.m, mt);
-    if (mnew != -INFINITY) mnew = Pair<ET>::lo(Pair<ET>::pack(fminf(mnew, 6.0e4f), 0.f));
+    if (__builtin_amdgcn_ballot_w64(mnew != -INFINITY && fabsf(mnew) > kRefMax) != 0) st.exact = true;
+    if (!st.exact && mnew != -INFINITY) mnew = Pair<ET>::lo(Pair<ET>::pack(mnew, 0.f));
     const bool none = mnew == -INFINITY;              // no visible key yet: nothing to rescale
     if (!first) {   // the first tile has nothing accumulated yet
       const float alpha = none ? 1.f : fast_exp2((st.m - mnew) * sc);

@@ -46,10 +46,12 @@ def test_attention_kernel(dtype, B, T, M, Hq, Hkv, hd, W):
     _attention_case(dtype, B, T, M, Hq, Hkv, hd, W)
 
 
-@pytest.mark.parametrize("dtype,qs", [("f16", 4.0), ("bf16", 4.0), ("f16", 12.0), ("f16", 24.0), ("bf16", 24.0)])
+@pytest.mark.parametrize("dtype,qs", [("f16", 4.0), ("bf16", 4.0), ("f16", 12.0), ("f16", 24.0), ("bf16", 24.0),
+                                      ("f16", 4000.0), ("bf16", 4000.0)])
 def test_attention_kernel_peaked_scores(dtype, qs):
-    """Queries scaled so scores spread over tens of units: the running max moves by more than the
-    lazy-rescale threshold across tiles, and most probabilities underflow."""
+    """Queries scaled so scores spread over tens of units: the reference max moves by more than the
+    growth threshold across tiles, and most probabilities underflow.  At x4000 raw scores pass
+    fp16's range (~1e5), where the fp16 kernel must keep its reference in fp32."""
     _attention_case(dtype, 2, 700, 100, 10, 2, 64, 300, qs)
 
 
