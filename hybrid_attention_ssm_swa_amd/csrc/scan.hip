@@ -196,7 +196,23 @@ __global__ __launch_bounds__(64 * (N / NS)) void selective_scan_kernel(
 // Decode: one token per sequence.  N/4 consecutive lanes share a channel, each
 // owning 4 states (one 16-byte state load and store); y is reduced across them.
 // grid (ceil(E * N/4 / 256), B): no division by a runtime size in the index math.
-template <typename T, int N>
+// kVec: the lane's 4 B and 4 C values come as two vector loads (the dispatcher
+// checks their alignment) instead of eight scalar ones.
+template <typename T> struct Four;
+template <> struct Four<half_t> {
+  __device__ static __forceinline__ void load(const half_t* p, float (&v)[4]) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    v[0] = f16lo(w.x); v[1] = f16hi(w.x); v[2] = f16lo(w.y); v[3] = f16hi(w.y);
+  }
+};
+template <> struct Four<float> {
+  __device__ static __forceinline__ void load(const float* p, float (&v)[4]) {
+    const float4 w = *reinterpret_cast<const float4*>(p);
+    v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+  }
+};
+
+template <typename T, int N, bool kVec>
 __global__ __launch_bounds__(256) void ssm_step_kernel(StepArgs<T> a) {
   constexpr int LPC = N / 4;
   const int i = blockIdx.x * blockDim.x + threadIdx.x;   // lane within the sequence
@@ -215,13 +231,22 @@ __global__ __launch_bounds__(256) void ssm_step_kernel(StepArgs<T> a) {
   const float4 a2 = *reinterpret_cast<const float4*>(a.A2 + (int64_t)c * N + 4 * q);
   float hs[4] = {hv.x, hv.y, hv.z, hv.w};
   const float a2s[4] = {a2.x, a2.y, a2.z, a2.w};
+  float bn[4], cn[4];
+  if constexpr (kVec) {
+    Four<T>::load(row + 4 * q, bn);
+    Four<T>::load(row + N + 4 * q, cn);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bn[j] = Elem<T>::load(row + 4 * q + j);
+      cn[j] = Elem<T>::load(row + N + 4 * q + j);
+    }
+  }
   float part = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int n = 4 * q + j;
-    const float bn = Elem<T>::load(row + n), cn = Elem<T>::load(row + N + n);
-    hs[j] = fmaf(fast_exp2(delta * a2s[j]), hs[j], du * bn);
-    part = fmaf(cn, hs[j], part);
+    hs[j] = fmaf(fast_exp2(delta * a2s[j]), hs[j], du * bn[j]);
+    part = fmaf(cn[j], hs[j], part);
   }
 #pragma unroll
   for (int off = 1; off < LPC; off <<= 1) part += __shfl_xor(part, off);
@@ -272,9 +297,13 @@ hipError_t step_dispatch(const StepArgs<T>& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
   if (a.B > 65535 || (int64_t)a.E * (a.N / 4) >= INT32_MAX) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(ceil_div((int64_t)a.E * (a.N / 4), 256)), static_cast<unsigned>(a.B)), block(256);
-  switch (a.N) {
-    case 8: hipLaunchKernelGGL((ssm_step_kernel<T, 8>), grid, block, 0, s, a); break;
-    case 16: hipLaunchKernelGGL((ssm_step_kernel<T, 16>), grid, block, 0, s, a); break;
+  // B/C as vector loads when every row's 4-state groups are aligned to the vector size
+  const bool vec = reinterpret_cast<uintptr_t>(a.bc) % (4 * sizeof(T)) == 0 && a.ld % 4 == 0 && a.N % 4 == 0;
+  switch (a.N * 2 + (vec ? 1 : 0)) {
+    case 16: hipLaunchKernelGGL((ssm_step_kernel<T, 8, false>), grid, block, 0, s, a); break;
+    case 17: hipLaunchKernelGGL((ssm_step_kernel<T, 8, true>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((ssm_step_kernel<T, 16, false>), grid, block, 0, s, a); break;
+    case 33: hipLaunchKernelGGL((ssm_step_kernel<T, 16, true>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
