@@ -23,8 +23,10 @@ the exact form x * Phi(x); the conv and the recurrence start from zeros before a
 state handed to a decode step is the last (width - 1) branch inputs u and h.
 
 Parity: the conv, the recurrence and GeLU are pinned by closed forms (impulse response,
-geometric series, the normal CDF at 1); the block as a model of Griffin is "parity unpinned"
-beyond its pieces and the prefill -> decode continuation.
+geometric series, the normal CDF at 1); the block's composition (which branch is convolved and
+recurs, where GeLU sits, what the gates read) by a hand-worked d = 1, D_RNN = 1, T = 2 case
+whose every value has a closed form (tests/golden/handworked.json), which swapped branches,
+a moved GeLU or gates fed the wrong input all fail; and by the prefill -> decode continuation.
 """
 from __future__ import annotations
 

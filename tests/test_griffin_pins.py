@@ -71,3 +71,61 @@ def test_lambda_init_puts_a_power_c_in_range():
     p = make_griffin_params(np.random.Generator(np.random.PCG64(1)), GRIFFIN_SMALL)
     ac = go.sigmoid(p.lam) ** GRIFFIN_SMALL.c
     assert np.all(ac > 0.9 - 1e-6) and np.all(ac < 0.999 + 1e-6)
+
+
+# ---- the block's composition, pinned by a hand-worked case (tests/golden/handworked.json) ----
+
+import json
+import os
+
+from hymba_synth.griffin import GriffinParams, GriffinShape
+
+_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "handworked.json")
+
+
+def _golden_block():
+    g = json.load(open(_GOLDEN))["griffin_block"]
+    ev = lambda s: float(eval(str(s), {"__builtins__": {}}, {"log": math.log, "sqrt": math.sqrt,   # noqa: E731
+                                                               "Phi1": g["Phi1"]}))
+    arr = lambda a: np.array([[ev(v) for v in row] for row in a], dtype=float)   # noqa: E731
+    shape = GriffinShape(d_model=g["d_model"], d_rnn=g["d_rnn"], dtype="f32", c=g["c"])
+    p = GriffinParams(shape, arr(g["w_in"]), arr(g["conv_w"]), arr(g["w_gate"]), np.array(g["lam"], float),
+                      arr(g["w_out"]))
+    x = arr(g["x"])
+    return p, x, np.array([ev(s) for s in g["expected_h"]]), np.array([ev(s) for s in g["expected_Y"]])
+
+
+def test_block_matches_the_handworked_case():
+    p, x, h_ref, y_ref = _golden_block()
+    out = go.griffin_block(p, x)
+    assert np.allclose(out.h[:, 0], h_ref, rtol=1e-13, atol=1e-15)
+    assert np.allclose(out.Y[:, 0], y_ref, rtol=1e-13, atol=1e-15)
+    assert np.allclose(out.xc[:, 0], [1.0, -0.5], rtol=0, atol=1e-15)
+
+
+def _composed(p, x, recur_in="u", gate_src="xc", gelu_on="v", conv_on="u"):
+    """The block assembled from the oracle's pieces with one part moved (a planted mistake)."""
+    R = p.shape.d_rnn
+    P = np.asarray(x, float) @ np.asarray(p.w_in, float).T
+    br = {"u": P[:, :R], "v": P[:, R:]}
+    xc = go.causal_conv(br[conv_on], p.conv_w)
+    src = {"xc": xc, "x": np.asarray(x, float), "u": br["u"]}[gate_src]
+    G = src @ np.asarray(p.w_gate, float).T
+    h, _ = go.rglru(xc if recur_in == "u" else br["v"], G[:, :R], G[:, R:], p.lam, p.shape.c)
+    other = br["v"] if gelu_on == "v" else br["u"]
+    Y = (h * go.gelu(other)) if gelu_on != "h" else (go.gelu(h) * br["v"])
+    return Y @ np.asarray(p.w_out, float).T
+
+
+@pytest.mark.parametrize("mistake", [
+    dict(conv_on="v", gelu_on="u"),     # branches swapped
+    dict(gelu_on="h"),                  # GeLU on the recurrent branch instead of the other one
+    dict(conv_on="v"),                  # the conv applied to the GeLU branch's input
+    dict(gate_src="x"),                 # gates fed the block input instead of the conv output
+    dict(gate_src="u"),                 # gates fed the branch input before the conv
+])
+def test_planted_composition_mistakes_fail_the_handworked_case(mistake):
+    p, x, _, y_ref = _golden_block()
+    assert np.allclose(_composed(p, x)[:, 0], y_ref, rtol=1e-13)        # the unchanged assembly passes
+    bad = _composed(p, x, **mistake)[:, 0]
+    assert np.max(np.abs(bad - y_ref)) > 1e-3 * np.max(np.abs(y_ref)), mistake
