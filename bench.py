@@ -39,9 +39,14 @@ N_CU, CLK = 256, 2.4e9
 PEAK_VALU_LANE_OPS = N_CU * 64 * CLK        # non-packed fp32 lane-ops/s (39.3 T)
 
 STAGES = ["in_proj", "kv_write", "attention", "w_o", "ssm", "epilogue", "out_proj", "convert", "rope"]
-# in a prefill the scan runs on a second stream beside attention and W_O: their durations include
-# the contention, so the headline roofline is taken over the kernels that run alone
+# in a prefill the scan runs on a second stream beside attention and W_O: their durations in the
+# overlapped schedule include the contention.  Each kernel is also timed alone, in the serial
+# schedule (every kernel on the launch stream, in order), which the per-kernel rooflines use.
 CONCURRENT = {"ssm": "attention, w_o", "attention": "ssm", "w_o": "ssm"}
+# the library's stage -> the kernel that stage launches (bf16 layers)
+KERNEL_OF = {"attention": "swa_meta_attn", "ssm": "selective_scan", "epilogue": "fused_epilogue",
+             "in_proj": "in_proj GEMM", "w_o": "W_O GEMM", "out_proj": "out_proj GEMM", "convert": "conversions",
+             "rope": "rope", "kv_write": "kv_write"}
 
 
 def log(*a):
@@ -179,6 +184,21 @@ def _time_loop(fn, steps):
     return t0.elapsed_time(t1) / steps
 
 
+def recorded(layers, fn, steps):
+    """One untimed step, then `steps` steps with the library recording a HIP event pair around every
+    kernel of each layer on its launch stream.  Returns (ms per step, per-layer stage means)."""
+    import torch
+    from hybrid_attention_ssm_swa_amd import _lib as L
+    fn(0)
+    torch.cuda.synchronize()
+    for lay in layers:
+        L.hymba_layer_profile(lay.handle, True)
+    ms_rec = _time_loop(fn, steps)
+    for lay in layers:
+        L.hymba_layer_profile(lay.handle, False)
+    return ms_rec, [L.hymba_layer_profile_read(lay.handle) for lay in layers]
+
+
 def timed(layers, fn, steps, warmup):
     """Runs `warmup` untimed steps, then times exactly `steps` steps between two events on the
     launch stream (the throughput figure).  A second timed region of `steps` steps follows with
@@ -220,23 +240,34 @@ def bench_prefill(cfg_id, steps, warmup, rope_base=0.0):
         kv = make_kv(*keep)
     del case
     y = torch.empty_like(x)
+    B, T = cfg.batch, cfg.seq
+    state = torch.empty((B, s.d_inner, s.d_state), dtype=torch.float32, device="cuda")   # final SSM state
     layer.prepare(kv)
     torch.cuda.synchronize()
-    ms, ms_rec, (stage_ms,) = timed([layer], lambda i: layer.prefill(x, kv, None, y), steps, warmup)
-    B, T = cfg.batch, cfg.seq
+    fn = lambda i: layer.prefill(x, kv, state, y)   # noqa: E731
+    ms, ms_rec, (stage_ms,) = timed([layer], fn, steps, warmup)
+    # the serial schedule last: every kernel alone on the launch stream (its dispatches are the
+    # last `steps` calls of each kernel, which the rocprofv3 summary averages)
+    layer.set_overlap(False)
+    ms_serial, (stage_alone,) = recorded([layer], fn, steps)
+    layer.set_overlap(True)
     work = prefill_work(s, B, T)
     ents = []
     for k, name in enumerate(STAGES):
-        if name in work and stage_ms[k] > 0:
-            e = roofline_entry(name, work[name][0], work[name][1], stage_ms[k])
+        if name in work and stage_alone[k] > 0:
+            e = roofline_entry(name, work[name][0], work[name][1], stage_alone[k])
             e["traffic"] = measured_traffic(name)
-            if name in CONCURRENT:
-                e["concurrent_with"] = CONCURRENT[name]
             ents.append(e)
-    ents.append(dict(scan_alu_entry(s, B, T, stage_ms[STAGES.index("ssm")]), concurrent_with=CONCURRENT["ssm"]))
+    ents.append(scan_alu_entry(s, B, T, stage_alone[STAGES.index("ssm")]))
+    for name in CONCURRENT:   # the same kernels inside the overlapped schedule, for context
+        k = STAGES.index(name)
+        if stage_ms[k] > 0:
+            ents.append(dict(roofline_entry(name, work[name][0], work[name][1], stage_ms[k]),
+                             concurrent_with=CONCURRENT[name]))
     out = {"tokens_per_s": B * T / (ms * 1e-3), "ms_per_step": ms, "ms_per_step_recording": ms_rec,
-           "batch": B, "seq": T,
-           "stage_ms": dict(zip(STAGES, stage_ms)), "kernels": ents}
+           "ms_per_step_serial": ms_serial, "batch": B, "seq": T,
+           "stage_ms": dict(zip(STAGES, stage_ms)), "stage_ms_alone": dict(zip(STAGES, stage_alone)),
+           "kernels": ents}
     layer.close()
     del x, y, keep
     torch.cuda.empty_cache()
@@ -350,6 +381,33 @@ def bench_griffin(steps, warmup, B=16, T=8192, decode_batch=128):
     return {"tokens_per_s": B * T / (ms * 1e-3), "ms_per_step": ms, "batch": B, "seq": T,
             "stage_ms": dict(zip(L.GRIFFIN_STAGES, stage)), "kernels": ents,
             "decode": {"batch": decode_batch, "ms_per_step": ms_d, "tokens_per_s": decode_batch / (ms_d * 1e-3)}}
+
+
+def graded_kernels(main_run, workloads):
+    """Each hand-written kernel of the path with its own roofline fraction, each timed alone:
+    attention on the MFMA peak, the scan on HBM and on the VALU issue rate, the epilogue on HBM,
+    and (from the decode pair) decode attention and the SSM step on HBM, per role."""
+    pick = lambda ents, name, bound=None: next((k for k in ents if k["kernel"] == name and   # noqa: E731
+                                                "concurrent_with" not in k and (bound is None or k["bound"] == bound)),
+                                               None)
+    g = {}
+    ents = main_run["kernels"]
+    for stage, key in (("attention", "swa_meta_attn"), ("epilogue", "fused_epilogue")):
+        e = pick(ents, stage)
+        if e:
+            g[key] = {k: e[k] for k in ("bound", "frac", "achieved", "unit", "ms")}
+    hb, alu = pick(ents, "ssm", "hbm"), pick(ents, "ssm", "alu")
+    if hb and alu:
+        g["selective_scan"] = {"hbm": {k: hb[k] for k in ("frac", "achieved", "unit")},
+                               "alu": {k: alu[k] for k in ("frac", "achieved", "unit")}, "ms": hb["ms"]}
+    dec = (workloads or {}).get("decode_b128_pair")
+    if dec:
+        for role in ("producer", "consumer"):
+            for stage, key in (("attention", "decode_attn"), ("ssm", "ssm_step")):
+                e = next((k for k in dec["kernels"][role] if k["kernel"] == stage), None)
+                if e:
+                    g.setdefault(key, {})[role] = {k: e[k] for k in ("bound", "frac", "achieved", "unit", "ms")}
+    return g
 
 
 # --- rocprofv3 summaries (run on the host after the profiled runs) ----------------------------
@@ -673,10 +731,12 @@ def main():
         log(f"[bench] Griffin block 8K prefill: {workloads['griffin_block_8k']['tokens_per_s']:.0f} tok/s; "
             f"decode B=128: {workloads['griffin_block_8k']['decode']['tokens_per_s']:.0f} tok/s")
 
-    kernels = [k for k in main_run["kernels"] if k["bound"] != "alu" and "concurrent_with" not in k]
-    dominant = max(kernels, key=lambda k: k["ms"])
-    roof = {k: dominant[k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac")}
-    roof["traffic"] = dominant.get("traffic")
+    # the headline roofline: the dominant hand-written kernel of the main workload, swa_meta_attn,
+    # timed alone (serial schedule) by HIP events on its launch stream
+    att = next(k for k in main_run["kernels"] if k["kernel"] == "attention" and "concurrent_with" not in k)
+    roof = {k: att[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    roof = {"kernel": "swa_meta_attn", **roof, "traffic": att.get("traffic"), "ms": att["ms"]}
+    graded = graded_kernels(main_run, workloads)
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     line = {
         "metric": METRIC,
@@ -690,12 +750,17 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
+        "dtype_note": "bf16 x, y and weight matrices at the layer boundary; activations and the attention, "
+                      "in_proj and W_O MFMA operands fp16 (11-bit significand, same MFMA rate); fp32 accumulation "
+                      "and SSM state; out_proj multiplies bf16. Activations beyond fp16's range are reported by "
+                      "hymba_layer_check (HYMBA_ERR_RANGE)",
         "data": "synthetic",
         "config": {"workload": "1.5B-shaped SWA mixer layer, 8K prefill, K/V handed from the previous layer: "
                                "B=16 x T=8192 (+128 meta), d=1600, 25 heads x 64 (5 KV heads), window 1024, "
                                "SSM d_inner 3200, state 16",
                    "global_batch": 16, "seq_len": 8192, "parallelism": "single-gpu"},
         "roofline": roof,
+        "graded_kernels": graded,
         "cpu_baseline": cpu,
         "stage_ms": main_run["stage_ms"],
         "kernels": main_run["kernels"],

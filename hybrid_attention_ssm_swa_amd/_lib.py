@@ -21,6 +21,7 @@ HYMBA_ERR_UNSUPPORTED = -2
 HYMBA_ERR_WORKSPACE = -3
 HYMBA_ERR_BIND = -4
 HYMBA_ERR_HIP = -5
+HYMBA_ERR_RANGE = -6
 HYMBA_F32 = 0
 HYMBA_BF16 = 1
 HYMBA_F16 = 2
@@ -33,6 +34,7 @@ EXPORTED = [
     "hymba_kernel_selective_scan", "hymba_kernel_epilogue", "hymba_kernel_gemm_rows",
     "hymba_kernel_gemm_rows_workspace",
     "hymba_layer_profile", "hymba_layer_profile_read", "hymba_stage_name",
+    "hymba_layer_check", "hymba_layer_set_overlap",
     "griffin_block_persistent_bytes", "griffin_block_prepare", "griffin_workspace_bytes",
     "griffin_block_prefill", "griffin_block_decode",
 ]
@@ -120,6 +122,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hymba_layer_profile": (c_int32, [P, c_int32]),
         "hymba_layer_profile_read": (c_int32, [P, POINTER(c_float), c_int32]),
         "hymba_stage_name": (c_char_p, [c_int32]),
+        "hymba_layer_check": (c_int32, [P, P]),
+        "hymba_layer_set_overlap": (c_int32, [P, c_int32]),
         "griffin_block_persistent_bytes": (c_size_t, [POINTER(griffin_block_cfg)]),
         "griffin_block_prepare": (c_int32, [POINTER(griffin_block_cfg), POINTER(griffin_block_weights), P,
                                             c_size_t, P]),
@@ -139,7 +143,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
 
 def status_name(status: int) -> str:
     names = {0: "HYMBA_OK", -1: "HYMBA_ERR_INVALID_ARG", -2: "HYMBA_ERR_UNSUPPORTED",
-             -3: "HYMBA_ERR_WORKSPACE", -4: "HYMBA_ERR_BIND", -5: "HYMBA_ERR_HIP"}
+             -3: "HYMBA_ERR_WORKSPACE", -4: "HYMBA_ERR_BIND", -5: "HYMBA_ERR_HIP", -6: "HYMBA_ERR_RANGE"}
     return names.get(status, "HYMBA_UNKNOWN_STATUS")
 
 
@@ -238,6 +242,14 @@ def hymba_kernel_gemm_rows(w_dtype, x_dtype, y_dtype, w, ldw, x, ldx, y, ldy, y3
 
 def hymba_kernel_gemm_rows_workspace(M: int, N: int, K: int) -> int:
     return load_library().hymba_kernel_gemm_rows_workspace(M, N, K)
+
+
+def hymba_layer_check(layer: int, stream: int) -> None:
+    _check(load_library().hymba_layer_check(layer, stream))
+
+
+def hymba_layer_set_overlap(layer: int, enable: bool) -> None:
+    _check(load_library().hymba_layer_set_overlap(layer, 1 if enable else 0))
 
 
 def hymba_layer_profile(layer: int, enable: bool) -> None:

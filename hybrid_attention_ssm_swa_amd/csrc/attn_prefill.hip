@@ -206,7 +206,6 @@ hipError_t launch_mfma(const AttnArgs<ET>& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_attn_prefill_mfma(const AttnArgs<half_t>& a, hipStream_t s) { return launch_mfma(a, s); }
-hipError_t launch_attn_prefill_mfma(const AttnArgs<bf16_t>& a, hipStream_t s) { return launch_mfma(a, s); }
 
 hipError_t launch_attn_prefill_f32(const AttnArgs<float>& a, hipStream_t stream) {
   const int64_t total = (int64_t)a.B * a.T * a.n_heads;

@@ -106,6 +106,7 @@ __global__ __launch_bounds__(kThreads) void decode_attn_kernel(DecAttnArgs<T> a)
   const int c = tid % LPK, slot = tid / LPK;
   const int C = a.cache_len;
   const int64_t p = a.pos[b];
+  if (p < 0 && a.flags && split == 0 && g == 0 && tid == 0) a.flags[1] = 1u;   // reported by the layer check
   const int64_t weff = a.window > 0 ? a.window : C;
   const int64_t lo = p - weff + 1 > 0 ? p - weff + 1 : 0;
   const int nkeys = a.n_meta + static_cast<int>(p - lo + 1 > 0 ? p - lo + 1 : 0);
@@ -353,6 +354,7 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecAttnArgs<half_t
   const int lane = threadIdx.x;
   const int C = a.cache_len;
   const int64_t p = a.pos[b];
+  if (p < 0 && a.flags && split == 0 && g == 0 && lane == 0) a.flags[1] = 1u;   // reported by the layer check
   const int64_t weff = a.window > 0 ? a.window : C;
   const int64_t lo = p - weff + 1 > 0 ? p - weff + 1 : 0;
   const int nkeys = a.n_meta + static_cast<int>(p - lo + 1 > 0 ? p - lo + 1 : 0);

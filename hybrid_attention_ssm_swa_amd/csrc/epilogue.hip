@@ -87,6 +87,9 @@ __global__ __launch_bounds__(kEpiThreads) void epilogue_kernel(EpiArgs<T, FT> a)
     ss1 += part[0][w];
     ss2 += part[1][w];
   }
+  // a statistic that is not finite means an activation left its type's range (or the input held
+  // inf/NaN): recorded for the caller's check, the row is written as computed
+  if (a.flags && tid == 0 && !(__builtin_isfinite(ss1) && __builtin_isfinite(ss2))) a.flags[0] = 1u;
   const float inv_e = 1.f / static_cast<float>(a.E);
   const float r1 = 1.f / sqrtf(ss1 * inv_e + a.eps);
   const float r2 = 1.f / sqrtf(ss2 * inv_e + a.eps);

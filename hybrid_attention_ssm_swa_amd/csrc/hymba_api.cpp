@@ -36,12 +36,14 @@ struct hymba_layer {
   float* h_meta = nullptr;     // [E, N]
   char* y_meta = nullptr;      // [M, d] storage type
   float* A2 = nullptr;         // [E, N] A * log2(e)
+  uint32_t* flags = nullptr;   // [2] device-side checks: non-finite branch statistic, bad decode position
   half_t* w_in16 = nullptr;    // bf16 layers: fp16 copies of the weights
   half_t* w_o16 = nullptr;
   bool prepared = false;
   // second stream of a prefill (the SSM branch runs beside attention and W_O), created on first use
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  bool overlap = true;                     // prefill: SSM branch on the side stream (false: all on the call's stream)
   int side_device = -1;
   bool weights_ready = false;
   const hymba_layer* producer = nullptr;   // consumer: bound producer
@@ -49,7 +51,7 @@ struct hymba_layer {
   const void* prep_kmeta = nullptr;        // consumer: meta K/V used by the last prepare
   const void* prep_vmeta = nullptr;
   // column offsets of the shared projection
-  int64_t n_in = 0, off_k = 0, off_v = 0, off_u = 0, off_z = 0, off_dt = 0, off_b = 0;
+  int64_t n_in = 0, ld_p = 0, off_k = 0, off_v = 0, off_u = 0, off_z = 0, off_dt = 0, off_b = 0;
   // stage timing: a pool of begin/end event pairs, one pair per timed interval of each hot call
   bool profiling = false;
   std::vector<hipEvent_t> ev;          // 2 * kProfPairs events once profiling was first enabled
@@ -162,7 +164,7 @@ int32_t check_cfg(const hymba_layer_cfg* c) {
 }
 
 struct PersistLayout {
-  size_t k_meta, v_meta, h_meta, y_meta, A2, w_in16, w_o16, total;
+  size_t k_meta, v_meta, h_meta, y_meta, A2, flags, w_in16, w_o16, total;
 };
 
 PersistLayout persist_layout(const hymba_layer_cfg& c) {
@@ -175,6 +177,7 @@ PersistLayout persist_layout(const hymba_layer_cfg& c) {
   p.h_meta = off; off += align_up((size_t)c.d_inner * c.d_state * 4);
   p.y_meta = off; off += align_up((size_t)c.n_meta * c.d_model * ss);
   p.A2 = off; off += align_up((size_t)c.d_inner * c.d_state * 4);
+  p.flags = off; off += align_up(2 * sizeof(uint32_t));
   if (is_bf16(c)) {
     const size_t hq = (size_t)c.n_heads * c.head_dim;
     p.w_in16 = off; off += align_up((size_t)n_in_of(c) * c.d_model * 2);
@@ -198,7 +201,7 @@ WsLayout ws_layout(const hymba_layer& L, int64_t batch, int64_t seq) {
   w.rows = rows;
   size_t off = 0;
   w.X16 = off; off += b16 ? align_up((size_t)rows * c.d_model * 2) : 0;
-  w.P = off; off += align_up((size_t)rows * L.n_in * as);
+  w.P = off; off += align_up((size_t)rows * L.ld_p * as);
   w.bc32 = off; off += b16 ? align_up((size_t)rows * 2 * c.d_state * 4) : 0;
   w.O = off; off += align_up((size_t)rows * c.n_heads * c.head_dim * as);
   w.Ao = off; off += align_up((size_t)rows * c.d_inner * as);
@@ -275,48 +278,40 @@ void meta_kv_of(const hymba_layer& L, const hymba_kv* kv, const void** km, const
   *vm = kv ? kv->v_meta : nullptr;
 }
 
-// Shared projection of `rows` rows of x (storage type) into P (activation type).
+// Shared projection of `rows` rows of x (storage type) into P (activation type).  A bf16 layer
+// also writes the B/C columns in fp32 to bc32 (from the fp32 accumulator): every channel's
+// normalised SSM output depends on sum_n C[n] B[n] of its token, so those shared columns keep fp32.
 template <typename CT>
-// bc32: also write the B/C columns in fp32 (the prefill scan reads them so; the decode step
-// reads them from P).
 int32_t in_projection(const hymba_layer& L, const void* x, int64_t rows, char* ws, const WsLayout& wl,
-                      bool bc32, hipStream_t s) {
+                      hipStream_t s) {
   const hymba_layer_cfg& c = L.cfg;
+  float* bc32 = reinterpret_cast<float*>(ws + wl.bc32);
   if (is_bf16(c) && skinny_fits(rows, L.n_in, c.d_model)) {
     // few rows: one weight-streaming GEMM reads x in bf16 (converted to fp16 on the way in) and
-    // writes P in fp16, plus the B/C columns in fp32 for the scan
+    // writes P in fp16, plus the B/C columns in fp32
     StageTimer st(L, ST_IN_PROJ, s);
     SkinnyArgs<half_t, bf16_t, half_t> a{L.w_in16, c.d_model, static_cast<const bf16_t*>(x), c.d_model,
-                                         reinterpret_cast<half_t*>(ws + wl.P), L.n_in,
-                                         bc32 ? reinterpret_cast<float*>(ws + wl.bc32) : nullptr, 2 * c.d_state,
+                                         reinterpret_cast<half_t*>(ws + wl.P), L.ld_p, bc32, 2 * c.d_state,
                                          static_cast<int>(L.off_b), static_cast<int>(L.off_b + 2 * c.d_state),
                                          static_cast<int>(rows), static_cast<int>(L.n_in), c.d_model};
-    HIP_TRY(launch_skinny_gemm(a, s),
-            "input projection (few rows) launch");
+    HIP_TRY(launch_skinny_gemm(a, s), "input projection (few rows) launch");
     return HYMBA_OK;
   }
   if (is_bf16(c)) {
     half_t* x16 = reinterpret_cast<half_t*>(ws + wl.X16);
     {
+      // x to fp16 for the GEMM, fused with the fp32 B/C columns
       StageTimer st(L, ST_CVT, s);
-      HIP_TRY(launch_convert(static_cast<const bf16_t*>(x), c.d_model, x16, c.d_model, rows, c.d_model, s),
-              "input conversion");
+      ConvBcArgs a{static_cast<const bf16_t*>(x), c.d_model, x16, c.d_model, L.w_in16 + L.off_b * c.d_model,
+                   c.d_model, bc32, 2 * c.d_state, rows, c.d_model, 2 * c.d_state};
+      HIP_TRY(launch_convert_bc(a, s), "input conversion");
     }
-    {
-      StageTimer st(L, ST_IN_PROJ, s);
-      STATUS_TRY(project(L, x16, c.d_model, L.w_in16, c.d_model, ws + wl.P, L.n_in, rows, L.n_in, c.d_model,
-                         false, ws, wl, s));
-    }
-    if (!bc32) return HYMBA_OK;
-    // B/C columns as fp32 for the scan
-    StageTimer st(L, ST_CVT, s);
-    HIP_TRY(launch_convert(reinterpret_cast<const half_t*>(ws + wl.P) + L.off_b, L.n_in,
-                           reinterpret_cast<float*>(ws + wl.bc32), 2 * c.d_state, rows, 2 * c.d_state, s),
-            "B/C conversion");
-    return HYMBA_OK;
+    StageTimer st(L, ST_IN_PROJ, s);
+    return project(L, x16, c.d_model, L.w_in16, c.d_model, ws + wl.P, L.ld_p, rows, L.n_in, c.d_model, false, ws,
+                   wl, s);
   }
   StageTimer st(L, ST_IN_PROJ, s);
-  return project(L, x, c.d_model, L.w.w_in, c.d_model, ws + wl.P, L.n_in, rows, L.n_in, c.d_model, false, ws, wl,
+  return project(L, x, c.d_model, L.w.w_in, c.d_model, ws + wl.P, L.ld_p, rows, L.n_in, c.d_model, false, ws, wl,
                  s);
 }
 
@@ -329,7 +324,7 @@ int32_t apply_rope(const hymba_layer& L, char* ws, const WsLayout& wl, int64_t r
   if (!(c.rope_base > 0.f)) return HYMBA_OK;
   StageTimer st(L, ST_ROPE, s);
   RopeArgs<CT> a{};
-  a.p = reinterpret_cast<CT*>(ws + wl.P); a.ld = L.n_in;
+  a.p = reinterpret_cast<CT*>(ws + wl.P); a.ld = L.ld_p;
   a.rows = rows; a.T = T;
   a.n_q_heads = c.n_heads; a.k_off = L.off_k; a.n_k_heads = c.own_kv ? c.n_kv_heads : 0; a.head_dim = c.head_dim;
   a.first = first; a.pos = pos;
@@ -364,10 +359,11 @@ int32_t epilogue_and_out(const hymba_layer& L, char* ws, const WsLayout& wl, int
     const CT* P = reinterpret_cast<const CT*>(ws + wl.P);
     e.ao = reinterpret_cast<const CT*>(ws + wl.Ao); e.ld_ao = c.d_inner;
     e.y = reinterpret_cast<const CT*>(ws + wl.Ys); e.ld_y = c.d_inner;
-    e.z = P + L.off_z; e.ld_z = L.n_in;
+    e.z = P + L.off_z; e.ld_z = L.ld_p;
     e.beta1 = L.w.beta1; e.beta2 = L.w.beta2;
     e.f = reinterpret_cast<FT*>(ws + wl.F); e.ld_f = c.d_inner;
     e.rows = rows; e.E = c.d_inner; e.eps = c.rms_eps;
+    e.flags = L.flags;
     HIP_TRY(launch_epilogue(e, s), "epilogue launch");
   }
   StageTimer st(L, ST_OUT, s);
@@ -406,11 +402,11 @@ ScanArgs<CT> scan_args(const hymba_layer& L, char* ws, const WsLayout& wl, int B
   const hymba_layer_cfg& c = L.cfg;
   const CT* P = reinterpret_cast<const CT*>(ws + wl.P);
   ScanArgs<CT> sa{};
-  sa.u = P + L.off_u; sa.dt = P + L.off_dt; sa.ld = L.n_in;
+  sa.u = P + L.off_u; sa.dt = P + L.off_dt; sa.ld = L.ld_p;
   if (is_bf16(c)) {
     sa.bc = reinterpret_cast<const float*>(ws + wl.bc32); sa.ld_bc = 2 * c.d_state;
   } else {
-    sa.bc = reinterpret_cast<const float*>(P + L.off_b); sa.ld_bc = L.n_in;
+    sa.bc = reinterpret_cast<const float*>(P + L.off_b); sa.ld_bc = L.ld_p;
   }
   sa.A2 = L.A2; sa.D = L.w.D; sa.dt_bias = L.w.dt_bias;
   sa.h0 = h0; sa.h0_bstride = 0;
@@ -425,6 +421,7 @@ int32_t prepare_impl(hymba_layer& L, const hymba_kv* kv, char* ws, const WsLayou
   const hymba_layer_cfg& c = L.cfg;
   const int M = c.n_meta;
   if (!L.weights_ready) {
+    HIP_TRY(launch_fill(reinterpret_cast<float*>(L.flags), 2, 0.f, s), "check flags clear");
     HIP_TRY(launch_scale_copy(L.w.A, L.A2, (int64_t)c.d_inner * c.d_state, kLog2e, s), "A scaling");
     if (is_bf16(c)) {
       const int64_t hq = (int64_t)c.n_heads * c.head_dim;
@@ -449,7 +446,7 @@ int32_t prepare_impl(hymba_layer& L, const hymba_kv* kv, char* ws, const WsLayou
     L.prep_kmeta = km; L.prep_vmeta = vm;
     return HYMBA_OK;
   }
-  STATUS_TRY(in_projection<CT>(L, L.w.meta, M, ws, wl, true, s));
+  STATUS_TRY(in_projection<CT>(L, L.w.meta, M, ws, wl, s));
   STATUS_TRY(apply_rope<CT>(L, ws, wl, M, M, 0, nullptr, s));   // meta rows at positions 0..M-1
   const CT* P = reinterpret_cast<const CT*>(ws + wl.P);
   const int64_t kvw = (int64_t)c.n_kv_heads * c.head_dim;
@@ -457,17 +454,17 @@ int32_t prepare_impl(hymba_layer& L, const hymba_kv* kv, char* ws, const WsLayou
   int64_t ld_kv;
   if (c.own_kv) {
     KvWriteArgs<CT> a{};
-    a.k_src = P + L.off_k; a.v_src = P + L.off_v; a.ld_src = L.n_in;
+    a.k_src = P + L.off_k; a.v_src = P + L.off_v; a.ld_src = L.ld_p;
     a.k_full = reinterpret_cast<CT*>(L.k_meta); a.v_full = reinterpret_cast<CT*>(L.v_meta);
     a.B = 1; a.T = M; a.n_kv_heads = c.n_kv_heads; a.head_dim = c.head_dim;
     HIP_TRY(launch_kv_write(a, s), "meta K/V write");
-    kk = P + L.off_k; vv = P + L.off_v; ld_kv = L.n_in;
+    kk = P + L.off_k; vv = P + L.off_v; ld_kv = L.ld_p;
     km = L.k_meta; vm = L.v_meta;
   } else {
     kk = static_cast<const CT*>(km); vv = static_cast<const CT*>(vm); ld_kv = kvw;
   }
   // meta rows attend causally among themselves: a global pass with no prefix
-  STATUS_TRY(run_attention<CT>(c, P, L.n_in, kk, vv, ld_kv, (int64_t)M * ld_kv, nullptr, nullptr, 0,
+  STATUS_TRY(run_attention<CT>(c, P, L.ld_p, kk, vv, ld_kv, (int64_t)M * ld_kv, nullptr, nullptr, 0,
                                reinterpret_cast<CT*>(ws + wl.O), (int64_t)c.n_heads * c.head_dim, 1, M, 0, s));
   HIP_TRY(launch_selective_scan(scan_args<CT>(L, ws, wl, 1, M, nullptr, L.h_meta), s), "meta scan launch");
   STATUS_TRY(tail<CT>(L, ws, wl, M, L.y_meta, s));
@@ -495,17 +492,17 @@ int32_t prefill_impl(hymba_layer& L, const void* x, int B, int T_, void* y, cons
   const hymba_layer_cfg& c = L.cfg;
   const int64_t rows = (int64_t)B * T_;
   const int64_t kvw = (int64_t)c.n_kv_heads * c.head_dim;
-  STATUS_TRY(in_projection<CT>(L, x, rows, ws, wl, true, s));
+  STATUS_TRY(in_projection<CT>(L, x, rows, ws, wl, s));
   STATUS_TRY(apply_rope<CT>(L, ws, wl, rows, T_, c.n_meta, nullptr, s));   // real token t at M + t
   const CT* P = reinterpret_cast<const CT*>(ws + wl.P);
   const CT *k, *v;
   int64_t ld_kv, seq_stride;
   if (c.own_kv) {
-    k = P + L.off_k; v = P + L.off_v; ld_kv = L.n_in; seq_stride = (int64_t)T_ * L.n_in;
+    k = P + L.off_k; v = P + L.off_v; ld_kv = L.ld_p; seq_stride = (int64_t)T_ * L.ld_p;
     if (kv && (kv->k || kv->k_cache)) {
       StageTimer st(L, ST_KV, s);
       KvWriteArgs<CT> a{};
-      a.k_src = P + L.off_k; a.v_src = P + L.off_v; a.ld_src = L.n_in;
+      a.k_src = P + L.off_k; a.v_src = P + L.off_v; a.ld_src = L.ld_p;
       a.k_full = static_cast<CT*>(kv->k); a.v_full = static_cast<CT*>(kv->v);
       a.k_cache = static_cast<CT*>(kv->k_cache); a.v_cache = static_cast<CT*>(kv->v_cache);
       a.cache_len = kv->cache_len;
@@ -519,23 +516,28 @@ int32_t prefill_impl(hymba_layer& L, const void* x, int B, int T_, void* y, cons
   const void *km, *vm;
   meta_kv_of(L, kv, &km, &vm);
   // The SSM branch depends only on the projection: it runs on the layer's side stream beside
-  // attention and W_O, and the epilogue waits for both.
-  STATUS_TRY(ensure_side_stream(L));
-  HIP_TRY(hipEventRecord(L.ev_fork, s), "fork event");
-  HIP_TRY(hipStreamWaitEvent(L.side, L.ev_fork, 0), "fork wait");
-  {
-    StageTimer st(L, ST_SSM, L.side);
-    HIP_TRY(launch_selective_scan(scan_args<CT>(L, ws, wl, B, T_, L.h_meta, state_out), L.side), "scan launch");
+  // attention and W_O, and the epilogue waits for both (or, with overlap off, first on the call's
+  // stream, so that every kernel runs alone).
+  hipStream_t ss = s;
+  if (L.overlap) {
+    STATUS_TRY(ensure_side_stream(L));
+    HIP_TRY(hipEventRecord(L.ev_fork, s), "fork event");
+    HIP_TRY(hipStreamWaitEvent(L.side, L.ev_fork, 0), "fork wait");
+    ss = L.side;
   }
-  HIP_TRY(hipEventRecord(L.ev_join, L.side), "join event");
+  {
+    StageTimer st(L, ST_SSM, ss);
+    HIP_TRY(launch_selective_scan(scan_args<CT>(L, ws, wl, B, T_, L.h_meta, state_out), ss), "scan launch");
+  }
+  if (L.overlap) HIP_TRY(hipEventRecord(L.ev_join, ss), "join event");
   {
     StageTimer st(L, ST_ATTN, s);
-    STATUS_TRY(run_attention<CT>(c, P, L.n_in, k, v, ld_kv, seq_stride, static_cast<const CT*>(km),
+    STATUS_TRY(run_attention<CT>(c, P, L.ld_p, k, v, ld_kv, seq_stride, static_cast<const CT*>(km),
                                  static_cast<const CT*>(vm), c.n_meta, reinterpret_cast<CT*>(ws + wl.O),
                                  (int64_t)c.n_heads * c.head_dim, B, T_, c.window, s));
   }
   STATUS_TRY(w_o_projection<CT>(L, ws, wl, rows, s));
-  HIP_TRY(hipStreamWaitEvent(s, L.ev_join, 0), "join wait");
+  if (L.overlap) HIP_TRY(hipStreamWaitEvent(s, L.ev_join, 0), "join wait");
   return epilogue_and_out<CT>(L, ws, wl, rows, y, s);
 }
 
@@ -544,13 +546,13 @@ int32_t decode_impl(hymba_layer& L, const void* x, const int64_t* pos, int B, vo
                     float* state, char* ws, const WsLayout& wl, hipStream_t s) {
   if (L.profiling) ++L.prof_calls;
   const hymba_layer_cfg& c = L.cfg;
-  STATUS_TRY(in_projection<CT>(L, x, B, ws, wl, false, s));
+  STATUS_TRY(in_projection<CT>(L, x, B, ws, wl, s));
   STATUS_TRY(apply_rope<CT>(L, ws, wl, B, 1, c.n_meta, pos, s));   // the new token at M + pos[b]
   const CT* P = reinterpret_cast<const CT*>(ws + wl.P);
   if (c.own_kv) {
     StageTimer st(L, ST_KV, s);
     KvWriteArgs<CT> a{};
-    a.k_src = P + L.off_k; a.v_src = P + L.off_v; a.ld_src = L.n_in;
+    a.k_src = P + L.off_k; a.v_src = P + L.off_v; a.ld_src = L.ld_p;
     a.k_cache = static_cast<CT*>(kv->k_cache); a.v_cache = static_cast<CT*>(kv->v_cache);
     a.cache_len = kv->cache_len; a.pos = pos;
     a.B = B; a.T = 1; a.n_kv_heads = c.n_kv_heads; a.head_dim = c.head_dim;
@@ -565,7 +567,7 @@ int32_t decode_impl(hymba_layer& L, const void* x, const int64_t* pos, int B, vo
   {
     StageTimer st(L, ST_ATTN, s);
     DecAttnArgs<CT> a{};
-    a.q = P; a.ld_q = L.n_in;
+    a.q = P; a.ld_q = L.ld_p;
     a.k_meta = static_cast<const CT*>(km); a.v_meta = static_cast<const CT*>(vm);
     a.ld_meta = (int64_t)c.n_kv_heads * c.head_dim; a.n_meta = c.n_meta;
     a.k_cache = static_cast<const CT*>(kv->k_cache); a.v_cache = static_cast<const CT*>(kv->v_cache);
@@ -574,13 +576,19 @@ int32_t decode_impl(hymba_layer& L, const void* x, const int64_t* pos, int B, vo
     a.part = reinterpret_cast<float*>(ws + wl.part);
     a.B = B; a.n_heads = c.n_heads; a.n_kv_heads = c.n_kv_heads; a.head_dim = c.head_dim;
     a.window = c.window; a.splits = splits;
+    a.flags = L.flags;
     a.scale_log2 = kLog2e / std::sqrt(static_cast<float>(c.head_dim));
     HIP_TRY(launch_decode_attn(a, s), "decode attention launch");
   }
   {
     StageTimer tm(L, ST_SSM, s);
     StepArgs<CT> st{};
-    st.u = P + L.off_u; st.dt = P + L.off_dt; st.bc = P + L.off_b; st.ld = L.n_in;
+    st.u = P + L.off_u; st.dt = P + L.off_dt; st.ld = L.ld_p;
+    if (is_bf16(c)) {
+      st.bc = reinterpret_cast<const float*>(ws + wl.bc32); st.ld_bc = 2 * c.d_state;
+    } else {
+      st.bc = reinterpret_cast<const float*>(P + L.off_b); st.ld_bc = L.ld_p;
+    }
     st.A2 = L.A2; st.D = L.w.D; st.dt_bias = L.w.dt_bias; st.h = state;
     st.y = reinterpret_cast<CT*>(ws + wl.Ys); st.ldy = c.d_inner;
     st.B = B; st.E = c.d_inner; st.N = c.d_state;
@@ -624,12 +632,16 @@ int32_t hymba_layer_create(const hymba_layer_cfg* cfg, const hymba_layer_weights
   L->h_meta = reinterpret_cast<float*>(base + pl.h_meta);
   L->y_meta = base + pl.y_meta;
   L->A2 = reinterpret_cast<float*>(base + pl.A2);
+  L->flags = reinterpret_cast<uint32_t*>(base + pl.flags);
   if (is_bf16(*cfg)) {
     L->w_in16 = reinterpret_cast<half_t*>(base + pl.w_in16);
     L->w_o16 = reinterpret_cast<half_t*>(base + pl.w_o16);
   }
   const int64_t q = (int64_t)cfg->n_heads * cfg->head_dim, kvw = (int64_t)cfg->n_kv_heads * cfg->head_dim;
   L->n_in = n_in_of(*cfg);
+  // row stride of the projection P: whole 64-element (128-byte for fp16) segments, so the
+  // per-channel column slices the scan and epilogue read start on cache-line boundaries
+  L->ld_p = (L->n_in + 63) / 64 * 64;
   L->off_k = q;
   L->off_v = q + kvw;
   L->off_u = q + (cfg->own_kv ? 2 * kvw : 0);
@@ -755,6 +767,28 @@ int32_t hymba_layer_meta_outputs(const hymba_layer* L, const void** k_meta, cons
   return HYMBA_OK;
 }
 
+int32_t hymba_layer_check(hymba_layer* L, void* stream) {
+  if (!L) return fail(HYMBA_ERR_INVALID_ARG, "layer is NULL");
+  if (!L->weights_ready) return HYMBA_OK;   // nothing has run on the device yet
+  HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "stream synchronize");
+  uint32_t f[2] = {0u, 0u};
+  HIP_TRY(hipMemcpy(f, L->flags, sizeof(f), hipMemcpyDeviceToHost), "check flags read");
+  if (f[0] == 0u && f[1] == 0u) return HYMBA_OK;
+  const uint32_t zero[2] = {0u, 0u};
+  HIP_TRY(hipMemcpy(L->flags, zero, sizeof(zero), hipMemcpyHostToDevice), "check flags clear");
+  if (f[0])
+    return fail(HYMBA_ERR_RANGE, "a row's attention or SSM branch output was not finite: an activation left the "
+                                 "range of the activation type (fp16 for bf16 layers: |value| > 65504) or the input "
+                                 "held inf/NaN%s", f[1] ? "; also a decode position was negative" : "");
+  return fail(HYMBA_ERR_RANGE, "a decode position was negative");
+}
+
+int32_t hymba_layer_set_overlap(hymba_layer* L, int32_t enable) {
+  if (!L) return fail(HYMBA_ERR_INVALID_ARG, "layer is NULL");
+  L->overlap = enable != 0;
+  return HYMBA_OK;
+}
+
 int32_t hymba_layer_profile(hymba_layer* L, int32_t enable) {
   if (!L) return fail(HYMBA_ERR_INVALID_ARG, "layer is NULL");
   if (!enable) {
@@ -812,6 +846,7 @@ const char* hymba_status_string(int32_t status) {
     case HYMBA_ERR_WORKSPACE: return "HYMBA_ERR_WORKSPACE";
     case HYMBA_ERR_BIND: return "HYMBA_ERR_BIND";
     case HYMBA_ERR_HIP: return "HYMBA_ERR_HIP";
+    case HYMBA_ERR_RANGE: return "HYMBA_ERR_RANGE";
     default: return "HYMBA_UNKNOWN_STATUS";
   }
 }
@@ -827,7 +862,10 @@ int32_t hymba_kernel_attention(int32_t dtype, const void* q, int64_t ld_q, const
   hymba_layer_cfg c{};
   c.n_heads = n_heads; c.n_kv_heads = n_kv_heads; c.head_dim = head_dim;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == HYMBA_F16 || dtype == HYMBA_BF16) {
+  if (dtype == HYMBA_BF16)
+    return fail(HYMBA_ERR_UNSUPPORTED, "16-bit attention runs on fp16 operands (HYMBA_F16): bf16 probabilities "
+                                       "would round the P.V operand to 8 significand bits");
+  if (dtype == HYMBA_F16) {
     if (!attn_mfma_supported(head_dim, n_heads, n_kv_heads, n_meta))
       return fail(HYMBA_ERR_UNSUPPORTED, "16-bit attention shape not supported");
     // 16-byte rows for the vector loads; row offsets within a 64-key tile fit 32 bits
@@ -836,15 +874,10 @@ int32_t hymba_kernel_attention(int32_t dtype, const void* q, int64_t ld_q, const
         ld_kv >= (1 << 24) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
         (n_meta > 0 && (!aligned(k_meta, 16) || !aligned(v_meta, 16))))
       return fail(HYMBA_ERR_INVALID_ARG, "strides: rows >= heads * hd, multiples of 8 elements, 16-byte aligned");
-    if (dtype == HYMBA_F16)
-      return run_attention<half_t>(c, static_cast<const half_t*>(q), ld_q, static_cast<const half_t*>(k),
-                                   static_cast<const half_t*>(v), ld_kv, kv_seq_stride,
-                                   static_cast<const half_t*>(k_meta), static_cast<const half_t*>(v_meta), n_meta,
-                                   static_cast<half_t*>(o), ld_o, B, T, window, s);
-    return run_attention<bf16_t>(c, static_cast<const bf16_t*>(q), ld_q, static_cast<const bf16_t*>(k),
-                                 static_cast<const bf16_t*>(v), ld_kv, kv_seq_stride,
-                                 static_cast<const bf16_t*>(k_meta), static_cast<const bf16_t*>(v_meta), n_meta,
-                                 static_cast<bf16_t*>(o), ld_o, B, T, window, s);
+    return run_attention<half_t>(c, static_cast<const half_t*>(q), ld_q, static_cast<const half_t*>(k),
+                                 static_cast<const half_t*>(v), ld_kv, kv_seq_stride,
+                                 static_cast<const half_t*>(k_meta), static_cast<const half_t*>(v_meta), n_meta,
+                                 static_cast<half_t*>(o), ld_o, B, T, window, s);
   }
   if (dtype != HYMBA_F32) return fail(HYMBA_ERR_INVALID_ARG, "bad dtype");
   if (head_dim != 32 && head_dim != 64) return fail(HYMBA_ERR_UNSUPPORTED, "fp32 attention head_dim");

@@ -26,7 +26,6 @@ struct AttnArgs {
 };
 // MFMA kernel (hd = 64), fp16 or bf16 operands, fp32 accumulation.
 hipError_t launch_attn_prefill_mfma(const AttnArgs<half_t>& a, hipStream_t s);
-hipError_t launch_attn_prefill_mfma(const AttnArgs<bf16_t>& a, hipStream_t s);
 // VALU kernel, fp32 (hd 32 or 64).
 hipError_t launch_attn_prefill_f32(const AttnArgs<float>& a, hipStream_t s);
 bool attn_mfma_supported(int head_dim, int n_heads, int n_kv_heads, int n_meta);
@@ -54,7 +53,8 @@ hipError_t launch_selective_scan(const ScanArgs<half_t>& a, hipStream_t s);
 // activation type, B at bc[0..N), C at bc[N..2N)).
 template <typename CT>
 struct StepArgs {
-  const CT* u; const CT* dt; const CT* bc; int64_t ld;
+  const CT* u; const CT* dt; int64_t ld;
+  const float* bc; int64_t ld_bc;   // B_t at bc[0, N), C_t at bc[N, 2N) of row b (fp32)
   const float* A2; const float* D; const float* dt_bias;
   float* h;
   CT* y; int64_t ldy;
@@ -74,6 +74,7 @@ struct EpiArgs {
   const float* beta1; const float* beta2;
   FT* f; int64_t ld_f;
   int64_t rows; int E; float eps;
+  uint32_t* flags;   // or null: word 0 set to 1 when a row's branch statistic is not finite
 };
 hipError_t launch_epilogue(const EpiArgs<float>& a, hipStream_t s);
 hipError_t launch_epilogue(const EpiArgs<half_t, bf16_t>& a, hipStream_t s);
@@ -109,6 +110,7 @@ struct DecAttnArgs {
   float* part;
   int B, n_heads, n_kv_heads, head_dim, window, splits;
   float scale_log2;
+  uint32_t* flags;   // or null: word 1 set to 1 when a sequence's position is negative
 };
 hipError_t launch_decode_attn(const DecAttnArgs<float>& a, hipStream_t s);
 hipError_t launch_decode_attn(const DecAttnArgs<half_t>& a, hipStream_t s);
@@ -204,6 +206,18 @@ constexpr int64_t kSkinnyMaxWeightBytes = int64_t(24) << 20;
 inline bool skinny_fits(int64_t rows, int64_t n, int64_t k) {
   return rows > 0 && rows <= kSkinnyMaxRows && n * k * 2 <= kSkinnyMaxWeightBytes;
 }
+
+// ---- input conversion fused with the fp32 B/C columns -------------------------------
+// x16 [rows, d] = fp16(x [rows, d] bf16); bc [rows, nbc] fp32 = x . wbc^T (wbc fp16 [nbc, d],
+// nbc = 2N = 16 or 32).  d, ldx, ldx16, ldw multiples of 8; 16-byte aligned rows.
+struct ConvBcArgs {
+  const bf16_t* x; int64_t ldx;
+  half_t* x16; int64_t ldx16;
+  const half_t* wbc; int64_t ldw;
+  float* bc; int64_t ldbc;
+  int64_t rows; int d; int nbc;
+};
+hipError_t launch_convert_bc(const ConvBcArgs& a, hipStream_t s);
 
 // ---- misc ----------------------------------------------------------------------
 hipError_t launch_scale_copy(const float* src, float* dst, int64_t n, float scale, hipStream_t s);

@@ -199,12 +199,6 @@ __global__ __launch_bounds__(64 * (N / NS)) void selective_scan_kernel(
 // kVec: the lane's 4 B and 4 C values come as two vector loads (the dispatcher
 // checks their alignment) instead of eight scalar ones.
 template <typename T> struct Four;
-template <> struct Four<half_t> {
-  __device__ static __forceinline__ void load(const half_t* p, float (&v)[4]) {
-    const uint2 w = *reinterpret_cast<const uint2*>(p);
-    v[0] = f16lo(w.x); v[1] = f16hi(w.x); v[2] = f16lo(w.y); v[3] = f16hi(w.y);
-  }
-};
 template <> struct Four<float> {
   __device__ static __forceinline__ void load(const float* p, float (&v)[4]) {
     const float4 w = *reinterpret_cast<const float4*>(p);
@@ -221,7 +215,7 @@ __global__ __launch_bounds__(256) void ssm_step_kernel(StepArgs<T> a) {
   const int q = i2 % LPC, c = i2 / LPC;
   const int64_t b = blockIdx.y;
   const int64_t ch = b * a.E + c;
-  const T* row = a.bc + b * a.ld;
+  const float* row = a.bc + b * a.ld_bc;
   const float uv = Elem<T>::load(a.u + b * a.ld + c);
   const float dv = Elem<T>::load(a.dt + b * a.ld + c);
   const float delta = softplus_f(dv + a.dt_bias[c]);
@@ -233,13 +227,13 @@ __global__ __launch_bounds__(256) void ssm_step_kernel(StepArgs<T> a) {
   const float a2s[4] = {a2.x, a2.y, a2.z, a2.w};
   float bn[4], cn[4];
   if constexpr (kVec) {
-    Four<T>::load(row + 4 * q, bn);
-    Four<T>::load(row + N + 4 * q, cn);
+    Four<float>::load(row + 4 * q, bn);
+    Four<float>::load(row + N + 4 * q, cn);
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      bn[j] = Elem<T>::load(row + 4 * q + j);
-      cn[j] = Elem<T>::load(row + N + 4 * q + j);
+      bn[j] = row[4 * q + j];
+      cn[j] = row[N + 4 * q + j];
     }
   }
   float part = 0.f;
@@ -298,7 +292,7 @@ hipError_t step_dispatch(const StepArgs<T>& a, hipStream_t s) {
   if (a.B > 65535 || (int64_t)a.E * (a.N / 4) >= INT32_MAX) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(ceil_div((int64_t)a.E * (a.N / 4), 256)), static_cast<unsigned>(a.B)), block(256);
   // B/C as vector loads when every row's 4-state groups are aligned to the vector size
-  const bool vec = reinterpret_cast<uintptr_t>(a.bc) % (4 * sizeof(T)) == 0 && a.ld % 4 == 0 && a.N % 4 == 0;
+  const bool vec = reinterpret_cast<uintptr_t>(a.bc) % 16 == 0 && a.ld_bc % 4 == 0 && a.N % 4 == 0;
   switch (a.N * 2 + (vec ? 1 : 0)) {
     case 16: hipLaunchKernelGGL((ssm_step_kernel<T, 8, false>), grid, block, 0, s, a); break;
     case 17: hipLaunchKernelGGL((ssm_step_kernel<T, 8, true>), grid, block, 0, s, a); break;

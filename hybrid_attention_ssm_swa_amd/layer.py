@@ -134,6 +134,13 @@ class MixerLayer:
                              ws.data_ptr(), ws.numel(), self.stream())
         return y
 
+    def check(self) -> None:
+        """Raises HymbaError(HYMBA_ERR_RANGE) if a device-side check failed since the last check."""
+        L.hymba_layer_check(self.handle, self.stream())
+
+    def set_overlap(self, enable: bool) -> None:
+        L.hymba_layer_set_overlap(self.handle, enable)
+
     def meta_outputs(self):
         """(k_meta, v_meta, h_meta, y_meta) as device tensors viewing the persistent buffer."""
         s = self.shape

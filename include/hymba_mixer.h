@@ -57,6 +57,7 @@ extern "C" {
 #define HYMBA_ERR_WORKSPACE (-3)   /* workspace or persistent buffer too small          */
 #define HYMBA_ERR_BIND (-4)        /* KV-sharing misuse                                  */
 #define HYMBA_ERR_HIP (-5)         /* HIP runtime / library error                         */
+#define HYMBA_ERR_RANGE (-6)       /* device-side check failed (see hymba_layer_check)    */
 
 /* Layer types (hymba_layer_cfg.dtype):
  *   HYMBA_F32:  x, y, weights and activations fp32.
@@ -211,6 +212,28 @@ const char* hymba_status_string(int32_t status);
  * enable creates the events (HYMBA_ERR_HIP on failure); nothing else touches
  * the device.                                                               */
 #define HYMBA_N_STAGES 9
+
+/* Device-side checks (async).  Every prefill and decode of the layer records
+ * in its persistent buffer whether (a) a row's attention or SSM branch output
+ * was not finite, which means an activation left the activation type's range
+ * (bf16 layers compute in fp16: any |x|, weight or projected value above
+ * 65504 overflows; values below 2^-14 lose relative precision as fp16
+ * subnormals, an absolute error of at most 2^-25 per element) or the input held
+ * inf/NaN, or (b) a decode position pos[b] was negative (such a sequence
+ * writes no cache slot and attends to the meta keys only).  Outputs are
+ * written as computed either way.  hymba_layer_check synchronises `stream`,
+ * reads and clears the record, and returns HYMBA_ERR_RANGE (with a message)
+ * if anything was recorded since the last check, else HYMBA_OK.  A global
+ * layer's decode at pos >= cache_len is not an error: it attends to the last
+ * cache_len real tokens (exact global attention needs cache_len >= pos + 1). */
+int32_t hymba_layer_check(hymba_layer* layer, void* stream);
+
+/* Prefill schedule.  enable = 1 (the default): the SSM branch (the selective
+ * scan) runs on the layer's second stream, beside attention and W_O.
+ * enable = 0: every kernel of a prefill runs in order on the call's stream,
+ * so stage timings measure each kernel alone.  Results are identical either
+ * way.  Host only. */
+int32_t hymba_layer_set_overlap(hymba_layer* layer, int32_t enable);
 int32_t hymba_layer_profile(hymba_layer* layer, int32_t enable);
 int32_t hymba_layer_profile_read(hymba_layer* layer, float* stage_ms, int32_t n);
 const char* hymba_stage_name(int32_t stage);
@@ -218,8 +241,10 @@ const char* hymba_stage_name(int32_t stage);
 /* ---- per-kernel entry points (parity tests and profiling) -----------------
  * Each runs one kernel of the path on caller buffers, with the same layouts
  * the layer uses internally.  dtype names the element type of the 16/32-bit
- * operands: HYMBA_F32, HYMBA_F16 (what bf16 layers use inside) or, for the
- * attention kernel only, HYMBA_BF16.                                          */
+ * operands: HYMBA_F32 or HYMBA_F16 (what bf16 layers use inside).  The
+ * attention entry returns HYMBA_ERR_UNSUPPORTED for HYMBA_BF16: bf16
+ * probabilities would round the P.V operand to 8 significand bits, which
+ * misses the 2e-2 RMS bar of a bf16 layer, so bf16 layers attend in fp16.   */
 
 /* Prefill attention.  q: rows (b*T + t), ld_q; head h at column h*hd.
  * k/v: row t of sequence b at k + b*kv_seq_stride + t*ld_kv, KV head g at

@@ -49,6 +49,12 @@ def check(name, got, ref, dtype):
 UNIT_ROUNDOFF = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
 
 
+def round_to(a, dtype: str) -> np.ndarray:
+    """a rounded to the 16-bit storage type (round to nearest even), back in fp64."""
+    t = torch.from_numpy(np.asarray(a, np.float64)).to(tdt(dtype))
+    return t.double().numpy()
+
+
 def check_stored(name, got, ref, dtype):
     """For a tensor stored in a 16-bit type (a layer's bf16 output, an fp16 activation):
     each element may also carry its own storage rounding, so the bar is
@@ -65,7 +71,10 @@ def check_stored(name, got, ref, dtype):
     bound = TOL[dtype] * rms + UNIT_ROUNDOFF[dtype] * np.abs(ref)
     r = float(np.max(np.abs(got - ref) / bound))
     e = rel_err(got, ref)
-    print(f"  {name}: max|err|/rms = {e:.3e}; max err/(bar*rms + u|ref|) = {r:.3f}", flush=True)
+    # the floor: the exact reference itself rounded to the storage type
+    floor = rel_err(round_to(ref, dtype), ref)
+    print(f"  {name}: max|err|/rms = {e:.3e} (storage-rounding floor {floor:.3e}); "
+          f"max err/(bar*rms + u|ref|) = {r:.3f}", flush=True)
     assert r <= 1.0, f"{name}: {r:.3f} > 1"
     return r
 

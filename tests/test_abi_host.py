@@ -350,3 +350,17 @@ def test_gemm_rows_rejects_bad_arguments():
     assert L.hymba_kernel_gemm_rows_workspace(128, 1600, 3200) == 0
     assert L.hymba_kernel_gemm_rows_workspace(300, 1600, 3200) == 0
     assert L.hymba_kernel_gemm_rows_workspace(128, 16384, 512) == 0
+
+
+def test_check_and_overlap_calls():
+    lib = L.load_library()
+    assert lib.hymba_layer_check(None, None) == L.HYMBA_ERR_INVALID_ARG
+    assert lib.hymba_layer_set_overlap(None, 1) == L.HYMBA_ERR_INVALID_ARG
+    assert H.hymba_status_string(L.HYMBA_ERR_RANGE) == "HYMBA_ERR_RANGE"
+    h = _create(_cfg())
+    try:
+        L.hymba_layer_set_overlap(h, False)     # host only
+        L.hymba_layer_set_overlap(h, True)
+        L.hymba_layer_check(h, None)            # nothing has run on the device: no device call, OK
+    finally:
+        L.hymba_layer_destroy(h)

@@ -12,7 +12,7 @@ import hybrid_attention_ssm_swa_amd as H
 from hymba_synth import bf16_round
 from oracle import hymba_oracle as orc
 
-from gpu_util import UNIT_ROUNDOFF, announce, check, check_bound, check_stored, dev, host
+from gpu_util import announce, check, check_stored, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -34,8 +34,6 @@ ATTN_CASES = [
     ("f16", 2, 130, 16, 8, 1, 64, 40),
     ("f16", 1, 2100, 128, 25, 5, 64, 1024),
     ("f16", 2, 150, 200, 8, 2, 64, 50),
-    ("bf16", 2, 300, 40, 10, 2, 64, 100),
-    ("bf16", 1, 130, 128, 8, 1, 64, 0),
     ("f32", 2, 150, 16, 2, 2, 32, 32),
     ("f32", 1, 70, 5, 6, 3, 64, 0),
 ]
@@ -46,13 +44,21 @@ def test_attention_kernel(dtype, B, T, M, Hq, Hkv, hd, W):
     _attention_case(dtype, B, T, M, Hq, Hkv, hd, W)
 
 
-@pytest.mark.parametrize("dtype,qs", [("f16", 4.0), ("bf16", 4.0), ("f16", 12.0), ("f16", 24.0), ("bf16", 24.0),
-                                      ("f16", 4000.0), ("bf16", 4000.0)])
+@pytest.mark.parametrize("dtype,qs", [("f16", 4.0), ("f16", 12.0), ("f16", 24.0), ("f16", 4000.0)])
 def test_attention_kernel_peaked_scores(dtype, qs):
     """Queries scaled so scores spread over tens of units: the reference max moves by more than the
     growth threshold across tiles, and most probabilities underflow.  At x4000 raw scores pass
     fp16's range (~1e5), where the fp16 kernel must keep its reference in fp32."""
     _attention_case(dtype, 2, 700, 100, 10, 2, 64, 300, qs)
+
+
+def test_attention_kernel_rejects_bf16_operands():
+    """bf16 layers attend in fp16: bf16 probabilities would round the P.V operand to 8 bits."""
+    q = torch.zeros((1, 4, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(H.HymbaError) as e:
+        H.hymba_kernel_attention(H.HYMBA_BF16, q.data_ptr(), 64, q.data_ptr(), q.data_ptr(), 64, 4 * 64, None, None, 0,
+                                 q.data_ptr(), 64, 1, 4, 1, 1, 64, 4, torch.cuda.current_stream().cuda_stream)
+    assert e.value.status == H.HYMBA_ERR_UNSUPPORTED
 
 
 def _attention_case(dtype, B, T, M, Hq, Hkv, hd, W, qs=1.0):
@@ -77,14 +83,7 @@ def _attention_case(dtype, B, T, M, Hq, Hkv, hd, W, qs=1.0):
         K = np.concatenate([km, k[b]])
         V = np.concatenate([vm, v[b]])
         ref = orc.attention(Q, K, V, M, W)[M:]
-        if dtype == "bf16":
-            # bf16 operands: the probabilities are rounded to bf16 before P.V, so
-            # |dO| <= u * max|V| (a convex combination of V with relative weight
-            # errors <= u), plus the output's own rounding u * |O|
-            u = UNIT_ROUNDOFF["bf16"]
-            check_bound(f"O[b={b}]", got[b], ref, u * (np.abs(V).max() + np.abs(ref)) + 1e-3 * np.sqrt(np.mean(ref**2)))
-        else:
-            check(f"O[b={b}]", got[b], ref, dtype)
+        check(f"O[b={b}]", got[b], ref, dtype)
 
 
 SCAN_CASES = [
