@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     hymba_kernel_gemm_rows_workspace,
     hymba_layer_profile, hymba_layer_profile_read, hymba_stage_name, HYMBA_N_STAGES,
     hymba_layer_check, hymba_layer_set_overlap, HYMBA_ERR_RANGE, HYMBA_ERR_UNSUPPORTED,
+    hymba_mixer_decode_static, HYMBA_ERR_INVALID_ARG, HYMBA_ERR_WORKSPACE,
     griffin_block_cfg, griffin_block_weights, griffin_block_persistent_bytes, griffin_block_prepare,
     griffin_workspace_bytes, griffin_block_prefill, griffin_block_decode, GRIFFIN_N_STAGES,
 )

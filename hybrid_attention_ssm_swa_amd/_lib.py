@@ -34,7 +34,7 @@ EXPORTED = [
     "hymba_kernel_selective_scan", "hymba_kernel_epilogue", "hymba_kernel_gemm_rows",
     "hymba_kernel_gemm_rows_workspace",
     "hymba_layer_profile", "hymba_layer_profile_read", "hymba_stage_name",
-    "hymba_layer_check", "hymba_layer_set_overlap",
+    "hymba_layer_check", "hymba_layer_set_overlap", "hymba_mixer_decode_static",
     "griffin_block_persistent_bytes", "griffin_block_prepare", "griffin_workspace_bytes",
     "griffin_block_prefill", "griffin_block_decode",
 ]
@@ -124,6 +124,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hymba_stage_name": (c_char_p, [c_int32]),
         "hymba_layer_check": (c_int32, [P, P]),
         "hymba_layer_set_overlap": (c_int32, [P, c_int32]),
+        "hymba_mixer_decode_static": (c_int32, [P, P, P, c_int32, P, POINTER(hymba_kv), P, P]),
         "griffin_block_persistent_bytes": (c_size_t, [POINTER(griffin_block_cfg)]),
         "griffin_block_prepare": (c_int32, [POINTER(griffin_block_cfg), POINTER(griffin_block_weights), P,
                                             c_size_t, P]),
@@ -206,6 +207,11 @@ def hymba_mixer_decode(layer: int, x_t: int, pos: int, B: int, y_t: int, kv, ssm
                        workspace_bytes: int, stream: int) -> None:
     _check(load_library().hymba_mixer_decode(layer, x_t, pos, B, y_t, _kv_ptr(kv), ssm_state, workspace,
                                               workspace_bytes, stream))
+
+
+def hymba_mixer_decode_static(layer: int, x_t: int, pos: int, B: int, y_t: int, kv, ssm_state: int,
+                              stream: int) -> None:
+    _check(load_library().hymba_mixer_decode_static(layer, x_t, pos, B, y_t, _kv_ptr(kv), ssm_state, stream))
 
 
 def hymba_layer_meta_outputs(layer: int):

@@ -16,6 +16,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <new>
 #include <type_traits>
 #include <string>
@@ -26,6 +27,11 @@
 #include "kernels.h"
 
 using namespace hymba;
+
+// Scratch of the allocation-free decode step (hymba_mixer_decode_static): every device the library
+// runs on holds its own copy until the process ends.
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
 
 struct hymba_layer {
   hymba_layer_cfg cfg;
@@ -190,6 +196,7 @@ PersistLayout persist_layout(const hymba_layer_cfg& c) {
 struct WsLayout {
   size_t X16, P, bc32, O, Ao, Ys, F, gemm, part, total;
   int64_t rows;
+  bool own_kernels_only = false;   // every projection on the hand-written GEMMs (no library workspace)
 };
 
 WsLayout ws_layout(const hymba_layer& L, int64_t batch, int64_t seq) {
@@ -214,6 +221,30 @@ WsLayout ws_layout(const hymba_layer& L, int64_t batch, int64_t seq) {
   return w;
 }
 
+// Workspace of a decode step that runs every projection on the hand-written GEMMs: no x
+// conversion buffer, no GEMM library workspace, and split-K partials for the call's own split
+// count.  0 if the key range has no split plan.
+WsLayout ws_layout_own_kernels(const hymba_layer& L, int64_t batch, int splits) {
+  const hymba_layer_cfg& c = L.cfg;
+  const size_t as = act_size(c);
+  const bool b16 = is_bf16(c);
+  WsLayout w{};
+  w.rows = batch;
+  w.own_kernels_only = true;
+  size_t off = 0;
+  w.X16 = off;
+  w.P = off; off += align_up((size_t)batch * L.ld_p * as);
+  w.bc32 = off; off += b16 ? align_up((size_t)batch * 2 * c.d_state * 4) : 0;
+  w.O = off; off += align_up((size_t)batch * c.n_heads * c.head_dim * as);
+  w.Ao = off; off += align_up((size_t)batch * c.d_inner * as);
+  w.Ys = off; off += align_up((size_t)batch * c.d_inner * as);
+  w.F = off; off += align_up((size_t)batch * c.d_inner * as);
+  w.gemm = off;
+  w.part = off; off += align_up((size_t)batch * c.n_heads * splits * (c.head_dim + 2) * 4);
+  w.total = off;
+  return w;
+}
+
 // Y[rows, out] = X[rows, in] . W[out, in]^T.  fp32 layers: fp32 kernel.  bf16
 // layers: hipBLASLt with fp32 accumulation; fp16 operands and output for the
 // input projection and W_O (bf16_out = false), bf16 operands and output for
@@ -221,7 +252,7 @@ WsLayout ws_layout(const hymba_layer& L, int64_t batch, int64_t seq) {
 int32_t project(const hymba_layer& L, const void* X, int64_t ldx, const void* W, int64_t ldw, void* Y,
                 int64_t ldy, int64_t rows, int64_t out, int64_t in, bool bf16_out, char* ws, const WsLayout& wl,
                 hipStream_t s) {
-  if (is_bf16(L.cfg) && skinny_fits(rows, out, in)) {   // few rows (decode): the weight-streaming kernel
+  if (is_bf16(L.cfg) && (wl.own_kernels_only || skinny_fits(rows, out, in))) {   // few rows: weight streaming
     hipError_t e;
     if (bf16_out) {
       SkinnyArgs<bf16_t, bf16_t, bf16_t> a{static_cast<const bf16_t*>(W), ldw, static_cast<const bf16_t*>(X), ldx,
@@ -286,7 +317,7 @@ int32_t in_projection(const hymba_layer& L, const void* x, int64_t rows, char* w
                       hipStream_t s) {
   const hymba_layer_cfg& c = L.cfg;
   float* bc32 = reinterpret_cast<float*>(ws + wl.bc32);
-  if (is_bf16(c) && skinny_fits(rows, L.n_in, c.d_model)) {
+  if (is_bf16(c) && (wl.own_kernels_only || skinny_fits(rows, L.n_in, c.d_model))) {
     // few rows: one weight-streaming GEMM reads x in bf16 (converted to fp16 on the way in) and
     // writes P in fp16, plus the B/C columns in fp32
     StageTimer st(L, ST_IN_PROJ, s);
@@ -599,6 +630,46 @@ int32_t decode_impl(hymba_layer& L, const void* x, const int64_t* pos, int B, vo
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+int32_t check_decode_args(const hymba_layer& L, const void* x_t, const int64_t* pos, int32_t B, const void* y_t,
+                          const hymba_kv* kv, const float* ssm_state) {
+  if (!x_t || !y_t || !pos || !ssm_state)
+    return fail(HYMBA_ERR_INVALID_ARG, "x_t, pos, y_t and ssm_state must be non-NULL");
+  if (B < 1) return fail(HYMBA_ERR_INVALID_ARG, "B must be >= 1");
+  if (B > 65535) return fail(HYMBA_ERR_UNSUPPORTED, "a decode step takes at most 65535 sequences (got %d)", B);
+  if (!kv || !kv->k_cache || !kv->v_cache) return fail(HYMBA_ERR_INVALID_ARG, "decode needs kv->k_cache and kv->v_cache");
+  const hymba_layer_cfg& c = L.cfg;
+  if (kv->cache_len < 1) return fail(HYMBA_ERR_INVALID_ARG, "cache_len must be >= 1");
+  if (c.window > 0 && kv->cache_len < c.window)
+    return fail(HYMBA_ERR_INVALID_ARG, "a sliding-window cache needs cache_len >= window (%d < %d)", kv->cache_len,
+                c.window);
+  if (!c.own_kv && !L.producer && c.n_meta > 0 && (!kv->k_meta || !kv->v_meta))
+    return fail(HYMBA_ERR_INVALID_ARG, "an unbound consumer needs kv->k_meta and kv->v_meta");
+  return HYMBA_OK;
+}
+
+// ---- the allocation-free decode step ---------------------------------------------------------
+// Scratch of hymba_mixer_decode_static: one array per device, in the library's code object.  Host
+// code never passes `scratch` itself (its name is a host-side stand-in, not a device address); it
+// takes the device address from hipGetSymbolAddress once per device and uses that.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_dev[kMaxDevices] = {};
+
+int32_t static_scratch(char** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HYMBA_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "scratch symbol address");
+    if (!p) return fail(HYMBA_ERR_HIP, "scratch symbol address is NULL");
+    g_scratch_dev[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return HYMBA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -735,23 +806,38 @@ int32_t hymba_mixer_prefill(hymba_layer* L, const void* x, int32_t B, int32_t T,
 int32_t hymba_mixer_decode(hymba_layer* L, const void* x_t, const int64_t* pos, int32_t B, void* y_t,
                            const hymba_kv* kv, float* ssm_state, void* ws, size_t ws_bytes, void* stream) {
   if (!L) return fail(HYMBA_ERR_INVALID_ARG, "layer is NULL");
-  if (!x_t || !y_t || !pos || !ssm_state || !ws)
-    return fail(HYMBA_ERR_INVALID_ARG, "x_t, pos, y_t, ssm_state and workspace must be non-NULL");
-  if (B < 1) return fail(HYMBA_ERR_INVALID_ARG, "B must be >= 1");
-  if (B > 65535) return fail(HYMBA_ERR_UNSUPPORTED, "a decode step takes at most 65535 sequences (got %d)", B);
-  if (!kv || !kv->k_cache || !kv->v_cache) return fail(HYMBA_ERR_INVALID_ARG, "decode needs kv->k_cache and kv->v_cache");
+  if (!ws) return fail(HYMBA_ERR_INVALID_ARG, "workspace must be non-NULL");
+  STATUS_TRY(check_decode_args(*L, x_t, pos, B, y_t, kv, ssm_state));
   const hymba_layer_cfg& c = L->cfg;
-  if (kv->cache_len < 1) return fail(HYMBA_ERR_INVALID_ARG, "cache_len must be >= 1");
-  if (c.window > 0 && kv->cache_len < c.window)
-    return fail(HYMBA_ERR_INVALID_ARG, "a sliding-window cache needs cache_len >= window (%d < %d)", kv->cache_len,
-                c.window);
-  if (!c.own_kv && !L->producer && c.n_meta > 0 && (!kv->k_meta || !kv->v_meta))
-    return fail(HYMBA_ERR_INVALID_ARG, "an unbound consumer needs kv->k_meta and kv->v_meta");
   const WsLayout wl = ws_layout(*L, B, 1);
   if (ws_bytes < wl.total) return fail(HYMBA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, wl.total);
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
   STATUS_TRY(ensure_prepared(*L, kv, w, wl, s));
+  return is_bf16(c) ? decode_impl<half_t>(*L, x_t, pos, B, y_t, kv, ssm_state, w, wl, s)
+                    : decode_impl<float>(*L, x_t, pos, B, y_t, kv, ssm_state, w, wl, s);
+}
+
+int32_t hymba_mixer_decode_static(hymba_layer* L, const void* x_t, const int64_t* pos, int32_t B, void* y_t,
+                                  const hymba_kv* kv, float* ssm_state, void* stream) {
+  if (!L) return fail(HYMBA_ERR_INVALID_ARG, "layer is NULL");
+  STATUS_TRY(check_decode_args(*L, x_t, pos, B, y_t, kv, ssm_state));
+  const hymba_layer_cfg& c = L->cfg;
+  if (!L->prepared || (!c.own_kv && !L->producer && c.n_meta > 0 &&
+                       (kv->k_meta != L->prep_kmeta || kv->v_meta != L->prep_vmeta)))
+    return fail(HYMBA_ERR_INVALID_ARG, "the allocation-free decode needs the layer prepared (hymba_layer_prepare) "
+                                       "with the meta K/V it is handed");
+  const int weff = c.window > 0 ? c.window : kv->cache_len;
+  const int splits = decode_attn_splits(B, c.n_kv_heads, c.n_meta + std::min(weff, kv->cache_len), c.head_dim,
+                                        static_cast<int>(act_size(c)));
+  if (splits < 1) return fail(HYMBA_ERR_UNSUPPORTED, "decode key range too long for the split-K kernel");
+  const WsLayout wl = ws_layout_own_kernels(*L, B, splits);
+  if (wl.total > kStaticScratchBytes)
+    return fail(HYMBA_ERR_WORKSPACE, "the allocation-free decode needs %zu bytes of scratch, at most %zu are "
+                "available (fewer sequences per call fit)", wl.total, kStaticScratchBytes);
+  char* w = nullptr;
+  STATUS_TRY(static_scratch(&w));
+  hipStream_t s = static_cast<hipStream_t>(stream);
   return is_bf16(c) ? decode_impl<half_t>(*L, x_t, pos, B, y_t, kv, ssm_state, w, wl, s)
                     : decode_impl<float>(*L, x_t, pos, B, y_t, kv, ssm_state, w, wl, s);
 }

@@ -183,6 +183,26 @@ int32_t hymba_mixer_decode(hymba_layer* layer, const void* x_t, const int64_t* p
                            void* y_t, const hymba_kv* kv, float* ssm_state, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* The decode step of hymba_mixer_decode without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  The call allocates
+ * nothing: its scratch is a 32 MiB array in the library's device code object,
+ * one copy per GPU, held until the process ends (its address is taken once
+ * per device, on the first call there).  Every projection runs on the
+ * library's own few-row MFMA GEMM (no GEMM-library workspace).  The layer must
+ * already be prepared (hymba_layer_prepare, which may allocate) with the meta
+ * K/V it is handed, else HYMBA_ERR_INVALID_ARG.  Scratch need: B * (Nin
+ * rounded up to 64, + 3*E + H*hd, all in the activation type, + 2*N fp32 for
+ * bf16 layers) + B * H * splits * (hd + 2) * 4 bytes (splits <= 64, each
+ * region rounded to 256 bytes); a call needing more than 32 MiB returns
+ * HYMBA_ERR_WORKSPACE before any device work (about 400 sequences of the
+ * 1.5B-shaped layer fit).  Results equal hymba_mixer_decode's up to the order
+ * of the projections' fp32 sums.  All calls on one GPU share its scratch and
+ * it keeps the last call's contents: calls that overlap on one GPU (two
+ * streams, two threads) race and must be serialised by the caller. */
+int32_t hymba_mixer_decode_static(hymba_layer* layer, const void* x_t, const int64_t* pos, int32_t B,
+                                  void* y_t, const hymba_kv* kv, float* ssm_state, void* stream);
+
 /* Device pointers of the prepared meta prefix inside the persistent buffer:
  * K/V [M, Hkv, hd] in the activation type (producer only, else NULL), SSM
  * state after the prefix [E, N] fp32, outputs of the meta rows [M, d] in the
