@@ -9,16 +9,17 @@
 // heads: query head h reads KV head floor(h * Hkv / H).
 //
 // Two kernels:
-//  * swa_meta_attn (MFMA): hd = 64, 16-bit operands (fp16 for the layer's
-//    activations, bf16 also instantiated) with v_mfma_f32_32x32x16_{f16,bf16}
-//    and fp32 accumulation.
+//  * swa_meta_attn (MFMA): hd = 64, fp16 operands (the activation type of bf16
+//    layers) with v_mfma_f32_32x32x16_f16 and fp32 accumulation.
 //    One workgroup = 4 waves = 128 consecutive queries of one query head (a
-//    32-query block per wave).  The K tiles and transposed V tiles of the keys
-//    those queries can see (meta, then the window span) stream through a
-//    double-buffered LDS stage loaded by all four waves; the heads of a GQA
-//    group reuse the same K/V through the L2 of the XCD their workgroups run on.
+//    32-query block per wave).  The K and V rows of the keys they can see
+//    (meta, then the window span) stream through LDS in 32-key stages, four
+//    buffers deep and loaded by the whole workgroup.  Each wave runs its stages as
+//    a three-step software pipeline -- scores of stage h, softmax of stage
+//    h - 1, P.V of stage h - 2 -- so that every step pairs 8 independent MFMAs
+//    with the VALU work of one softmax in straight-line code.
 //    Scores are computed transposed (S^T = K Q^T) so each lane owns one query
-//    column and 16 keys of a 32-key block: the softmax max needs one exchange
+//    column and 16 keys of a 32-key stage: the softmax max needs one exchange
 //    with lane l^32, and the probabilities feed the P.V product as the B
 //    operand without any cross-lane movement.
 //  * attn_f32: fp32 storage, one thread per (query, head), online softmax on
@@ -33,27 +34,203 @@ namespace {
 
 using namespace attn;
 
-// One workgroup = 4 waves = kQG consecutive queries (one 32-query block per
-// wave) of one query head.  The workgroup streams the key tiles its queries
-// can see -- the meta tiles, then the window span [q0 - W + 1, q0 + kQG) (all
-// earlier keys for a global layer) -- through a double-buffered LDS stage that
-// all four waves load and share; a wave skips tiles outside its own window.
-// Work items are numbered (sequence, KV head, query group, head of the group)
-// for SWA -- so consecutive items reuse one window of K/V -- and with the
-// longest query groups first for global layers; consecutive items go to the
-// same XCD (the dispatcher deals workgroups round-robin over the 8 XCDs), so
-// an XCD's L2 holds the K/V its workgroups share.
-constexpr int kQG = 4 * kQB;
+constexpr int kWaves = 4;               // waves per workgroup
+constexpr int kQG = kWaves * kQB;       // queries per workgroup
+constexpr int kHT = 32;                 // keys per LDS stage
+constexpr int kStages = 4;              // LDS buffers (see the kernel's note on reuse)
 constexpr int kXcds = 8;
 
-template <typename ET>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void swa_meta_attn_kernel(AttnArgs<ET> a) {
-  __shared__ AttnSmem sm;
+typedef f16x8_t QV;
+
+// Online-softmax state of one wave (lane l: query l % 32, 16 keys of each stage).  Each query
+// keeps a reference m, the largest score seen when the reference last moved: a probability is
+// 2^(sc s - sc m), one FMA and one exp per score, with no per-stage max.  The reference moves only
+// when a stage would give some lane a probability sum above kGrowSum (every probability then stays
+// far below fp16's overflow), or while the query has no reference yet; the rounding of sc m is
+// common to every probability of the query and cancels in the normalisation.
+struct Col {
+  f32x16_t acc[2];   // O^T dims [0, 32) and [32, 64); column = query
+  float m;           // reference, raw score units (-inf before the query's first visible key)
+  float l;           // this lane's part of the row sum, relative to m
+};
+constexpr float kGrowSum = 4096.f;
+
+// max of the lane's 16 scores of a stage, combined with lane l ^ 32 (the column's 32 keys)
+__device__ __forceinline__ float block_max(const f32x16_t& s) {
+  float mt = max3f(s[0], s[1], s[2]);
+#pragma unroll
+  for (int r = 3; r < 15; r += 2) mt = max3f(mt, s[r], s[r + 1]);
+  mt = fmaxf(mt, s[15]);
+  return max_xor32(mt);
+}
+
+// P^T of a stage as fp16 pairs (the B fragments of two P.V steps) and the lane's sum of exactly
+// those rounded values: p = 2^(sc s - sc m) (0 for a masked score).
+__device__ __forceinline__ float probs(const f32x16_t& s, float sc, float m, U4 (&pw)[2]) {
+  const float off = m == -INFINITY ? 0.f : -m * sc;
+  float psum = 0.f;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = fast_exp2(fmaf(s[hh * 8 + j], sc, off));
+    U4 w;
+    w.x = pack_f16x2(p[0], p[1]);
+    w.y = pack_f16x2(p[2], p[3]);
+    w.z = pack_f16x2(p[4], p[5]);
+    w.w = pack_f16x2(p[6], p[7]);
+    psum = Op<half_t>::add_pair(w.x, psum);
+    psum = Op<half_t>::add_pair(w.y, psum);
+    psum = Op<half_t>::add_pair(w.z, psum);
+    psum = Op<half_t>::add_pair(w.w, psum);
+    pw[hh] = w;
+  }
+  return psum;
+}
+
+// Which keys of a stage the wave's queries may see.
+struct Stage {
+  int key0;             // index of its first key (meta index, or real index for window keys)
+  int lo_key, hi_key;   // visible range before causality
+  bool meta;            // meta keys: no causality, no window
+  bool mask;            // some key of the stage is hidden from some query of the wave
+};
+
+// Mask of a stage: key j is kept iff lo_key <= j < hi_key and, for a real query tq, j <= tq and
+// (win <= 0 or j > tq - win).  Register r holds key key0 + 4 half + o with o = 8 (r/4) + r%4
+// (< 32); the lane's visible offsets form one range [a, b), kept as a 32-bit mask, so each score
+// costs a bit extract and a bit select.
+__device__ __forceinline__ void mask_stage(f32x16_t& s, const Stage& st, int tq, int win, int half) {
+  int lo = st.lo_key, hi = st.hi_key;
+  if (!st.meta) {
+    hi = min(hi, tq + 1);
+    if (win > 0) lo = max(lo, tq - win + 1);
+  }
+  const int base = st.key0 + 4 * half;
+  const int a = min(max(lo - base, 0), 32), b = min(max(hi - base, 0), 32);
+  const uint32_t below_b = b >= 32 ? ~0u : (1u << b) - 1u;
+  const uint32_t below_a = a >= 32 ? ~0u : (1u << a) - 1u;
+  const uint32_t keep = below_b & ~below_a;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int bit = 8 * (r >> 2) + (r & 3);
+    const uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(keep << (31 - bit)) >> 31);
+    s[r] = __uint_as_float((__float_as_uint(s[r]) & m) | (0xff800000u & ~m));   // -inf: exp2 gives 0
+  }
+}
+
+// S^T = K Q^T of a stage (K rows ks, row stride kKStr).
+__device__ __forceinline__ void qk(f32x16_t& s, const QV (&q)[4], const uint16_t* ks, int lane) {
+  const uint16_t* krow = ks + (lane & 31) * kKStr + (lane >> 5) * 8;
+  s = f32x16_t{};
+#pragma unroll
+  for (int st4 = 0; st4 < 4; ++st4)
+    s = Op<half_t>::mfma(as_vec<half_t>(*reinterpret_cast<const U4*>(krow + st4 * 16)), q[st4], s);
+}
+
+// O^T += V^T P^T over a stage.  PV k-step s2 covers the stage's keys [16 s2, 16 s2 + 16); k-index
+// 8 h + j <-> key 16 s2 + 8 (j/4) + 4 h + j%4, which is where the score layout puts them.  The A
+// fragment (lane l: dim 32 db + l % 32) comes from two transposed reads: lane group g = l / 16
+// reads rows 16 s2 + 4 h (+ 8) + (l % 16) / 4 at dims 32 db + 16 (g % 2) + 4 (l % 4).
+__device__ __forceinline__ void pv(Col& c, const U4 (&p)[2], const uint16_t* vs, int lane) {
+  const uint16_t* vlane =
+      vs + (4 * (lane >> 5) + ((lane & 15) >> 2)) * kVStr + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const uint2 lo = v_tr4(vlane + 16 * s2 * kVStr + 32 * db);
+      const uint2 hi = v_tr4(vlane + (16 * s2 + 8) * kVStr + 32 * db);
+      c.acc[db] = Op<half_t>::mfma(as_vec<half_t>(U4{lo.x, lo.y, hi.x, hi.y}), as_vec<half_t>(p[s2]), c.acc[db]);
+    }
+  }
+}
+
+// End of a step, for the stage whose probabilities p it just formed: if some lane's sum is too
+// large, or some query has no reference yet, the reference moves to max(m, the stage max) -- the
+// stage's scores recomputed from its K rows still in LDS and masked like it -- the accumulators and
+// sums are rescaled and the probabilities recomputed; then the sums take the stage's.
+__device__ __forceinline__ void settle(Col& c, U4 (&p)[2], float psum, const QV (&q)[4], const uint16_t* ks,
+                                       const Stage& st, int tq, int win, float sc, int lane) {
+  if (__builtin_amdgcn_ballot_w64(!(psum <= kGrowSum) || c.m == -INFINITY) != 0) {
+    f32x16_t s;
+    qk(s, q, ks, lane);
+    if (st.mask) mask_stage(s, st, tq, win, lane >> 5);
+    const float mnew = fmaxf(c.m, block_max(s));
+    const float alpha = mnew == -INFINITY ? 1.f : fast_exp2((c.m - mnew) * sc);   // m = -inf: 0
+    c.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) c.acc[db][r] *= alpha;
+    c.m = mnew;
+    psum = probs(s, sc, mnew, p);
+  }
+  c.l += psum;
+}
+
+// The calling thread's share of a stage (K rows at kbase, V rows at vbase, row stride ld elements,
+// nvalid >= 1 valid rows): threads [0, 128) load K, [128, 256) V (a wave-uniform choice); chunk
+// it + 128 j (j < 2) is row (it >> 3) + 16 j, dims 8 (it & 7) + 0..7.  The lane's row offset is
+// recomputed per stage from an opaque copy of its row index, so that the compiler does not keep
+// hoisted offsets per row and per key source live across the loop.  Rows past nvalid read the last
+// valid row and are zero-filled.
+struct StageRegs {
+  U4 r[2];
+};
+__device__ __forceinline__ void fetch_stage(StageRegs& t, const half_t* kbase, const half_t* vbase, int ld,
+                                            int nvalid, bool is_k, int it) {
+  const char* base = reinterpret_cast<const char*>(is_k ? kbase : vbase);
+  int row0 = it >> 3;
+  asm volatile("" : "+v"(row0));
+  const int col = (it & 7) * 8;
+  if (nvalid >= kHT) {
+    const uint32_t voff = static_cast<uint32_t>((row0 * ld + col) * 2);
+    const int64_t step = (int64_t)16 * ld * 2;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) t.r[j] = *reinterpret_cast<const U4*>(base + j * step + voff);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = row0 + 16 * j;
+      t.r[j] = masked_load(base + (static_cast<int64_t>(min(row, nvalid - 1)) * ld + col) * 2, row < nvalid);
+    }
+  }
+}
+__device__ __forceinline__ void store_stage(const StageRegs& t, uint16_t* ks, uint16_t* vs, bool is_k, int it) {
+  uint16_t* base = is_k ? ks : vs;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    *reinterpret_cast<uint4*>(base + ((it >> 3) + 16 * j) * kKStr + (it & 7) * 8) =
+        make_uint4(t.r[j].x, t.r[j].y, t.r[j].z, t.r[j].w);
+}
+
+struct AttnStages {
+  uint16_t kw[kStages][kHT * kKStr];   // K rows [key][dim]
+  uint16_t vw[kStages][kHT * kVStr];   // V rows [key][dim]
+};
+
+// Work items are numbered (sequence, KV head, query group, head of the group) for SWA -- so
+// consecutive items share one window of K/V -- and with the longest query groups first for global
+// layers; consecutive items go to the same XCD (the dispatcher deals workgroups round-robin over
+// the 8 XCDs), so an XCD's L2 holds the K/V its workgroups share.
+//
+// Step i of a wave: scores of stage i, the previous stage's softmax, the P.V product of stage i - 2:
+//   S(i) = K(i) Q^T (4 MFMAs) ; O += V(i - 2)^T P(i - 2) (4 MFMAs) ; P(i - 1) = softmax(S(i - 1))
+// The eight MFMAs are independent of the softmax, so they issue beside its VALU work.  A stage's
+// K is read at step i and again (rare rescale) at step i + 1, its V at step i + 2.  Stage i is
+// stored (into buffer i mod 4) after the barrier of stage i - 1, which every wave passes only once
+// it has finished step i - 2; a wave still in step i - 1 reads stages i - 3 .. i - 1, so with four
+// buffers and one barrier per stage no store overwrites what another wave still reads.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void swa_meta_attn_kernel(
+    AttnArgs<half_t> a) {
+  __shared__ AttnStages sm;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, col = lane & 31;
   const int group = a.n_heads / a.n_kv_heads;
   const int nqg = static_cast<int>(ceil_div(a.T, kQG));
   const float sc = a.scale_log2;
+  const int win = a.window;
 
   // ---- work item: XCD-aware renumbering, then (b, g, qg, hh) ------------------
   const int nwork = gridDim.x, L = blockIdx.x;
@@ -62,7 +239,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int hh = work % group;
   work /= group;
   int b, g, qg;
-  if (a.window > 0) {
+  if (win > 0) {
     qg = work % nqg; work /= nqg;
     g = work % a.n_kv_heads; b = work / a.n_kv_heads;
   } else {
@@ -72,85 +249,120 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int h = g * group + hh;
   const int q0 = qg * kQG;
   const int qa = q0 + wave * kQB;               // this wave's first query
-  const bool wave_active = qa < a.T;
-  const int qlast = min(qa + kQB, a.T) - 1;     // this wave's last query
+  const int qlast = min(qa + kQB, a.T) - 1;     // this wave's last query (qa - 1 for an idle wave)
   const int tq = min(qa + col, a.T - 1);
 
-  // ---- key tiles: meta first, then the window span [lo, hi) ------------------
-  const int n_mt = static_cast<int>(ceil_div(a.n_meta, kKT));
-  const int lo = a.window > 0 ? max(0, q0 - a.window + 1) : 0;
+  // ---- stages: the meta keys, then the workgroup's window span [lo, hi) --------
+  const int n_ms = static_cast<int>(ceil_div(a.n_meta, kHT));
+  const int lo = win > 0 ? max(0, q0 - win + 1) : 0;
   const int hi = min(a.T, q0 + kQG);
-  const int n_tiles = n_mt + static_cast<int>(ceil_div(hi - lo, kKT));
-  const ET* kseq = a.k + (int64_t)b * a.kv_seq_stride + g * kHd;
-  const ET* vseq = a.v + (int64_t)b * a.kv_seq_stride + g * kHd;
+  const int n_st = n_ms + static_cast<int>(ceil_div(hi - lo, kHT));
+  const half_t* kseq = a.k + (int64_t)b * a.kv_seq_stride + g * kHd;
+  const half_t* vseq = a.v + (int64_t)b * a.kv_seq_stride + g * kHd;
   const int ld_meta = static_cast<int>(a.ld_meta), ld_kv = static_cast<int>(a.ld_kv);
-  auto fetch = [&](TileRegs& r, int i) {
-    if (i < n_mt) {
-      const int64_t off = (int64_t)i * kKT * a.ld_meta + g * kHd;
-      tile_fetch(r, a.k_meta + off, a.v_meta + off, ld_meta, a.n_meta - i * kKT, tid);
+  const bool is_k = wave < 2;
+  const int it = tid & 127;
+  auto fetch = [&](StageRegs& r, int i) {
+    if (i < n_ms) {
+      const int64_t off = (int64_t)i * kHT * a.ld_meta + g * kHd;
+      fetch_stage(r, a.k_meta + off, a.v_meta + off, ld_meta, a.n_meta - i * kHT, is_k, it);
     } else {
-      const int t0 = lo + (i - n_mt) * kKT;
-      tile_fetch(r, kseq + (int64_t)t0 * a.ld_kv, vseq + (int64_t)t0 * a.ld_kv, ld_kv, hi - t0, tid);
+      const int t0 = lo + (i - n_ms) * kHT;
+      fetch_stage(r, kseq + (int64_t)t0 * a.ld_kv, vseq + (int64_t)t0 * a.ld_kv, ld_kv, hi - t0, is_k, it);
     }
   };
-
+  auto stage_of = [&](int i) {   // branch-free (scalar selects)
+    Stage st;
+    const bool meta = i < n_ms;
+    const int t0 = lo + (i - n_ms) * kHT;
+    const bool full = (t0 + kHT - 1 <= qa) & ((win <= 0) | (t0 > qlast - win)) & (t0 + kHT <= hi);
+    st.meta = meta;
+    st.key0 = meta ? i * kHT : t0;
+    st.lo_key = meta ? 0 : t0;
+    st.hi_key = meta ? a.n_meta : hi;
+    st.mask = meta ? (i * kHT + kHT > a.n_meta) : !full;
+    return st;
+  };
   // Q^T fragments: k-step s holds dims 16 s + 8 (lane/32) .. +7 of query tq
-  typename Op<ET>::vec qf[4];
+  QV qf[4];
   {
-    const ET* qrow = a.q + ((int64_t)b * a.T + tq) * a.ld_q + h * kHd + (lane >> 5) * 8;
+    const half_t* qrow = a.q + ((int64_t)b * a.T + tq) * a.ld_q + h * kHd + (lane >> 5) * 8;
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) qf[s4] = as_vec<ET>(*reinterpret_cast<const U4*>(qrow + s4 * 16));
+    for (int s4 = 0; s4 < 4; ++s4) qf[s4] = as_vec<half_t>(*reinterpret_cast<const U4*>(qrow + s4 * 16));
   }
-  WaveState st;
-  st.acc[0] = f32x16_t{};
-  st.acc[1] = f32x16_t{};
-  st.m = -INFINITY;
-  st.l = 0.f;
-  st.bias = (lane >> 5) ? 0u : Pair<ET>::pack(INFINITY, 0.f);
-  st.exact = false;
+  Col c;
+  c.acc[0] = c.acc[1] = f32x16_t{};
+  c.m = -INFINITY;
+  c.l = 0.f;
 
-  TileRegs pre;
+  // pipeline registers: scores of stage i - 1, probabilities of stage i - 2
+  f32x16_t s1 = f32x16_t{};
+  U4 p2[2] = {};
+  StageRegs pre;
   fetch(pre, 0);
-  for (int i = 0; i < n_tiles; ++i) {
-    const int buf = i & 1;
-    tile_store(pre, sm.kw[buf], sm.vw[buf], tid);
-    __syncthreads();
-    if (i + 1 < n_tiles) fetch(pre, i + 1);
-    // Every wave runs every tile of the workgroup: a tile outside a wave's window (or a wave past
-    // the end of the sequence) is simply all masked and adds nothing.  Branching around it splits
-    // the loop-carried accumulators across paths and costs a 32-register copy per tile.
-    int key0, lo_key, hi_key, tqm;
-    bool mask;
-    if (i < n_mt) {
-      // meta keys: visible to every real query; only the padding tail is masked
-      key0 = i * kKT; lo_key = 0; hi_key = a.n_meta; tqm = -1;
-      mask = key0 + kKT > a.n_meta;
-    } else {
-      const int t0 = lo + (i - n_mt) * kKT;
-      key0 = t0; lo_key = t0; hi_key = hi; tqm = tq;
-      mask = !((t0 + kKT - 1 <= qa) && (a.window <= 0 || t0 > qlast - a.window) && (t0 + kKT <= hi));
-    }
-    attend_tile<ET>(st, qf, sm.kw[buf], sm.vw[buf], kVStr, sc, lane, key0, lo_key, hi_key, tqm, a.window, mask, i == 0);
-  }
-
-  if (wave_active) {
-    const float ltot = sum_xor32(st.l);
-    const float inv = 1.f / ltot;
-    const int t = qa + col;
-    if (t < a.T) {
-      ET* orow = a.o + ((int64_t)b * a.T + t) * a.ld_o + h * kHd;
-      const int half = lane >> 5;
+  // the step's common part: scores of stage i (if any), P.V of stage i - 2 (if any), softmax of
+  // stage i - 1 (if any); the rare settle and the edge masking come after it
+  auto step = [&](int i, bool do_qk, bool do_pv, bool do_soft) {
+    const int buf = i % kStages;
+    const Stage st_cur = stage_of(i), st_prev = stage_of(i - 1);
+    f32x16_t s0;
+    if (do_qk) qk(s0, qf, sm.kw[buf], lane);
+    if (do_pv) pv(c, p2, sm.vw[(i + 2) % kStages], lane);     // stage i - 2
+    if (do_soft) {
+      U4 p1[2];
+      const float ps = probs(s1, sc, c.m, p1);
+      if (do_qk && do_pv) {   // the steady step: one MFMA, then a share of the softmax VALU, eight times
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int dim = db * 32 + 8 * r4 + 4 * half;
-          uint2 w;
-          w.x = Pair<ET>::pack(st.acc[db][r4 * 4 + 0] * inv, st.acc[db][r4 * 4 + 1] * inv);
-          w.y = Pair<ET>::pack(st.acc[db][r4 * 4 + 2] * inv, st.acc[db][r4 * 4 + 3] * inv);
-          *reinterpret_cast<uint2*>(orow + dim) = w;
+        for (int k = 0; k < 8; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
         }
+      }
+      const int pb = (i + 3) % kStages;                        // stage i - 1
+      settle(c, p1, ps, qf, sm.kw[pb], st_prev, tq, win, sc, lane);
+      p2[0] = p1[0];
+      p2[1] = p1[1];
     }
+    if (do_qk) {
+      if (st_cur.mask) mask_stage(s0, st_cur, tq, win, lane >> 5);
+      s1 = s0;
+    }
+  };
+  auto load = [&](int i) {   // stage i into its buffer, visible to the workgroup; stage i + 1 requested
+    store_stage(pre, sm.kw[i % kStages], sm.vw[i % kStages], is_k, it);
+    __syncthreads();
+    fetch(pre, min(i + 1, n_st - 1));
+  };
+  // prologue (n_st >= 1)
+  load(0);
+  step(0, true, false, false);
+  if (n_st > 1) {
+    load(1);
+    step(1, true, false, true);
+  }
+  // steady state: all three parts
+  for (int i = 2; i < n_st; ++i) {
+    load(i);
+    step(i, true, true, true);
+  }
+  // drain
+  step(n_st, false, n_st >= 2, true);
+  step(n_st + 1, false, true, false);
+
+  if (qa < a.T && qa + col < a.T) {
+    const float inv = 1.f / sum_xor32(c.l);
+    half_t* orow = a.o + ((int64_t)b * a.T + qa + col) * a.ld_o + h * kHd;
+    const int half = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dim = db * 32 + 8 * r4 + 4 * half;
+        uint2 w;
+        w.x = pack_f16x2(c.acc[db][r4 * 4 + 0] * inv, c.acc[db][r4 * 4 + 1] * inv);
+        w.y = pack_f16x2(c.acc[db][r4 * 4 + 2] * inv, c.acc[db][r4 * 4 + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + dim) = w;
+      }
   }
 }
 
@@ -194,18 +406,15 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs<float> a) {
 }
 
 
-template <typename ET>
-hipError_t launch_mfma(const AttnArgs<ET>& a, hipStream_t stream) {
+}  // namespace
+
+hipError_t launch_attn_prefill_mfma(const AttnArgs<half_t>& a, hipStream_t stream) {
   const int group = a.n_heads / a.n_kv_heads;
   const int64_t nwork = (int64_t)a.B * a.n_kv_heads * group * ceil_div(a.T, kQG);
   if (nwork > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((swa_meta_attn_kernel<ET>), dim3(static_cast<unsigned>(nwork)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(swa_meta_attn_kernel, dim3(static_cast<unsigned>(nwork)), dim3(kWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
-
-}  // namespace
-
-hipError_t launch_attn_prefill_mfma(const AttnArgs<half_t>& a, hipStream_t s) { return launch_mfma(a, s); }
 
 hipError_t launch_attn_prefill_f32(const AttnArgs<float>& a, hipStream_t stream) {
   const int64_t total = (int64_t)a.B * a.T * a.n_heads;
