@@ -63,7 +63,8 @@ hipError_t conv(const S* src, int64_t ld_src, D* dst, int64_t ld_dst, int64_t ro
 // the row.  One wave = RG groups of 16 rows; in each 32-column step a lane holds row l % 16 of
 // every group and the 8 input columns [8 (l/16), +8) -- its fp16 A fragments, which it also
 // stores to x16.  The weight rows W_bc (fp16, <= 32 x d, L2-resident) are the B fragments, loaded
-// once per step for the RG groups; the next step's loads are issued before this step's work.  The
+// once per step for the RG groups.  Steps go in pairs (each row's whole 128-byte line), the next
+// pair's loads issued before this pair's work.  The
 // C fragment gives lane l column l % 16 of rows 4 (l/16) + 0..3.
 template <int NCB, int RG>   // NCB: 16-column blocks of B/C (1: N = 8, 2: N = 16); RG: row groups
 __global__ __launch_bounds__(256) void convert_bc_kernel(ConvBcArgs a) {
@@ -88,39 +89,48 @@ __global__ __launch_bounds__(256) void convert_bc_kernel(ConvBcArgs a) {
   for (int g = 0; g < RG; ++g)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[g][cb] = f32x4_t{};
-  // d % 8 == 0: a lane's 8 columns of a step are all in or all out
-  auto load = [&](int k0, uint4 (&xv)[RG], uint4 (&wv)[NCB]) {
-    const bool k_ok = k0 + 8 * kq < a.d;
+  // a pair of 32-column steps: each row's whole 128-byte line.  d % 8 == 0: a lane's 8 columns of
+  // a step are all in or all out.
+  struct Pair2 { uint4 x[2][RG]; uint4 w[2][NCB]; };
+  auto load = [&](int k0, Pair2& p) {
 #pragma unroll
-    for (int g = 0; g < RG; ++g)
-      xv[g] = k_ok ? *reinterpret_cast<const uint4*>(xr[g] + k0) : make_uint4(0u, 0u, 0u, 0u);
+    for (int h = 0; h < 2; ++h) {
+      const int k = k0 + 32 * h;
+      const bool k_ok = k + 8 * kq < a.d;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-      wv[cb] = k_ok ? *reinterpret_cast<const uint4*>(wr[cb] + k0) : make_uint4(0u, 0u, 0u, 0u);
-  };
-  uint4 xv[RG], wv[NCB];
-  load(0, xv, wv);
-  for (int k0 = 0; k0 < a.d; k0 += 32) {
-    uint4 xn[RG], wn[NCB];
-    if (k0 + 32 < a.d) load(k0 + 32, xn, wn);
-    const bool k_ok = k0 + 8 * kq < a.d;
-#pragma unroll
-    for (int g = 0; g < RG; ++g) {
-      uint4 hv;
-      hv.x = pack_f16x2(bf16lo(xv[g].x), bf16hi(xv[g].x));
-      hv.y = pack_f16x2(bf16lo(xv[g].y), bf16hi(xv[g].y));
-      hv.z = pack_f16x2(bf16lo(xv[g].z), bf16hi(xv[g].z));
-      hv.w = pack_f16x2(bf16lo(xv[g].w), bf16hi(xv[g].w));
-      if (k_ok && row_ok[g]) *reinterpret_cast<uint4*>(xo[g] + k0) = hv;
+      for (int g = 0; g < RG; ++g)
+        p.x[h][g] = k_ok ? *reinterpret_cast<const uint4*>(xr[g] + k) : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
-        acc[g][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, hv),
-                                                            __builtin_bit_cast(f16x8_t, wv[cb]), acc[g][cb], 0, 0, 0);
+        p.w[h][cb] = k_ok ? *reinterpret_cast<const uint4*>(wr[cb] + k) : make_uint4(0u, 0u, 0u, 0u);
     }
+  };
+  Pair2 cur;
+  load(0, cur);
+  for (int k0 = 0; k0 < a.d; k0 += 64) {
+    Pair2 nxt;
+    if (k0 + 64 < a.d) load(k0 + 64, nxt);
 #pragma unroll
-    for (int g = 0; g < RG; ++g) xv[g] = xn[g];
+    for (int h = 0; h < 2; ++h) {
+      const int k = k0 + 32 * h;
+      const bool k_ok = k + 8 * kq < a.d;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) wv[cb] = wn[cb];
+      for (int g = 0; g < RG; ++g) {
+        const uint4 xv = cur.x[h][g];
+        uint4 hv;
+        hv.x = pack_f16x2(bf16lo(xv.x), bf16hi(xv.x));
+        hv.y = pack_f16x2(bf16lo(xv.y), bf16hi(xv.y));
+        hv.z = pack_f16x2(bf16lo(xv.z), bf16hi(xv.z));
+        hv.w = pack_f16x2(bf16lo(xv.w), bf16hi(xv.w));
+        if (k_ok && row_ok[g]) *reinterpret_cast<uint4*>(xo[g] + k) = hv;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          acc[g][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, hv),
+                                                              __builtin_bit_cast(f16x8_t, cur.w[h][cb]), acc[g][cb],
+                                                              0, 0, 0);
+      }
+    }
+    cur = nxt;
   }
 #pragma unroll
   for (int g = 0; g < RG; ++g)
@@ -135,11 +145,90 @@ __global__ __launch_bounds__(256) void convert_bc_kernel(ConvBcArgs a) {
 
 constexpr int kConvRowGroups = 2;
 
+// Few rows (a decode step, the meta prefix): the same products and conversion, with one workgroup
+// of kRowsWaves waves per 16 rows and the 32-column steps of K split over its waves.  Each wave
+// issues the loads of kRowsBatch steps before it uses any, and the waves' partial sums meet in LDS,
+// added in wave order.  With whole rows per wave a 128-row call would run on one CU, bound by the
+// rate at which a single CU can load (measured ~46 us for the 1.5B layer's 128 x 1600 inputs).
+constexpr int kRowsWaves = 8;
+constexpr int kRowsBatch = 8;
+constexpr int64_t kFewRows = 2048;   // up to this many rows take the split-K kernel
+
+template <int NCB>
+__global__ __launch_bounds__(64 * kRowsWaves) void convert_bc_rows_kernel(ConvBcArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = lane & 15, kq = lane >> 4;
+  const int64_t row = (int64_t)blockIdx.x * 16 + i;
+  const bool row_ok = row < a.rows;
+  const bf16_t* xr = a.x + (row_ok ? row : a.rows - 1) * a.ldx + 8 * kq;
+  half_t* xo = a.x16 + row * a.ldx16 + 8 * kq;
+  const half_t* wr[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) wr[cb] = a.wbc + (int64_t)(16 * cb + i) * a.ldw + 8 * kq;
+  const int nsteps = (a.d + 31) / 32;
+  const int s0 = wave * nsteps / kRowsWaves, s1 = (wave + 1) * nsteps / kRowsWaves;
+  f32x4_t acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4_t{};
+  for (int sb = s0; sb < s1; sb += kRowsBatch) {
+    uint4 xv[kRowsBatch], wv[kRowsBatch][NCB];
+#pragma unroll
+    for (int j = 0; j < kRowsBatch; ++j) {
+      const int k = (sb + j) * 32;   // xr, wr, xo already point at the lane's 8 columns
+      const bool ok = sb + j < s1 && k + 8 * kq < a.d;   // d % 8 == 0: the 8 columns are all in or out
+      xv[j] = ok ? *reinterpret_cast<const uint4*>(xr + k) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        wv[j][cb] = ok ? *reinterpret_cast<const uint4*>(wr[cb] + k) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < kRowsBatch; ++j) {
+      const int k = (sb + j) * 32;
+      const bool ok = sb + j < s1 && k + 8 * kq < a.d;
+      uint4 hv;
+      hv.x = pack_f16x2(bf16lo(xv[j].x), bf16hi(xv[j].x));
+      hv.y = pack_f16x2(bf16lo(xv[j].y), bf16hi(xv[j].y));
+      hv.z = pack_f16x2(bf16lo(xv[j].z), bf16hi(xv[j].z));
+      hv.w = pack_f16x2(bf16lo(xv[j].w), bf16hi(xv[j].w));
+      if (ok && row_ok) *reinterpret_cast<uint4*>(xo + k) = hv;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, hv),
+                                                         __builtin_bit_cast(f16x8_t, wv[j][cb]), acc[cb], 0, 0, 0);
+    }
+  }
+  __shared__ f32x4_t part[kRowsWaves][NCB][64];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) part[wave][cb][lane] = acc[cb];
+  __syncthreads();
+  if (wave < NCB) {   // wave cb adds block cb over the waves in order
+    const int cb = wave;
+    f32x4_t sum = part[0][cb][lane];
+#pragma unroll
+    for (int w = 1; w < kRowsWaves; ++w) {
+      const f32x4_t v = part[w][cb][lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sum[r] += v[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t orow = (int64_t)blockIdx.x * 16 + 4 * kq + r;
+      if (orow < a.rows) a.bc[orow * a.ldbc + 16 * cb + i] = sum[r];
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_convert_bc(const ConvBcArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
   if (a.d % 8 || (a.nbc != 16 && a.nbc != 32) || a.ldx % 8 || a.ldx16 % 8 || a.ldw % 8) return hipErrorInvalidValue;
+  if (a.rows <= kFewRows) {
+    const dim3 grid(static_cast<unsigned>(ceil_div(a.rows, 16))), block(64 * kRowsWaves);
+    if (a.nbc == 32) hipLaunchKernelGGL((convert_bc_rows_kernel<2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((convert_bc_rows_kernel<1>), grid, block, 0, s, a);
+    return hipGetLastError();
+  }
   const dim3 grid(static_cast<unsigned>(ceil_div(a.rows, 4 * 16 * kConvRowGroups))), block(256);
   if (a.nbc == 32) hipLaunchKernelGGL((convert_bc_kernel<2, kConvRowGroups>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((convert_bc_kernel<1, kConvRowGroups>), grid, block, 0, s, a);
