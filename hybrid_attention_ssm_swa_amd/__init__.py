@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     hymba_layer_meta_outputs, hymba_last_error, hymba_status_string,
     hymba_kernel_attention, hymba_kernel_selective_scan, hymba_kernel_epilogue, hymba_kernel_gemm_rows,
     hymba_kernel_gemm_rows_workspace,
+    hymba_kernel_selective_scan_workspace,
     hymba_layer_profile, hymba_layer_profile_read, hymba_stage_name, HYMBA_N_STAGES,
     hymba_layer_check, hymba_layer_set_overlap, HYMBA_ERR_RANGE, HYMBA_ERR_UNSUPPORTED,
     hymba_mixer_decode_static, HYMBA_ERR_INVALID_ARG, HYMBA_ERR_WORKSPACE,

@@ -32,7 +32,7 @@ EXPORTED = [
     "hymba_mixer_prefill", "hymba_mixer_decode", "hymba_layer_meta_outputs",
     "hymba_last_error", "hymba_status_string", "hymba_kernel_attention",
     "hymba_kernel_selective_scan", "hymba_kernel_epilogue", "hymba_kernel_gemm_rows",
-    "hymba_kernel_gemm_rows_workspace",
+    "hymba_kernel_gemm_rows_workspace", "hymba_kernel_selective_scan_workspace",
     "hymba_layer_profile", "hymba_layer_profile_read", "hymba_stage_name",
     "hymba_layer_check", "hymba_layer_set_overlap", "hymba_mixer_decode_static",
     "griffin_block_persistent_bytes", "griffin_block_prepare", "griffin_workspace_bytes",
@@ -119,6 +119,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hymba_kernel_gemm_rows": (c_int32, [c_int32, c_int32, c_int32, P, c_int64, P, c_int64, P, c_int64, P,
                                              c_int64, c_int32, c_int32, c_int32, c_int32, c_int32, P, c_size_t, P]),
         "hymba_kernel_gemm_rows_workspace": (c_size_t, [c_int32, c_int32, c_int32]),
+        "hymba_kernel_selective_scan_workspace": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
         "hymba_layer_profile": (c_int32, [P, c_int32]),
         "hymba_layer_profile_read": (c_int32, [P, POINTER(c_float), c_int32]),
         "hymba_stage_name": (c_char_p, [c_int32]),
@@ -248,6 +249,10 @@ def hymba_kernel_gemm_rows(w_dtype, x_dtype, y_dtype, w, ldw, x, ldx, y, ldy, y3
 
 def hymba_kernel_gemm_rows_workspace(M: int, N: int, K: int) -> int:
     return load_library().hymba_kernel_gemm_rows_workspace(M, N, K)
+
+
+def hymba_kernel_selective_scan_workspace(B: int, T: int, E: int, N: int) -> int:
+    return load_library().hymba_kernel_selective_scan_workspace(B, T, E, N)
 
 
 def hymba_layer_check(layer: int, stream: int) -> None:

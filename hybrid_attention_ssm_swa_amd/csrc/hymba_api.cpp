@@ -194,7 +194,7 @@ PersistLayout persist_layout(const hymba_layer_cfg& c) {
 }
 
 struct WsLayout {
-  size_t X16, P, bc32, O, Ao, Ys, F, gemm, part, total;
+  size_t X16, P, bc32, O, Ao, Ys, F, gemm, part, seg, seg_bytes, total;
   int64_t rows;
   bool own_kernels_only = false;   // every projection on the hand-written GEMMs (no library workspace)
 };
@@ -217,6 +217,12 @@ WsLayout ws_layout(const hymba_layer& L, int64_t batch, int64_t seq) {
   w.gemm = off; off += b16 ? kGemmWorkspaceBytes : 0;
   w.part = off;
   off += align_up((size_t)std::max<int64_t>(batch, 1) * c.n_heads * kDecodeMaxSplits * (c.head_dim + 2) * 4);
+  // time-segment summaries of the prefill scan (and of the meta-prefix scan)
+  w.seg = off;
+  w.seg_bytes = std::max(scan_segment_bytes((int)std::max<int64_t>(batch, 1), (int)std::max<int64_t>(seq, 1),
+                                            c.d_inner, c.d_state),
+                         scan_segment_bytes(1, std::max(c.n_meta, 1), c.d_inner, c.d_state));
+  off += align_up(w.seg_bytes);
   w.total = off;
   return w;
 }
@@ -444,6 +450,7 @@ ScanArgs<CT> scan_args(const hymba_layer& L, char* ws, const WsLayout& wl, int B
   sa.y = reinterpret_cast<CT*>(ws + wl.Ys); sa.ldy = c.d_inner;
   sa.h_out = h_out;
   sa.B = B; sa.T = T_; sa.E = c.d_inner; sa.N = c.d_state;
+  sa.seg = reinterpret_cast<float*>(ws + wl.seg); sa.seg_bytes = wl.seg_bytes;
   return sa;
 }
 
@@ -985,16 +992,21 @@ int32_t hymba_kernel_selective_scan(int32_t dtype, const void* u, const void* dt
   if (dtype != HYMBA_F16 && dtype != HYMBA_F32)
     return fail(HYMBA_ERR_INVALID_ARG, "scan dtype must be HYMBA_F32 or HYMBA_F16");
   if (ws_bytes < (size_t)E * N * 4) return fail(HYMBA_ERR_WORKSPACE, "workspace too small");
+  if (B > 65535) return fail(HYMBA_ERR_UNSUPPORTED, "at most 65535 sequences per call");
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* A2 = static_cast<float*>(ws);
+  // beyond the scaled A: room for the time-segment summaries, if the caller gave it
+  const size_t a2_bytes = align_up((size_t)E * N * 4);
+  float* seg = ws_bytes > a2_bytes ? reinterpret_cast<float*>(static_cast<char*>(ws) + a2_bytes) : nullptr;
+  const size_t seg_bytes = seg ? ws_bytes - a2_bytes : 0;
   HIP_TRY(launch_scale_copy(A, A2, (int64_t)E * N, kLog2e, s), "A scaling");
   if (dtype == HYMBA_F16) {
     ScanArgs<half_t> a{static_cast<const half_t*>(u), static_cast<const half_t*>(dt), ld, bc, ld_bc, A2, D,
-                       dt_bias, h0, 0, static_cast<half_t*>(y), ldy, h_out, B, T, E, N};
+                       dt_bias, h0, 0, static_cast<half_t*>(y), ldy, h_out, B, T, E, N, seg, seg_bytes};
     HIP_TRY(launch_selective_scan(a, s), "scan launch");
   } else if (dtype == HYMBA_F32) {
     ScanArgs<float> a{static_cast<const float*>(u), static_cast<const float*>(dt), ld, bc, ld_bc, A2, D, dt_bias,
-                      h0, 0, static_cast<float*>(y), ldy, h_out, B, T, E, N};
+                      h0, 0, static_cast<float*>(y), ldy, h_out, B, T, E, N, seg, seg_bytes};
     HIP_TRY(launch_selective_scan(a, s), "scan launch");
   } else {
     return fail(HYMBA_ERR_INVALID_ARG, "scan dtype must be HYMBA_F32 or HYMBA_F16");
@@ -1026,6 +1038,11 @@ int32_t hymba_kernel_epilogue(int32_t dtype, const void* ao, int64_t ld_ao, cons
     return fail(HYMBA_ERR_INVALID_ARG, "epilogue dtype must be HYMBA_F32 or HYMBA_F16");
   }
   return HYMBA_OK;
+}
+
+size_t hymba_kernel_selective_scan_workspace(int32_t B, int32_t T, int32_t E, int32_t N) {
+  if (B < 1 || T < 1 || E < 1 || (N != 8 && N != 16)) return 0;
+  return align_up((size_t)E * N * 4) + scan_segment_bytes(B, T, E, N);
 }
 
 size_t hymba_kernel_gemm_rows_workspace(int32_t M, int32_t N, int32_t K) {

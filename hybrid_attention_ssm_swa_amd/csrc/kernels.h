@@ -45,7 +45,10 @@ struct ScanArgs {
   CT* y; int64_t ldy;
   float* h_out;
   int B, T, E, N;
+  float* seg = nullptr; size_t seg_bytes = 0;   // time-segment summaries (scan_segment_bytes); may be NULL
 };
+// Workspace for the time-segment summaries of a scan of B sequences of T steps (0: one pass).
+size_t scan_segment_bytes(int B, int T, int E, int N);
 hipError_t launch_selective_scan(const ScanArgs<float>& a, hipStream_t s);
 hipError_t launch_selective_scan(const ScanArgs<half_t>& a, hipStream_t s);
 

@@ -37,17 +37,32 @@ namespace {
 // step (B/C as broadcast reads).  Each wave's partial sums over its states
 // meet in LDS once per chunk; the wave that prepared step s also adds the skip
 // term D*u and stores y.
+//
+// Time segments.  When B * E / 64 channel groups give too few waves to fill the SIMDs (few
+// long sequences), time is cut into S segments of seg_len steps (a multiple of the chunk) and
+// the scan runs in two launches.  The summary launch runs every segment but the last from a zero
+// state and keeps only its end state h_end[j] and its total step sum_t delta_t per channel.  The
+// scan launch then runs every segment at once: segment j starts from the true state at its
+// beginning, which the recurrence being linear in h gives in closed form from the summaries,
+//   H_0 = h0,  H_{i+1} = exp2(A2 * sum_delta_i) * H_i + h_end[i]
+// (the product of a segment's decays exp2(delta_t A2) is exp2(A2 sum_t delta_t)), and writes y.
+// That is about 1.6 times the arithmetic of one pass, for S times the waves.
 constexpr int kTC = 16;
 
 template <int NS> struct BcVec { typedef float4 type; };
 template <> struct BcVec<2> { typedef float2 type; };
 
-template <typename T, int N, int NS>
+// kSummary: the summary launch (no y; end state and step sum of segment blockIdx.z into seg_h,
+// seg_d).  Otherwise segment blockIdx.z of seg_len steps, started from the summaries of the
+// segments before it; the last segment writes h_out.  One segment of T_len steps is the plain scan.
+// seg_h: [S - 1][B][E][N], seg_d: [S - 1][B][E] (fp32).
+template <typename T, int N, int NS, bool kSummary>
 __global__ __launch_bounds__(64 * (N / NS)) void selective_scan_kernel(
     const T* __restrict__ u, const T* __restrict__ dt, int64_t ld, const float* __restrict__ bc, int64_t ld_bc,
     const float* __restrict__ A2, const float* __restrict__ Dp, const float* __restrict__ dt_bias,
     const float* __restrict__ h0, int64_t h0_bstride, T* __restrict__ y, int64_t ldy,
-    float* __restrict__ h_out, int T_len, int E) {
+    float* __restrict__ h_out, int T_len, int E, int seg_len, float* __restrict__ seg_h,
+    float* __restrict__ seg_d) {
   constexpr int WPC = N / NS;
   constexpr int SPW = kTC / WPC;                   // steps each wave prepares per chunk
   constexpr int ROW4 = 2 * N / 4;                  // float4 per B/C row
@@ -62,24 +77,37 @@ __global__ __launch_bounds__(64 * (N / NS)) void selective_scan_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int b = blockIdx.y;
+  const int nb = gridDim.y;
+  const int seg = blockIdx.z;
   const int c = blockIdx.x * 64 + lane;
   const bool active = c < E;
   const int cc = active ? c : E - 1;
   const int n0 = wave * NS;
+  const int t_begin = seg * seg_len;
+  const int T_seg = min(seg_len, T_len - t_begin);   // >= 1: the launch has ceil(T_len / seg_len) segments
   float a2[NS], h[NS];
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
     a2[n] = A2[(int64_t)cc * N + n0 + n];
-    h[n] = h0 ? h0[b * h0_bstride + (int64_t)cc * N + n0 + n] : 0.f;
+    h[n] = (!kSummary && h0) ? h0[b * h0_bstride + (int64_t)cc * N + n0 + n] : 0.f;
+  }
+  if constexpr (!kSummary) {
+    for (int i = 0; i < seg; ++i) {   // carry the state over the segments before this one
+      const int64_t ch = ((int64_t)i * nb + b) * E + cc;
+      const float sd = seg_d[ch];
+#pragma unroll
+      for (int n = 0; n < NS; ++n) h[n] = fmaf(fast_exp2(sd * a2[n]), h[n], seg_h[ch * N + n0 + n]);
+    }
   }
   const float Dc = Dp[cc];
   const float bias = dt_bias[cc];
-  const int64_t row0 = (int64_t)b * T_len;
+  const int64_t row0 = (int64_t)b * T_len + t_begin;
   const T* up = u + row0 * ld + cc;
   const T* dp = dt + row0 * ld + cc;
   const float* bcrow = bc + row0 * ld_bc;
   T* yrow = y + row0 * ldy + c;
-  const int last = T_len - 1;
+  const int last = T_seg - 1;
+  float dsum = 0.f;   // summary: this wave's share of the segment's step sum
 
   T un[SPW], dn[SPW];
   float4 bcr[PER_T];
@@ -100,15 +128,16 @@ __global__ __launch_bounds__(64 * (N / NS)) void selective_scan_kernel(
       }
     }
   };
-  // publish the fetched chunk into LDS buffer bb; returns D * u of this wave's steps
+  // publish the chunk fetched for step t into LDS buffer bb; returns D * u of this wave's steps
   float skip_next[SPW];
-  auto publish = [&](int bb) {
+  auto publish = [&](int bb, int t) {
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const float uv = static_cast<float>(un[j]);
       const float delta = softplus_f(static_cast<float>(dn[j]) + bias);
       dd[bb][wave + WPC * j][lane] = make_float2(delta, delta * uv);
       skip_next[j] = Dc * uv;
+      if (kSummary && t + wave + WPC * j <= last) dsum += delta;
     }
 #pragma unroll
     for (int k = 0; k < PER_T; ++k) {
@@ -118,17 +147,17 @@ __global__ __launch_bounds__(64 * (N / NS)) void selective_scan_kernel(
   };
 
   fetch(0);
-  publish(0);
+  publish(0, 0);
   float skip[SPW];
 #pragma unroll
   for (int j = 0; j < SPW; ++j) skip[j] = skip_next[j];
   fetch(kTC);
   __syncthreads();
   int buf = 0;
-  for (int t0 = 0; t0 < T_len; t0 += kTC) {
-    publish(buf ^ 1);          // chunk t0 + kTC (fetched one chunk ago)
+  for (int t0 = 0; t0 < T_seg; t0 += kTC) {
+    publish(buf ^ 1, t0 + kTC);   // chunk t0 + kTC (fetched one chunk ago)
     fetch(t0 + 2 * kTC);
-    const int len = min(kTC, T_len - t0);
+    const int len = min(kTC, T_seg - t0);
     const float* bcsf = reinterpret_cast<const float*>(&bcs[buf][0][0]);
     float part[kTC];
     // full chunks take a branch-free copy of the step loop; only the last chunk checks len
@@ -142,18 +171,22 @@ __global__ __launch_bounds__(64 * (N / NS)) void selective_scan_kernel(
 #pragma unroll
           for (int q = 0; q < NS / VW; ++q) {
             const BV vb = *reinterpret_cast<const BV*>(bcsf + s * 2 * N + n0 + VW * q);
-            const BV vc = *reinterpret_cast<const BV*>(bcsf + s * 2 * N + N + n0 + VW * q);
             const float* pb = reinterpret_cast<const float*>(&vb);
-            const float* pc = reinterpret_cast<const float*>(&vc);
 #pragma unroll
-            for (int e = 0; e < VW; ++e) { bb[VW * q + e] = pb[e]; cb[VW * q + e] = pc[e]; }
+            for (int e = 0; e < VW; ++e) bb[VW * q + e] = pb[e];
+            if constexpr (!kSummary) {
+              const BV vc = *reinterpret_cast<const BV*>(bcsf + s * 2 * N + N + n0 + VW * q);
+              const float* pc = reinterpret_cast<const float*>(&vc);
+#pragma unroll
+              for (int e = 0; e < VW; ++e) cb[VW * q + e] = pc[e];
+            }
           }
           float acc = 0.f;
 #pragma unroll
           for (int n = 0; n < NS; ++n) {
             const float dA = fast_exp2(d.x * a2[n]);
             h[n] = fmaf(dA, h[n], d.y * bb[n]);
-            acc = fmaf(cb[n], h[n], acc);
+            if constexpr (!kSummary) acc = fmaf(cb[n], h[n], acc);
           }
           part[s] = acc;
         }
@@ -161,7 +194,9 @@ __global__ __launch_bounds__(64 * (N / NS)) void selective_scan_kernel(
     };
     if (len == kTC) steps(std::true_type{});
     else steps(std::false_type{});
-    if constexpr (WPC == 1) {
+    if constexpr (kSummary) {
+      __syncthreads();         // the next chunk's LDS buffer is ready
+    } else if constexpr (WPC == 1) {
 #pragma unroll
       for (int s = 0; s < kTC; ++s)
         if (s < len && active) Elem<T>::store(yrow + (int64_t)(t0 + s) * ldy, part[s] + skip[s]);
@@ -186,7 +221,21 @@ __global__ __launch_bounds__(64 * (N / NS)) void selective_scan_kernel(
     for (int j = 0; j < SPW; ++j) skip[j] = skip_next[j];
     buf ^= 1;
   }
-  if (active && h_out) {
+  if constexpr (kSummary) {
+    const int64_t ch = ((int64_t)seg * nb + b) * E + c;
+    if (active) {
+#pragma unroll
+      for (int n = 0; n < NS; ++n) seg_h[ch * N + n0 + n] = h[n];
+    }
+    ys[WPC > 1 ? wave : 0][0][lane] = dsum;   // the waves' step sums, added in wave order
+    __syncthreads();
+    if (wave == 0) {
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < WPC; ++w) tot += ys[w][0][lane];
+      if (active) seg_d[ch] = tot;
+    }
+  } else if (active && h_out && seg == (int)gridDim.z - 1) {
     float* ho = h_out + ((int64_t)b * E + c) * N + n0;
 #pragma unroll
     for (int n = 0; n < NS; ++n) ho[n] = h[n];
@@ -255,6 +304,11 @@ __global__ __launch_bounds__(256) void ssm_step_kernel(StepArgs<T> a) {
 #ifndef HYMBA_SCAN_WAVES
 #define HYMBA_SCAN_WAVES 3072
 #endif
+#ifndef HYMBA_SCAN_MAX_SEGMENTS
+#define HYMBA_SCAN_MAX_SEGMENTS 8
+#endif
+constexpr int kMinSegLen = 256;   // shorter segments spend more on the summary pass than they gain
+
 inline int scan_states_per_wave(int B, int E, int N) {
   const int64_t groups = (int64_t)B * ceil_div(E, 64);
   int ns = N < 8 ? N : 8;   // one wave holding all 16 states runs out of registers
@@ -262,24 +316,54 @@ inline int scan_states_per_wave(int B, int E, int N) {
   return ns;
 }
 
+struct ScanPlan { int ns; int nseg; int seg_len; };
+
+// One pass when the channel groups give ~HYMBA_SCAN_WAVES waves at 4 states per wave (or the
+// sequences are short); otherwise 4 states per wave and enough time segments to get there.
+ScanPlan scan_plan(int B, int T, int E, int N) {
+  ScanPlan p{scan_states_per_wave(B, E, N), 1, T};
+  const int64_t waves = (int64_t)B * ceil_div(E, 64) * (N / 4);
+  int64_t nseg = std::min<int64_t>(HYMBA_SCAN_MAX_SEGMENTS, ceil_div(HYMBA_SCAN_WAVES, waves));
+  nseg = std::min<int64_t>(nseg, T / kMinSegLen);
+  if (nseg >= 2) {
+    p.ns = 4;
+    p.seg_len = static_cast<int>(ceil_div(ceil_div(T, nseg), kTC) * kTC);
+    p.nseg = static_cast<int>(ceil_div(T, p.seg_len));
+  }
+  return p;
+}
+
 template <typename T, int N, int NS>
-void scan_launch(const ScanArgs<T>& a, hipStream_t s) {
-  dim3 grid(static_cast<unsigned>(ceil_div(a.E, 64)), a.B), block(64 * (N / NS));
-  hipLaunchKernelGGL((selective_scan_kernel<T, N, NS>), grid, block, 0, s, a.u, a.dt, a.ld, a.bc, a.ld_bc, a.A2,
-                     a.D, a.dt_bias, a.h0, a.h0_bstride, a.y, a.ldy, a.h_out, a.T, a.E);
+void scan_launch(const ScanArgs<T>& a, const ScanPlan& p, hipStream_t s) {
+  dim3 block(64 * (N / NS));
+  float* seg_h = a.seg;
+  float* seg_d = a.seg + (int64_t)(p.nseg - 1) * a.B * a.E * N;
+  if (p.nseg > 1) {
+    dim3 g1(static_cast<unsigned>(ceil_div(a.E, 64)), a.B, p.nseg - 1);
+    hipLaunchKernelGGL((selective_scan_kernel<T, N, NS, true>), g1, block, 0, s, a.u, a.dt, a.ld, a.bc, a.ld_bc,
+                       a.A2, a.D, a.dt_bias, a.h0, a.h0_bstride, a.y, a.ldy, a.h_out, a.T, a.E, p.seg_len, seg_h,
+                       seg_d);
+  }
+  dim3 grid(static_cast<unsigned>(ceil_div(a.E, 64)), a.B, p.nseg);
+  hipLaunchKernelGGL((selective_scan_kernel<T, N, NS, false>), grid, block, 0, s, a.u, a.dt, a.ld, a.bc, a.ld_bc,
+                     a.A2, a.D, a.dt_bias, a.h0, a.h0_bstride, a.y, a.ldy, a.h_out, a.T, a.E, p.seg_len, seg_h,
+                     seg_d);
 }
 
 template <typename T>
 hipError_t scan_dispatch(const ScanArgs<T>& a, hipStream_t s) {
-  const int ns = scan_states_per_wave(a.B, a.E, a.N);
+  if (a.B < 1 || a.T < 1 || a.B > 65535) return hipErrorInvalidValue;
+  ScanPlan p = scan_plan(a.B, a.T, a.E, a.N);
+  if (p.nseg > 1 && (!a.seg || a.seg_bytes < scan_segment_bytes(a.B, a.T, a.E, a.N)))
+    p = ScanPlan{scan_states_per_wave(a.B, a.E, a.N), 1, a.T};   // no room for the summaries: one pass
   if (a.N == 8) {
-    if (ns == 8) scan_launch<T, 8, 8>(a, s);
-    else if (ns == 4) scan_launch<T, 8, 4>(a, s);
-    else scan_launch<T, 8, 2>(a, s);
+    if (p.ns == 8) scan_launch<T, 8, 8>(a, p, s);
+    else if (p.ns == 4) scan_launch<T, 8, 4>(a, p, s);
+    else scan_launch<T, 8, 2>(a, p, s);
   } else if (a.N == 16) {
-    if (ns == 8) scan_launch<T, 16, 8>(a, s);
-    else if (ns == 4) scan_launch<T, 16, 4>(a, s);
-    else scan_launch<T, 16, 2>(a, s);
+    if (p.ns == 8) scan_launch<T, 16, 8>(a, p, s);
+    else if (p.ns == 4) scan_launch<T, 16, 4>(a, p, s);
+    else scan_launch<T, 16, 2>(a, p, s);
   } else {
     return hipErrorInvalidValue;
   }
@@ -315,6 +399,11 @@ __global__ void fill_kernel(float* __restrict__ dst, int64_t n, float value) {
 }
 
 }  // namespace
+
+size_t scan_segment_bytes(int B, int T, int E, int N) {
+  const ScanPlan p = scan_plan(B, T, E, N);
+  return p.nseg > 1 ? (size_t)(p.nseg - 1) * B * E * (N + 1) * sizeof(float) : 0;
+}
 
 hipError_t launch_selective_scan(const ScanArgs<float>& a, hipStream_t s) { return scan_dispatch(a, s); }
 hipError_t launch_selective_scan(const ScanArgs<half_t>& a, hipStream_t s) { return scan_dispatch(a, s); }

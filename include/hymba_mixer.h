@@ -282,7 +282,14 @@ int32_t hymba_kernel_attention(int32_t dtype, const void* q, int64_t ld_q, const
  * fp32 (A is the decay rate, not scaled).  h0 [E, N] fp32 shared initial
  * state or NULL (zero).  y [B*T, E] (row stride ldy) receives the ungated
  * output; h_out [B, E, N] fp32 the final state (may be NULL).
- * workspace: >= E*N*4 bytes. */
+ * workspace: >= E*N*4 bytes, 256-byte aligned.  With
+ * hymba_kernel_selective_scan_workspace(B, T, E, N) bytes, few long
+ * sequences (too few channel groups to fill the GPU) are cut into time
+ * segments: a first launch keeps each segment's end state from zero and its
+ * summed step, and the scan starts every segment from the state the
+ * recurrence carries into it (the product of a segment's decays is
+ * exp(A * the sum of its steps)).  With less, one pass.  Either way the same
+ * recurrence, to fp32 rounding.  B <= 65535. */
 int32_t hymba_kernel_selective_scan(int32_t dtype, const void* u, const void* dt, int64_t ld,
                                     const float* bc, int64_t ld_bc, const float* A, const float* D,
                                     const float* dt_bias, const float* h0, void* y, int64_t ldy,
@@ -322,6 +329,10 @@ int32_t hymba_kernel_gemm_rows(int32_t w_dtype, int32_t x_dtype, int32_t y_dtype
  * never splits K across workgroups (kept so that callers size it the same way if
  * a later kernel does). */
 size_t hymba_kernel_gemm_rows_workspace(int32_t M, int32_t N, int32_t K);
+
+/* Workspace bytes of hymba_kernel_selective_scan for B sequences of T steps
+ * (E channels, N states) that let it split time; 0 for invalid sizes. */
+size_t hymba_kernel_selective_scan_workspace(int32_t B, int32_t T, int32_t E, int32_t N);
 
 #ifdef __cplusplus
 }

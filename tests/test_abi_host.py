@@ -352,6 +352,25 @@ def test_gemm_rows_rejects_bad_arguments():
     assert L.hymba_kernel_gemm_rows_workspace(128, 16384, 512) == 0
 
 
+def test_scan_workspace_sizes():
+    """The scan's workspace: the scaled A (E*N fp32, 256-byte aligned), plus (S - 1) segment
+    summaries of B*E*(N + 1) fp32 when too few channel groups would fill the GPU: S segments of a
+    multiple of 16 steps, S <= 8, each >= 256 steps, enough for ~3072 waves at 4 states per wave."""
+    ws = L.hymba_kernel_selective_scan_workspace
+    # 1.5B 8K SWA prefill: 16 x 50 channel groups x 4 waves = 3200 waves, one pass
+    assert ws(16, 8192, 3200, 16) == 3200 * 16 * 4
+    # global 8K prefill, B = 8: 1600 waves -> 2 segments of 4096 steps
+    assert ws(8, 8192, 3200, 16) == 3200 * 16 * 4 + 1 * 8 * 3200 * 17 * 4
+    # 300M ablation, B = 8, T = 2048: 1024 waves -> 3 segments of 688 steps
+    assert ws(8, 2048, 2048, 16) == 2048 * 16 * 4 + 2 * 8 * 2048 * 17 * 4
+    # short sequences never split (segments of >= 256 steps)
+    assert ws(1, 300, 520, 16) == 520 * 16 * 4
+    assert ws(2, 511, 520, 8) == 520 * 8 * 4 + 256 * 0   # 511 // 256 = 1 segment
+    assert ws(2, 1100, 520, 8) == 520 * 8 * 4 + 3 * 2 * 520 * 9 * 4   # 4 segments of 288 steps
+    assert ws(1, 100000, 64, 16) == 64 * 16 * 4 + 7 * 1 * 64 * 17 * 4   # at most 8 segments
+    assert ws(0, 10, 64, 16) == 0 and ws(1, 10, 64, 12) == 0
+
+
 def test_check_and_overlap_calls():
     lib = L.load_library()
     assert lib.hymba_layer_check(None, None) == L.HYMBA_ERR_INVALID_ARG

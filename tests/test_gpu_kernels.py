@@ -133,6 +133,53 @@ def test_selective_scan_kernel(dtype, B, T, E, N, with_h0):
         check(f"h_T[b={b}]", gh[b], rh, dtype)
 
 
+@pytest.mark.parametrize("dtype,B,T,E,N,with_h0", [
+    ("f16", 2, 1100, 520, 16, True),    # 4 segments of 288 steps, the last ragged
+    ("f32", 2, 1100, 520, 8, False),
+    ("f16", 1, 4000, 136, 16, True),    # 8 segments
+])
+def test_selective_scan_time_segments(dtype, B, T, E, N, with_h0):
+    """Few long sequences: with the workspace the size query asks for, the scan splits time into
+    segments (a summary launch, then every segment from its carried-in state)."""
+    announce(f"segmented scan {dtype} B={B} T={T} E={E} N={N} h0={with_h0}")
+    r = np.random.Generator(np.random.PCG64(400 + T + E))
+    ld = 2 * E + 8
+    P = _round(r.standard_normal((B * T, ld)).astype(np.float32), dtype)
+    ldbc = 2 * N + 4
+    BC = _round(r.standard_normal((B * T, ldbc)).astype(np.float32), dtype)
+    A = (-np.exp(r.uniform(0, np.log(8), (E, N)))).astype(np.float32)
+    D = r.standard_normal(E).astype(np.float32)
+    bias = np.full(E, -2.0, np.float32)
+    h0 = r.standard_normal((E, N)).astype(np.float32) if with_h0 else None
+    dP = dev(P, dtype)
+    t32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()   # noqa: E731
+    dBC, dA, dD, db = t32(BC), t32(A), t32(D), t32(bias)
+    dh0 = t32(h0) if with_h0 else None
+    nws = H.hymba_kernel_selective_scan_workspace(B, T, E, N)
+    assert nws > E * N * 4            # the shape is one that splits
+    ws = torch.full((nws,), 255, dtype=torch.uint8, device="cuda")   # NaN bytes: every summary is written
+    es = dP.element_size()
+    base = dP.data_ptr()
+    outs = []
+    for nbytes in (nws, E * N * 4):   # segmented, then one pass
+        y = torch.empty((B * T, E), dtype=dP.dtype, device="cuda")
+        hT = torch.empty((B, E, N), dtype=torch.float32, device="cuda")
+        H.hymba_kernel_selective_scan(CODE[dtype], base, base + E * es, ld, dBC.data_ptr(), ldbc, dA.data_ptr(),
+                                      dD.data_ptr(), db.data_ptr(), dh0.data_ptr() if with_h0 else None,
+                                      y.data_ptr(), E, hT.data_ptr(), B, T, E, N, ws.data_ptr(), nbytes,
+                                      torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        outs.append((host(y).reshape(B, T, E), host(hT)))
+    for b in range(B):
+        Pb = P[b * T:(b + 1) * T].astype(np.float64)
+        BCb = BC[b * T:(b + 1) * T].astype(np.float64)
+        ry, rh = orc.selective_scan(Pb[:, :E], Pb[:, E:2 * E], BCb[:, :N], BCb[:, N:2 * N],
+                                    A, D, bias, h0 if with_h0 else np.zeros((E, N)))
+        for tag, (gy, gh) in zip(("segmented", "one pass"), outs):
+            check_stored(f"{tag} y[b={b}]", gy[b], ry, dtype)
+            check(f"{tag} h_T[b={b}]", gh[b], rh, dtype)
+
+
 @pytest.mark.parametrize("dtype,rows,E", [("f16", 37, 3200), ("f16", 5, 64), ("f16", 3, 8200), ("f16", 4, 2048),
                                           ("f16", 2, 4104), ("f32", 19, 136), ("f32", 3, 2056),
                                           # thousands of rows (workgroups over the whole grid)
