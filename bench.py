@@ -66,9 +66,10 @@ def visible_keys(s, T):
 
 
 def conversion_bytes(s, R):
-    """bf16 layers: x bf16 -> fp16 (read 2 + write 2 B per element) and the B/C columns
-    fp16 -> fp32 (2 + 4)."""
-    return float(R * s.d_model * 4 + R * 2 * s.d_state * 6)
+    """bf16 layers: x bf16 -> fp16 (read 2 + write 2 B per element), the B/C columns of the shared
+    projection computed from the same x rows and written in fp32 (4 B each), and their weight
+    columns read once (2 B)."""
+    return float(R * s.d_model * 4 + R * 2 * s.d_state * 4 + 2 * s.d_state * s.d_model * 2)
 
 
 def prefill_work(s, B, T):
@@ -80,8 +81,8 @@ def prefill_work(s, B, T):
         "attention": ("mfma", 4.0 * s.head_dim * s.n_heads * B * visible_keys(s, T)),
         "w_o": ("mfma", 2.0 * R * hq * E),
         "out_proj": ("mfma", 2.0 * R * E * d),
-        # u, dt read; y written; B, C read; final state written
-        "ssm": ("hbm", float(R * E * es * 3 + R * 2 * N * es + B * E * N * 4)),
+        # u, dt read; y written; B, C read (fp32); final state written
+        "ssm": ("hbm", float(R * E * es * 3 + R * 2 * N * 4 + B * E * N * 4)),
         # Ao, y, z read; F written
         "epilogue": ("hbm", float(R * E * es * 4)),
     }
@@ -105,7 +106,7 @@ def decode_work(s, B, pos, cache_len):
         "in_proj": ("hbm", float(s.n_in * d * es + B * d * es + B * s.n_in * es)),
         "attention": ("hbm", float(B * keys * kvb * 2 + s.n_meta * kvb * 2 + B * s.n_heads * s.head_dim * es * 2)),
         "w_o": ("hbm", float(E * s.n_heads * s.head_dim * es)),
-        "ssm": ("hbm", float(B * E * N * 4 * 2 + B * E * es * 3 + B * 2 * N * es)),
+        "ssm": ("hbm", float(B * E * N * 4 * 2 + B * E * es * 3 + B * 2 * N * 4)),
         "epilogue": ("hbm", float(B * E * es * 4)),
         "out_proj": ("hbm", float(d * E * es)),
     }
@@ -324,6 +325,36 @@ def bench_decode(cfg_id, steps, warmup, case=None):
     return out
 
 
+def bench_attention_alone(steps, warmup):
+    """swa_meta_attn alone at the 1.5B 8K SWA shape (16 x 8192 queries, 25 heads, 5 KV heads, window 1024,
+    128 meta keys), fp16 operands in the layer's layout (q rows of the projection, K/V handed in),
+    through the per-kernel entry point.  For counter passes: the only launches are this kernel's."""
+    import torch
+    from hybrid_attention_ssm_swa_amd import _lib as L
+    from hymba_synth import CONFIGS
+    s = CONFIGS[2].shape
+    B, T, M, Hq, Hkv, hd, W = 16, 8192, s.n_meta, s.n_heads, s.n_kv_heads, s.head_dim, s.window
+    ld_q = (s.n_in + 63) // 64 * 64
+    g = torch.Generator(device="cuda").manual_seed(0)
+    q = torch.randn(B * T, ld_q, device="cuda", generator=g).half()
+    k = torch.randn(B, T, Hkv, hd, device="cuda", generator=g).half()
+    v = torch.randn(B, T, Hkv, hd, device="cuda", generator=g).half()
+    km = torch.randn(M, Hkv, hd, device="cuda", generator=g).half()
+    vm = torch.randn(M, Hkv, hd, device="cuda", generator=g).half()
+    o = torch.empty(B * T, Hq * hd, device="cuda", dtype=torch.half)
+    st = torch.cuda.current_stream().cuda_stream
+    fn = lambda i: L.hymba_kernel_attention(L.HYMBA_F16, q.data_ptr(), ld_q, k.data_ptr(), v.data_ptr(),  # noqa
+                                            Hkv * hd, T * Hkv * hd, km.data_ptr(), vm.data_ptr(), M, o.data_ptr(),
+                                            Hq * hd, B, T, Hq, Hkv, hd, W, st)
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    ms = _time_loop(fn, steps)
+    flops = 4.0 * hd * Hq * B * visible_keys(s, T)
+    return {"kernel": "swa_meta_attn", "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+            "frac": flops / (ms * 1e-3) / PEAK_BF16}
+
+
 def griffin_work(shape, B, T):
     """Algorithmic work of the Griffin block's stages (prefill of B x T, or decode with T = 1)."""
     es = 2 if shape.dtype == "bf16" else 4
@@ -430,8 +461,8 @@ def copy_probe():
 def _kernel_stage(name):
     for key, st in (("swa_meta_attn", "attention"), ("attn_f32", "attention"), ("decode_attn", "attention"),
                     ("decode_combine", "attention"), ("selective_scan", "ssm"), ("ssm_step", "ssm"),
-                    ("epilogue_kernel", "epilogue"), ("convert_kernel", "convert"), ("kv_write", "kv_write"),
-                    ("neg_kernel", "copy_probe")):
+                    ("epilogue_kernel", "epilogue"), ("convert_kernel", "convert"), ("convert_bc_kernel", "convert"),
+                    ("kv_write", "kv_write"), ("neg_kernel", "copy_probe")):
         if key in name:
             return st
     if "Cijk" in name or "gemm" in name.lower():   # hipBLASLt (Tensile) kernels
@@ -513,6 +544,9 @@ def summarize_rocprof(trace_dir, bench_json, fetch_dir, write_dir, command, out_
         txt = [l for l in open(bench_json).read().splitlines() if l.startswith("{")]
         bench = json.loads(txt[-1]) if txt else None
     lines.append("## per-stage kernel of the timed steps (kernel_trace.csv, dispatch-order attribution)")
+    lines.append("## avg_us: the last calls of each kernel, which bench.py runs in the serial schedule (every kernel")
+    lines.append("## alone on the launch stream); bench_us: bench.py's event means in the overlapped schedule, where")
+    lines.append("## the scan runs beside attention and W_O")
     lines.append(f"{'stage':<10} {'calls':>5} {'avg_us':>10} {'bench_us':>10}  grid            kernel")
     for st in STAGES + ["copy_probe"]:
         if st not in per_stage:
@@ -622,6 +656,139 @@ def summarize_decode(trace_dir, bench_json, command, out_txt):
     print("\n".join(lines))
 
 
+def summarize_counters(pmc_dirs, durations_dir, command, out_txt, kernel="swa_meta_attn", n_cu=N_CU, n_xcd=8):
+    """SQ counters of one kernel (several --pmc passes of the same command, counter_collection.csv),
+    averaged over its dispatches after the first, with the derived utilisations.  GRBM_GUI_ACTIVE is
+    read as summed over the XCDs: per XCD it is the kernel's length in shader-clock cycles, which
+    with the same dispatch's duration gives the average clock; MFMA busy / (cycles x SIMDs) is the
+    fraction of the matrix pipes' cycles spent issuing MFMAs.  Ratios are formed within one pass."""
+    passes = []
+    for d in pmc_dirs:
+        per, dur = {}, {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            did = int(r["Dispatch_Id"])
+            per.setdefault(did, {}).setdefault(r["Counter_Name"], 0.0)
+            per[did][r["Counter_Name"]] += float(r["Counter_Value"])
+            dur[did] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        ds = sorted(per)[1:] or sorted(per)
+        mean = {c: sum(per[i][c] for i in ds) / len(ds) for c in per[ds[0]]}
+        mean["_duration_s"] = sum(dur[i] for i in ds) / len(ds)
+        passes.append(mean)
+    trace = [r for r in _csv_rows(durations_dir, "kernel_trace.csv") if kernel in r["Kernel_Name"]] \
+        if durations_dir else []
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e9 for r in trace[1:]]
+    lines = [f"# rocprofv3 counters: {command['title']}", "# profiled commands (repository root, one MI355X):"]
+    lines += [f"#   {c}" for c in command["trace"]]
+    lines += ["# summarized on the host with:", f"#   {command['summary']}", ""]
+    if durs:
+        lines.append(f"kernel duration without counters (kernel trace, mean of {len(durs)}): "
+                     f"{sum(durs) / len(durs) * 1e3:.4f} ms")
+    for k, m in enumerate(passes):
+        lines += ["", f"## pass {k + 1}: mean per dispatch (dispatch duration under counters "
+                      f"{m['_duration_s'] * 1e3:.4f} ms)"]
+        for c in sorted(x for x in m if not x.startswith("_")):
+            lines.append(f"{c:<30} {m[c]:>18.5g}")
+        if "GRBM_GUI_ACTIVE" not in m:
+            continue
+        cyc = m["GRBM_GUI_ACTIVE"] / n_xcd
+        simd_cycles = cyc * n_cu * 4
+        lines.append(f"-> shader clock (GRBM_GUI_ACTIVE / {n_xcd} XCDs / duration): "
+                     f"{cyc / m['_duration_s'] / 1e9:.3f} GHz")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            lines.append(f"-> MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {n_cu * 4} SIMDs) = "
+                         f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:.3f}")
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in m and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            lines.append(f"-> VALU co-issued during MFMA: SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES = "
+                         f"{m['SQ_VALU_MFMA_COEXEC_CYCLES'] / m['SQ_VALU_MFMA_BUSY_CYCLES']:.3f}")
+        if "SQ_ACTIVE_INST_VALU" in m:
+            lines.append(f"-> VALU issue: SQ_ACTIVE_INST_VALU / (cycles x {n_cu * 4} SIMDs) = "
+                         f"{m['SQ_ACTIVE_INST_VALU'] / simd_cycles:.3f}")
+        if "SQ_INSTS_VALU" in m and "SQ_INSTS_MFMA" in m:
+            lines.append(f"-> VALU instructions per MFMA: {m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.2f}")
+        if "SQ_LDS_BANK_CONFLICT" in m and "SQ_LDS_IDX_ACTIVE" in m:
+            lines.append(f"-> LDS bank-conflict cycles / LDS active cycles = "
+                         f"{m['SQ_LDS_BANK_CONFLICT'] / m['SQ_LDS_IDX_ACTIVE']:.3f}")
+        if "SQ_WAIT_ANY" in m and "SQ_BUSY_CYCLES" in m:
+            lines.append(f"-> SQ_WAIT_INST_LDS / SQ_WAIT_ANY = {m.get('SQ_WAIT_INST_LDS', 0) / m['SQ_WAIT_ANY']:.3f}")
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_decode_traffic(fetch_dir, write_dir, trace_dir, bench_json, command, out_txt, min_calls=4,
+                             call_marker="convert_bc"):
+    """FETCH_SIZE and WRITE_SIZE per decode kernel and role (producer, consumer) from two --pmc
+    passes of bench.py --decode-only --copy-probe, scaled by the copy kernel's readings, next to
+    the kernels' median durations (kernel trace) and the resulting rate.  A pair step calls the
+    producer, then the consumer, and each layer call starts with the input conversion
+    (`call_marker`): dispatches take the role of the call they fall in.  Kernels with fewer than
+    `min_calls` dispatches per role (GEMM candidate timing, set-up) are left out."""
+    def total(r):
+        if "Grid_Size_X" in r:
+            return str(int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
+        return r.get("Grid_Size", "?")
+
+    def by_role(rows, value):
+        """{(kernel, threads, role): [value per dispatch, in order]}"""
+        per = {}
+        for r in rows:
+            per.setdefault(int(r["Dispatch_Id"]), [r, 0.0])
+            per[int(r["Dispatch_Id"])][1] += value(r)
+        out, calls = {}, -1
+        for did in sorted(per):
+            r, v = per[did]
+            if call_marker in r["Kernel_Name"]:
+                calls += 1
+            if calls < 0 or "neg_kernel" in r["Kernel_Name"]:
+                continue
+            out.setdefault((r["Kernel_Name"], total(r), ("producer", "consumer")[calls % 2]), []).append(v)
+        return out
+
+    def probe(d, cname):
+        v = [float(r["Counter_Value"]) for r in _csv_rows(d, "counter_collection.csv")
+             if r["Counter_Name"] == cname and "neg_kernel" in r["Kernel_Name"]]
+        return sum(v) / len(v)
+    cnt = lambda d, c: [r for r in _csv_rows(d, "counter_collection.csv") if r["Counter_Name"] == c]   # noqa: E731
+    fetch = by_role(cnt(fetch_dir, "FETCH_SIZE"), lambda r: float(r["Counter_Value"]))
+    write = by_role(cnt(write_dir, "WRITE_SIZE"), lambda r: float(r["Counter_Value"]))
+    f_fetch = COPY_PROBE_BYTES / (probe(fetch_dir, "FETCH_SIZE") * 1024)
+    f_write = COPY_PROBE_BYTES / (probe(write_dir, "WRITE_SIZE") * 1024)
+    durs = by_role(_csv_rows(trace_dir, "kernel_trace.csv") if trace_dir else [],
+                   lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    keys = [k for k in fetch if k in write and len(fetch[k]) >= min_calls]
+    lines = [f"# rocprofv3 HBM traffic: {command['title']}", "# profiled commands (repository root, one MI355X):"]
+    lines += [f"#   {c}" for c in command["trace"]]
+    lines += ["# summarized on the host with:", f"#   {command['summary']}", "",
+              f"## L2<->HBM bytes per launch (mean after the first), counters scaled by the plain copy kernel: "
+              f"fetch x{f_fetch:.4f}, write x{f_write:.4f}",
+              "## median_us from the kernel trace (same kernel and role); GB/s = (fetch + write) / median",
+              f"{'role':<9} {'fetch_MB':>9} {'write_MB':>9} {'total_MB':>9} {'median_us':>10} {'GB/s':>8}  "
+              f"{'threads':<9} kernel"]
+    for key in sorted(keys, key=lambda k: (k[2] != "producer", -sum(fetch[k]) / len(fetch[k]))):
+        sel_f, sel_w = fetch[key][1:], write[key][1:]
+        if not sel_f or not sel_w:
+            continue
+        fb = sum(sel_f) / len(sel_f) * 1024 * f_fetch / 1e6
+        wb = sum(sel_w) / len(sel_w) * 1024 * f_write / 1e6
+        dd = sorted(durs.get(key, [])[1:])
+        med = dd[len(dd) // 2] if dd else 0.0
+        gbs = (fb + wb) * 1e6 / (med * 1e-6) / 1e9 if med > 0 else 0.0
+        lines.append(f"{key[2]:<9} {fb:>9.2f} {wb:>9.2f} {fb + wb:>9.2f} {med:>10.2f} {gbs:>8.0f}  "
+                     f"{key[1]:<9} {key[0][:90]}")
+    if bench_json and os.path.exists(bench_json):
+        txt = [l for l in open(bench_json).read().splitlines() if l.startswith("{")]
+        if txt:
+            b = json.loads(txt[-1])
+            lines += ["", "## algorithmic bytes per launch (bench.py decode_work), MB"]
+            for role in ("producer", "consumer"):
+                ents = b.get("kernels", {}).get(role, [])
+                lines.append(f"  {role}: " + ", ".join(f"{e['kernel']} {e['achieved'] * e['ms']:.2f}"
+                                                       for e in ents if e.get("bound") == "hbm"))
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # --- CPU baseline: the fp64 oracle on a bounded sample ---------------------------------------
 
 def cpu_baseline(budget_s=12.0, max_seqs=3):
@@ -658,6 +825,8 @@ def main():
     ap.add_argument("--pmc-fetch", help="with --summarize-rocprof: rocprofv3 --pmc FETCH_SIZE output dir")
     ap.add_argument("--pmc-write", help="with --summarize-rocprof: rocprofv3 --pmc WRITE_SIZE output dir")
     ap.add_argument("--profile-cmd", help="with --summarize-rocprof: the profiled command, for the header")
+    ap.add_argument("--attention-only", action="store_true",
+                    help="time only swa_meta_attn at the 8K SWA shape (K/V handed in), through the kernel entry")
     ap.add_argument("--griffin-only", action="store_true",
                     help="time only the Griffin block (8K prefill and B=128 decode); prints its JSON record")
     ap.add_argument("--summarize-griffin", metavar="TRACE_DIR",
@@ -666,7 +835,27 @@ def main():
                     help="time only the 128-sequence decode pair; prints its JSON record")
     ap.add_argument("--summarize-decode", metavar="TRACE_DIR",
                     help="host only: write profiles/kernels_decode_b128.txt from a kernel trace and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
+                    help="host only: write profiles/counters_swa_meta_attn_8k.txt from --pmc passes and exit "
+                         "(--trace-dir: a kernel trace for the durations)")
+    ap.add_argument("--summarize-decode-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="host only: write profiles/traffic_decode_b128.txt from FETCH_SIZE and WRITE_SIZE passes "
+                         "of --decode-only --copy-probe and exit (--trace-dir: a kernel trace for durations)")
+    ap.add_argument("--trace-dir", help="with --summarize-counters / --summarize-decode-traffic")
     args = ap.parse_args()
+    summary_cmd = "python3 " + shlex.join(os.path.relpath(a) if os.path.exists(a) else a for a in sys.argv)
+    if args.summarize_counters:
+        cmd = {"title": "swa_meta_attn alone (serial schedule) in the 1.5B-shaped SWA 8K prefill, B=16 x 8192",
+               "trace": (args.profile_cmd or "(not given)").split(" ;; "), "summary": summary_cmd}
+        summarize_counters(args.summarize_counters, args.trace_dir, cmd,
+                           os.path.join(ROOT, "profiles", "counters_swa_meta_attn_8k.txt"))
+        return
+    if args.summarize_decode_traffic:
+        cmd = {"title": "decode of 128 sequences at position 8192, KV-sharing pair of 1.5B-shaped SWA layers",
+               "trace": (args.profile_cmd or "(not given)").split(" ;; "), "summary": summary_cmd}
+        summarize_decode_traffic(args.summarize_decode_traffic[0], args.summarize_decode_traffic[1], args.trace_dir,
+                                 args.bench_json, cmd, os.path.join(ROOT, "profiles", "traffic_decode_b128.txt"))
+        return
     if args.summarize_decode:
         cmd = {"title": "KV-sharing producer/consumer pair of 1.5B-shaped SWA layers, decode of 128 sequences "
                         "at position 8192 (1024-slot ring + 128 meta keys), bf16",
@@ -707,6 +896,9 @@ def main():
         return
     if args.decode_only:
         print(json.dumps(bench_decode(4, args.steps, args.warmup)), flush=True)
+        return
+    if args.attention_only:
+        print(json.dumps(bench_attention_alone(args.steps, args.warmup)), flush=True)
         return
     main_run = bench_prefill(2, args.steps, args.warmup)
     log(f"[bench] 8K SWA prefill: {main_run['tokens_per_s']:.0f} tok/s, {main_run['ms_per_step']:.3f} ms/step")
