@@ -791,7 +791,7 @@ def summarize_decode_traffic(fetch_dir, write_dir, trace_dir, bench_json, comman
 
 # --- CPU baseline: the fp64 oracle on a bounded sample ---------------------------------------
 
-def cpu_baseline(budget_s=12.0, max_seqs=3):
+def cpu_baseline(budget_s=15.0, max_seqs=6):
     from hymba_synth.generate import make_config_case
     from oracle import hymba_oracle as orc
     try:

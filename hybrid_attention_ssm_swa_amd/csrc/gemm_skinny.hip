@@ -28,11 +28,20 @@ namespace hymba {
 
 namespace {
 
+#ifndef HYMBA_RW_WAVES
+#define HYMBA_RW_WAVES 8
+#endif
+#ifndef HYMBA_RW_PHASE_K
+#define HYMBA_RW_PHASE_K 512
+#endif
+#ifndef HYMBA_RW_DEPTH
+#define HYMBA_RW_DEPTH 2
+#endif
 constexpr int kRwR = 32;                   // rows per workgroup
-constexpr int kRwWaves = 8;
+constexpr int kRwWaves = HYMBA_RW_WAVES;
 constexpr int kRwThreads = 64 * kRwWaves;
-constexpr int kRwPhaseK = 512;             // k per phase
-constexpr int kRwDepth = 2;                // phases in flight
+constexpr int kRwPhaseK = HYMBA_RW_PHASE_K;   // k per phase
+constexpr int kRwDepth = HYMBA_RW_DEPTH;      // phases in flight
 constexpr int kRwStr = kRwPhaseK + 8;      // LDS row stride in 16-bit words (conflict-free MFMA reads)
 constexpr int kRwSegs = kRwPhaseK / 8;     // 16-byte segments of a row's phase
 constexpr int kRwChunks = kRwPhaseK / 64 / kRwWaves;   // 64-k chunks per wave and phase
