@@ -2,6 +2,8 @@
 // and blocks 4-element aligned): bf16 inputs and weights to the fp16
 // activation type and fp32/fp16 results to the bf16 output; and the input
 // conversion fused with the fp32 B/C columns of the shared projection.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -146,40 +148,36 @@ __global__ __launch_bounds__(256) void convert_bc_kernel(ConvBcArgs a) {
 constexpr int kConvRowGroups = 2;
 
 // Few rows (a decode step, the meta prefix): the same products and conversion, with one workgroup
-// of kRowsWaves waves per 16 rows and the 32-column steps of K split over its waves.  Each wave
-// issues the loads of kRowsBatch steps before it uses any, and the waves' partial sums meet in LDS,
-// added in wave order.  With whole rows per wave a 128-row call would run on one CU, bound by the
-// rate at which a single CU can load (measured ~46 us for the 1.5B layer's 128 x 1600 inputs).
+// of kRowsWaves waves per 16 rows and 16-column block of B/C, and the 32-column steps of K split
+// over its waves.  Each wave issues the loads of kRowsBatch steps before it uses any, and the
+// waves' partial sums meet in LDS, added in wave order; the workgroups of column block 0 also
+// store x16.  With whole rows per wave a 128-row call would run on a single CU, bound by the
+// rate at which one CU can load (measured ~46 us for the 1.5B layer's 128 x 1600 inputs).
 constexpr int kRowsWaves = 8;
 constexpr int kRowsBatch = 8;
 constexpr int64_t kFewRows = 2048;   // up to this many rows take the split-K kernel
 
-template <int NCB>
 __global__ __launch_bounds__(64 * kRowsWaves) void convert_bc_rows_kernel(ConvBcArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i = lane & 15, kq = lane >> 4;
+  const int cb = blockIdx.y;   // 16-column block of B/C
+  const bool store_x = cb == 0;
   const int64_t row = (int64_t)blockIdx.x * 16 + i;
   const bool row_ok = row < a.rows;
   const bf16_t* xr = a.x + (row_ok ? row : a.rows - 1) * a.ldx + 8 * kq;
   half_t* xo = a.x16 + row * a.ldx16 + 8 * kq;
-  const half_t* wr[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) wr[cb] = a.wbc + (int64_t)(16 * cb + i) * a.ldw + 8 * kq;
+  const half_t* wr = a.wbc + (int64_t)(16 * cb + i) * a.ldw + 8 * kq;
   const int nsteps = (a.d + 31) / 32;
   const int s0 = wave * nsteps / kRowsWaves, s1 = (wave + 1) * nsteps / kRowsWaves;
-  f32x4_t acc[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4_t{};
+  f32x4_t acc = f32x4_t{};
   for (int sb = s0; sb < s1; sb += kRowsBatch) {
-    uint4 xv[kRowsBatch], wv[kRowsBatch][NCB];
+    uint4 xv[kRowsBatch], wv[kRowsBatch];
 #pragma unroll
     for (int j = 0; j < kRowsBatch; ++j) {
       const int k = (sb + j) * 32;   // xr, wr, xo already point at the lane's 8 columns
       const bool ok = sb + j < s1 && k + 8 * kq < a.d;   // d % 8 == 0: the 8 columns are all in or out
       xv[j] = ok ? *reinterpret_cast<const uint4*>(xr + k) : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-        wv[j][cb] = ok ? *reinterpret_cast<const uint4*>(wr[cb] + k) : make_uint4(0u, 0u, 0u, 0u);
+      wv[j] = ok ? *reinterpret_cast<const uint4*>(wr + k) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int j = 0; j < kRowsBatch; ++j) {
@@ -190,23 +188,19 @@ __global__ __launch_bounds__(64 * kRowsWaves) void convert_bc_rows_kernel(ConvBc
       hv.y = pack_f16x2(bf16lo(xv[j].y), bf16hi(xv[j].y));
       hv.z = pack_f16x2(bf16lo(xv[j].z), bf16hi(xv[j].z));
       hv.w = pack_f16x2(bf16lo(xv[j].w), bf16hi(xv[j].w));
-      if (ok && row_ok) *reinterpret_cast<uint4*>(xo + k) = hv;
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, hv),
-                                                         __builtin_bit_cast(f16x8_t, wv[j][cb]), acc[cb], 0, 0, 0);
+      if (store_x && ok && row_ok) *reinterpret_cast<uint4*>(xo + k) = hv;
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, hv),
+                                                   __builtin_bit_cast(f16x8_t, wv[j]), acc, 0, 0, 0);
     }
   }
-  __shared__ f32x4_t part[kRowsWaves][NCB][64];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) part[wave][cb][lane] = acc[cb];
+  __shared__ f32x4_t part[kRowsWaves][64];
+  part[wave][lane] = acc;
   __syncthreads();
-  if (wave < NCB) {   // wave cb adds block cb over the waves in order
-    const int cb = wave;
-    f32x4_t sum = part[0][cb][lane];
+  if (wave == 0) {   // the waves' sums in order
+    f32x4_t sum = part[0][lane];
 #pragma unroll
     for (int w = 1; w < kRowsWaves; ++w) {
-      const f32x4_t v = part[w][cb][lane];
+      const f32x4_t v = part[w][lane];
 #pragma unroll
       for (int r = 0; r < 4; ++r) sum[r] += v[r];
     }
@@ -218,15 +212,43 @@ __global__ __launch_bounds__(64 * kRowsWaves) void convert_bc_rows_kernel(ConvBc
   }
 }
 
+// Records in *flag whether any of the n fp16 values at p is inf or NaN (all exponent bits set):
+// a bf16 weight beyond fp16's range became inf in the layer's fp16 copy.  Lane 0 of a wave that
+// saw one stores 1 (every writer stores the same value).
+__global__ __launch_bounds__(256) void nonfinite16_kernel(const uint16_t* __restrict__ p, int64_t n,
+                                                          uint32_t* __restrict__ flag) {
+  const int64_t n8 = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  bool bad = false;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
+    const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bad |= ((w[j] & 0x7c00u) == 0x7c00u) | ((w[j] & 0x7c000000u) == 0x7c000000u);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    for (int64_t i = 8 * n8; i < n; ++i) bad |= (p[i] & 0x7c00u) == 0x7c00u;
+  if (__builtin_amdgcn_ballot_w64(bad) != 0 && (threadIdx.x & 63) == 0) *flag = 1u;
+}
+
 }  // namespace
+
+hipError_t launch_nonfinite16_check(const half_t* p, int64_t n, uint32_t* flag, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (reinterpret_cast<uintptr_t>(p) % 16) return hipErrorInvalidValue;
+  const unsigned blocks = static_cast<unsigned>(std::min<int64_t>(1024, std::max<int64_t>(1, ceil_div(n / 8, 256))));
+  hipLaunchKernelGGL(nonfinite16_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const uint16_t*>(p), n,
+                     flag);
+  return hipGetLastError();
+}
 
 hipError_t launch_convert_bc(const ConvBcArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
   if (a.d % 8 || (a.nbc != 16 && a.nbc != 32) || a.ldx % 8 || a.ldx16 % 8 || a.ldw % 8) return hipErrorInvalidValue;
   if (a.rows <= kFewRows) {
-    const dim3 grid(static_cast<unsigned>(ceil_div(a.rows, 16))), block(64 * kRowsWaves);
-    if (a.nbc == 32) hipLaunchKernelGGL((convert_bc_rows_kernel<2>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((convert_bc_rows_kernel<1>), grid, block, 0, s, a);
+    const dim3 grid(static_cast<unsigned>(ceil_div(a.rows, 16)), static_cast<unsigned>(a.nbc / 16)),
+        block(64 * kRowsWaves);
+    hipLaunchKernelGGL(convert_bc_rows_kernel, grid, block, 0, s, a);
     return hipGetLastError();
   }
   const dim3 grid(static_cast<unsigned>(ceil_div(a.rows, 4 * 16 * kConvRowGroups))), block(256);

@@ -42,7 +42,8 @@ struct hymba_layer {
   float* h_meta = nullptr;     // [E, N]
   char* y_meta = nullptr;      // [M, d] storage type
   float* A2 = nullptr;         // [E, N] A * log2(e)
-  uint32_t* flags = nullptr;   // [2] device-side checks: non-finite branch statistic, bad decode position
+  uint32_t* flags = nullptr;   // [3] device-side checks: non-finite branch statistic, bad decode position,
+                               // a weight beyond fp16's range (sticky)
   half_t* w_in16 = nullptr;    // bf16 layers: fp16 copies of the weights
   half_t* w_o16 = nullptr;
   bool prepared = false;
@@ -183,7 +184,7 @@ PersistLayout persist_layout(const hymba_layer_cfg& c) {
   p.h_meta = off; off += align_up((size_t)c.d_inner * c.d_state * 4);
   p.y_meta = off; off += align_up((size_t)c.n_meta * c.d_model * ss);
   p.A2 = off; off += align_up((size_t)c.d_inner * c.d_state * 4);
-  p.flags = off; off += align_up(2 * sizeof(uint32_t));
+  p.flags = off; off += align_up(3 * sizeof(uint32_t));
   if (is_bf16(c)) {
     const size_t hq = (size_t)c.n_heads * c.head_dim;
     p.w_in16 = off; off += align_up((size_t)n_in_of(c) * c.d_model * 2);
@@ -459,7 +460,7 @@ int32_t prepare_impl(hymba_layer& L, const hymba_kv* kv, char* ws, const WsLayou
   const hymba_layer_cfg& c = L.cfg;
   const int M = c.n_meta;
   if (!L.weights_ready) {
-    HIP_TRY(launch_fill(reinterpret_cast<float*>(L.flags), 2, 0.f, s), "check flags clear");
+    HIP_TRY(launch_fill(reinterpret_cast<float*>(L.flags), 3, 0.f, s), "check flags clear");
     HIP_TRY(launch_scale_copy(L.w.A, L.A2, (int64_t)c.d_inner * c.d_state, kLog2e, s), "A scaling");
     if (is_bf16(c)) {
       const int64_t hq = (int64_t)c.n_heads * c.head_dim;
@@ -467,6 +468,9 @@ int32_t prepare_impl(hymba_layer& L, const hymba_kv* kv, char* ws, const WsLayou
                              c.d_model, s), "weight conversion");
       HIP_TRY(launch_convert(static_cast<const bf16_t*>(L.w.w_o), hq, L.w_o16, hq, c.d_inner, hq, s),
               "weight conversion");
+      // a bf16 weight beyond fp16's range is inf in the copies: recorded for hymba_layer_check
+      HIP_TRY(launch_nonfinite16_check(L.w_in16, L.n_in * c.d_model, L.flags + 2, s), "weight range check");
+      HIP_TRY(launch_nonfinite16_check(L.w_o16, (int64_t)c.d_inner * hq, L.flags + 2, s), "weight range check");
     }
     L.weights_ready = true;
   }
@@ -864,11 +868,15 @@ int32_t hymba_layer_check(hymba_layer* L, void* stream) {
   if (!L) return fail(HYMBA_ERR_INVALID_ARG, "layer is NULL");
   if (!L->weights_ready) return HYMBA_OK;   // nothing has run on the device yet
   HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "stream synchronize");
-  uint32_t f[2] = {0u, 0u};
+  uint32_t f[3] = {0u, 0u, 0u};
   HIP_TRY(hipMemcpy(f, L->flags, sizeof(f), hipMemcpyDeviceToHost), "check flags read");
-  if (f[0] == 0u && f[1] == 0u) return HYMBA_OK;
-  const uint32_t zero[2] = {0u, 0u};
+  if (f[0] == 0u && f[1] == 0u && f[2] == 0u) return HYMBA_OK;
+  const uint32_t zero[2] = {0u, 0u};   // the weight record stays: the weights do not change
   HIP_TRY(hipMemcpy(L->flags, zero, sizeof(zero), hipMemcpyHostToDevice), "check flags clear");
+  if (f[2])
+    return fail(HYMBA_ERR_RANGE, "a weight of W_in or W_O is beyond fp16's range (|w| > 65504): bf16 layers compute "
+                                 "with fp16 copies of these weights%s",
+                f[0] ? "; a branch output was not finite" : "");
   if (f[0])
     return fail(HYMBA_ERR_RANGE, "a row's attention or SSM branch output was not finite: an activation left the "
                                  "range of the activation type (fp16 for bf16 layers: |value| > 65504) or the input "

@@ -221,6 +221,8 @@ struct ConvBcArgs {
   int64_t rows; int d; int nbc;
 };
 hipError_t launch_convert_bc(const ConvBcArgs& a, hipStream_t s);
+// *flag = 1 if any of the n fp16 values at p (16-byte aligned) is inf or NaN; else untouched.
+hipError_t launch_nonfinite16_check(const half_t* p, int64_t n, uint32_t* flag, hipStream_t s);
 
 // ---- misc ----------------------------------------------------------------------
 hipError_t launch_scale_copy(const float* src, float* dst, int64_t n, float scale, hipStream_t s);

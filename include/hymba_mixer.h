@@ -241,9 +241,12 @@ const char* hymba_status_string(int32_t status);
  * subnormals, an absolute error of at most 2^-25 per element) or the input held
  * inf/NaN, or (b) a decode position pos[b] was negative (such a sequence
  * writes no cache slot and attends to the meta keys only).  Outputs are
- * written as computed either way.  hymba_layer_check synchronises `stream`,
- * reads and clears the record, and returns HYMBA_ERR_RANGE (with a message)
- * if anything was recorded since the last check, else HYMBA_OK.  A global
+ * written as computed either way.  Preparing a bf16 layer also records (c)
+ * whether a weight of W_in or W_O lies beyond fp16's range (it is inf in the
+ * layer's fp16 copy); W_out is used in bf16 and not checked.
+ * hymba_layer_check synchronises `stream`, reads the record, clears (a) and
+ * (b) (the weight record stays), and returns HYMBA_ERR_RANGE (with a message)
+ * if anything is recorded, else HYMBA_OK.  A global
  * layer's decode at pos >= cache_len is not an error: it attends to the last
  * cache_len real tokens (exact global attention needs cache_len >= pos + 1). */
 int32_t hymba_layer_check(hymba_layer* layer, void* stream);

@@ -8,6 +8,8 @@
 - An input beyond fp16's range (the activation type of bf16 layers): the layer records it and
   hymba_layer_check reports HYMBA_ERR_RANGE instead of passing inf on silently.
 - A negative decode position: recorded and reported the same way.
+- A bf16 weight beyond fp16's range: recorded when the layer is prepared and reported by every
+  check.
 - The serial prefill schedule (every kernel on the call's stream) gives the bitwise result of
   the overlapped one.
 """
@@ -116,6 +118,26 @@ def test_input_beyond_fp16_range_is_reported():
     y = host(layer.prefill(x))
     layer.check()
     assert np.all(np.isfinite(y))
+
+
+def test_weight_beyond_fp16_range_is_reported():
+    """A bf16 weight of W_in above 65504 is inf in the layer's fp16 copy: preparing the layer
+    records it, and every check reports it (the weights do not change)."""
+    announce("bf16 weight beyond fp16's range: hymba_layer_check reports it at every check")
+    case = make_prefill_case(SMALL, 1, 20, seed=103)
+    case.params.w_in = case.params.w_in.copy()
+    case.params.w_in[5, 17] = 1.0e5
+    layer = MixerLayer(SMALL, case.params)
+    layer.prepare()
+    for _ in range(2):
+        with pytest.raises(H.HymbaError) as e:
+            layer.check()
+        assert e.value.status == H.HYMBA_ERR_RANGE and "weight" in str(e.value)
+    layer.close()
+    ok = MixerLayer(SMALL, make_prefill_case(SMALL, 1, 20, seed=103).params)
+    ok.prepare()
+    ok.check()
+    ok.close()
 
 
 def test_negative_decode_position_is_reported():
