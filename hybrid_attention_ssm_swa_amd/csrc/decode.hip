@@ -259,23 +259,23 @@ __device__ __forceinline__ float sum_xor16(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One 64-key tile (K rows ks [64][kKStr], V rows vs [64][kVStr16]) for 16 query columns: S^T =
-// K Q^T in four 16-key blocks, online softmax (lazy rescale as in the prefill step), O^T +=
-// V^T P^T in two 32-key steps.  Keys from nvalid on are masked.  The lane's scores s[kb][r] are
-// keys 16 kb + 4 q + r (q = lane/16); as the B operand of PV step m they fill k-slots 8 q + j =
-// keys 32 m + 4 q + j (j < 4) and 32 m + 16 + 4 q + j - 4 (j >= 4), and the V^T reads follow the
-// same order, so P needs no cross-lane movement.
-__device__ __forceinline__ void attend_tile16(WaveState16& st, const attn::U4 (&qf)[2], const uint16_t* ks,
-                                              const uint16_t* vs, float sc, int lane, int nvalid) {
+// One 64-key tile for 16 query columns, in two parts.  tile_scores16: S^T = K Q^T in four 16-key
+// blocks, with the tile's K rows in registers in the A layout (kr[kb][h]: key 16 kb + lane % 16,
+// dims 32 h + 8 (lane / 16) + 0..7), keys from nvalid on masked.  attend_tile16: online softmax
+// (lazy rescale as in the prefill step) and O^T += V^T P^T in two 32-key steps, V rows in LDS
+// (vs [64][kVStr16]).  The lane's scores s[kb][r] are keys 16 kb + 4 q + r (q = lane/16); as the
+// B operand of PV step m they fill k-slots 8 q + j = keys 32 m + 4 q + j (j < 4) and
+// 32 m + 16 + 4 q + j - 4 (j >= 4), and the V^T reads follow the same order, so P needs no
+// cross-lane movement.
+__device__ __forceinline__ void tile_scores16(f32x4_t (&s)[4], const attn::U4 (&qf)[2], const attn::U4 (&kr)[4][2],
+                                              int lane, int nvalid) {
   using namespace attn;
-  const int col = lane & 15, q = lane >> 4;
-  f32x4_t s[4];
+  const int q = lane >> 4;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     s[kb] = f32x4_t{};
-    const uint16_t* krow = ks + (16 * kb + col) * kKStr + 8 * q;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) s[kb] = mfma16(*reinterpret_cast<const U4*>(krow + 32 * h), qf[h], s[kb]);
+    for (int h = 0; h < 2; ++h) s[kb] = mfma16(kr[kb][h], qf[h], s[kb]);
   }
   if (nvalid < kKT) {
 #pragma unroll
@@ -284,6 +284,12 @@ __device__ __forceinline__ void attend_tile16(WaveState16& st, const attn::U4 (&
       for (int r = 0; r < 4; ++r)
         if (16 * kb + 4 * q + r >= nvalid) s[kb][r] = -INFINITY;
   }
+}
+
+__device__ __forceinline__ void attend_tile16(WaveState16& st, f32x4_t (&s)[4], const uint16_t* vs, float sc,
+                                              int lane) {
+  using namespace attn;
+  const int q = lane >> 4;
   float mt = max3f(s[0][0], s[0][1], s[0][2]);
   mt = max3f(mt, s[0][3], s[1][0]);
   mt = max3f(mt, s[1][1], s[1][2]);
@@ -340,15 +346,19 @@ __device__ __forceinline__ void attend_tile16(WaveState16& st, const attn::U4 (&
 // MFMA decode attention (fp16 K/V, head dim 64): one wave per (split, KV head, sequence).  The
 // G query heads of the KV group are the query columns of a 16-column tile step
 // (v_mfma_f32_16x16x32_f16, S^T = K Q^T; columns G..15 carry zero queries and are dropped).  The
-// wave walks its split's keys in 64-key tiles: the next tile's K rows and V blocks are loaded
-// into registers while the current one, staged in LDS (K rows straight, V transposed), goes
-// through the online softmax.  The split's (acc, max, sum) per head go to `part` as in the VALU
-// kernel, and the same combine kernel merges the splits.
+// wave walks its split's keys in 64-key tiles.  K goes straight from memory into registers in the
+// score MFMA's A layout (each lane loads 16 bytes of 8 rows; a load instruction covers 64
+// bytes of 16 consecutive rows); V goes through LDS, whose transposed reads give the P.V
+// product's A operand.  The next tile's loads are issued once the current tile's scores have
+// consumed its K registers, and land during its softmax and P.V.  With only V in LDS (10 KB per
+// wave) and one register set per operand, every wave of the ring decode can be resident at once.
+// The split's (acc, max, sum) per head go to `part` as in the VALU kernel, and the same combine
+// kernel merges the splits.
 template <int G>
-__global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecAttnArgs<half_t> a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void decode_attn_mfma_kernel(
+    DecAttnArgs<half_t> a) {
   using namespace attn;
   static_assert(G >= 1 && G <= 16, "query heads of a KV group must fit 16 columns");
-  __shared__ __align__(16) uint16_t ks[kKT * kKStr];
   __shared__ __align__(16) uint16_t vs[kKT * kVStr16];
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
@@ -388,10 +398,10 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecAttnArgs<half_t
     if (slot >= C) slot -= C;
     return (ring + slot) * kHd;
   };
-  // a lane's 16 loads of the tile starting at key t0 with nvalid keys: items lane and lane + 64
-  // of the K chunks and of the V chunks (each 4 rows 16 apart);
-  // rows past nvalid read the last valid row (their scores are masked)
-  auto fetch = [&](int t0, int nvalid, U4 (&kr)[2][4], U4 (&vr)[2][4]) {
+  // the tile starting at key t0 with nvalid keys: K rows 16 kb + c16 at dims 32 h + 8 q (the A
+  // layout), and V chunks lane + 64 it (rows (item >> 3) + 16 j, dims 8 (item & 7)); rows past
+  // nvalid read the last valid row (their scores are masked)
+  auto fetch = [&](int t0, int nvalid, U4 (&kr)[4][2], U4 (&vr)[2][4]) {
     // A full tile wholly in the meta rows, or wholly in one unwrapped stretch of the ring, is a
     // strided block: one base for the tile and 32-bit row offsets.  Other tiles (the one across
     // the meta/window boundary, the one across the ring's wrap, a partial last tile) take the
@@ -405,59 +415,49 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecAttnArgs<half_t
       const half_t* vb = meta ? a.v_meta + (int64_t)t0 * a.ld_meta + g * kHd : a.v_cache + (ring + s0) * kHd;
       const int stride = meta ? static_cast<int>(a.ld_meta) : kHd;
 #pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          kr[kk][h] = *reinterpret_cast<const U4*>(kb + (16 * kk + c16) * stride + 32 * h + 8 * q);
+#pragma unroll
       for (int it = 0; it < 2; ++it) {
         const int item = lane + 64 * it;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = (item & 7) * 8;
-          kr[it][j] = *reinterpret_cast<const U4*>(kb + ((item >> 3) + 16 * j) * stride + col);
-          vr[it][j] = *reinterpret_cast<const U4*>(vb + ((item >> 3) + 16 * j) * stride + col);
-        }
+        for (int j = 0; j < 4; ++j)
+          vr[it][j] = *reinterpret_cast<const U4*>(vb + ((item >> 3) + 16 * j) * stride + (item & 7) * 8);
       }
       return;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int64_t ko = row_off(t0 + min(16 * kk + c16, nvalid - 1));
+      const half_t* krow = (ko < 0 ? a.k_meta + (-1 - ko) : a.k_cache + ko) + 8 * q;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) kr[kk][h] = *reinterpret_cast<const U4*>(krow + 32 * h);
     }
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int item = lane + 64 * it;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int krow = (item >> 3) + 16 * j, kcol = (item & 7) * 8;
-        const int64_t ko = row_off(t0 + min(krow, nvalid - 1));
-        kr[it][j] = *reinterpret_cast<const U4*>((ko < 0 ? a.k_meta + (-1 - ko) : a.k_cache + ko) + kcol);
         const int vrow = (item >> 3) + 16 * j, vcol = (item & 7) * 8;
         const int64_t vo = row_off(t0 + min(vrow, nvalid - 1));
         vr[it][j] = *reinterpret_cast<const U4*>((vo < 0 ? a.v_meta + (-1 - vo) : a.v_cache + vo) + vcol);
       }
     }
   };
-  auto stage = [&](const U4 (&kr)[2][4], const U4 (&vr)[2][4]) {
+  U4 kr[4][2], vr[2][4];
+  if (k0 < k1) fetch(k0, min(kKT, k1 - k0), kr, vr);
+  for (int t0 = k0; t0 < k1; t0 += kKT) {
+    const int nvalid = min(kKT, k1 - t0);
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      chunk_store(kr[it], ks, kKStr, lane + 64 * it);     // K chunks
-      chunk_store(vr[it], vs, kVStr16, lane + 64 * it);   // V chunks
-    }
+    for (int it = 0; it < 2; ++it) chunk_store(vr[it], vs, kVStr16, lane + 64 * it);   // V chunks
     __syncthreads();
-  };
-  U4 kr[2][4], vr[2][4];
-  if (k1 - k0 > kKT && k1 - k0 <= 2 * kKT) {
-    // two tiles (the usual split length): both in flight from the start, straight-line code
-    U4 kr2[2][4], vr2[2][4];
-    fetch(k0, kKT, kr, vr);
-    fetch(k0 + kKT, k1 - k0 - kKT, kr2, vr2);
-    stage(kr, vr);
-    attend_tile16(st, qf, ks, vs, a.scale_log2, lane, kKT);
+    f32x4_t s[4];
+    tile_scores16(s, qf, kr, lane, nvalid);
+    if (t0 + kKT < k1) fetch(t0 + kKT, min(kKT, k1 - t0 - kKT), kr, vr);   // next tile in flight
+    attend_tile16(st, s, vs, a.scale_log2, lane);
     __syncthreads();
-    stage(kr2, vr2);
-    attend_tile16(st, qf, ks, vs, a.scale_log2, lane, k1 - k0 - kKT);
-  } else {
-    if (k0 < k1) fetch(k0, min(kKT, k1 - k0), kr, vr);
-    for (int t0 = k0; t0 < k1; t0 += kKT) {
-      const int nvalid = min(kKT, k1 - t0);
-      stage(kr, vr);
-      if (t0 + kKT < k1) fetch(t0 + kKT, min(kKT, k1 - t0 - kKT), kr, vr);   // next tile in flight
-      attend_tile16(st, qf, ks, vs, a.scale_log2, lane, nvalid);
-      __syncthreads();
-    }
   }
 
   // this split's partials of heads g G + c16 (c16 < G): acc over the lane's 16 dims, max (log2
