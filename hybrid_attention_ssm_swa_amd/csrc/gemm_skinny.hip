@@ -311,10 +311,13 @@ hipError_t rows_dispatch(const SkinnyArgs<WT, XT, OT>& a, hipStream_t s) {
 
 // Feature tile: 64 when that gives at least 128 workgroups, else 32 (twice the workgroups, X
 // read twice as often).
+#ifndef HYMBA_RW_F64_MIN_GROUPS
+#define HYMBA_RW_F64_MIN_GROUPS 128
+#endif
 SkinnyPlan skinny_plan(int M, int N, int K) {
   (void)K;
   SkinnyPlan p;
-  p.F = ceil_div(N, 64) * ceil_div(M, kRwR) >= 128 ? 64 : 32;
+  p.F = ceil_div(N, 64) * ceil_div(M, kRwR) >= HYMBA_RW_F64_MIN_GROUPS ? 64 : 32;
   return p;
 }
 
