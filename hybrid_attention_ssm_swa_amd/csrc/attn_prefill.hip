@@ -210,10 +210,10 @@ struct AttnStages {
   uint16_t vw[kStages][kHT * kVStr];   // V rows [key][dim]
 };
 
-// Work items are numbered (sequence, KV head, query group, head of the group) for SWA -- so
-// consecutive items share one window of K/V -- and with the longest query groups first for global
-// layers; consecutive items go to the same XCD (the dispatcher deals workgroups round-robin over
-// the 8 XCDs), so an XCD's L2 holds the K/V its workgroups share.
+// Work items are numbered (sequence, KV head, query group, head of the group) -- so consecutive
+// items share one window of K/V, or for a global layer one causal prefix, taken longest first --
+// and consecutive items go to the same XCD (the dispatcher deals workgroups round-robin over the
+// 8 XCDs), so an XCD's L2 holds the K/V its workgroups share.
 //
 // Step i of a wave: scores of stage i, the previous stage's softmax, the P.V product of stage i - 2:
 //   S(i) = K(i) Q^T (4 MFMAs) ; O += V(i - 2)^T P(i - 2) (4 MFMAs) ; P(i - 1) = softmax(S(i - 1))
@@ -239,13 +239,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   const int hh = work % group;
   work /= group;
   int b, g, qg;
-  if (win > 0) {
-    qg = work % nqg; work /= nqg;
-    g = work % a.n_kv_heads; b = work / a.n_kv_heads;
-  } else {
-    g = work % a.n_kv_heads; work /= a.n_kv_heads;
-    b = work % a.B; qg = nqg - 1 - work / a.B;
-  }
+  qg = work % nqg; work /= nqg;
+  g = work % a.n_kv_heads; b = work / a.n_kv_heads;
+  if (win <= 0) qg = nqg - 1 - qg;   // global: the longest query groups of a (sequence, KV head) first
   const int h = g * group + hh;
   const int q0 = qg * kQG;
   const int qa = q0 + wave * kQB;               // this wave's first query
