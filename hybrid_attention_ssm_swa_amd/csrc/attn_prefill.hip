@@ -51,6 +51,7 @@ typedef f16x8_t QV;
 struct Col {
   f32x16_t acc[2];   // O^T dims [0, 32) and [32, 64); column = query
   float m;           // reference, raw score units (-inf before the query's first visible key)
+  float off;         // the exponent's offset -m sc (0 while m = -inf), kept with m
   float l;           // this lane's part of the row sum, relative to m
 };
 constexpr float kGrowSum = 4096.f;
@@ -65,9 +66,8 @@ __device__ __forceinline__ float block_max(const f32x16_t& s) {
 }
 
 // P^T of a stage as fp16 pairs (the B fragments of two P.V steps) and the lane's sum of exactly
-// those rounded values: p = 2^(sc s - sc m) (0 for a masked score).
-__device__ __forceinline__ float probs(const f32x16_t& s, float sc, float m, U4 (&pw)[2]) {
-  const float off = m == -INFINITY ? 0.f : -m * sc;
+// those rounded values: p = 2^(sc s + off), off = -sc m (0 for m = -inf; 0 for a masked score).
+__device__ __forceinline__ float probs(const f32x16_t& s, float sc, float off, U4 (&pw)[2]) {
   float psum = 0.f;
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
@@ -164,32 +164,40 @@ __device__ __forceinline__ void settle(Col& c, U4 (&p)[2], float psum, const QV 
 #pragma unroll
       for (int r = 0; r < 16; ++r) c.acc[db][r] *= alpha;
     c.m = mnew;
-    psum = probs(s, sc, mnew, p);
+    c.off = mnew == -INFINITY ? 0.f : -mnew * sc;
+    psum = probs(s, sc, c.off, p);
   }
   c.l += psum;
 }
 
 // The calling thread's share of a stage (K rows at kbase, V rows at vbase, row stride ld elements,
 // nvalid >= 1 valid rows): threads [0, 128) load K, [128, 256) V (a wave-uniform choice); chunk
-// it + 128 j (j < 2) is row (it >> 3) + 16 j, dims 8 (it & 7) + 0..7.  The lane's row offset is
-// recomputed per stage from an opaque copy of its row index, so that the compiler does not keep
-// hoisted offsets per row and per key source live across the loop.  Rows past nvalid read the last
-// valid row and are zero-filled.
+// it + 128 j (j < 2) is row (it >> 3) + 16 j, dims 8 (it & 7) + 0..7, at byte offset voff + 32 j ld
+// for a full stage.  Rows past nvalid read the last valid row and are zero-filled.
 struct StageRegs {
   U4 r[2];
 };
+// A buffer resource for the 32 rows (row stride ld elements) from p: base and size are
+// wave-uniform, so they live in scalar registers and a full stage's loads need no vector
+// address arithmetic (the per-lane byte offset voff is computed once per kernel).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stage_rsrc(const void* p, int ld) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32)));
+  const uint64_t u = static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), 0, kHT * ld * 2, 0x00020000);
+}
 __device__ __forceinline__ void fetch_stage(StageRegs& t, const half_t* kbase, const half_t* vbase, int ld,
-                                            int nvalid, bool is_k, int it) {
+                                            uint32_t voff, int nvalid, bool is_k, int it) {
   const char* base = reinterpret_cast<const char*>(is_k ? kbase : vbase);
-  int row0 = it >> 3;
-  asm volatile("" : "+v"(row0));
-  const int col = (it & 7) * 8;
   if (nvalid >= kHT) {
-    const uint32_t voff = static_cast<uint32_t>((row0 * ld + col) * 2);
-    const int64_t step = (int64_t)16 * ld * 2;
+    const auto rs = stage_rsrc(base, ld);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) t.r[j] = *reinterpret_cast<const U4*>(base + j * step + voff);
+    for (int j = 0; j < 2; ++j)
+      t.r[j] = __builtin_bit_cast(U4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, j * 16 * ld * 2, 0));
   } else {
+    int row0 = it >> 3;
+    const int col = (it & 7) * 8;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int row = row0 + 16 * j;
@@ -222,7 +230,8 @@ struct AttnStages {
 // stored (into buffer i mod 4) after the barrier of stage i - 1, which every wave passes only once
 // it has finished step i - 2; a wave still in step i - 1 reads stages i - 3 .. i - 1, so with four
 // buffers and one barrier per stage no store overwrites what another wave still reads.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void swa_meta_attn_kernel(
+// Register budget: 4 waves per SIMD, at most 128 VGPRs (8 bytes of spills, outside the stage loop).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void swa_meta_attn_kernel(
     AttnArgs<half_t> a) {
   __shared__ AttnStages sm;
   const int tid = threadIdx.x;
@@ -258,13 +267,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   const int ld_meta = static_cast<int>(a.ld_meta), ld_kv = static_cast<int>(a.ld_kv);
   const bool is_k = wave < 2;
   const int it = tid & 127;
+  const uint32_t voff_meta = static_cast<uint32_t>(((it >> 3) * ld_meta + (it & 7) * 8) * 2);
+  const uint32_t voff_kv = static_cast<uint32_t>(((it >> 3) * ld_kv + (it & 7) * 8) * 2);
   auto fetch = [&](StageRegs& r, int i) {
     if (i < n_ms) {
       const int64_t off = (int64_t)i * kHT * a.ld_meta + g * kHd;
-      fetch_stage(r, a.k_meta + off, a.v_meta + off, ld_meta, a.n_meta - i * kHT, is_k, it);
+      fetch_stage(r, a.k_meta + off, a.v_meta + off, ld_meta, voff_meta, a.n_meta - i * kHT, is_k, it);
     } else {
       const int t0 = lo + (i - n_ms) * kHT;
-      fetch_stage(r, kseq + (int64_t)t0 * a.ld_kv, vseq + (int64_t)t0 * a.ld_kv, ld_kv, hi - t0, is_k, it);
+      fetch_stage(r, kseq + (int64_t)t0 * a.ld_kv, vseq + (int64_t)t0 * a.ld_kv, ld_kv, voff_kv, hi - t0, is_k,
+                  it);
     }
   };
   auto stage_of = [&](int i) {   // branch-free (scalar selects)
@@ -279,6 +291,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     st.mask = meta ? (i * kHT + kHT > a.n_meta) : !full;
     return st;
   };
+  // whether some key of stage i is hidden from some query of the wave, as a wave-uniform integer in
+  // a scalar register (a bool select here cost vector instructions every stage)
+  auto masked = [&](int i) {
+    const int meta = i < n_ms;
+    const int t0 = lo + (i - n_ms) * kHT;
+    const int full = (t0 + kHT - 1 <= qa) & ((win <= 0) | (t0 > qlast - win)) & (t0 + kHT <= hi);
+    const int part_meta = i * kHT + kHT > a.n_meta;
+    return __builtin_amdgcn_readfirstlane((meta & part_meta) | ((meta ^ 1) & (full ^ 1)));
+  };
   // Q^T fragments: k-step s holds dims 16 s + 8 (lane/32) .. +7 of query tq
   QV qf[4];
   {
@@ -289,6 +310,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   Col c;
   c.acc[0] = c.acc[1] = f32x16_t{};
   c.m = -INFINITY;
+  c.off = 0.f;
   c.l = 0.f;
 
   // pipeline registers: scores of stage i - 1, probabilities of stage i - 2
@@ -306,7 +328,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     if (do_pv) pv(c, p2, sm.vw[(i + 2) % kStages], lane);     // stage i - 2
     if (do_soft) {
       U4 p1[2];
-      const float ps = probs(s1, sc, c.m, p1);
+      const float ps = probs(s1, sc, c.off, p1);
       if (do_qk && do_pv) {   // the steady step: one MFMA, then a share of the softmax VALU, eight times
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -320,7 +342,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
       p2[1] = p1[1];
     }
     if (do_qk) {
-      if (st_cur.mask) mask_stage(s0, st_cur, tq, win, lane >> 5);
+      if (masked(i)) mask_stage(s0, st_cur, tq, win, lane >> 5);
       s1 = s0;
     }
   };
