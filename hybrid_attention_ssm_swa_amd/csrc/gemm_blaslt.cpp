@@ -185,9 +185,12 @@ int gemm_16(GemmType in_type, GemmType out_type, const void* X, int64_t ldx, con
       if (cap == hipStreamCaptureStatusNone && env_flag("HYMBA_GEMM_TUNE", true)) {
         if (2.0 * rows * out * in > 5e10) add_same_tile_algos(handle, p, in_type, out_type, res, n, ws_bytes, cand);
         const bool log = env_flag("HYMBA_GEMM_TUNE_LOG", false);
+        // a few-microsecond GEMM (a decode step's projection) is timed over more runs: two runs
+        // of ~20 us each left the choice to timer noise
+        const int reps = 2.0 * rows * out * in < 1e11 ? 12 : 2;
         float best_ms = -1.f;
         for (size_t i = 0; cand.size() > 1 && i < cand.size(); ++i) {
-          const float ms = time_candidate(handle, p, cand[i], W, X, Y, ws, ws_bytes, s, 2);
+          const float ms = time_candidate(handle, p, cand[i], W, X, Y, ws, ws_bytes, s, reps);
           if (log)
             std::fprintf(stderr, "[hymba gemm] rows %lld out %lld in %lld candidate %zu: %.4f ms\n",
                          (long long)rows, (long long)out, (long long)in, i, ms);
