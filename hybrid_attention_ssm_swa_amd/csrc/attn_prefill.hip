@@ -291,15 +291,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     st.mask = meta ? (i * kHT + kHT > a.n_meta) : !full;
     return st;
   };
-  // whether some key of stage i is hidden from some query of the wave, as a wave-uniform integer in
-  // a scalar register (a bool select here cost vector instructions every stage)
-  auto masked = [&](int i) {
-    const int meta = i < n_ms;
-    const int t0 = lo + (i - n_ms) * kHT;
-    const int full = (t0 + kHT - 1 <= qa) & ((win <= 0) | (t0 > qlast - win)) & (t0 + kHT <= hi);
-    const int part_meta = i * kHT + kHT > a.n_meta;
-    return __builtin_amdgcn_readfirstlane((meta & part_meta) | ((meta ^ 1) & (full ^ 1)));
-  };
+  // Whether some key of stage i is hidden from some query of the wave.  Window stage w = i - n_ms
+  // starts at t0 = lo + 32 w, and it is whole for the wave iff t0 + 31 <= qa (below the diagonal),
+  // t0 + 32 <= hi, and t0 > qlast - win (inside every query's window): w in [w_edge, w_end], one
+  // range, fixed once per wave.  The meta stages are whole except a partial last one.  So the test
+  // is two scalar compares per stage (floor divisions by 32 as arithmetic shifts).
+  const int w_end = min((qa - lo - (kHT - 1)) >> 5, (hi - lo - kHT) >> 5);
+  const int w_edge = win > 0 ? max(((qlast - win - lo) >> 5) + 1, 0) : 0;
+  const int m_first = n_ms - (a.n_meta % kHT != 0 ? 1 : 0);   // first masked stage at or before the window
+  const int i_edge = n_ms + w_edge, i_end = n_ms + w_end;
+  auto masked = [&](int i) { return (i >= m_first && i < i_edge) || i > i_end; };
   // Q^T fragments: k-step s holds dims 16 s + 8 (lane/32) .. +7 of query tq
   QV qf[4];
   {
