@@ -34,11 +34,18 @@ namespace {
 
 using namespace attn;
 
-constexpr int kWaves = 4;               // waves per workgroup
-constexpr int kQG = kWaves * kQB;       // queries per workgroup
+#ifndef HYMBA_ATTN_WAVES
+#define HYMBA_ATTN_WAVES 4
+#endif
+constexpr int kWaves = HYMBA_ATTN_WAVES;   // waves per workgroup
+constexpr int kQG = kWaves * kQB;          // queries per workgroup
 constexpr int kHT = 32;                 // keys per LDS stage
 constexpr int kStages = 4;              // LDS buffers (see the kernel's note on reuse)
 constexpr int kXcds = 8;
+constexpr int kLoadThreads = kWaves * 32;               // threads loading K (and as many loading V)
+constexpr int kChunks = kHT * kHd * 2 / 16 / kLoadThreads;   // 16-byte chunks per thread and stage
+constexpr int kRowStep = kLoadThreads / 8;              // rows between a thread's chunks
+static_assert(kChunks >= 1 && kChunks * kLoadThreads * 16 == kHT * kHd * 2, "stage load shape");
 
 typedef f16x8_t QV;
 
@@ -171,11 +178,12 @@ __device__ __forceinline__ void settle(Col& c, U4 (&p)[2], float psum, const QV 
 }
 
 // The calling thread's share of a stage (K rows at kbase, V rows at vbase, row stride ld elements,
-// nvalid >= 1 valid rows): threads [0, 128) load K, [128, 256) V (a wave-uniform choice); chunk
-// it + 128 j (j < 2) is row (it >> 3) + 16 j, dims 8 (it & 7) + 0..7, at byte offset voff + 32 j ld
-// for a full stage.  Rows past nvalid read the last valid row and are zero-filled.
+// nvalid >= 1 valid rows): the first half of the workgroup's threads load K, the second half V (a
+// wave-uniform choice); thread it's chunk j is row (it >> 3) + kRowStep j, dims 8 (it & 7) + 0..7,
+// at byte offset voff + 2 kRowStep j ld for a full stage.  Rows past nvalid read the last valid
+// row and are zero-filled.
 struct StageRegs {
-  U4 r[2];
+  U4 r[kChunks];
 };
 // A buffer resource for the 32 rows (row stride ld elements) from p: base and size are
 // wave-uniform, so they live in scalar registers and a full stage's loads need no vector
@@ -193,14 +201,14 @@ __device__ __forceinline__ void fetch_stage(StageRegs& t, const half_t* kbase, c
   if (nvalid >= kHT) {
     const auto rs = stage_rsrc(base, ld);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      t.r[j] = __builtin_bit_cast(U4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, j * 16 * ld * 2, 0));
+    for (int j = 0; j < kChunks; ++j)
+      t.r[j] = __builtin_bit_cast(U4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, j * kRowStep * ld * 2, 0));
   } else {
     int row0 = it >> 3;
     const int col = (it & 7) * 8;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int row = row0 + 16 * j;
+    for (int j = 0; j < kChunks; ++j) {
+      const int row = row0 + kRowStep * j;
       t.r[j] = masked_load(base + (static_cast<int64_t>(min(row, nvalid - 1)) * ld + col) * 2, row < nvalid);
     }
   }
@@ -208,8 +216,8 @@ __device__ __forceinline__ void fetch_stage(StageRegs& t, const half_t* kbase, c
 __device__ __forceinline__ void store_stage(const StageRegs& t, uint16_t* ks, uint16_t* vs, bool is_k, int it) {
   uint16_t* base = is_k ? ks : vs;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    *reinterpret_cast<uint4*>(base + ((it >> 3) + 16 * j) * kKStr + (it & 7) * 8) =
+  for (int j = 0; j < kChunks; ++j)
+    *reinterpret_cast<uint4*>(base + ((it >> 3) + kRowStep * j) * kKStr + (it & 7) * 8) =
         make_uint4(t.r[j].x, t.r[j].y, t.r[j].z, t.r[j].w);
 }
 
@@ -231,7 +239,7 @@ struct AttnStages {
 // it has finished step i - 2; a wave still in step i - 1 reads stages i - 3 .. i - 1, so with four
 // buffers and one barrier per stage no store overwrites what another wave still reads.
 // Register budget: 4 waves per SIMD, at most 128 VGPRs (8 bytes of spills, outside the stage loop).
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void swa_meta_attn_kernel(
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void swa_meta_attn_kernel(
     AttnArgs<half_t> a) {
   __shared__ AttnStages sm;
   const int tid = threadIdx.x;
@@ -265,8 +273,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
   const half_t* kseq = a.k + (int64_t)b * a.kv_seq_stride + g * kHd;
   const half_t* vseq = a.v + (int64_t)b * a.kv_seq_stride + g * kHd;
   const int ld_meta = static_cast<int>(a.ld_meta), ld_kv = static_cast<int>(a.ld_kv);
-  const bool is_k = wave < 2;
-  const int it = tid & 127;
+  const bool is_k = wave < kWaves / 2;
+  const int it = tid & (kLoadThreads - 1);
   const uint32_t voff_meta = static_cast<uint32_t>(((it >> 3) * ld_meta + (it & 7) * 8) * 2);
   const uint32_t voff_kv = static_cast<uint32_t>(((it >> 3) * ld_kv + (it & 7) * 8) * 2);
   auto fetch = [&](StageRegs& r, int i) {
