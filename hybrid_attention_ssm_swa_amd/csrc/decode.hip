@@ -618,13 +618,16 @@ hipError_t launch_decode_attn(const DecAttnArgs<float>& a, hipStream_t s) { retu
 hipError_t launch_decode_attn(const DecAttnArgs<half_t>& a, hipStream_t s) { return dec_dispatch(a, s); }
 
 // Splits per (sequence, KV head): enough for ~2048 workgroups (8 per CU), at
-// least one load round (256 / lanes per key row * kDecPasses keys) per split
-// when the key range allows, never fewer than 64 keys per split, at most
-// kDecodeMaxSplits.  Longer splits run several rounds.
+// least one load round per split when the key range allows (the VALU kernel: 256 / lanes
+// per key row * kDecPasses keys; the MFMA kernel for 16-bit K/V of head dim 64: three of its
+// 64-key tiles -- 1152 ring keys then give 6 splits, 3840 one-wave workgroups, all resident at
+// once, 1 % faster per decode pair step than four tiles per split), never fewer than 64 keys per
+// split, at most kDecodeMaxSplits.  Longer splits run several rounds.
 int decode_attn_splits(int B, int n_kv_heads, int n_keys_max, int head_dim, int elem_bytes) {
   const int lpk = head_dim * elem_bytes / 16;
   if (lpk < 2 || lpk > 16 || B < 1 || n_kv_heads < 1) return -1;
-  const int64_t per_round = (int64_t)(kThreads / lpk) * kDecPasses;
+  const bool mfma = elem_bytes == 2 && head_dim == attn::kHd;
+  const int64_t per_round = mfma ? 3 * attn::kKT : (int64_t)(kThreads / lpk) * kDecPasses;
   const int64_t pairs = (int64_t)B * n_kv_heads;
   int64_t s = std::max<int64_t>(ceil_div(n_keys_max, per_round), ceil_div(2048, pairs));
   s = std::min<int64_t>(s, std::max<int64_t>(1, ceil_div(n_keys_max, 64)));
