@@ -31,6 +31,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+from hymba_synth import ABLATION_300M, DECODE_B128, GLOBAL_8K, SWA_8K, workload  # noqa: E402  (numpy only)
+
 METRIC = "hybrid-head mixer tokens/s (8K prefill, B=128 decode) + % HBM/MFMA peak"
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15         # dense bf16 MFMA FLOP/s
@@ -221,16 +223,16 @@ def timed(layers, fn, steps, warmup):
     return ms, ms_rec, [L.hymba_layer_profile_read(lay.handle) for lay in layers]
 
 
-def bench_prefill(cfg_id, steps, warmup, rope_base=0.0):
+def bench_prefill(name, steps, warmup, rope_base=0.0):
     import torch
     from hybrid_attention_ssm_swa_amd.layer import MixerLayer, make_kv, upload
-    from hymba_synth import config_by_id
+    from hymba_synth import workload
     from hymba_synth.generate import make_config_case
-    cfg = config_by_id(cfg_id)
+    cfg = workload(name)
     s = cfg.shape.with_(rope_base=rope_base)
     t = time.time()
-    case = make_config_case(cfg_id)
-    log(f"[bench] config {cfg_id} ({cfg.name}) inputs generated in {time.time() - t:.1f}s")
+    case = make_config_case(name)
+    log(f"[bench] {cfg.name} inputs generated in {time.time() - t:.1f}s")
     dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
     layer = MixerLayer(s, case.params)
     x = upload(case.x, dt, "cuda")
@@ -275,14 +277,14 @@ def bench_prefill(cfg_id, steps, warmup, rope_base=0.0):
     return out
 
 
-def bench_decode(cfg_id, steps, warmup, case=None):
+def bench_decode(name, steps, warmup, case=None):
     """B=128 decode of a KV-sharing producer/consumer pair (the workload's ring cache), or, with
     `case`, that decode case (e.g. a global layer over a full cache)."""
     import torch
     from hybrid_attention_ssm_swa_amd.layer import MixerLayer, make_kv, upload
     from hymba_synth.generate import make_config_case
     if case is None:
-        case = make_config_case(cfg_id)
+        case = make_config_case(name)
     s, sc = case.shape, case.consumer_shape
     dt = torch.bfloat16
     prod = MixerLayer(s, case.producer)
@@ -331,8 +333,8 @@ def bench_attention_alone(steps, warmup):
     through the per-kernel entry point.  For counter passes: the only launches are this kernel's."""
     import torch
     from hybrid_attention_ssm_swa_amd import _lib as L
-    from hymba_synth import CONFIGS
-    s = CONFIGS[2].shape
+    from hymba_synth import SWA_8K, workload
+    s = workload(SWA_8K).shape
     B, T, M, Hq, Hkv, hd, W = 16, 8192, s.n_meta, s.n_heads, s.n_kv_heads, s.head_dim, s.window
     ld_q = (s.n_in + 63) // 64 * 64
     g = torch.Generator(device="cuda").manual_seed(0)
@@ -799,7 +801,7 @@ def cpu_baseline(budget_s=15.0, max_seqs=6):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    case = make_config_case(2)
+    case = make_config_case(SWA_8K)
     done, t0 = 0, time.time()
     while done < max_seqs and (time.time() - t0) < budget_s:
         orc.layer_forward(case.params, case.x[done], case.k_meta, case.v_meta, case.k[done], case.v[done])
@@ -880,7 +882,7 @@ def main():
                           os.path.join(ROOT, "profiles", "pmc_traffic.json"))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -895,29 +897,28 @@ def main():
         print(json.dumps(bench_griffin(args.steps, args.warmup)), flush=True)
         return
     if args.decode_only:
-        print(json.dumps(bench_decode(4, args.steps, args.warmup)), flush=True)
+        print(json.dumps(bench_decode(DECODE_B128, args.steps, args.warmup)), flush=True)
         return
     if args.attention_only:
         print(json.dumps(bench_attention_alone(args.steps, args.warmup)), flush=True)
         return
-    main_run = bench_prefill(2, args.steps, args.warmup)
+    main_run = bench_prefill(SWA_8K, args.steps, args.warmup)
     log(f"[bench] 8K SWA prefill: {main_run['tokens_per_s']:.0f} tok/s, {main_run['ms_per_step']:.3f} ms/step")
     workloads = {}
     if not args.main_only:
-        workloads["decode_b128_pair"] = bench_decode(4, args.steps, args.warmup)
+        workloads["decode_b128_pair"] = bench_decode(DECODE_B128, args.steps, args.warmup)
         log(f"[bench] decode: {workloads['decode_b128_pair']['tokens_per_s_per_layer']:.0f} tok/s/layer")
-        from hymba_synth import CONFIGS
         from hymba_synth.generate import make_decode_case
-        g = CONFIGS[3].shape
+        g = workload(GLOBAL_8K).shape
         workloads["global_decode_b8_full_cache"] = bench_decode(
-            3, args.steps, args.warmup, make_decode_case(g, g.with_(own_kv=False), 8, 8192, 1003, cache_len=8193))
+            GLOBAL_8K, args.steps, args.warmup, make_decode_case(g, g.with_(own_kv=False), 8, 8192, 1003, cache_len=8193))
         log(f"[bench] global decode (B=8, 8193 keys + meta): "
             f"{workloads['global_decode_b8_full_cache']['tokens_per_s_per_layer']:.0f} tok/s/layer")
-        workloads["global_8k_prefill"] = bench_prefill(3, max(3, args.steps // 2), args.warmup)
+        workloads["global_8k_prefill"] = bench_prefill(GLOBAL_8K, max(3, args.steps // 2), args.warmup)
         log(f"[bench] 8K global prefill: {workloads['global_8k_prefill']['tokens_per_s']:.0f} tok/s")
-        workloads["rope_swa_8k_prefill"] = bench_prefill(2, args.steps, args.warmup, rope_base=10000.0)
+        workloads["rope_swa_8k_prefill"] = bench_prefill(SWA_8K, args.steps, args.warmup, rope_base=10000.0)
         log(f"[bench] 8K SWA prefill with RoPE (base 1e4): {workloads['rope_swa_8k_prefill']['tokens_per_s']:.0f} tok/s")
-        workloads["ablation300m_prefill"] = bench_prefill(1, args.steps, args.warmup)
+        workloads["ablation300m_prefill"] = bench_prefill(ABLATION_300M, args.steps, args.warmup)
         log(f"[bench] 300M SWA prefill: {workloads['ablation300m_prefill']['tokens_per_s']:.0f} tok/s")
         workloads["griffin_block_8k"] = bench_griffin(args.steps, args.warmup)
         log(f"[bench] Griffin block 8K prefill: {workloads['griffin_block_8k']['tokens_per_s']:.0f} tok/s; "

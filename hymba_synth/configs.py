@@ -47,7 +47,7 @@ class LayerShape:
 
 @dataclass(frozen=True)
 class Config:
-    cfg_id: int
+    seed: int                      # base seed of the workload's inputs
     name: str
     kind: str                      # "prefill" or "decode"
     batch: int
@@ -64,20 +64,31 @@ _C1 = LayerShape(d_model=1024, n_heads=16, head_dim=64, n_kv_heads=4, d_inner=20
 _15B = LayerShape(d_model=1600, n_heads=25, head_dim=64, n_kv_heads=5, d_inner=3200, d_state=16,
                   n_meta=128, window=1024, own_kv=True, dtype="bf16")
 
-CONFIGS = [
-    Config(0, "tiny-f32", "prefill", 1, 128, _C0,
+WORKLOADS = [
+    Config(1000, "tiny-f32", "prefill", 1, 128, _C0,
            note="tiny fp32 mixer, SWA 32, 16 meta tokens"),
-    Config(1, "300m-ablation-swa", "prefill", 8, 2048, _C1,
+    Config(1001, "300m-ablation-swa", "prefill", 8, 2048, _C1,
            note="300M-ablation-shaped SWA layer, bf16"),
-    Config(2, "1.5b-swa-8k-kvshare", "prefill", 16, 8192, _15B.with_(own_kv=False),
+    Config(1002, "1.5b-swa-8k-kvshare", "prefill", 16, 8192, _15B.with_(own_kv=False),
            note="1.5B-shaped SWA layer at 8K, K/V handed from the preceding layer"),
-    Config(3, "1.5b-global-8k", "prefill", 8, 8192, _15B.with_(window=0),
+    Config(1003, "1.5b-global-8k", "prefill", 8, 8192, _15B.with_(window=0),
            note="1.5B-shaped global-attention layer at 8K"),
-    Config(4, "1.5b-decode-b128", "decode", 128, 8192, _15B,
+    Config(1004, "1.5b-decode-b128", "decode", 128, 8192, _15B,
            consumer_shape=_15B.with_(own_kv=False),
            note="decode step at real index 8192, SWA ring 1024 shared by a producer/consumer pair"),
 ]
 
 
-def config_by_id(cfg_id: int) -> Config:
-    return CONFIGS[cfg_id]
+TINY_F32 = "tiny-f32"
+ABLATION_300M = "300m-ablation-swa"
+SWA_8K = "1.5b-swa-8k-kvshare"
+GLOBAL_8K = "1.5b-global-8k"
+DECODE_B128 = "1.5b-decode-b128"
+
+
+def workload(name: str) -> Config:
+    """The workload of that name (KeyError for an unknown one)."""
+    for c in WORKLOADS:
+        if c.name == name:
+            return c
+    raise KeyError(name)

@@ -18,7 +18,7 @@ from typing import Optional
 
 import numpy as np
 
-from .configs import Config, LayerShape, config_by_id
+from .configs import Config, LayerShape, workload
 
 DT_BIAS = -2.0
 
@@ -134,10 +134,10 @@ def make_decode_case(shape: LayerShape, consumer_shape: LayerShape, batch: int, 
                       state_p, state_c, x_c)
 
 
-def make_config_case(cfg_id: int):
-    """The workload's inputs, seeded with 1000 + id."""
-    cfg: Config = config_by_id(cfg_id)
-    seed = 1000 + cfg_id
+def make_config_case(name: str):
+    """The named workload's inputs, seeded with its base seed."""
+    cfg: Config = workload(name)
+    seed = cfg.seed
     if cfg.kind == "prefill":
         return make_prefill_case(cfg.shape, cfg.batch, cfg.seq, seed)
     return make_decode_case(cfg.shape, cfg.consumer_shape, cfg.batch, cfg.seq, seed)

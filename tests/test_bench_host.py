@@ -7,24 +7,24 @@ import os
 import pytest
 
 import bench
-from hymba_synth import CONFIGS
+from hymba_synth import ABLATION_300M, SWA_8K, TINY_F32, workload
 
 
 def test_visible_keys_matches_brute_force():
     for M, W, T in [(3, 4, 10), (0, 1, 5), (2, 0, 7), (5, 16, 9)]:
-        s = CONFIGS[0].shape.with_(n_meta=M, window=W)
+        s = workload(TINY_F32).shape.with_(n_meta=M, window=W)
         brute = sum(M + (i + 1 if W == 0 else min(i + 1, W)) for i in range(T))
         assert bench.visible_keys(s, T) == brute
 
 
 def test_prefill_work_stages():
-    s = CONFIGS[2].shape
+    s = workload(SWA_8K).shape
     w = bench.prefill_work(s, 16, 8192)
     assert set(w) == {"in_proj", "attention", "w_o", "out_proj", "ssm", "epilogue", "convert"}
     R = 16 * 8192
     assert w["in_proj"] == ("mfma", 2.0 * R * s.d_model * s.n_in)
     assert w["epilogue"] == ("hbm", float(R * s.d_inner * 2 * 4))
-    assert "kv_write" in bench.prefill_work(CONFIGS[1].shape, 8, 2048)
+    assert "kv_write" in bench.prefill_work(workload(ABLATION_300M).shape, 8, 2048)
 
 
 def _trace_rows():

@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 import torch
 
-from hymba_synth import CONFIGS, LayerShape, bf16_round, make_layer_params
+from hymba_synth import GLOBAL_8K, SWA_8K, LayerShape, bf16_round, make_layer_params, workload
 from hymba_synth.generate import _store, draw_normal
 from oracle import hymba_oracle as orc
 
@@ -72,12 +72,12 @@ def _handoff(shape, B, T, cache_len, seed, seqs):
 
 def test_handoff_8k_swa_pair():
     announce("prefill 8192 -> decode at 8192, 1.5B SWA pair, ring of 1024")
-    _handoff(CONFIGS[2].shape, 2, 8192, 1024, seed=501, seqs=[1])
+    _handoff(workload(SWA_8K).shape, 2, 8192, 1024, seed=501, seqs=[1])
 
 
 def test_handoff_8k_global_pair():
     announce("prefill 8192 -> decode at 8192, 1.5B global pair, full cache")
-    _handoff(CONFIGS[3].shape, 2, 8192, 8200, seed=503, seqs=[0])
+    _handoff(workload(GLOBAL_8K).shape, 2, 8192, 8200, seed=503, seqs=[0])
 
 
 CHAIN = LayerShape(d_model=256, n_heads=8, head_dim=64, n_kv_heads=2, d_inner=512, d_state=16, n_meta=64,

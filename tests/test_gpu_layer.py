@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 import torch
 
-from hymba_synth import CONFIGS, LayerShape, make_decode_case, make_prefill_case
+from hymba_synth import (DECODE_B128, GLOBAL_8K, ABLATION_300M, SWA_8K, TINY_F32, LayerShape, make_decode_case,
+                         make_prefill_case, workload)
 from hymba_synth.generate import make_config_case
 from oracle import hymba_oracle as orc
 
@@ -57,10 +58,10 @@ SMALL_BF16 = LayerShape(d_model=256, n_heads=8, head_dim=64, n_kv_heads=2, d_inn
     (SMALL_BF16.with_(window=1, n_meta=20), 1, 70),
     (SMALL_BF16, 2, 1),
     (SMALL_BF16.with_(n_kv_heads=8, n_meta=64), 1, 130),
-    (CONFIGS[0].shape.with_(window=5, n_meta=3), 2, 41),
+    (workload(TINY_F32).shape.with_(window=5, n_meta=3), 2, 41),
     (SMALL_BF16.with_(rope_base=10000.0), 2, 150),
     (SMALL_BF16.with_(rope_base=500.0, window=0, n_meta=40), 1, 130),
-    (CONFIGS[0].shape.with_(rope_base=100.0), 1, 60),
+    (workload(TINY_F32).shape.with_(rope_base=100.0), 1, 60),
 ])
 def test_small_layer_prefill(shape, B, T):
     announce(f"small prefill {shape} B={B} T={T}")
@@ -70,7 +71,7 @@ def test_small_layer_prefill(shape, B, T):
 
 def test_meta_prefix_outputs():
     """The prepared meta prefix (K/V, SSM state, meta-row outputs) equals the oracle's meta rows."""
-    for shape in (SMALL_BF16, CONFIGS[0].shape, SMALL_BF16.with_(rope_base=1000.0)):
+    for shape in (SMALL_BF16, workload(TINY_F32).shape, SMALL_BF16.with_(rope_base=1000.0)):
         announce(f"meta prefix {shape.dtype}")
         case = make_prefill_case(shape, 1, 8, seed=11)
         layer = MixerLayer(shape, case.params)
@@ -86,23 +87,23 @@ def test_meta_prefix_outputs():
 
 
 def test_config0_tiny_f32_full():
-    announce("config 0 (tiny fp32) full")
-    _check_prefill(make_config_case(0), [0], "f32")
+    announce("tiny fp32 layer, full")
+    _check_prefill(make_config_case(TINY_F32), [0], "f32")
 
 
 def test_config1_full_size():
-    announce("config 1 (300M-ablation SWA, 8x2048) full size, all sequences")
-    _check_prefill(make_config_case(1), range(8), "bf16")
+    announce("300M-ablation SWA layer, 8x2048, full size, all sequences")
+    _check_prefill(make_config_case(ABLATION_300M), range(8), "bf16")
 
 
 def test_config2_full_size_sampled():
-    announce("config 2 (1.5B SWA KV-consumer, 16x8192) full size, sequences 0 and 15")
-    _check_prefill(make_config_case(2), [0, 15], "bf16")
+    announce("1.5B SWA KV-consumer layer, 16x8192, full size, sequences 0 and 15")
+    _check_prefill(make_config_case(SWA_8K), [0, 15], "bf16")
 
 
 def test_config3_full_size_sampled():
-    announce("config 3 (1.5B global, 8x8192) full size, sequences 0 and 7")
-    _check_prefill(make_config_case(3), [0, 7], "bf16")
+    announce("1.5B global layer, 8x8192, full size, sequences 0 and 7")
+    _check_prefill(make_config_case(GLOBAL_8K), [0, 7], "bf16")
 
 
 def _decode_pair_gpu(case, cache_len=None):
@@ -136,8 +137,8 @@ def _decode_pair_oracle(case, seqs):
 
 
 def test_config4_decode_full_size():
-    announce("config 4 (decode pair, B=128 at 8192) full size, all sequences")
-    case = make_config_case(4)
+    announce("1.5B decode pair, B=128 at 8192, full size, all sequences")
+    case = make_config_case(DECODE_B128)
     _, _, yp, yc, stp, stc, kc, vc = _decode_pair_gpu(case)
     ref = _decode_pair_oracle(case, range(case.batch))
     Y_p = np.stack([ref[b][0].Y for b in ref])
@@ -160,7 +161,7 @@ def test_global_decode_full_cache():
     """Global-attention decode at the 1.5B global layer's shape: 8 sequences at position 8192 over a
     full cache (every earlier real token plus the meta prefix), producer/consumer pair."""
     announce("global decode B=8, pos 8192, full cache")
-    s = CONFIGS[3].shape
+    s = workload(GLOBAL_8K).shape
     case = make_decode_case(s, s.with_(own_kv=False), 8, 8192, seed=77, cache_len=8193)
     _, _, yp, yc, stp, stc, kc, _ = _decode_pair_gpu(case)
     ref = _decode_pair_oracle(case, range(case.batch))
@@ -174,7 +175,7 @@ def test_global_decode_full_cache():
 def test_decode_small_mixed_positions(dtype, rope):
     """Positions differ per sequence: before the window fills, at the wrap, far beyond."""
     announce(f"decode small {dtype} rope {rope}")
-    base = SMALL_BF16 if dtype == "bf16" else CONFIGS[0].shape.with_(n_meta=6)
+    base = SMALL_BF16 if dtype == "bf16" else workload(TINY_F32).shape.with_(n_meta=6)
     s = base.with_(window=16, rope_base=rope)
     case = make_decode_case(s, s.with_(own_kv=False), 6, 0, seed=21, cache_len=16)
     case.pos = np.array([0, 3, 15, 16, 17, 1000], dtype=np.int64)

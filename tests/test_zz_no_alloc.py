@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import hybrid_attention_ssm_swa_amd as H
+from hymba_synth import DECODE_B128
 from hymba_synth.generate import make_config_case
 from oracle import hymba_oracle as orc
 
@@ -44,7 +45,7 @@ def _static_decode(layer, x, pos, kv, state):
 
 
 def test_static_decode_matches_the_workspace_entry():
-    case = make_config_case(4)
+    case = make_config_case(DECODE_B128)
     prod, cons = _pair(case)
     kmp, vmp = orc.meta_kv(case.producer)
     for B in (128, 40):
@@ -74,7 +75,7 @@ def test_static_decode_matches_the_workspace_entry():
 
 
 def test_static_decode_rejects_what_does_not_fit():
-    case = make_config_case(4)
+    case = make_config_case(DECODE_B128)
     s = case.shape
     prod = MixerLayer(s, case.producer)
     x = torch.zeros((600, s.d_model), dtype=torch.bfloat16, device="cuda")
