@@ -50,6 +50,10 @@ constexpr int kRwMaxUnrolled = 8;          // K walks of up to this many phases 
 
 struct __align__(16) Q4 { uint32_t x, y, z, w; };
 
+// cache policy of the weight loads: non-temporal (the nt bit on gfx950).  Each weight byte is read
+// once per call, so it need not displace the decode step's K/V caches in the MALL.
+constexpr int kNonTemporal = 2;
+
 // v if keep, else zeros: per 32-bit word (a select of the whole struct is lowered through
 // scratch memory)
 __device__ __forceinline__ Q4 keep_or_zero(bool keep, Q4 v) {
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(kRwThreads) void rows_gemm_kernel(SkinnyArgs<WT, XT
     const uint32_t kb = live ? static_cast<uint32_t>(p) * kRwPhaseK * 2 : 0u;
 #pragma unroll
     for (int q = 0; q < LW; ++q)
-      ph.r[q] = __builtin_bit_cast(Q4, __builtin_amdgcn_raw_buffer_load_b128(rw, vw[q] + kb, 0, 0));
+      ph.r[q] = __builtin_bit_cast(Q4, __builtin_amdgcn_raw_buffer_load_b128(rw, vw[q] + kb, 0, kNonTemporal));
 #pragma unroll
     for (int q = 0; q < LX; ++q)
       ph.r[LW + q] = __builtin_bit_cast(Q4, __builtin_amdgcn_raw_buffer_load_b128(rx, vx[q] + kb, 0, 0));

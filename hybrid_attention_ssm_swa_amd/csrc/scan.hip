@@ -270,7 +270,12 @@ __global__ __launch_bounds__(256) void ssm_step_kernel(StepArgs<T> a) {
   const float delta = softplus_f(dv + a.dt_bias[c]);
   const float du = delta * uv;
   float4* hp = reinterpret_cast<float4*>(a.h + ch * N + 4 * q);
-  float4 hv = *hp;
+  // The state is read and written once per step with non-temporal hints: written normally, its
+  // 26 MB per 1.5B layer and 128 sequences would sit dirty in the 256 MB MALL and be written back
+  // to HBM while the next kernels stream their K/V caches (the ring-decode pair step: 1.20 ->
+  // 1.245 M tokens/s per layer, the producer's attention 45.8 -> 40.4 us in the step).
+  const f32x4_t hv4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(hp));
+  const float4 hv = make_float4(hv4[0], hv4[1], hv4[2], hv4[3]);
   const float4 a2 = *reinterpret_cast<const float4*>(a.A2 + (int64_t)c * N + 4 * q);
   float hs[4] = {hv.x, hv.y, hv.z, hv.w};
   const float a2s[4] = {a2.x, a2.y, a2.z, a2.w};
@@ -294,7 +299,7 @@ __global__ __launch_bounds__(256) void ssm_step_kernel(StepArgs<T> a) {
 #pragma unroll
   for (int off = 1; off < LPC; off <<= 1) part += __shfl_xor(part, off);
   if (active) {
-    *hp = make_float4(hs[0], hs[1], hs[2], hs[3]);
+    __builtin_nontemporal_store(f32x4_t{hs[0], hs[1], hs[2], hs[3]}, reinterpret_cast<f32x4_t*>(hp));
     if (q == 0) Elem<T>::store(a.y + b * a.ldy + c, part + a.D[c] * uv);
   }
 }
