@@ -11,6 +11,7 @@
 // operands matter: these GEMMs run power-limited, and bit toggling in the
 // data moves the clock.
 #include "gemm_blaslt.h"
+#include "kernels.h"
 
 #include <hipblaslt/hipblaslt.h>
 #include <hipblaslt/hipblaslt-ext.hpp>
@@ -57,9 +58,12 @@ bool env_flag(const char* name, bool dflt) {
 }
 
 // Mean milliseconds of `reps` runs of one candidate (after one untimed run), or a negative value if
-// it fails.
+// it fails.  With `spin_us` > 0 a wait kernel of that length runs first, so that the timed calls are
+// all queued before the first starts and run back to back: for a few-microsecond GEMM the
+// library's host time per call (~17 us) is longer than the kernel, and without the wait the
+// candidates would all time at the host's pace.
 float time_candidate(hipblasLtHandle_t handle, const Plan& p, const hipblasLtMatmulAlgo_t& algo, const void* W,
-                     const void* X, void* Y, void* ws, size_t ws_bytes, hipStream_t s, int reps) {
+                     const void* X, void* Y, void* ws, size_t ws_bytes, hipStream_t s, int reps, int spin_us) {
   const float alpha = 1.f, beta = 0.f;
   hipEvent_t e0, e1;
   if (hipEventCreate(&e0) != hipSuccess) return -1.f;
@@ -67,6 +71,7 @@ float time_candidate(hipblasLtHandle_t handle, const Plan& p, const hipblasLtMat
   float ms = -1.f;
   bool ok = hipblasLtMatmul(handle, p.desc, &alpha, W, p.la, X, p.lb, &beta, Y, p.lc, Y, p.lc, &algo, ws,
                             ws_bytes, s) == HIPBLAS_STATUS_SUCCESS;
+  ok = ok && (spin_us <= 0 || launch_spin(spin_us, s) == hipSuccess);
   ok = ok && hipEventRecord(e0, s) == hipSuccess;
   for (int r = 0; ok && r < reps; ++r)
     ok = hipblasLtMatmul(handle, p.desc, &alpha, W, p.la, X, p.lb, &beta, Y, p.lc, Y, p.lc, &algo, ws, ws_bytes,
@@ -190,7 +195,8 @@ int gemm_16(GemmType in_type, GemmType out_type, const void* X, int64_t ldx, con
         const int reps = 2.0 * rows * out * in < 1e11 ? 12 : 2;
         float best_ms = -1.f;
         for (size_t i = 0; cand.size() > 1 && i < cand.size(); ++i) {
-          const float ms = time_candidate(handle, p, cand[i], W, X, Y, ws, ws_bytes, s, reps);
+          const float ms = time_candidate(handle, p, cand[i], W, X, Y, ws, ws_bytes, s, reps,
+                                          reps > 2 ? 40 * reps : 0);
           if (log)
             std::fprintf(stderr, "[hymba gemm] rows %lld out %lld in %lld candidate %zu: %.4f ms\n",
                          (long long)rows, (long long)out, (long long)in, i, ms);

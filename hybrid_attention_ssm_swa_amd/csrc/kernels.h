@@ -227,5 +227,8 @@ hipError_t launch_nonfinite16_check(const half_t* p, int64_t n, uint32_t* flag, 
 // ---- misc ----------------------------------------------------------------------
 hipError_t launch_scale_copy(const float* src, float* dst, int64_t n, float scale, hipStream_t s);
 hipError_t launch_fill(float* dst, int64_t n, float value, hipStream_t s);
+// Keeps the stream busy for about `microseconds` (one thread, a bounded wait on the wall clock), so
+// that work queued behind it meanwhile then runs back to back.
+hipError_t launch_spin(int microseconds, hipStream_t s);
 
 }  // namespace hymba
