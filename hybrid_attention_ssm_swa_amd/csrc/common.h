@@ -77,6 +77,16 @@ template <> struct Vec16<float> {
   __device__ static __forceinline__ void store(float* p, const float (&v)[4]) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   }
+  // non-temporal forms (nt cache policy) for data read or written once
+  __device__ static __forceinline__ void load_nt(const float* p, float (&v)[4]) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+  }
+  __device__ static __forceinline__ void store_nt(float* p, const float (&v)[4]) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(p));
+  }
 };
 template <typename T> struct Vec16H {   // 16-bit element types
   static constexpr int n = 8;
@@ -90,6 +100,18 @@ template <typename T> struct Vec16H {   // 16-bit element types
     x.x = Pair<T>::pack(v[0], v[1]); x.y = Pair<T>::pack(v[2], v[3]);
     x.z = Pair<T>::pack(v[4], v[5]); x.w = Pair<T>::pack(v[6], v[7]);
     *reinterpret_cast<uint4*>(p) = x;
+  }
+  __device__ static __forceinline__ void load_nt(const T* p, float (&v)[8]) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    v[0] = Pair<T>::lo(x[0]); v[1] = Pair<T>::hi(x[0]); v[2] = Pair<T>::lo(x[1]); v[3] = Pair<T>::hi(x[1]);
+    v[4] = Pair<T>::lo(x[2]); v[5] = Pair<T>::hi(x[2]); v[6] = Pair<T>::lo(x[3]); v[7] = Pair<T>::hi(x[3]);
+  }
+  __device__ static __forceinline__ void store_nt(T* p, const float (&v)[8]) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 x{Pair<T>::pack(v[0], v[1]), Pair<T>::pack(v[2], v[3]),
+                  Pair<T>::pack(v[4], v[5]), Pair<T>::pack(v[6], v[7])};
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(p));
   }
 };
 template <> struct Vec16<bf16_t> : Vec16H<bf16_t> {};
