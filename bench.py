@@ -142,12 +142,12 @@ def scan_alu_entry(s, B, T, ms):
 
 # --- traffic measured by rocprofv3 counters (optional, committed under profiles/) ---------
 
-# sources whose change invalidates a stage's recorded counters: the kernel file and the tile
-# headers it includes (GEMMs: the plan selection code)
-KERNEL_SOURCES = {"attention": ("attn_prefill.hip", "attn_tile.h"), "ssm": ("scan.hip",),
-                  "epilogue": ("epilogue.hip",), "in_proj": ("gemm_blaslt.cpp",), "w_o": ("gemm_blaslt.cpp",),
-                  "out_proj": ("gemm_blaslt.cpp",), "convert": ("convert.hip",),
-                  "kv_write": ("decode.hip", "attn_tile.h")}
+# sources whose change invalidates a stage's recorded counters: the kernel file and the headers
+# of device code it includes (GEMMs: the plan selection code)
+KERNEL_SOURCES = {"attention": ("attn_prefill.hip", "attn_tile.h", "common.h"), "ssm": ("scan.hip", "common.h"),
+                  "epilogue": ("epilogue.hip", "common.h"), "in_proj": ("gemm_blaslt.cpp",),
+                  "w_o": ("gemm_blaslt.cpp",), "out_proj": ("gemm_blaslt.cpp",), "convert": ("convert.hip", "common.h"),
+                  "kv_write": ("decode.hip", "attn_tile.h", "common.h")}
 
 
 def source_sha(stage):
