@@ -31,6 +31,7 @@ SOURCES = [
     "convert.hip",
     "griffin.hip",
     "griffin_api.cpp",
+    "util.hip",
 ]
 
 ARCH = "gfx950"

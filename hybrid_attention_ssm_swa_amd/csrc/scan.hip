@@ -392,24 +392,6 @@ hipError_t step_dispatch(const StepArgs<T>& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-__global__ void scale_copy_kernel(const float* __restrict__ src, float* __restrict__ dst, int64_t n,
-                                  float scale) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) dst[i] = src[i] * scale;
-}
-
-// One thread waits until the constant-rate wall clock has advanced by `ticks` (a bounded loop).
-__global__ void spin_kernel(int64_t ticks) {
-  if (threadIdx.x != 0) return;
-  const int64_t t0 = wall_clock64();
-  while (wall_clock64() - t0 < ticks) __builtin_amdgcn_s_sleep(32);
-}
-
-__global__ void fill_kernel(float* __restrict__ dst, int64_t n, float value) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) dst[i] = value;
-}
-
 }  // namespace
 
 size_t scan_segment_bytes(int B, int T, int E, int N) {
@@ -421,29 +403,5 @@ hipError_t launch_selective_scan(const ScanArgs<float>& a, hipStream_t s) { retu
 hipError_t launch_selective_scan(const ScanArgs<half_t>& a, hipStream_t s) { return scan_dispatch(a, s); }
 hipError_t launch_ssm_step(const StepArgs<float>& a, hipStream_t s) { return step_dispatch(a, s); }
 hipError_t launch_ssm_step(const StepArgs<half_t>& a, hipStream_t s) { return step_dispatch(a, s); }
-
-hipError_t launch_scale_copy(const float* src, float* dst, int64_t n, float scale, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(scale_copy_kernel, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, s,
-                     src, dst, n, scale);
-  return hipGetLastError();
-}
-
-hipError_t launch_spin(int microseconds, hipStream_t s) {
-  int rate_khz = 0;   // wall-clock ticks per millisecond
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || rate_khz <= 0)
-    rate_khz = 100000;   // gfx9's 100 MHz
-  const int64_t ticks = static_cast<int64_t>(microseconds) * rate_khz / 1000;
-  hipLaunchKernelGGL(spin_kernel, dim3(1), dim3(64), 0, s, ticks);
-  return hipGetLastError();
-}
-
-hipError_t launch_fill(float* dst, int64_t n, float value, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_kernel, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, s, dst, n, value);
-  return hipGetLastError();
-}
 
 }  // namespace hymba
