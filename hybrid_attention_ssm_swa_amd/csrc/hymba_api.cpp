@@ -641,12 +641,24 @@ int32_t decode_impl(hymba_layer& L, const void* x, const int64_t* pos, int B, vo
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// The kernels move activations, K/V rows and states in 16-byte vectors, and the workspace is carved
+// into 256-byte-aligned regions from its start.
+int32_t check_kv_alignment(const hymba_kv* kv) {
+  if (kv && (!aligned(kv->k_meta, 16) || !aligned(kv->v_meta, 16) || !aligned(kv->k, 16) || !aligned(kv->v, 16) ||
+             !aligned(kv->k_cache, 16) || !aligned(kv->v_cache, 16)))
+    return fail(HYMBA_ERR_INVALID_ARG, "the K/V pointers of kv must be 16-byte aligned");
+  return HYMBA_OK;
+}
+
 int32_t check_decode_args(const hymba_layer& L, const void* x_t, const int64_t* pos, int32_t B, const void* y_t,
                           const hymba_kv* kv, const float* ssm_state) {
   if (!x_t || !y_t || !pos || !ssm_state)
     return fail(HYMBA_ERR_INVALID_ARG, "x_t, pos, y_t and ssm_state must be non-NULL");
   if (B < 1) return fail(HYMBA_ERR_INVALID_ARG, "B must be >= 1");
   if (B > 65535) return fail(HYMBA_ERR_UNSUPPORTED, "a decode step takes at most 65535 sequences (got %d)", B);
+  if (!aligned(x_t, 16) || !aligned(y_t, 16) || !aligned(ssm_state, 16) || !aligned(pos, 8))
+    return fail(HYMBA_ERR_INVALID_ARG, "x_t, y_t and ssm_state must be 16-byte aligned, pos 8-byte aligned");
+  STATUS_TRY(check_kv_alignment(kv));
   if (!kv || !kv->k_cache || !kv->v_cache) return fail(HYMBA_ERR_INVALID_ARG, "decode needs kv->k_cache and kv->v_cache");
   const hymba_layer_cfg& c = L.cfg;
   if (kv->cache_len < 1) return fail(HYMBA_ERR_INVALID_ARG, "cache_len must be >= 1");
@@ -699,6 +711,8 @@ int32_t hymba_layer_create(const hymba_layer_cfg* cfg, const hymba_layer_weights
   if (!w->w_in || !w->w_o || !w->w_out || !w->A || !w->D || !w->dt_bias || !w->beta1 || !w->beta2)
     return fail(HYMBA_ERR_INVALID_ARG, "a weight pointer is NULL");
   if (cfg->n_meta > 0 && !w->meta) return fail(HYMBA_ERR_INVALID_ARG, "meta rows pointer is NULL");
+  if (!aligned(w->w_in, 16) || !aligned(w->w_o, 16) || !aligned(w->w_out, 16) || !aligned(w->meta, 16))
+    return fail(HYMBA_ERR_INVALID_ARG, "weight matrices and meta rows must be 16-byte aligned");
   if (!persistent) return fail(HYMBA_ERR_INVALID_ARG, "persistent buffer is NULL");
   if (!aligned(persistent, kAlign)) return fail(HYMBA_ERR_INVALID_ARG, "persistent buffer must be 256-byte aligned");
   const PersistLayout pl = persist_layout(*cfg);
@@ -783,6 +797,8 @@ size_t hymba_mixer_workspace_bytes(const hymba_layer* L, int32_t batch, int32_t 
 int32_t hymba_layer_prepare(hymba_layer* L, const hymba_kv* kv, void* ws, size_t ws_bytes, void* stream) {
   if (!L) return fail(HYMBA_ERR_INVALID_ARG, "layer is NULL");
   if (!ws) return fail(HYMBA_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(ws, kAlign)) return fail(HYMBA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  STATUS_TRY(check_kv_alignment(kv));
   const WsLayout wl = ws_layout(*L, 1, 1);
   if (ws_bytes < wl.total) return fail(HYMBA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, wl.total);
   L->prepared = false;
@@ -794,6 +810,10 @@ int32_t hymba_mixer_prefill(hymba_layer* L, const void* x, int32_t B, int32_t T,
   if (!L) return fail(HYMBA_ERR_INVALID_ARG, "layer is NULL");
   if (!x || !y || !ws) return fail(HYMBA_ERR_INVALID_ARG, "x, y and workspace must be non-NULL");
   if (B < 1 || T < 1) return fail(HYMBA_ERR_INVALID_ARG, "B and T must be >= 1 (got %d, %d)", B, T);
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ssm_state_out, 16))
+    return fail(HYMBA_ERR_INVALID_ARG, "x, y and ssm_state_out must be 16-byte aligned");
+  if (!aligned(ws, kAlign)) return fail(HYMBA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  STATUS_TRY(check_kv_alignment(kv));
   const hymba_layer_cfg& c = L->cfg;
   if (!c.own_kv) {
     if (!kv || !kv->k || !kv->v) return fail(HYMBA_ERR_INVALID_ARG, "a consumer needs kv->k and kv->v");
@@ -818,6 +838,7 @@ int32_t hymba_mixer_decode(hymba_layer* L, const void* x_t, const int64_t* pos, 
                            const hymba_kv* kv, float* ssm_state, void* ws, size_t ws_bytes, void* stream) {
   if (!L) return fail(HYMBA_ERR_INVALID_ARG, "layer is NULL");
   if (!ws) return fail(HYMBA_ERR_INVALID_ARG, "workspace must be non-NULL");
+  if (!aligned(ws, kAlign)) return fail(HYMBA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   STATUS_TRY(check_decode_args(*L, x_t, pos, B, y_t, kv, ssm_state));
   const hymba_layer_cfg& c = L->cfg;
   const WsLayout wl = ws_layout(*L, B, 1);

@@ -93,7 +93,8 @@ typedef struct hymba_layer_cfg {
                          0: no position encoding                              */
 } hymba_layer_cfg;
 
-/* Device pointers.  Matrices in the storage dtype; vectors fp32. */
+/* Device pointers.  Matrices in the storage dtype, 16-byte aligned; vectors
+ * fp32. */
 typedef struct hymba_layer_weights {
   const void* w_in;     /* [Nin, d]                                         */
   const void* w_o;      /* [E, H*hd]                                        */
@@ -107,8 +108,8 @@ typedef struct hymba_layer_weights {
 } hymba_layer_weights;
 
 /* K/V handed between layers and kept for decode.  Device pointers in the
- * layer's activation type (fp32 for HYMBA_F32, fp16 for HYMBA_BF16); any of
- * them may be NULL where noted. */
+ * layer's activation type (fp32 for HYMBA_F32, fp16 for HYMBA_BF16), 16-byte
+ * aligned; any of them may be NULL where noted. */
 typedef struct hymba_kv {
   /* Meta K/V [M, Hkv, hd] of an unbound consumer (read).  Ignored by a
    * producer and by a consumer bound with hymba_kv_share_bind. */
@@ -151,7 +152,9 @@ void hymba_layer_destroy(hymba_layer* layer);
 int32_t hymba_kv_share_bind(hymba_layer* consumer, const hymba_layer* producer);
 
 /* Workspace bytes for prefill of [batch, seq] or decode (seq = 1) of `batch`
- * sequences; covers the meta-prefix preparation as well. */
+ * sequences; covers the meta-prefix preparation as well.  Every call that
+ * takes a workspace needs it 256-byte aligned, and x, y and the SSM states
+ * 16-byte aligned (HYMBA_ERR_INVALID_ARG otherwise, before any device work). */
 size_t hymba_mixer_workspace_bytes(const hymba_layer* layer, int32_t batch, int32_t seq);
 
 /* Runs the layer on its meta rows alone (Hymba summary section 2.3): fills

@@ -104,6 +104,42 @@ def test_create_checks_buffers():
     assert e.value.status == L.HYMBA_ERR_INVALID_ARG
 
 
+def test_layer_calls_check_alignment():
+    """The kernels move rows in 16-byte vectors and carve the workspace into 256-byte regions:
+    misaligned pointers are rejected before any device work."""
+    cfg = _cfg()
+    n = L.hymba_layer_persistent_bytes(cfg)
+    w = _weights()
+    w.w_in = FAKE + 2
+    with pytest.raises(L.HymbaError) as e:
+        L.hymba_layer_create(cfg, w, FAKE, n)
+    assert e.value.status == L.HYMBA_ERR_INVALID_ARG
+    h = _create(_cfg())
+    try:
+        ws = L.hymba_mixer_workspace_bytes(h, 1, 4)
+        for x, y, st, wsp in [(FAKE + 8, FAKE, None, FAKE), (FAKE, FAKE + 4, None, FAKE),
+                              (FAKE, FAKE, FAKE + 4, FAKE), (FAKE, FAKE, None, FAKE + 16)]:
+            with pytest.raises(L.HymbaError) as e:
+                L.hymba_mixer_prefill(h, x, 1, 4, y, None, st, wsp, ws, None)
+            assert e.value.status == L.HYMBA_ERR_INVALID_ARG
+        kv = L.hymba_kv()
+        kv.k_cache, kv.v_cache, kv.cache_len = FAKE + 2, FAKE, 16
+        with pytest.raises(L.HymbaError) as e:
+            L.hymba_mixer_decode(h, FAKE, FAKE, 1, FAKE, kv, FAKE, FAKE, 1 << 30, None)
+        assert e.value.status == L.HYMBA_ERR_INVALID_ARG
+        kv.k_cache = FAKE
+        for x, pos, st, wsp in [(FAKE + 2, FAKE, FAKE, FAKE), (FAKE, FAKE + 4, FAKE, FAKE),
+                                (FAKE, FAKE, FAKE + 8, FAKE), (FAKE, FAKE, FAKE, FAKE + 64)]:
+            with pytest.raises(L.HymbaError) as e:
+                L.hymba_mixer_decode(h, x, pos, 1, FAKE, kv, st, wsp, 1 << 30, None)
+            assert e.value.status == L.HYMBA_ERR_INVALID_ARG
+        with pytest.raises(L.HymbaError) as e:
+            L.hymba_layer_prepare(h, None, FAKE + 16, 1 << 30, None)
+        assert e.value.status == L.HYMBA_ERR_INVALID_ARG
+    finally:
+        L.hymba_layer_destroy(h)
+
+
 def test_bind_rules():
     prod = _create(_cfg(own_kv=1))
     cons = _create(_cfg(own_kv=0))
