@@ -637,19 +637,24 @@ hipError_t launch_kv_write(const KvWriteArgs<half_t>& a, hipStream_t s) { return
 hipError_t launch_decode_attn(const DecAttnArgs<float>& a, hipStream_t s) { return dec_dispatch(a, s); }
 hipError_t launch_decode_attn(const DecAttnArgs<half_t>& a, hipStream_t s) { return dec_dispatch(a, s); }
 
-// Splits per (sequence, KV head): enough for ~2048 workgroups (8 per CU), at
-// least one load round per split when the key range allows (the VALU kernel: 256 / lanes
-// per key row * kDecPasses keys; the MFMA kernel for 16-bit K/V of head dim 64: three of its
-// 64-key tiles -- 1152 ring keys then give 6 splits, 3840 one-wave workgroups, all resident at
-// once, 1 % faster per decode pair step than four tiles per split), never fewer than 64 keys per
-// split, at most kDecodeMaxSplits.  Longer splits run several rounds.
+// Splits per (sequence, KV head), never fewer than 64 keys per split, at most kDecodeMaxSplits.
+//  * MFMA kernel (16-bit K/V, head dim 64; one wave per workgroup): as few splits as give about
+//    seven workgroups per CU (1792 in all), each streaming up to 16 of its 64-key tiles.  The
+//    1152-key ring at B = 128 then takes 3 splits of 6 tiles, the 8193-key global cache at B = 8
+//    45 splits of 3 tiles.  Measured on the decode pairs against ~2048 workgroups with at most
+//    3 tiles per split (6 and 52 splits): 1.34 against 1.32 M tokens/s per layer for the ring,
+//    120-122 k against 116-117 k for the global decode; ~4096 workgroups were slower for both.
+//  * VALU kernel: enough for ~2048 workgroups (8 per CU), at least one load round per split
+//    (256 / lanes per key row * kDecPasses keys).
+// Longer splits run several rounds.
 int decode_attn_splits(int B, int n_kv_heads, int n_keys_max, int head_dim, int elem_bytes) {
   const int lpk = head_dim * elem_bytes / 16;
   if (lpk < 2 || lpk > 16 || B < 1 || n_kv_heads < 1) return -1;
   const bool mfma = elem_bytes == 2 && head_dim == attn::kHd;
-  const int64_t per_round = mfma ? 3 * attn::kKT : (int64_t)(kThreads / lpk) * kDecPasses;
   const int64_t pairs = (int64_t)B * n_kv_heads;
-  int64_t s = std::max<int64_t>(ceil_div(n_keys_max, per_round), ceil_div(2048, pairs));
+  int64_t s = mfma ? std::max<int64_t>(ceil_div(n_keys_max, 16 * attn::kKT), ceil_div(1792, pairs))
+                   : std::max<int64_t>(ceil_div(n_keys_max, (int64_t)(kThreads / lpk) * kDecPasses),
+                                       ceil_div(2048, pairs));
   s = std::min<int64_t>(s, std::max<int64_t>(1, ceil_div(n_keys_max, 64)));
   s = std::min<int64_t>(s, kDecodeMaxSplits);
   return static_cast<int>(std::max<int64_t>(s, 1));

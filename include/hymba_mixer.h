@@ -198,7 +198,7 @@ int32_t hymba_mixer_decode(hymba_layer* layer, const void* x_t, const int64_t* p
  * rounded up to 64, + 3*E + H*hd, all in the activation type, + 2*N fp32 for
  * bf16 layers) + B * H * splits * (hd + 2) * 4 bytes (splits <= 64, each
  * region rounded to 256 bytes); a call needing more than 32 MiB returns
- * HYMBA_ERR_WORKSPACE before any device work (about 395 sequences of the
+ * HYMBA_ERR_WORKSPACE before any device work (about 560 sequences of the
  * 1.5B-shaped layer fit).  Results equal hymba_mixer_decode's up to the order
  * of the projections' fp32 sums.  All calls on one GPU share its scratch and
  * it keeps the last call's contents: calls that overlap on one GPU (two
