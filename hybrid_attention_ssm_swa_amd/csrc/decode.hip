@@ -386,7 +386,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void de
   const int64_t weff = a.window > 0 ? a.window : C;
   const int64_t lo = p - weff + 1 > 0 ? p - weff + 1 : 0;
   const int nkeys = a.n_meta + static_cast<int>(p - lo + 1 > 0 ? p - lo + 1 : 0);
-  const int per = static_cast<int>(ceil_div(nkeys, a.splits));
+  // whole tiles per split (a partial tile costs a full one); trailing splits may be empty
+  const int per = static_cast<int>(ceil_div(ceil_div(nkeys, a.splits), kKT) * kKT);
   const int k0 = split * per;
   const int k1 = min(nkeys, k0 + per);
   const int lo_mod = static_cast<int>(lo % C);   // ring slot of the first window key
@@ -639,11 +640,15 @@ hipError_t launch_decode_attn(const DecAttnArgs<half_t>& a, hipStream_t s) { ret
 
 // Splits per (sequence, KV head), never fewer than 64 keys per split, at most kDecodeMaxSplits.
 //  * MFMA kernel (16-bit K/V, head dim 64; one wave per workgroup): as few splits as give about
-//    seven workgroups per CU (1792 in all), each streaming up to 16 of its 64-key tiles.  The
-//    1152-key ring at B = 128 then takes 3 splits of 6 tiles, the 8193-key global cache at B = 8
-//    45 splits of 3 tiles.  Measured on the decode pairs against ~2048 workgroups with at most
-//    3 tiles per split (6 and 52 splits): 1.34 against 1.32 M tokens/s per layer for the ring,
-//    120-122 k against 116-117 k for the global decode; ~4096 workgroups were slower for both.
+//    five workgroups per CU (1280 in all), each a whole number of its 64-key tiles, at most 16,
+//    and no split left empty at the longest key range.  The 1152-key ring at B = 128 then takes
+//    2 splits of 9 tiles, the 8193-key global cache at B = 8 27 splits of 5 tiles.  A split
+//    that ends in a nearly empty tile pays for the whole tile: with splits of ceil(keys / splits)
+//    keys the global decode measured 116-117 k tokens/s per layer at 32 splits (261 keys: 4
+//    tiles and 5 keys) and 120-122 k at 44 (190 keys, just under 3 tiles).  Measured against the
+//    earlier rule (~2048 workgroups, at most 3 tiles per split: 6 and 52 splits): 1.38 against
+//    1.32 M tokens/s per layer for the ring decode pair, 122-123 k against 116-117 k for the
+//    global decode; more workgroups (~4096) were slower for both.
 //  * VALU kernel: enough for ~2048 workgroups (8 per CU), at least one load round per split
 //    (256 / lanes per key row * kDecPasses keys).
 // Longer splits run several rounds.
@@ -652,9 +657,15 @@ int decode_attn_splits(int B, int n_kv_heads, int n_keys_max, int head_dim, int 
   if (lpk < 2 || lpk > 16 || B < 1 || n_kv_heads < 1) return -1;
   const bool mfma = elem_bytes == 2 && head_dim == attn::kHd;
   const int64_t pairs = (int64_t)B * n_kv_heads;
-  int64_t s = mfma ? std::max<int64_t>(ceil_div(n_keys_max, 16 * attn::kKT), ceil_div(1792, pairs))
-                   : std::max<int64_t>(ceil_div(n_keys_max, (int64_t)(kThreads / lpk) * kDecPasses),
-                                       ceil_div(2048, pairs));
+  int64_t s;
+  if (mfma) {
+    const int64_t tiles = std::max<int64_t>(1, ceil_div(n_keys_max, attn::kKT));
+    int64_t s0 = std::max<int64_t>(ceil_div(tiles, 16), ceil_div(1280, pairs));
+    s0 = std::min<int64_t>(s0, std::min<int64_t>(tiles, kDecodeMaxSplits));
+    s = ceil_div(tiles, ceil_div(tiles, s0));   // the fewest splits of that many tiles each
+  } else {
+    s = std::max<int64_t>(ceil_div(n_keys_max, (int64_t)(kThreads / lpk) * kDecPasses), ceil_div(2048, pairs));
+  }
   s = std::min<int64_t>(s, std::max<int64_t>(1, ceil_div(n_keys_max, 64)));
   s = std::min<int64_t>(s, kDecodeMaxSplits);
   return static_cast<int>(std::max<int64_t>(s, 1));
