@@ -562,6 +562,48 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecAttn
   Elem<T>::store(a.o + (int64_t)b * a.ld_o + h * hd + d, num / den);
 }
 
+// Eight splits or fewer: one thread per (sequence, head, dim), 256 / hd heads to a block, the
+// same single merge the kernel above makes with one group (so the same results).
+template <typename T>
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_few_kernel(DecAttnArgs<T> a) {
+  const int hd = a.head_dim;
+  const int64_t bh = (int64_t)blockIdx.x * (kCombineThreads / hd) + threadIdx.x / hd;
+  if (bh >= (int64_t)a.B * a.n_heads) return;
+  const int d = threadIdx.x % hd;
+  const float* part = a.part + bh * a.splits * (hd + 2);
+  float mv[8], ov[8], lv[8];
+  float mb = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    mv[j] = -INFINITY; ov[j] = 0.f; lv[j] = 0.f;
+    if (j < a.splits) {
+      const float* ps = part + (int64_t)j * (hd + 2);
+      mv[j] = ps[hd];
+      ov[j] = ps[d];
+      lv[j] = ps[hd + 1];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) mb = fmaxf(mb, mv[j]);
+  float num = 0.f, den = 0.f;
+  if (mb != -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < a.splits) {
+        const float w = fast_exp2(mv[j] - mb);
+        num = fmaf(w, ov[j], num);
+        den = fmaf(w, lv[j], den);
+      }
+    }
+  }
+  const int64_t b = bh / a.n_heads;
+  const int h = static_cast<int>(bh % a.n_heads);
+  Elem<T>::store(a.o + b * a.ld_o + h * hd + d, num / den);
+}
+
+template <typename T>
+hipError_t launch_combine(const DecAttnArgs<T>& a, hipStream_t s);
+
 // groups of head_dim threads: about one per 8 splits, at most kCombineThreads threads
 template <typename T>
 unsigned combine_threads(const DecAttnArgs<T>& a) {
@@ -619,15 +661,26 @@ hipError_t dec_dispatch(const DecAttnArgs<T>& a, hipStream_t s) {
     if (a.head_dim == 64) {
       e = dec_dispatch_mfma(a, s);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((decode_combine_kernel<T>), dim3(a.B * a.n_heads), dim3(combine_threads(a)), 0, s, a);
-      return hipGetLastError();
+      return launch_combine(a, s);
     }
   }
   if (a.head_dim == 64) e = dec_dispatch_hd<T, 64>(a, s);
   else if (a.head_dim == 32) e = dec_dispatch_hd<T, 32>(a, s);
   else return hipErrorInvalidValue;
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<T>), dim3(a.B * a.n_heads), dim3(combine_threads(a)), 0, s, a);
+  return launch_combine(a, s);
+}
+
+template <typename T>
+hipError_t launch_combine(const DecAttnArgs<T>& a, hipStream_t s) {
+  if (a.splits <= 8) {
+    const int per_block = kCombineThreads / a.head_dim;
+    hipLaunchKernelGGL((decode_combine_few_kernel<T>),
+                       dim3(static_cast<unsigned>(ceil_div((int64_t)a.B * a.n_heads, per_block))),
+                       dim3(kCombineThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((decode_combine_kernel<T>), dim3(a.B * a.n_heads), dim3(combine_threads(a)), 0, s, a);
+  }
   return hipGetLastError();
 }
 
