@@ -223,7 +223,7 @@ def timed(layers, fn, steps, warmup):
     return ms, ms_rec, [L.hymba_layer_profile_read(lay.handle) for lay in layers]
 
 
-def bench_prefill(name, steps, warmup, rope_base=0.0):
+def bench_prefill(name, steps, warmup, rope_base=0.0, gemm_backend=0):   # 0: library, 1: tiled
     import torch
     from hybrid_attention_ssm_swa_amd.layer import MixerLayer, make_kv, upload
     from hymba_synth import workload
@@ -235,6 +235,7 @@ def bench_prefill(name, steps, warmup, rope_base=0.0):
     log(f"[bench] {cfg.name} inputs generated in {time.time() - t:.1f}s")
     dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
     layer = MixerLayer(s, case.params)
+    layer.set_gemm(gemm_backend)
     x = upload(case.x, dt, "cuda")
     keep = []
     kv = None
@@ -355,6 +356,35 @@ def bench_attention_alone(steps, warmup):
     flops = 4.0 * hd * Hq * B * visible_keys(s, T)
     return {"kernel": "swa_meta_attn", "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
             "frac": flops / (ms * 1e-3) / PEAK_BF16}
+
+
+def bench_gemm_alone(steps, warmup):
+    """The tiled projection GEMM alone on the 8K prefill input projection of the 1.5B KV-consumer
+    layer (16 x 8192 rows of bf16 x, 11232 columns of bf16 W_in, K = 1600; P in fp16 at its padded
+    row stride 11264, the 32 B/C columns also in fp32), through the per-kernel entry point.  For
+    counter passes: the only launches are this kernel's."""
+    import torch
+    from hybrid_attention_ssm_swa_amd import _lib as L
+    from hymba_synth import SWA_8K, workload
+    s = workload(SWA_8K).shape
+    M, N, K = 16 * 8192, s.n_in, s.d_model
+    ldy = (N + 63) // 64 * 64
+    g = torch.Generator(device="cuda").manual_seed(0)
+    x = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+    w = (torch.randn(N, K, device="cuda", generator=g) / K ** 0.5).to(torch.bfloat16)
+    y = torch.empty(M, ldy, device="cuda", dtype=torch.half)
+    y32 = torch.empty(M, 2 * s.d_state, device="cuda", dtype=torch.float32)
+    c0 = N - 2 * s.d_state
+    st = torch.cuda.current_stream().cuda_stream
+    fn = lambda i: L.hymba_kernel_gemm_tiles(L.HYMBA_BF16, L.HYMBA_F16, w.data_ptr(), K, x.data_ptr(), K,  # noqa
+                                             y.data_ptr(), ldy, y32.data_ptr(), 2 * s.d_state, c0, N, M, N, K, st)
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    ms = _time_loop(fn, steps)
+    flops = 2.0 * M * N * K
+    return {"kernel": "gemm_tiles in_proj", "M": M, "N": N, "K": K, "ms": ms,
+            "tflops": flops / (ms * 1e-3) / 1e12, "frac": flops / (ms * 1e-3) / PEAK_BF16}
 
 
 def griffin_work(shape, B, T):
@@ -819,6 +849,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--main-only", action="store_true", help="time only the 8K prefill workload")
+    ap.add_argument("--tiled-gemm", action="store_true",
+                    help="prefill projections on the hand-written tiled matrix-core GEMM instead of hipBLASLt")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain copy kernel of known size (for scaling HBM counters)")
     ap.add_argument("--summarize-rocprof", metavar="TRACE_DIR",
@@ -829,6 +861,8 @@ def main():
     ap.add_argument("--profile-cmd", help="with --summarize-rocprof: the profiled command, for the header")
     ap.add_argument("--attention-only", action="store_true",
                     help="time only swa_meta_attn at the 8K SWA shape (K/V handed in), through the kernel entry")
+    ap.add_argument("--gemm-only", action="store_true",
+                    help="time the tiled projection GEMM alone on the 8K input projection shape")
     ap.add_argument("--griffin-only", action="store_true",
                     help="time only the Griffin block (8K prefill and B=128 decode); prints its JSON record")
     ap.add_argument("--summarize-griffin", metavar="TRACE_DIR",
@@ -899,10 +933,13 @@ def main():
     if args.decode_only:
         print(json.dumps(bench_decode(DECODE_B128, args.steps, args.warmup)), flush=True)
         return
+    if args.gemm_only:
+        print(json.dumps(bench_gemm_alone(args.steps, args.warmup)), flush=True)
+        return
     if args.attention_only:
         print(json.dumps(bench_attention_alone(args.steps, args.warmup)), flush=True)
         return
-    main_run = bench_prefill(SWA_8K, args.steps, args.warmup)
+    main_run = bench_prefill(SWA_8K, args.steps, args.warmup, gemm_backend=1 if args.tiled_gemm else 0)
     log(f"[bench] 8K SWA prefill: {main_run['tokens_per_s']:.0f} tok/s, {main_run['ms_per_step']:.3f} ms/step")
     workloads = {}
     if not args.main_only:

@@ -25,6 +25,8 @@ HYMBA_ERR_RANGE = -6
 HYMBA_F32 = 0
 HYMBA_BF16 = 1
 HYMBA_F16 = 2
+HYMBA_GEMM_LIBRARY = 0
+HYMBA_GEMM_TILED = 1
 
 EXPORTED = [
     "hymba_layer_persistent_bytes", "hymba_layer_create", "hymba_layer_destroy",
@@ -35,6 +37,7 @@ EXPORTED = [
     "hymba_kernel_gemm_rows_workspace", "hymba_kernel_selective_scan_workspace",
     "hymba_layer_profile", "hymba_layer_profile_read", "hymba_stage_name",
     "hymba_layer_check", "hymba_layer_set_overlap", "hymba_mixer_decode_static",
+    "hymba_kernel_gemm_tiles", "hymba_layer_set_gemm",
     "griffin_block_persistent_bytes", "griffin_block_prepare", "griffin_workspace_bytes",
     "griffin_block_prefill", "griffin_block_decode",
 ]
@@ -119,6 +122,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "hymba_kernel_gemm_rows": (c_int32, [c_int32, c_int32, c_int32, P, c_int64, P, c_int64, P, c_int64, P,
                                              c_int64, c_int32, c_int32, c_int32, c_int32, c_int32, P, c_size_t, P]),
         "hymba_kernel_gemm_rows_workspace": (c_size_t, [c_int32, c_int32, c_int32]),
+        "hymba_kernel_gemm_tiles": (c_int32, [c_int32, c_int32, P, c_int64, P, c_int64, P, c_int64, P, c_int64,
+                                              c_int32, c_int32, c_int64, c_int32, c_int32, P]),
+        "hymba_layer_set_gemm": (c_int32, [P, c_int32]),
         "hymba_kernel_selective_scan_workspace": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
         "hymba_layer_profile": (c_int32, [P, c_int32]),
         "hymba_layer_profile_read": (c_int32, [P, POINTER(c_float), c_int32]),
@@ -245,6 +251,16 @@ def hymba_kernel_gemm_rows(w_dtype, x_dtype, y_dtype, w, ldw, x, ldx, y, ldy, y3
                            workspace, workspace_bytes, stream) -> None:
     _check(load_library().hymba_kernel_gemm_rows(w_dtype, x_dtype, y_dtype, w, ldw, x, ldx, y, ldy, y32, ldy32,
                                                  c0, c1, M, N, K, workspace, workspace_bytes, stream))
+
+
+def hymba_kernel_gemm_tiles(in_dtype, y_dtype, w, ldw, x, ldx, y, ldy, y32, ldy32, c0, c1, M, N, K,
+                            stream) -> None:
+    _check(load_library().hymba_kernel_gemm_tiles(in_dtype, y_dtype, w, ldw, x, ldx, y, ldy, y32, ldy32, c0, c1,
+                                                  M, N, K, stream))
+
+
+def hymba_layer_set_gemm(layer: int, backend: int) -> None:
+    _check(load_library().hymba_layer_set_gemm(layer, backend))
 
 
 def hymba_kernel_gemm_rows_workspace(M: int, N: int, K: int) -> int:

@@ -28,6 +28,7 @@ SOURCES = [
     "decode.hip",
     "gemm_f32.hip",
     "gemm_skinny.hip",
+    "gemm_mfma.hip",
     "convert.hip",
     "griffin.hip",
     "griffin_api.cpp",

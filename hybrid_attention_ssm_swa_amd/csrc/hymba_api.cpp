@@ -57,6 +57,7 @@ struct hymba_layer {
   const hymba_layer* consumer = nullptr;   // producer: its bound consumer (pairs only)
   const void* prep_kmeta = nullptr;        // consumer: meta K/V used by the last prepare
   const void* prep_vmeta = nullptr;
+  int gemm_backend = HYMBA_GEMM_LIBRARY;   // bf16 prefill projections (HYMBA_GEMM_LIBRARY or _TILED)
   // column offsets of the shared projection
   int64_t n_in = 0, ld_p = 0, off_k = 0, off_v = 0, off_u = 0, off_z = 0, off_dt = 0, off_b = 0;
   // stage timing: a pool of begin/end event pairs, one pair per timed interval of each hot call
@@ -275,6 +276,13 @@ int32_t project(const hymba_layer& L, const void* X, int64_t ldx, const void* W,
     HIP_TRY(e, "projection (few rows) launch");
     return HYMBA_OK;
   }
+  if (is_bf16(L.cfg) && L.gemm_backend == HYMBA_GEMM_TILED) {   // many rows: the tiled matrix-core GEMM
+    MfmaGemmArgs a{X, ldx, W, ldw, Y, ldy, nullptr, 0, 0, 0, rows, static_cast<int>(out), static_cast<int>(in)};
+    const int t = bf16_out ? GT_BF16 : GT_F16;
+    if (!mfma_gemm_shape_ok(a)) return fail(HYMBA_ERR_UNSUPPORTED, "projection GEMM: unsupported shape or alignment");
+    HIP_TRY(launch_mfma_gemm(a, t, t, s), "projection GEMM launch");
+    return HYMBA_OK;
+  }
   if (is_bf16(L.cfg)) {
     const char* err = nullptr;
     const GemmType t = bf16_out ? GT_BF16 : GT_F16;
@@ -333,6 +341,17 @@ int32_t in_projection(const hymba_layer& L, const void* x, int64_t rows, char* w
                                          static_cast<int>(L.off_b), static_cast<int>(L.off_b + 2 * c.d_state),
                                          static_cast<int>(rows), static_cast<int>(L.n_in), c.d_model};
     HIP_TRY(launch_skinny_gemm(a, s), "input projection (few rows) launch");
+    return HYMBA_OK;
+  }
+  if (is_bf16(c) && L.gemm_backend == HYMBA_GEMM_TILED) {
+    // many rows: the tiled GEMM multiplies bf16 x and W_in directly, writes P in fp16 and the
+    // B/C columns in fp32 from its accumulator
+    StageTimer st(L, ST_IN_PROJ, s);
+    MfmaGemmArgs a{x, c.d_model, L.w.w_in, c.d_model, ws + wl.P, L.ld_p, bc32, 2 * c.d_state,
+                   static_cast<int>(L.off_b), static_cast<int>(L.off_b + 2 * c.d_state), rows,
+                   static_cast<int>(L.n_in), c.d_model};
+    if (!mfma_gemm_shape_ok(a)) return fail(HYMBA_ERR_UNSUPPORTED, "input projection: unsupported shape or alignment");
+    HIP_TRY(launch_mfma_gemm(a, GT_BF16, GT_F16, s), "input projection launch");
     return HYMBA_OK;
   }
   if (is_bf16(c)) {
@@ -911,6 +930,14 @@ int32_t hymba_layer_set_overlap(hymba_layer* L, int32_t enable) {
   return HYMBA_OK;
 }
 
+int32_t hymba_layer_set_gemm(hymba_layer* layer, int32_t backend) {
+  if (!layer) return fail(HYMBA_ERR_INVALID_ARG, "NULL layer");
+  if (backend != HYMBA_GEMM_LIBRARY && backend != HYMBA_GEMM_TILED)
+    return fail(HYMBA_ERR_INVALID_ARG, "backend must be HYMBA_GEMM_LIBRARY or HYMBA_GEMM_TILED");
+  layer->gemm_backend = backend;
+  return HYMBA_OK;
+}
+
 int32_t hymba_layer_profile(hymba_layer* L, int32_t enable) {
   if (!L) return fail(HYMBA_ERR_INVALID_ARG, "layer is NULL");
   if (!enable) {
@@ -1072,6 +1099,25 @@ int32_t hymba_kernel_epilogue(int32_t dtype, const void* ao, int64_t ld_ao, cons
 size_t hymba_kernel_selective_scan_workspace(int32_t B, int32_t T, int32_t E, int32_t N) {
   if (B < 1 || T < 1 || E < 1 || (N != 8 && N != 16)) return 0;
   return align_up((size_t)E * N * 4) + scan_segment_bytes(B, T, E, N);
+}
+
+int32_t hymba_kernel_gemm_tiles(int32_t in_dtype, int32_t y_dtype, const void* w, int64_t ldw, const void* x,
+                                int64_t ldx, void* y, int64_t ldy, float* y32, int64_t ldy32, int32_t c0, int32_t c1,
+                                int64_t M, int32_t N, int32_t K, void* stream) {
+  if (!w || !x || !y) return fail(HYMBA_ERR_INVALID_ARG, "NULL pointer");
+  if (M < 0 || N < 1 || K < 1) return fail(HYMBA_ERR_INVALID_ARG, "bad dimensions");
+  if ((in_dtype != HYMBA_F16 && in_dtype != HYMBA_BF16) || (y_dtype != HYMBA_F16 && y_dtype != HYMBA_BF16))
+    return fail(HYMBA_ERR_UNSUPPORTED, "types: x and w HYMBA_F16 or HYMBA_BF16, y HYMBA_F16 or HYMBA_BF16");
+  if (N % 4 || K % 8) return fail(HYMBA_ERR_UNSUPPORTED, "N must be a multiple of 4 and K of 8");
+  MfmaGemmArgs a{x, ldx, w, ldw, y, ldy, y32, ldy32, c0, c1, M, N, K};
+  if (!mfma_gemm_shape_ok(a))
+    return fail(HYMBA_ERR_INVALID_ARG, "strides: ldw, ldx >= K, multiples of 8 (16-byte aligned x, w); ldy >= N, "
+                                       "a multiple of 4 (8-byte aligned y); y32: 0 <= c0 <= c1 <= N multiples of 4, "
+                                       "ldy32 >= c1 - c0 (of 4), 16-byte aligned");
+  if (M == 0) return HYMBA_OK;
+  const int ti = in_dtype == HYMBA_BF16 ? GT_BF16 : GT_F16, to = y_dtype == HYMBA_BF16 ? GT_BF16 : GT_F16;
+  HIP_TRY(launch_mfma_gemm(a, ti, to, static_cast<hipStream_t>(stream)), "tiled GEMM launch");
+  return HYMBA_OK;
 }
 
 size_t hymba_kernel_gemm_rows_workspace(int32_t M, int32_t N, int32_t K) {

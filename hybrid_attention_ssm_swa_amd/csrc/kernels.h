@@ -210,6 +210,22 @@ inline bool skinny_fits(int64_t rows, int64_t n, int64_t k) {
   return rows > 0 && rows <= kSkinnyMaxRows && n * k * 2 <= kSkinnyMaxWeightBytes;
 }
 
+// ---- many-row projection GEMM on the matrix cores ----------------------------------
+// Y[m, n] = sum_k X[m, k] W[n, k] (16-bit X and W of one type, fp32 accumulation, 16-bit Y);
+// the columns [c0, c1) are also written in fp32 to y32[m, n - c0] when y32 is set.
+// K % 8 == 0, N % 4 == 0, ldx and ldw multiples of 8, ldy of 4, 16-byte aligned X and W,
+// 8-byte aligned Y; c0, c1, ldy32 multiples of 4 and y32 16-byte aligned.
+struct MfmaGemmArgs {
+  const void* x; int64_t ldx;
+  const void* w; int64_t ldw;
+  void* y; int64_t ldy;
+  float* y32; int64_t ldy32; int c0; int c1;
+  int64_t M; int N; int K;
+};
+bool mfma_gemm_shape_ok(const MfmaGemmArgs& a);
+// in_type, out_type: 0 = fp16, 1 = bf16 (the GEMM type codes of the library path)
+hipError_t launch_mfma_gemm(const MfmaGemmArgs& a, int in_type, int out_type, hipStream_t s);
+
 // ---- input conversion fused with the fp32 B/C columns -------------------------------
 // x16 [rows, d] = fp16(x [rows, d] bf16); bc [rows, nbc] fp32 = x . wbc^T (wbc fp16 [nbc, d],
 // nbc = 2N = 16 or 32).  d, ldx, ldx16, ldw multiples of 8; 16-byte aligned rows.

@@ -141,6 +141,11 @@ class MixerLayer:
     def set_overlap(self, enable: bool) -> None:
         L.hymba_layer_set_overlap(self.handle, enable)
 
+    def set_gemm(self, backend: int) -> None:
+        """bf16 prefill projections: HYMBA_GEMM_LIBRARY (0, hipBLASLt, the default) or HYMBA_GEMM_TILED
+        (1, the hand-written tiled matrix-core GEMM)."""
+        L.hymba_layer_set_gemm(self.handle, backend)
+
     def meta_outputs(self):
         """(k_meta, v_meta, h_meta, y_meta) as device tensors viewing the persistent buffer."""
         s = self.shape

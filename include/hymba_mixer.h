@@ -260,6 +260,19 @@ int32_t hymba_layer_check(hymba_layer* layer, void* stream);
  * so stage timings measure each kernel alone.  Results are identical either
  * way.  Host only. */
 int32_t hymba_layer_set_overlap(hymba_layer* layer, int32_t enable);
+/* Prefill projections of a bf16 layer (more than 256 rows).
+ * HYMBA_GEMM_LIBRARY (0, the default): hipBLASLt on fp16 copies, x converted
+ * by a separate pass that also computes the fp32 B/C columns.
+ * HYMBA_GEMM_TILED (1): the hand-written tiled matrix-core GEMM of
+ * hymba_kernel_gemm_tiles, which multiplies the bf16 x and W_in directly and
+ * writes the fp32 B/C columns from its accumulator (no conversion pass).
+ * Both round the same exact products' fp32 sums; results differ only in
+ * summation order.  The library is the default because it is faster on
+ * every prefill shape measured (8K input projection 3.5 ms against 4.4 ms).
+ * Host only; returns HYMBA_ERR_INVALID_ARG for other values. */
+#define HYMBA_GEMM_LIBRARY 0
+#define HYMBA_GEMM_TILED 1
+int32_t hymba_layer_set_gemm(hymba_layer* layer, int32_t backend);
 int32_t hymba_layer_profile(hymba_layer* layer, int32_t enable);
 int32_t hymba_layer_profile_read(hymba_layer* layer, float* stage_ms, int32_t n);
 const char* hymba_stage_name(int32_t stage);
@@ -330,6 +343,24 @@ int32_t hymba_kernel_gemm_rows(int32_t w_dtype, int32_t x_dtype, int32_t y_dtype
                                float* y32, int64_t ldy32, int32_t c0, int32_t c1, int32_t M,
                                int32_t N, int32_t K, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/* Many-row projection, the tiled matrix-core GEMM bf16 layers use for more
+ * than 256 rows (prefill): y[M, N] = x[M, K] . w[N, K]^T with fp32
+ * accumulation and one rounding to y's type ([H] §2.1 Eq. 3: the shared
+ * input projection, W_O and the output projection; [G] §3.3: the O(T D^2)
+ * linear layers).  in_dtype names x and w (both HYMBA_F16 or both
+ * HYMBA_BF16: the products are taken in that type, bf16 x is not converted);
+ * y_dtype is HYMBA_F16 or HYMBA_BF16.  Row-major; x, w 16-byte aligned with
+ * ldx, ldw multiples of 8 and >= K; y 8-byte aligned with ldy a multiple of
+ * 4 and >= N; N % 4 == 0, K % 8 == 0, M >= 0.  y32 (fp32, 16-byte aligned,
+ * row stride ldy32 a multiple of 4) or NULL: also receives the columns
+ * [c0, c1) (multiples of 4) as y32[m, c - c0], straight from the fp32
+ * accumulator.  No workspace.  Deterministic: each output's K sum is taken
+ * in one fixed order.  Asynchronous on `stream`. */
+int32_t hymba_kernel_gemm_tiles(int32_t in_dtype, int32_t y_dtype, const void* w, int64_t ldw,
+                                const void* x, int64_t ldx, void* y, int64_t ldy, float* y32,
+                                int64_t ldy32, int32_t c0, int32_t c1, int64_t M, int32_t N,
+                                int32_t K, void* stream);
 
 /* Workspace bytes hymba_kernel_gemm_rows needs for [M, N, K]: 0, since the kernel
  * never splits K across workgroups (kept so that callers size it the same way if

@@ -388,6 +388,34 @@ def test_gemm_rows_rejects_bad_arguments():
     assert L.hymba_kernel_gemm_rows_workspace(128, 16384, 512) == 0
 
 
+def test_gemm_tiles_rejects_bad_arguments():
+    """Validated before any device work (fake aligned pointers)."""
+    args = dict(w=FAKE, ldw=8, x=FAKE, ldx=8, y=FAKE, ldy=8, y32=None, ldy32=0, c0=0, c1=0, M=1, N=8, K=8)
+    cases = [
+        (dict(types=(L.HYMBA_F32, L.HYMBA_F16)), L.HYMBA_ERR_UNSUPPORTED),
+        (dict(types=(L.HYMBA_BF16, L.HYMBA_F32)), L.HYMBA_ERR_UNSUPPORTED),
+        (dict(N=6), L.HYMBA_ERR_UNSUPPORTED),
+        (dict(K=12, ldw=16, ldx=16), L.HYMBA_ERR_UNSUPPORTED),
+        (dict(ldx=4), L.HYMBA_ERR_INVALID_ARG),
+        (dict(ldy=6), L.HYMBA_ERR_INVALID_ARG),
+        (dict(x=FAKE + 8), L.HYMBA_ERR_INVALID_ARG),
+        (dict(y=FAKE + 4), L.HYMBA_ERR_INVALID_ARG),
+        (dict(y32=FAKE, ldy32=4, c0=0, c1=8), L.HYMBA_ERR_INVALID_ARG),   # ldy32 < c1 - c0
+        (dict(y32=FAKE, ldy32=8, c0=2, c1=6), L.HYMBA_ERR_INVALID_ARG),   # c0, c1 not multiples of 4
+        (dict(y=None), L.HYMBA_ERR_INVALID_ARG),
+        (dict(M=-1), L.HYMBA_ERR_INVALID_ARG),
+    ]
+    for kw, code in cases:
+        a = dict(args, types=(L.HYMBA_BF16, L.HYMBA_F16))
+        a.update(kw)
+        with pytest.raises(L.HymbaError) as e:
+            L.hymba_kernel_gemm_tiles(*a["types"], a["w"], a["ldw"], a["x"], a["ldx"], a["y"], a["ldy"], a["y32"],
+                                      a["ldy32"], a["c0"], a["c1"], a["M"], a["N"], a["K"], None)
+        assert e.value.status == code, (kw, L.hymba_last_error())
+    # zero rows: nothing to do
+    L.hymba_kernel_gemm_tiles(L.HYMBA_F16, L.HYMBA_F16, FAKE, 8, FAKE, 8, FAKE, 8, None, 0, 0, 0, 0, 8, 8, None)
+
+
 def test_scan_workspace_sizes():
     """The scan's workspace: the scaled A (E*N fp32, 256-byte aligned), plus (S - 1) segment
     summaries of B*E*(N + 1) fp32 when too few channel groups would fill the GPU: S segments of a
@@ -411,11 +439,17 @@ def test_check_and_overlap_calls():
     lib = L.load_library()
     assert lib.hymba_layer_check(None, None) == L.HYMBA_ERR_INVALID_ARG
     assert lib.hymba_layer_set_overlap(None, 1) == L.HYMBA_ERR_INVALID_ARG
+    assert lib.hymba_layer_set_gemm(None, 0) == L.HYMBA_ERR_INVALID_ARG
     assert H.hymba_status_string(L.HYMBA_ERR_RANGE) == "HYMBA_ERR_RANGE"
     h = _create(_cfg())
     try:
         L.hymba_layer_set_overlap(h, False)     # host only
         L.hymba_layer_set_overlap(h, True)
+        L.hymba_layer_set_gemm(h, L.HYMBA_GEMM_TILED)
+        L.hymba_layer_set_gemm(h, L.HYMBA_GEMM_LIBRARY)
+        with pytest.raises(L.HymbaError) as e:
+            L.hymba_layer_set_gemm(h, 2)
+        assert e.value.status == L.HYMBA_ERR_INVALID_ARG
         L.hymba_layer_check(h, None)            # nothing has run on the device: no device call, OK
     finally:
         L.hymba_layer_destroy(h)

@@ -13,6 +13,7 @@ import torch
 from hymba_synth import (DECODE_B128, GLOBAL_8K, ABLATION_300M, SWA_8K, TINY_F32, LayerShape, make_decode_case,
                          make_prefill_case, workload)
 from hymba_synth.generate import make_config_case
+from hybrid_attention_ssm_swa_amd import _lib as H
 from oracle import hymba_oracle as orc
 
 from gpu_util import MixerLayer, act, announce, check, check_stored, dev, host, make_kv
@@ -20,9 +21,11 @@ from gpu_util import MixerLayer, act, announce, check, check_stored, dev, host, 
 pytestmark = pytest.mark.gpu
 
 
-def _prefill_gpu(case, layer=None, state=False, kv_extra=None):
+def _prefill_gpu(case, layer=None, state=False, kv_extra=None, gemm=None):
     s = case.shape
     layer = layer or MixerLayer(s, case.params)
+    if gemm is not None:
+        layer.set_gemm(gemm)
     x = dev(case.x, s.dtype)
     kv = None
     keep = []
@@ -38,8 +41,8 @@ def _prefill_gpu(case, layer=None, state=False, kv_extra=None):
     return layer, host(y), (host(st) if state else None)
 
 
-def _check_prefill(case, seqs, dtype):
-    layer, y, st = _prefill_gpu(case, state=True)
+def _check_prefill(case, seqs, dtype, gemm=None):
+    layer, y, st = _prefill_gpu(case, state=True, gemm=gemm)
     outs = orc.prefill_batch(case, seqs)
     for b in seqs:
         check_stored(f"Y[b={b}]", y[b], outs[b].Y, dtype)
@@ -67,6 +70,18 @@ def test_small_layer_prefill(shape, B, T):
     announce(f"small prefill {shape} B={B} T={T}")
     case = make_prefill_case(shape, B, T, seed=7 + T)
     _check_prefill(case, range(B), shape.dtype)
+
+
+@pytest.mark.parametrize("shape,B,T", [
+    (SMALL_BF16, 3, 200),
+    (SMALL_BF16.with_(rope_base=10000.0, own_kv=False), 2, 150),
+    (SMALL_BF16.with_(window=0, n_meta=0), 2, 333),
+])
+def test_small_layer_prefill_tiled_gemm(shape, B, T):
+    """The prefill projections on the hand-written tiled GEMM (more than 256 rows each)."""
+    announce(f"small prefill, tiled GEMM {shape} B={B} T={T}")
+    case = make_prefill_case(shape, B, T, seed=17 + T)
+    _check_prefill(case, range(B), shape.dtype, gemm=H.HYMBA_GEMM_TILED)
 
 
 def test_meta_prefix_outputs():
@@ -99,6 +114,12 @@ def test_config1_full_size():
 def test_config2_full_size_sampled():
     announce("1.5B SWA KV-consumer layer, 16x8192, full size, sequences 0 and 15")
     _check_prefill(make_config_case(SWA_8K), [0, 15], "bf16")
+
+
+@pytest.mark.parametrize("name,seqs", [(SWA_8K, [0, 15]), (ABLATION_300M, [0, 7])])
+def test_full_size_tiled_gemm(name, seqs):
+    announce(f"{name}, full size, prefill projections on the tiled GEMM, sequences {seqs}")
+    _check_prefill(make_config_case(name), seqs, "bf16", gemm=H.HYMBA_GEMM_TILED)
 
 
 def test_config3_full_size_sampled():
