@@ -154,7 +154,7 @@ struct Loads {
   int sx, sw, k0;    // pass strides and the step's first element
 };
 
-template <typename AT, bool READ, bool STORE, bool LOAD>
+template <typename AT, bool READ, int STORE, bool LOAD>
 __device__ __forceinline__ void slice_slots(const Frags& f, f32x16_t (&acc)[4][4], const Stage& rs, int wrow,
                                             int xrow, int kk, Frags& nf, Stage& ws, int tid, Chunk (&rx)[kPasses],
                                             Chunk (&rw)[kPasses], const Loads& ld) {
@@ -173,12 +173,14 @@ __device__ __forceinline__ void slice_slots(const Frags& f, f32x16_t (&acc)[4][4
         else nf.a[x] = *reinterpret_cast<const Chunk*>(&rs.w[(wrow ^ (16 * kk)) + x * 32 * kStr]);
       }
     }
-    if constexpr (STORE) {
-      const int p = q / 2;
-      if (q % 2 == 0)
-        *reinterpret_cast<uint4*>(&ws.x[o + kRowsPerPass * p * kStr]) = make_uint4(rx[p].x, rx[p].y, rx[p].z, rx[p].w);
-      else
-        *reinterpret_cast<uint4*>(&ws.w[o + kRowsPerPass * p * kStr]) = make_uint4(rw[p].x, rw[p].y, rw[p].z, rw[p].w);
+    if constexpr (STORE > 0) {
+      if (q % 2 == 0) {   // chunk 8 (STORE - 1) + q / 2 of the prefetched step: x and w alternate
+        const int qq = (STORE - 1) * 8 + q / 2, p = qq / 2;
+        if (qq % 2 == 0)
+          *reinterpret_cast<uint4*>(&ws.x[o + kRowsPerPass * p * kStr]) = make_uint4(rx[p].x, rx[p].y, rx[p].z, rx[p].w);
+        else
+          *reinterpret_cast<uint4*>(&ws.w[o + kRowsPerPass * p * kStr]) = make_uint4(rw[p].x, rw[p].y, rw[p].z, rw[p].w);
+      }
     }
     if constexpr (LOAD) {
       const int p = q / 2;
@@ -228,9 +230,9 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(MfmaGemmArgs a) {
 
   // Pipeline per K step s (stage s % 2 in LDS; the chunks of steps s + 1 and s + 2 in two
   // register sets, set (s + 1) % 2 holding step s + 1):
-  //   slices 0, 1: products beside the fragment reads of the next slice;
-  //   slice 2: products beside the reads of slice 3 and the stores of step s + 1 to the other
-  //     stage (free: every wave passed the previous barrier after its last read of it);
+  //   slice 0: products beside the fragment reads of the next slice;
+  //   slices 1, 2: products beside the reads of the next slice and the stores of step s + 1 to
+  //     the other stage (free: every wave passed the previous barrier after its last read of it);
   //   barrier;
   //   slice 3: products beside the reads of step s + 1's slice 0 and the global loads of
   //     step s + 3 into the set just stored.
@@ -261,11 +263,11 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(MfmaGemmArgs a) {
     const Stage& st = lds[s & 1];
     Stage& nx = lds[(s + 1) & 1];
     const Loads ld = loads_of(s + 3);
-    slice_slots<AT, true, false, false>(f0, acc, st, wrow, xrow, 1, f1, nx, tid, rx, rw, ld);
-    slice_slots<AT, true, false, false>(f1, acc, st, wrow, xrow, 2, f0, nx, tid, rx, rw, ld);
-    slice_slots<AT, true, true, false>(f0, acc, st, wrow, xrow, 3, f1, nx, tid, rx, rw, ld);
+    slice_slots<AT, true, 0, false>(f0, acc, st, wrow, xrow, 1, f1, nx, tid, rx, rw, ld);
+    slice_slots<AT, true, 1, false>(f1, acc, st, wrow, xrow, 2, f0, nx, tid, rx, rw, ld);
+    slice_slots<AT, true, 2, false>(f0, acc, st, wrow, xrow, 3, f1, nx, tid, rx, rw, ld);
     __syncthreads();
-    slice_slots<AT, true, false, true>(f1, acc, nx, wrow, xrow, 0, f0, nx, tid, rx, rw, ld);
+    slice_slots<AT, true, 0, true>(f1, acc, nx, wrow, xrow, 0, f0, nx, tid, rx, rw, ld);
   };
   int s = 0;
   for (; s + 1 < steps; s += 2) {
