@@ -243,8 +243,9 @@ __global__ __launch_bounds__(64 * (N / NS)) void selective_scan_kernel(
 }
 
 // Decode: one token per sequence.  N/4 consecutive lanes share a channel, each
-// owning 4 states (one 16-byte state load and store); y is reduced across them.
-// grid (ceil(E * N/4 / 256), B): no division by a runtime size in the index math.
+// owning 4 states of two sequences (two 16-byte state loads in flight, then the two updates
+// and stores); y is reduced across the lanes of a channel.
+// grid (ceil(E * N/4 / 256), ceil(B / 2)): no division by a runtime size in the index math.
 // kVec: the lane's 4 B and 4 C values come as two vector loads (the dispatcher
 // checks their alignment) instead of eight scalar ones.
 template <typename T> struct Four;
@@ -258,49 +259,62 @@ template <> struct Four<float> {
 template <typename T, int N, bool kVec>
 __global__ __launch_bounds__(256) void ssm_step_kernel(StepArgs<T> a) {
   constexpr int LPC = N / 4;
+  constexpr int RB = 2;   // sequences per thread: both states' loads are in flight together
   const int i = blockIdx.x * blockDim.x + threadIdx.x;   // lane within the sequence
   const bool active = i < a.E * LPC;
   const int i2 = active ? i : a.E * LPC - 1;
   const int q = i2 % LPC, c = i2 / LPC;
-  const int64_t b = blockIdx.y;
-  const int64_t ch = b * a.E + c;
-  const float* row = a.bc + b * a.ld_bc;
-  const float uv = Elem<T>::load(a.u + b * a.ld + c);
-  const float dv = Elem<T>::load(a.dt + b * a.ld + c);
-  const float delta = softplus_f(dv + a.dt_bias[c]);
-  const float du = delta * uv;
-  float4* hp = reinterpret_cast<float4*>(a.h + ch * N + 4 * q);
+  const int64_t b0 = (int64_t)blockIdx.y * RB;
+  // the second sequence of the last block row may not exist: it then repeats the first, unstored
+  const bool has[RB] = {true, b0 + 1 < a.B};
+  int64_t bs[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) bs[r] = has[r] ? b0 + r : b0;
   // The state is read and written once per step with non-temporal hints: written normally, its
   // 26 MB per 1.5B layer and 128 sequences would sit dirty in the 256 MB MALL and be written back
   // to HBM while the next kernels stream their K/V caches (the ring-decode pair step: 1.20 ->
   // 1.245 M tokens/s per layer, the producer's attention 45.8 -> 40.4 us in the step).
-  const f32x4_t hv4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(hp));
-  const float4 hv = make_float4(hv4[0], hv4[1], hv4[2], hv4[3]);
+  f32x4_t hv[RB];
+  float uv[RB], dv[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    hv[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(a.h + (bs[r] * a.E + c) * N + 4 * q));
+    uv[r] = Elem<T>::load(a.u + bs[r] * a.ld + c);
+    dv[r] = Elem<T>::load(a.dt + bs[r] * a.ld + c);
+  }
   const float4 a2 = *reinterpret_cast<const float4*>(a.A2 + (int64_t)c * N + 4 * q);
-  float hs[4] = {hv.x, hv.y, hv.z, hv.w};
   const float a2s[4] = {a2.x, a2.y, a2.z, a2.w};
-  float bn[4], cn[4];
-  if constexpr (kVec) {
-    Four<float>::load(row + 4 * q, bn);
-    Four<float>::load(row + N + 4 * q, cn);
-  } else {
+  const float bias = a.dt_bias[c], dskip = a.D[c];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const float* row = a.bc + bs[r] * a.ld_bc;
+    const float delta = softplus_f(dv[r] + bias);
+    const float du = delta * uv[r];
+    float bn[4], cn[4];
+    if constexpr (kVec) {
+      Four<float>::load(row + 4 * q, bn);
+      Four<float>::load(row + N + 4 * q, cn);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bn[j] = row[4 * q + j];
+        cn[j] = row[N + 4 * q + j];
+      }
+    }
+    float hs[4] = {hv[r][0], hv[r][1], hv[r][2], hv[r][3]};
+    float part = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      bn[j] = row[4 * q + j];
-      cn[j] = row[N + 4 * q + j];
+      hs[j] = fmaf(fast_exp2(delta * a2s[j]), hs[j], du * bn[j]);
+      part = fmaf(cn[j], hs[j], part);
     }
-  }
-  float part = 0.f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    hs[j] = fmaf(fast_exp2(delta * a2s[j]), hs[j], du * bn[j]);
-    part = fmaf(cn[j], hs[j], part);
-  }
-#pragma unroll
-  for (int off = 1; off < LPC; off <<= 1) part += __shfl_xor(part, off);
-  if (active) {
-    __builtin_nontemporal_store(f32x4_t{hs[0], hs[1], hs[2], hs[3]}, reinterpret_cast<f32x4_t*>(hp));
-    if (q == 0) Elem<T>::store(a.y + b * a.ldy + c, part + a.D[c] * uv);
+    for (int off = 1; off < LPC; off <<= 1) part += __shfl_xor(part, off);
+    if (active && has[r]) {
+      __builtin_nontemporal_store(f32x4_t{hs[0], hs[1], hs[2], hs[3]},
+                                  reinterpret_cast<f32x4_t*>(a.h + (bs[r] * a.E + c) * N + 4 * q));
+      if (q == 0) Elem<T>::store(a.y + bs[r] * a.ldy + c, part + dskip * uv[r]);
+    }
   }
 }
 
@@ -379,7 +393,8 @@ template <typename T>
 hipError_t step_dispatch(const StepArgs<T>& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
   if (a.B > 65535 || (int64_t)a.E * (a.N / 4) >= INT32_MAX) return hipErrorInvalidValue;
-  dim3 grid(static_cast<unsigned>(ceil_div((int64_t)a.E * (a.N / 4), 256)), static_cast<unsigned>(a.B)), block(256);
+  dim3 grid(static_cast<unsigned>(ceil_div((int64_t)a.E * (a.N / 4), 256)), static_cast<unsigned>(ceil_div(a.B, 2))),
+      block(256);
   // B/C as vector loads when every row's 4-state groups are aligned to the vector size
   const bool vec = reinterpret_cast<uintptr_t>(a.bc) % 16 == 0 && a.ld_bc % 4 == 0 && a.N % 4 == 0;
   switch (a.N * 2 + (vec ? 1 : 0)) {
