@@ -7,7 +7,7 @@ Shapes: the 8K prefill projections of the 1.5B KV-consumer layer at full size (s
 every column), the 300M layer's input projection, and ragged ones: rows and columns not
 multiples of the 256 x 256 tile, K not a multiple of the 64-wide step, tile counts that are
 and are not multiples of 8 (the XCD deal), padded strides, the fp32 copy of a column range,
-a single row and an empty call.
+a single row and an empty call; two calls on the same operands are bitwise equal.
 """
 import numpy as np
 import pytest
@@ -113,3 +113,23 @@ def test_gemm_tiles_empty_and_bad_args():
         L.hymba_kernel_gemm_tiles(L.HYMBA_F32, L.HYMBA_F16, w.data_ptr(), 16, w.data_ptr(), 16, y.data_ptr(), 8,
                                   None, 0, 0, 0, 4, 8, 16, s)
     torch.cuda.synchronize()
+
+
+def test_gemm_tiles_deterministic():
+    """Two calls on the same operands give bitwise-equal results (each output's K sum is taken
+    in one fixed order; no split-K, no atomics)."""
+    announce("gemm_tiles: two calls, bitwise-equal outputs")
+    M, N, K = 3000, 11232, 1600
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    w = torch.randn(N, K, generator=gen, device="cuda").to(torch.bfloat16)
+    x = torch.randn(M, K, generator=gen, device="cuda").to(torch.bfloat16)
+    outs = []
+    for _ in range(2):
+        y = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+        y32 = torch.full((M, 32), float("nan"), dtype=torch.float32, device="cuda")
+        L.hymba_kernel_gemm_tiles(L.HYMBA_BF16, L.HYMBA_F16, w.data_ptr(), K, x.data_ptr(), K, y.data_ptr(), N,
+                                  y32.data_ptr(), 32, N - 32, N, M, N, K, torch.cuda.current_stream().cuda_stream)
+        outs.append((y, y32))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert torch.isfinite(outs[0][0]).all()
